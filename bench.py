@@ -1,0 +1,210 @@
+"""Benchmark: row-wise TopK on one MI355X, one JSON line on stdout.
+
+A step is one ds_topk call (one kernel launch: stream, cut, merge, epilogue)
+over one batch of the sampler workload (fp32 logits 64 x 129,280, k = 1024,
+sorted by value, values and int64 indices).  Inputs are resident in HBM before
+timing starts and rotate over enough copies that every call reads cold from
+HBM rather than from the 256 MB Infinity Cache.
+
+value        effective GB/s = valid input bytes / (timed wall time / steps),
+             the pages' metric (effective memory bandwidth).
+roofline     the kernel's own average duration from HIP events around every
+             launch, against MI355X's 8 TB/s HBM peak; traffic (FETCH_SIZE /
+             WRITE_SIZE per launch) comes from the committed rocprofv3 counter
+             summary when the kernel source still matches it.
+cpu_baseline the CPU oracle (full stable sort per row) on the host cores.
+
+  python bench.py [--steps K] [--warmup W] [--config N] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "effective HBM GB/s and µs/call for row-wise TopK (bf16 k=512, fp32 k=1024)"
+HBM_PEAK_GBPS = 8000.0
+MALL_BYTES = 256 << 20
+KERNEL_SRC = os.path.join(ROOT, "row_wise_topk_amd", "csrc", "topk_kernels.hip")
+
+
+def _parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--config", type=int, default=2, help="workload number (2 = sampler)")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--no-torch", action="store_true", help="skip the torch.topk context timing")
+    return p.parse_args()
+
+
+def _kernel_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def _traffic(workload_name: str):
+    """Per-launch HBM bytes from the committed counter summary, if current."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        data = json.load(open(path))
+        rec = data.get(workload_name)
+        if not rec or rec.get("kernel_sha256_16") != _kernel_hash():
+            return None
+        return rec.get("bytes_per_launch")
+    except Exception:
+        return None
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(rows shard across GPUs without any exchange; see the design notes).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import workloads
+    from tests.build_util import ensure_built
+    ensure_built()
+    import row_wise_topk_amd as rt
+
+    w = workloads.workload(args.config)
+    x_np, end_np = workloads.make_input(w)
+    alg_bytes = workloads.algorithmic_bytes(w, end_np)
+    out_bytes = workloads.output_bytes(w)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    copy_bytes = x_np.nbytes
+    n_copies = max(2, math.ceil(2 * MALL_BYTES / copy_bytes))
+    if w.dtype == workloads.BF16:
+        base = torch.from_numpy(x_np.view(np.int16)).view(torch.bfloat16).to(dev)
+    else:
+        base = torch.from_numpy(x_np).to(dev)
+    copies = [base] + [base.clone() for _ in range(n_copies - 1)]
+    views = [c[:, : w.n_cols] for c in copies]
+    end_t = None if end_np is None else torch.from_numpy(end_np).to(dev)
+    it = torch.int64 if w.index_dtype == "int64" else torch.int32
+    values = torch.empty((w.batch, w.k), dtype=base.dtype, device=dev) if w.return_values else None
+    indices = torch.empty((w.batch, w.k), dtype=it, device=dev)
+    status = torch.empty((w.batch,), dtype=torch.int32, device=dev)
+    out = (values, indices, status)
+
+    def call(i):
+        rt.topk(views[i % n_copies], w.k, end=end_t, sorted=w.sorted,
+                return_values=w.return_values, index_dtype=it, out=out)
+
+    for i in range(args.warmup):
+        call(i)
+    torch.cuda.synchronize()
+    assert int(status.abs().sum().item()) == 0, "row status set on clean input"
+
+    # Whole-job timing: K back-to-back calls, synchronised on both sides.
+    stream = torch.cuda.current_stream(dev)
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    t_start.record(stream)
+    for i in range(args.steps):
+        call(i)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_total = t_start.elapsed_time(t_end)
+    ms_per_step = ms_total / args.steps
+
+    # Kernel duration: events around every launch, on the launch stream.
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for i in range(args.steps):
+        evs[i][0].record(stream)
+        call(i)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    per = sorted(a.elapsed_time(b) for a, b in evs)
+    kernel_ms = sum(per) / len(per)
+    kernel_med_ms = per[len(per) // 2]
+
+    value = alg_bytes / (ms_per_step * 1e-3) / 1e9
+    achieved = alg_bytes / (kernel_ms * 1e-3) / 1e9
+    traffic = _traffic(w.name)
+
+    torch_us = None
+    if not args.no_torch:
+        xs = views[0]
+        for _ in range(3):
+            torch.topk(xs, w.k, dim=1, sorted=True)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 20
+        a.record(stream)
+        for i in range(reps):
+            torch.topk(views[i % n_copies], w.k, dim=1, sorted=True)
+        b.record(stream)
+        torch.cuda.synchronize()
+        torch_us = a.elapsed_time(b) * 1e3 / reps
+
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+        cores = len(os.sched_getaffinity(0))
+        used = min(cores, w.batch)
+        idx_np = np.int64 if w.index_dtype == "int64" else np.int32
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.topk(x_np, w.k, dtype=w.dtype, n_cols=w.n_cols, end=end_np, sorted=w.sorted,
+                        return_values=w.return_values, index_dtype=idx_np, n_threads=used)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds or reps >= 1000:
+                break
+        cpu = {"value": round(alg_bytes * reps / el / 1e9, 4), "unit": "GB/s", "cores": used,
+               "kind": "oracle",
+               "sample": f"the full workload ({w.batch} rows), {reps} repetitions in "
+                         f"{el:.1f} s, {used} threads, one row per thread at a time"}
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if w.dtype == workloads.FP32 else "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "n_cols": w.n_cols,
+                   "row_stride": w.row_stride, "k": w.k, "sorted": w.sorted,
+                   "return_values": w.return_values, "index_dtype": w.index_dtype,
+                   "input_copies": n_copies, "input_sha256": workloads.digest(x_np, end_np)[:16]},
+        "us_per_call": round(ms_per_step * 1e3, 3),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic, "kernel_us_mean": round(kernel_ms * 1e3, 3),
+                     "kernel_us_median": round(kernel_med_ms * 1e3, 3),
+                     "algorithmic_bytes": alg_bytes},
+        "effective_GBps_with_outputs": round((alg_bytes + out_bytes) / (ms_per_step * 1e-3) / 1e9, 2),
+        "torch_topk_us": None if torch_us is None else round(torch_us, 2),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

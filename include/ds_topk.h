@@ -1,0 +1,179 @@
+/*
+ * ds_topk.h -- row-wise TopK on AMD Instinct MI355X (gfx950), C ABI.
+ *
+ * The operation and its options follow the public descriptions of DeepSelect:
+ *   [NC] narracomm.com, "DeepSeek releases DeepSelect, a TopK kernel for sparse
+ *        attention and sampling": the method paragraph (a monotone threshold T,
+ *        rows read once in contiguous blocks of B visited in random order, a
+ *        candidate buffer cut back to k by radix select when it reaches k+B2);
+ *        the coverage paragraph (bf16 and fp32 inputs, k <= 4096, int32 or
+ *        int64 indices); the install/API paragraph (rows contiguous in the last
+ *        dimension, a stride requirement with padding for unaligned rows,
+ *        sorted_index, return_value); the NaN paragraph (always checked).
+ *   [AF] aifluxnews.com, "DeepSeek 在 GitHub 发布 DeepSelect v1.0.0", section
+ *        "PyTorch 接口与 CUDA 环境要求": per-row `end` for variable-length rows,
+ *        stride constraints on inputs and outputs.
+ *   [XH] xhh.club, "DeepSeek开源DeepSelect：比torch.topk快二十倍！", Q&A: the
+ *        call topk(x, topk, sorted_index, indices_type, return_value); results
+ *        are stable.
+ *   [IT] deepseek-v4-pro.uk, "Inside DeepSeek V4.1's New Open Inference
+ *        Toolkit", section "DeepSelect: a fast, deliberately narrow TopK": a
+ *        NaN trap aborts the process, which a service has to isolate.
+ *
+ * Result of a row i (the same definition the method reaches exactly):
+ *   L = end ? end[i] : n_cols; the row is x[i*row_stride + j], 0 <= j < L.
+ *   Order: a precedes b iff x[a] > x[b], or x[a] == x[b] and a < b (numeric
+ *   comparison: -0.0 == +0.0; -inf and +inf are ordinary values).
+ *   The result is the first m = min(k, L) elements in that order.
+ *
+ * Conventions for every entry point:
+ *   - All array pointers passed to ds_topk / ds_topk_ex are DEVICE pointers
+ *     owned by the caller.  The library allocates no memory and keeps no
+ *     state between calls.
+ *   - Calls are asynchronous on `stream`; the library never synchronises and
+ *     never prints.  Argument errors are returned before anything is launched.
+ *   - Data errors never abort (unlike the trap of [NC]/[IT]): they set bits in
+ *     row_status[i] and that row's outputs become index -1, value qNaN.
+ */
+#ifndef DS_TOPK_H_
+#define DS_TOPK_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Input dtypes: fp32 (sampler path) and bf16 (Lightning Indexer path) [NC coverage]. */
+typedef enum { DS_FP32 = 0, DS_BF16 = 1 } ds_dtype_t;
+
+/* Index dtypes of the output [NC coverage; XH indices_type]. */
+typedef enum { DS_INT32 = 0, DS_INT64 = 1 } ds_index_dtype_t;
+
+/* Output order.  1 (also "true") = by value, larger first, then lower index;
+ * 2 = by index ascending (the pages' sorted_index); 0 = unsorted: the m
+ * results in an unspecified order [NC install/API]. */
+typedef enum { DS_UNSORTED = 0, DS_SORTED_VALUE = 1, DS_SORTED_INDEX = 2 } ds_sorted_t;
+
+typedef enum {
+  DS_OK = 0,
+  DS_ERR_NULL = 1,          /* a required pointer is NULL                          */
+  DS_ERR_DTYPE = 2,         /* dtype is not DS_FP32 / DS_BF16                      */
+  DS_ERR_INDEX_DTYPE = 3,   /* index_dtype is not DS_INT32 / DS_INT64              */
+  DS_ERR_K_RANGE = 4,       /* k < 1 or k > DS_TOPK_MAX_K                          */
+  DS_ERR_SHAPE = 5,         /* batch < 0, n_cols < 0, n_cols > INT32_MAX, row_stride < n_cols */
+  DS_ERR_ALIGN = 6,         /* x not 16-B aligned, row_stride*elem not a multiple of 16 B,
+                               or an output / end / row_status pointer misaligned   */
+  DS_ERR_SORTED_MODE = 7,   /* sorted not in {0, 1, 2}                             */
+  DS_ERR_WORKSPACE = 8,     /* workspace NULL, too small or not 16-B aligned       */
+  DS_ERR_HIP = 9,           /* the HIP runtime reported an error at launch         */
+  DS_ERR_PLAN = 10          /* a ds_topk_plan_t field is out of range              */
+} ds_status_t;
+
+#define DS_TOPK_MAX_K 4096            /* [NC coverage]: topk must be 4096 or less   */
+#define DS_ROW_NAN 1                  /* row_status bit: a NaN in x[i, 0:L)          */
+#define DS_ROW_BAD_END 2              /* row_status bit: end[i] < 0 or end[i] > n_cols */
+
+/*
+ * ds_topk -- top-k of every row of a 2-D array [IT "DeepSelect" section; NC
+ * method, coverage, install/API and NaN paragraphs; AF "PyTorch 接口" section].
+ *
+ *   x            device, row-major [batch, row_stride] of dtype; the last
+ *                dimension is contiguous.  Base 16-B aligned and
+ *                row_stride * sizeof(dtype) a multiple of 16 B (see
+ *                ds_topk_stride_requirement); callers with other layouts pad.
+ *                The allocation must span batch * row_stride elements: reads
+ *                use 16-B vectors, and a vector that starts inside [0, L) may
+ *                cover elements up to the next 16-B boundary (never past
+ *                row_stride).  Elements at or past L are never used or checked.
+ *   dtype        DS_FP32 or DS_BF16.
+ *   batch        rows (>= 0; 0 launches nothing).
+ *   n_cols       row length when `end` is NULL, and the upper bound of end[i].
+ *   row_stride   elements between row starts (>= n_cols).
+ *   end          device int32 [batch] or NULL: row i uses columns [0, end[i]).
+ *   k            1..DS_TOPK_MAX_K; k > L is allowed (the tail is padded).
+ *   sorted       ds_sorted_t.
+ *   return_values  0: `values` is not written and may be NULL ([NC]: skipping
+ *                the values output is faster).
+ *   index_dtype  DS_INT32 or DS_INT64.
+ *   values       device [batch, k] of dtype (dense, natural alignment): bit
+ *                copies of the selected inputs; slots m..k-1 hold -inf.
+ *   indices      device [batch, k] of index_dtype (dense, natural alignment):
+ *                0-based columns; slots m..k-1 hold -1.
+ *   row_status   device int32 [batch]: 0, or DS_ROW_NAN / DS_ROW_BAD_END, in
+ *                which case the row's indices are -1 and values qNaN.
+ *   workspace    device scratch of at least ds_topk_workspace_size(...)
+ *                bytes, 16-B aligned, ZEROED before its first use; every call
+ *                leaves it zeroed again.  May be NULL when that size is 0.
+ *                Calls that may overlap in time need distinct workspaces.
+ *   stream       HIP stream the single kernel launch is queued on.
+ * Returns DS_OK or the first argument error found (nothing launched), or
+ * DS_ERR_HIP if the launch failed.
+ */
+ds_status_t ds_topk(const void* x, ds_dtype_t dtype, int64_t batch, int64_t n_cols,
+                    int64_t row_stride, const int32_t* end, int32_t k, int32_t sorted,
+                    int32_t return_values, ds_index_dtype_t index_dtype, void* values,
+                    void* indices, int32_t* row_status, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Launch plan.  Any plan gives bit-identical indices and values (for
+ * DS_UNSORTED: the same set); the plan only changes speed.  ds_topk uses the
+ * automatic plan.  [NC method]: blocks are visited in a random order and B,
+ * B2 are tuning parameters.
+ *   segments     workgroups that share one row (0 = automatic, else 1..256).
+ *   perm_seed    seed of the per-row block permutation (any value).
+ *   in_order     1 = visit blocks in address order instead.
+ *   flush_at     candidate count that triggers a cut back to k (0 = automatic;
+ *                else k+1 .. the buffer's fixed trigger for this k class).
+ */
+typedef struct {
+  int32_t segments;
+  uint32_t perm_seed;
+  int32_t in_order;
+  int32_t flush_at;
+} ds_topk_plan_t;
+
+/* ds_topk with an explicit plan (plan may be NULL = automatic).  Same
+ * arguments, ownership and errors as ds_topk, plus DS_ERR_PLAN. */
+ds_status_t ds_topk_ex(const void* x, ds_dtype_t dtype, int64_t batch, int64_t n_cols,
+                       int64_t row_stride, const int32_t* end, int32_t k, int32_t sorted,
+                       int32_t return_values, ds_index_dtype_t index_dtype, void* values,
+                       void* indices, int32_t* row_status, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream, const ds_topk_plan_t* plan);
+
+/* The argument checks of ds_topk_ex alone: no HIP call, no launch, pointers
+ * are only tested for NULL and alignment.  Returns what ds_topk_ex would
+ * return before launching. */
+ds_status_t ds_topk_validate(const void* x, ds_dtype_t dtype, int64_t batch, int64_t n_cols,
+                             int64_t row_stride, const int32_t* end, int32_t k, int32_t sorted,
+                             int32_t return_values, ds_index_dtype_t index_dtype,
+                             const void* values, const void* indices, const int32_t* row_status,
+                             const void* workspace, size_t workspace_bytes,
+                             const ds_topk_plan_t* plan);
+
+/* Workspace bytes ds_topk needs for this problem (0 when one workgroup per
+ * row suffices).  Host only; needs no GPU.  Invalid arguments give 0. */
+size_t ds_topk_workspace_size(ds_dtype_t dtype, int64_t batch, int64_t n_cols, int32_t k);
+
+/* Workspace bytes ds_topk_ex needs with `plan` (NULL = automatic).  Host
+ * only: the automatic plan depends on the problem shape alone. */
+size_t ds_topk_workspace_size_ex(ds_dtype_t dtype, int64_t batch, int64_t n_cols, int32_t k,
+                                 const ds_topk_plan_t* plan);
+
+/* Row strides must be a multiple of this many elements (16 B / sizeof(dtype));
+ * the counterpart of the pages' get_stride_requirement [NC install/API].
+ * Returns 0 for an unknown dtype. */
+int64_t ds_topk_stride_requirement(ds_dtype_t dtype);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* ds_topk_status_string(ds_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DS_TOPK_H_ */

@@ -1,0 +1,216 @@
+// Host side of the C ABI in include/ds_topk.h: argument checks, launch plan,
+// workspace layout, one kernel launch on the caller's stream.
+//
+// The interface follows the pages' description of DeepSelect's topk call
+// (xhh.club, "DeepSeek开源DeepSelect：比torch.topk快二十倍！", Q&A; narracomm.com,
+// "DeepSeek releases DeepSelect, a TopK kernel for sparse attention and
+// sampling", coverage and install/API paragraphs; aifluxnews.com,
+// "DeepSeek 在 GitHub 发布 DeepSelect v1.0.0", section "PyTorch 接口与 CUDA
+// 环境要求").  The kernels are chosen per problem shape, as those pages say the
+// fastest TopK depends on dtype, batch, vocabulary and k.
+
+#include <stdint.h>
+
+#include <climits>
+
+#include "ds_topk.h"
+#include "topk_internal.h"
+
+namespace {
+
+using namespace dstk;
+
+struct Plan {
+  int cls;
+  int segments;
+  uint32_t seed;
+  int in_order;
+  int trigger;
+};
+
+int elem_size(ds_dtype_t d) { return d == DS_FP32 ? 4 : 2; }
+
+bool misaligned(const void* p, uintptr_t a) {
+  return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0;
+}
+
+int auto_segments(int64_t batch, int64_t n_cols, int cls) {
+  const int64_t nb = (n_cols + kBlockElems - 1) / kBlockElems;
+  if (batch <= 0 || nb <= 1) return 1;
+  const int64_t target = static_cast<int64_t>(kNumCU) * class_wgs_per_cu(cls);
+  int64_t s = (target + batch - 1) / batch;
+  const int64_t most = (nb + 1) / 2;   // at least two blocks per workgroup
+  if (s > most) s = most;
+  if (s > kMaxSegments) s = kMaxSegments;
+  if (s < 1) s = 1;
+  return static_cast<int>(s);
+}
+
+// Fills `out`; returns DS_ERR_PLAN for an out-of-range override.
+ds_status_t resolve_plan(int64_t batch, int64_t n_cols, int32_t k, const ds_topk_plan_t* p,
+                         Plan* out) {
+  Plan pl{};
+  pl.cls = class_of_k(k);
+  pl.segments = auto_segments(batch, n_cols, pl.cls);
+  pl.seed = 0x5EEDu;
+  pl.in_order = 0;
+  pl.trigger = class_trigger(pl.cls);
+  if (p) {
+    if (p->segments < 0 || p->segments > kMaxSegments) return DS_ERR_PLAN;
+    if (p->in_order != 0 && p->in_order != 1) return DS_ERR_PLAN;
+    if (p->flush_at != 0 && (p->flush_at <= k || p->flush_at > class_trigger(pl.cls)))
+      return DS_ERR_PLAN;
+    if (p->segments > 0) pl.segments = p->segments;
+    pl.seed = p->perm_seed;
+    pl.in_order = p->in_order;
+    if (p->flush_at) pl.trigger = p->flush_at;
+  }
+  *out = pl;
+  return DS_OK;
+}
+
+size_t workspace_bytes_for(int64_t batch, int segments, int32_t k) {
+  if (segments <= 1 || batch <= 0) return 0;
+  return ws_layout(batch, segments, k).total;
+}
+
+ds_status_t check_scalars(ds_dtype_t dtype, int64_t batch, int64_t n_cols, int64_t row_stride,
+                          int32_t k, int32_t sorted, ds_index_dtype_t index_dtype) {
+  if (dtype != DS_FP32 && dtype != DS_BF16) return DS_ERR_DTYPE;
+  if (index_dtype != DS_INT32 && index_dtype != DS_INT64) return DS_ERR_INDEX_DTYPE;
+  if (sorted < 0 || sorted > 2) return DS_ERR_SORTED_MODE;
+  if (k < 1 || k > DS_TOPK_MAX_K) return DS_ERR_K_RANGE;
+  if (batch < 0 || batch > INT32_MAX || n_cols < 0 || n_cols > INT32_MAX || row_stride < n_cols)
+    return DS_ERR_SHAPE;
+  if (batch > 0 && row_stride > (INT64_MAX / 8) / batch) return DS_ERR_SHAPE;
+  return DS_OK;
+}
+
+ds_status_t validate(const void* x, ds_dtype_t dtype, int64_t batch, int64_t n_cols,
+                     int64_t row_stride, const int32_t* end, int32_t k, int32_t sorted,
+                     int32_t return_values, ds_index_dtype_t index_dtype, const void* values,
+                     const void* indices, const int32_t* row_status, const void* workspace,
+                     size_t workspace_bytes, const ds_topk_plan_t* plan, Plan* pl) {
+  ds_status_t st = check_scalars(dtype, batch, n_cols, row_stride, k, sorted, index_dtype);
+  if (st != DS_OK) return st;
+  st = resolve_plan(batch, n_cols, k, plan, pl);
+  if (st != DS_OK) return st;
+  if (batch == 0) return DS_OK;
+  if (!indices || !row_status || (return_values && !values) || (n_cols > 0 && !x))
+    return DS_ERR_NULL;
+  const int es = elem_size(dtype);
+  if ((x && misaligned(x, 16)) || (row_stride * es) % 16 != 0) return DS_ERR_ALIGN;
+  if (misaligned(indices, index_dtype == DS_INT64 ? 8 : 4)) return DS_ERR_ALIGN;
+  if (return_values && misaligned(values, static_cast<uintptr_t>(es))) return DS_ERR_ALIGN;
+  if (misaligned(row_status, 4) || (end && misaligned(end, 4))) return DS_ERR_ALIGN;
+  if (batch * static_cast<int64_t>(pl->segments) > INT32_MAX) return DS_ERR_SHAPE;
+  const size_t need = workspace_bytes_for(batch, pl->segments, k);
+  if (need > 0 && (!workspace || workspace_bytes < need || misaligned(workspace, 16)))
+    return DS_ERR_WORKSPACE;
+  return DS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ds_status_t ds_topk_validate(const void* x, ds_dtype_t dtype, int64_t batch, int64_t n_cols,
+                             int64_t row_stride, const int32_t* end, int32_t k, int32_t sorted,
+                             int32_t return_values, ds_index_dtype_t index_dtype,
+                             const void* values, const void* indices, const int32_t* row_status,
+                             const void* workspace, size_t workspace_bytes,
+                             const ds_topk_plan_t* plan) {
+  Plan pl;
+  return validate(x, dtype, batch, n_cols, row_stride, end, k, sorted, return_values,
+                  index_dtype, values, indices, row_status, workspace, workspace_bytes, plan,
+                  &pl);
+}
+
+ds_status_t ds_topk_ex(const void* x, ds_dtype_t dtype, int64_t batch, int64_t n_cols,
+                       int64_t row_stride, const int32_t* end, int32_t k, int32_t sorted,
+                       int32_t return_values, ds_index_dtype_t index_dtype, void* values,
+                       void* indices, int32_t* row_status, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream, const ds_topk_plan_t* plan) {
+  Plan pl;
+  ds_status_t st = validate(x, dtype, batch, n_cols, row_stride, end, k, sorted, return_values,
+                            index_dtype, values, indices, row_status, workspace,
+                            workspace_bytes, plan, &pl);
+  if (st != DS_OK || batch == 0) return st;
+
+  KArgs a{};
+  a.x = x;
+  a.row_stride = row_stride;
+  a.n_cols = static_cast<int32_t>(n_cols);
+  a.batch = static_cast<int32_t>(batch);
+  a.end = end;
+  a.k = k;
+  a.sorted = sorted;
+  a.return_values = return_values ? 1 : 0;
+  a.idx64 = index_dtype == DS_INT64 ? 1 : 0;
+  a.values = return_values ? values : nullptr;
+  a.indices = indices;
+  a.row_status = row_status;
+  a.segments = pl.segments;
+  a.perm_seed = pl.seed;
+  a.in_order = pl.in_order;
+  a.trigger = pl.trigger;
+  if (pl.segments > 1) {
+    const WsLayout l = ws_layout(batch, pl.segments, k);
+    char* w = static_cast<char*>(workspace);
+    a.ws_thr = reinterpret_cast<unsigned long long*>(w + l.thr);
+    a.ws_done = reinterpret_cast<uint32_t*>(w + l.done);
+    a.ws_flags = reinterpret_cast<uint32_t*>(w + l.flags);
+    a.ws_cnt = reinterpret_cast<uint32_t*>(w + l.cnt);
+    a.ws_val = reinterpret_cast<uint32_t*>(w + l.val);
+    a.ws_idx = reinterpret_cast<uint32_t*>(w + l.idx);
+  }
+  const int err = launch_topk(a, dtype == DS_BF16 ? 1 : 0, pl.cls, stream);
+  return err == 0 ? DS_OK : DS_ERR_HIP;
+}
+
+ds_status_t ds_topk(const void* x, ds_dtype_t dtype, int64_t batch, int64_t n_cols,
+                    int64_t row_stride, const int32_t* end, int32_t k, int32_t sorted,
+                    int32_t return_values, ds_index_dtype_t index_dtype, void* values,
+                    void* indices, int32_t* row_status, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream) {
+  return ds_topk_ex(x, dtype, batch, n_cols, row_stride, end, k, sorted, return_values,
+                    index_dtype, values, indices, row_status, workspace, workspace_bytes, stream,
+                    nullptr);
+}
+
+size_t ds_topk_workspace_size_ex(ds_dtype_t dtype, int64_t batch, int64_t n_cols, int32_t k,
+                                 const ds_topk_plan_t* plan) {
+  if (check_scalars(dtype, batch, n_cols, n_cols, k, 1, DS_INT32) != DS_OK) return 0;
+  Plan pl;
+  if (resolve_plan(batch, n_cols, k, plan, &pl) != DS_OK) return 0;
+  return workspace_bytes_for(batch, pl.segments, k);
+}
+
+size_t ds_topk_workspace_size(ds_dtype_t dtype, int64_t batch, int64_t n_cols, int32_t k) {
+  return ds_topk_workspace_size_ex(dtype, batch, n_cols, k, nullptr);
+}
+
+int64_t ds_topk_stride_requirement(ds_dtype_t dtype) {
+  if (dtype == DS_FP32) return 4;
+  if (dtype == DS_BF16) return 8;
+  return 0;
+}
+
+const char* ds_topk_status_string(ds_status_t status) {
+  switch (status) {
+    case DS_OK: return "ok";
+    case DS_ERR_NULL: return "a required pointer is NULL";
+    case DS_ERR_DTYPE: return "unsupported input dtype (fp32 or bf16)";
+    case DS_ERR_INDEX_DTYPE: return "unsupported index dtype (int32 or int64)";
+    case DS_ERR_K_RANGE: return "k must be in 1..4096";
+    case DS_ERR_SHAPE: return "invalid shape (batch, n_cols, row_stride)";
+    case DS_ERR_ALIGN: return "misaligned pointer or row stride (16-byte rows required)";
+    case DS_ERR_SORTED_MODE: return "sorted must be 0 (unsorted), 1 (by value) or 2 (by index)";
+    case DS_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
+    case DS_ERR_HIP: return "HIP launch error";
+    case DS_ERR_PLAN: return "plan field out of range";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

@@ -1,0 +1,69 @@
+// Internal interface between the host API (topk_api.hip) and the kernels
+// (topk_kernels.hip).  Not installed; not part of the C ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+namespace dstk {
+
+// Fixed geometry shared by host planning and the kernels.
+constexpr int kBlockElems = 4096;   // B: contiguous elements per block (both dtypes)
+constexpr int kNumCU = 256;         // MI355X compute units (planning constant)
+constexpr int kMaxSegments = 256;
+
+// k classes: each has its own buffer capacity, threads per workgroup and trigger.
+constexpr int kNumClasses = 4;
+constexpr int class_kmax(int c) { return c == 0 ? 256 : c == 1 ? 1024 : c == 2 ? 2048 : 4096; }
+constexpr int class_threads(int c) { return c == 3 ? 512 : 256; }
+// B2 (extra candidates collected before a cut) per class.
+constexpr int class_b2(int c) { return c == 0 ? 1024 : class_kmax(c); }
+// Buffer capacity: k + B2 candidates plus one whole block admitted at once.
+constexpr int class_cap(int c) { return class_kmax(c) + class_b2(c) + kBlockElems; }
+constexpr int class_trigger(int c) { return class_cap(c) - kBlockElems; }
+// LDS bytes per workgroup (value + index arrays, histogram, scalars).
+constexpr int class_lds_bytes(int c) { return class_cap(c) * 8 + 2048 * 4 + 512; }
+constexpr int class_wgs_per_cu(int c) {
+  return (160 * 1024) / class_lds_bytes(c) > 0 ? (160 * 1024) / class_lds_bytes(c) : 1;
+}
+inline int class_of_k(int k) { return k <= 256 ? 0 : k <= 1024 ? 1 : k <= 2048 ? 2 : 3; }
+
+struct KArgs {
+  const void* x;
+  int64_t row_stride;     // elements
+  int32_t n_cols;
+  int32_t batch;
+  const int32_t* end;     // nullable
+  int32_t k;
+  int32_t sorted;
+  int32_t return_values;
+  int32_t idx64;
+  void* values;
+  void* indices;
+  int32_t* row_status;
+  int32_t segments;       // workgroups per row
+  uint32_t perm_seed;
+  int32_t in_order;
+  int32_t trigger;        // candidate count that triggers a cut
+  // workspace (segments > 1), all device pointers into one caller buffer
+  unsigned long long* ws_thr;   // [batch]  shared threshold per row
+  uint32_t* ws_done;            // [batch]  arrivals per row
+  uint32_t* ws_flags;           // [batch]  OR of row status bits
+  uint32_t* ws_cnt;             // [batch * segments]
+  uint32_t* ws_val;             // [batch * segments * k]
+  uint32_t* ws_idx;             // [batch * segments * k]
+};
+
+// Workspace layout for `segments` workgroups per row (bytes, 16-B aligned parts).
+struct WsLayout {
+  size_t thr, done, flags, cnt, val, idx, total;
+};
+WsLayout ws_layout(int64_t batch, int segments, int k);
+
+// Queue the kernel for class `cls` and dtype (0 fp32, 1 bf16).  Returns the
+// hipError_t of the launch.
+int launch_topk(const KArgs& a, int dtype, int cls, hipStream_t stream);
+
+}  // namespace dstk
