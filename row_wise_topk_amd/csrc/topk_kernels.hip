@@ -700,11 +700,21 @@ __global__ __launch_bounds__(class_threads(CLS)) void topk_kernel(KArgs a) {
       if (gfin > sm.thr) sm.thr = gfin;
       sm.flags |= __hip_atomic_load(&a.ws_flags[row], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+    // The workspace must be all zero again when the call ends, whatever layout
+    // the next call uses: clear this workgroup's own survivors now, and every
+    // other slot and count as it is read below.
+    for (uint32_t j = t; j < mine; j += NT) {
+      wv[j] = 0u;
+      wi[j] = 0u;
+    }
     // Per-segment counts -> exclusive offsets (own segment counted as 0).
     hist_clear(sm);
     __syncthreads();
-    for (int s2 = t; s2 < S; s2 += NT)
-      sm.hist[s2] = s2 == seg ? 0u : a.ws_cnt[static_cast<int64_t>(row) * S + s2];
+    for (int s2 = t; s2 < S; s2 += NT) {
+      const int64_t sl = static_cast<int64_t>(row) * S + s2;
+      sm.hist[s2] = s2 == seg ? 0u : a.ws_cnt[sl];
+      a.ws_cnt[sl] = 0u;
+    }
     __syncthreads();
     hist_exclusive_scan(sm);   // hist[s] = first flat position of segment s
     for (int s2 = t; s2 < S; s2 += NT) sm.segoff[s2] = sm.hist[s2];
@@ -731,6 +741,8 @@ __global__ __launch_bounds__(class_threads(CLS)) void topk_kernel(KArgs a) {
           const uint32_t j = fpos - sm.segoff[lo];
           mv[q] = a.ws_val[sl * k + j];
           mi[q] = a.ws_idx[sl * k + j];
+          a.ws_val[sl * k + j] = 0u;
+          a.ws_idx[sl * k + j] = 0u;
         }
       }
       uint64_t mm[PER];

@@ -206,3 +206,27 @@ def test_repeat_determinism():
         again0 = gpu_topk(x, w.dtype, w.n_cols, w.k, 0, False, xt=xt)
         assert np.array_equal(np.sort(first0[1], axis=1), np.sort(again0[1], axis=1))
     torch.cuda.synchronize()
+
+
+def test_workspace_all_zero_after_every_call():
+    """Calls with different (batch, segments, k) share one workspace: each must
+    leave it entirely zero, since the next layout may put counters anywhere."""
+    import torch
+    import row_wise_topk_amd as rt
+    from tests.gpu_util import to_device
+    rng = np.random.Generator(np.random.PCG64(12))
+    shapes = [(8, 129280, 1024, {}), (5, 50001, 1024, {}), (8, 131072, 512, {}),
+              (3, 9000, 7, {}), (2, 262144, 1, {}), (6, 129280, 1024, {"segments": 64}),
+              (1, 1 << 20, 4096, {}), (64, 20000, 300, {"segments": 3})]
+    for i, (batch, n, k, plan) in enumerate(shapes):
+        dtype = BF16 if i % 2 else FP32
+        step = 8 if dtype == BF16 else 4
+        stride = (n + step - 1) // step * step
+        f = np.full((batch, stride), np.nan, dtype=np.float32)
+        f[:, :n] = rng.standard_normal((batch, n)).astype(np.float32)
+        x = workloads.to_bf16_bits(f) if dtype == BF16 else f
+        say(f"workspace reuse batch={batch} n={n} k={k} plan={plan}")
+        check_case(x, dtype, n, k, 1, plan=plan or None, name="workspace reuse")
+        torch.cuda.synchronize()
+        for buf in rt._workspaces.values():
+            assert int(torch.count_nonzero(buf).item()) == 0, "workspace left dirty"
