@@ -160,7 +160,7 @@ ds_status_t ds_topk_ex(const void* x, ds_dtype_t dtype, int64_t batch, int64_t n
     a.ws_thr = reinterpret_cast<unsigned long long*>(w + l.thr);
     a.ws_done = reinterpret_cast<uint32_t*>(w + l.done);
     a.ws_flags = reinterpret_cast<uint32_t*>(w + l.flags);
-    a.ws_cnt = reinterpret_cast<uint32_t*>(w + l.cnt);
+    a.ws_fill = reinterpret_cast<uint32_t*>(w + l.fill);
     a.ws_val = reinterpret_cast<uint32_t*>(w + l.val);
     a.ws_idx = reinterpret_cast<uint32_t*>(w + l.idx);
   }

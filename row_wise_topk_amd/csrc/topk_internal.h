@@ -19,12 +19,12 @@ constexpr int kNumClasses = 4;
 constexpr int class_kmax(int c) { return c == 0 ? 256 : c == 1 ? 1024 : c == 2 ? 2048 : 4096; }
 constexpr int class_threads(int c) { return c == 3 ? 512 : 256; }
 // B2 (extra candidates collected before a cut) per class.
-constexpr int class_b2(int c) { return c == 0 ? 1024 : class_kmax(c); }
+constexpr int class_b2(int c) { return c == 0 ? 1024 : c == 1 ? 3072 : class_kmax(c); }
 // Buffer capacity: k + B2 candidates plus one whole block admitted at once.
 constexpr int class_cap(int c) { return class_kmax(c) + class_b2(c) + kBlockElems; }
 constexpr int class_trigger(int c) { return class_cap(c) - kBlockElems; }
 // LDS bytes per workgroup (value + index arrays, histogram, scalars).
-constexpr int class_lds_bytes(int c) { return class_cap(c) * 8 + 2048 * 4 + 512; }
+constexpr int class_lds_bytes(int c) { return class_cap(c) * 8 + 2048 * 4 + 1536; }
 constexpr int class_wgs_per_cu(int c) {
   return (160 * 1024) / class_lds_bytes(c) > 0 ? (160 * 1024) / class_lds_bytes(c) : 1;
 }
@@ -51,14 +51,14 @@ struct KArgs {
   unsigned long long* ws_thr;   // [batch]  shared threshold per row
   uint32_t* ws_done;            // [batch]  arrivals per row
   uint32_t* ws_flags;           // [batch]  OR of row status bits
-  uint32_t* ws_cnt;             // [batch * segments]
-  uint32_t* ws_val;             // [batch * segments * k]
+  uint32_t* ws_fill;            // [batch]  survivors written so far per row
+  uint32_t* ws_val;             // [batch * segments * k]  survivors, contiguous per row
   uint32_t* ws_idx;             // [batch * segments * k]
 };
 
 // Workspace layout for `segments` workgroups per row (bytes, 16-B aligned parts).
 struct WsLayout {
-  size_t thr, done, flags, cnt, val, idx, total;
+  size_t thr, done, flags, fill, val, idx, total;
 };
 WsLayout ws_layout(int64_t batch, int segments, int k);
 

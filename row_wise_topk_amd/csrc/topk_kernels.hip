@@ -10,21 +10,23 @@
 //
 //  * one workgroup (256 or 512 lanes) streams a row, or a share of a row's
 //    blocks when several workgroups cooperate on one row;
-//  * a block is B = 4096 elements: every lane issues 16-byte loads, and the
-//    next block's loads are in flight while the current one is filtered;
+//  * a block is B = 4096 elements; every lane issues 16-byte loads, and the
+//    loads of the next 2-3 blocks are always in flight (a register ring whose
+//    loads are issued unconditionally, so the compiler can wait for exactly
+//    the block being filtered);
 //  * the filter runs on the raw fp32 values (bf16 is widened by a shift), with
 //    a wave-wide early-out on each lane's running maximum; survivors are
 //    compacted into LDS with ballot / mbcnt and one LDS atomic per wave;
 //  * the cut (radix select) is an 11-bit LDS histogram over the live key range
 //    [T, max], refined only when the boundary bin is too full; exact ties on a
-//    key are cut by index with the same histogram on the index;
+//    key are cut by column with the same histogram on the column;
 //  * several workgroups on one row share T through a 64-bit atomicMax in
 //    device memory; the last to finish merges the others' survivors;
-//  * the epilogue orders the k results by value or by index with a histogram
+//  * the epilogue orders the k results by value or by column with a histogram
 //    grouping plus an in-bin rank, and writes indices / values / status.
 //
 // Order and tie-break (xhh.club, "DeepSeek开源DeepSelect：比torch.topk快二十倍！",
-// Q&A on stable results): larger value first, then lower index.  A value v at
+// Q&A on stable results): larger value first, then lower column.  A value v at
 // column i has the 64-bit composite  (key(v) << 32) | ~i,  where key() maps
 // fp32 sign-magnitude onto unsigned offset binary so that -0.0 and +0.0 share
 // one key.  The threshold T is a composite too: an element is admitted iff its
@@ -47,6 +49,9 @@ constexpr int kBins = 1 << kRadixBits;
 constexpr uint32_t kBias = 0x80000000u;
 constexpr uint32_t kQNaN32 = 0x7FC00000u;
 constexpr uint32_t kNegInf32 = 0xFF800000u;
+
+// 16 bytes of a row: one vector load per lane.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------- keys
 __device__ __forceinline__ uint32_t key_of_bits(uint32_t b) {
@@ -89,19 +94,82 @@ __device__ __forceinline__ uint32_t mbcnt64(uint64_t m) {
                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
 }
 
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = max(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), o)));
-  return v;
+// A value every lane holds the same copy of (read from LDS after a barrier,
+// say), moved to a scalar register so that branches on it are scalar.
+__device__ __forceinline__ uint32_t uniform(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(v)));
+}
+__device__ __forceinline__ uint64_t uniform64(uint64_t v) {
+  return (static_cast<uint64_t>(uniform(static_cast<uint32_t>(v >> 32))) << 32) |
+         uniform(static_cast<uint32_t>(v));
 }
 
-__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = min(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), o)));
-  return v;
+// DPP move: lanes whose source is outside the row, or whose row is masked off,
+// receive `IDENT`.
+template <int CTRL, int ROW_MASK, uint32_t IDENT>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+      static_cast<int>(IDENT), static_cast<int>(v), CTRL, ROW_MASK, 0xF, false));
+}
+
+// Inclusive scan over the 64 lanes of a wave (all lanes active): row_shr
+// 1/2/4/8 inside each 16-lane row, then row_bcast 15 and 31 across rows.
+template <typename Op, uint32_t IDENT>
+__device__ __forceinline__ uint32_t wave_scan(uint32_t x, Op op) {
+  x = op(x, dpp<0x111, 0xF, IDENT>(x));
+  x = op(x, dpp<0x112, 0xF, IDENT>(x));
+  x = op(x, dpp<0x114, 0xF, IDENT>(x));
+  x = op(x, dpp<0x118, 0xF, IDENT>(x));
+  x = op(x, dpp<0x142, 0xA, IDENT>(x));
+  x = op(x, dpp<0x143, 0xC, IDENT>(x));
+  return x;
+}
+
+struct OpAdd { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a + b; } };
+struct OpMax { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a > b ? a : b; } };
+struct OpMin { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a < b ? a : b; } };
+
+__device__ __forceinline__ uint32_t wave_prefix_sum(uint32_t x) {
+  return wave_scan<OpAdd, 0u>(x, OpAdd{});
+}
+__device__ __forceinline__ uint32_t wave_max(uint32_t x) {
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_readlane(static_cast<int>(wave_scan<OpMax, 0u>(x, OpMax{})), 63));
+}
+__device__ __forceinline__ uint32_t wave_min(uint32_t x) {
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(
+      static_cast<int>(wave_scan<OpMin, 0xFFFFFFFFu>(x, OpMin{})), 63));
+}
+
+template <int CTRL, int ROW_MASK, uint64_t IDENT>
+__device__ __forceinline__ uint64_t dpp64(uint64_t v) {
+  const uint32_t lo = dpp<CTRL, ROW_MASK, static_cast<uint32_t>(IDENT)>(static_cast<uint32_t>(v));
+  const uint32_t hi = dpp<CTRL, ROW_MASK, static_cast<uint32_t>(IDENT >> 32)>(static_cast<uint32_t>(v >> 32));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+template <bool MAX>
+__device__ __forceinline__ uint64_t wave_extreme64(uint64_t x) {
+  constexpr uint64_t I = MAX ? 0ull : ~0ull;
+  auto op = [](uint64_t a, uint64_t b) { return MAX ? (a > b ? a : b) : (a < b ? a : b); };
+  x = op(x, dpp64<0x111, 0xF, I>(x));
+  x = op(x, dpp64<0x112, 0xF, I>(x));
+  x = op(x, dpp64<0x114, 0xF, I>(x));
+  x = op(x, dpp64<0x118, 0xF, I>(x));
+  x = op(x, dpp64<0x142, 0xA, I>(x));
+  x = op(x, dpp64<0x143, 0xC, I>(x));
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(x)), 63));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(x >> 32)), 63));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
 __device__ __forceinline__ uint32_t bit_length(uint32_t v) { return v ? 32u - __clz(v) : 0u; }
+__device__ __forceinline__ uint32_t bit_length64(uint64_t v) { return v ? 64u - __clzll(v) : 0u; }
+
+__device__ __forceinline__ uint32_t shift_for_span(uint32_t span) {
+  const uint32_t b = bit_length(span);
+  return b > kRadixBits ? b - kRadixBits : 0u;
+}
 
 // Relaxed agent-scope accesses to the shared per-row threshold.
 __device__ __forceinline__ uint64_t load_thr(const unsigned long long* p) {
@@ -110,6 +178,21 @@ __device__ __forceinline__ uint64_t load_thr(const unsigned long long* p) {
 __device__ __forceinline__ void publish_thr(unsigned long long* p, uint64_t v) {
   __hip_atomic_fetch_max(p, static_cast<unsigned long long>(v), __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_agent(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until every memory access this wave has issued is complete.  Used
+// before the arrival counter of a row moves: the survivors were written with
+// agent-scope atomic stores, so once complete they are visible to the
+// workgroup that reads them after seeing the counter.
+__device__ __forceinline__ void wait_all_memory() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
 // ---------------------------------------------------------------- block order
@@ -149,25 +232,27 @@ struct BlockOrder {
 // ---------------------------------------------------------------- LDS
 template <int CAP, int NT>
 struct Smem {
-  uint32_t val[CAP];      // candidate value bits (fp32, or bf16 widened to fp32)
-  uint32_t idx[CAP];      // candidate columns
-  uint32_t hist[kBins];
+  uint32_t val[CAP];          // candidate value bits (fp32, or bf16 widened to fp32)
+  uint32_t idx[CAP];          // candidate columns
+  uint32_t hist[kBins];       // zero whenever not in use
   uint32_t wsum[NT / 64];
   uint32_t res[4];
-  uint32_t cnt[2];        // append counters; cur receives appends, cur^1 the next cut
+  uint32_t cnt[2];            // append counters; cur receives appends, cur^1 the next cut
   uint32_t snap[2][NT / 64];  // per-wave count after its last append, by step parity
   uint32_t segoff[kMaxSegments];  // merge: first flat position of each segment
-  uint32_t hikey;         // upper bound of every candidate key
-  uint32_t flags;         // row status bits
+  uint32_t hikey;             // upper bound of every candidate key
+  uint32_t flags;             // row status bits
   uint32_t is_last;
-  unsigned long long thr; // the workgroup's threshold (composite)
+  uint32_t nwork;             // epilogue sort: pending segments (pairs in segoff)
+  unsigned long long rng[2];  // epilogue sort: min / max order key of a segment
+  unsigned long long thr;     // the workgroup's threshold (composite)
 };
 
-// Suffix search: higher bins first.  Finds b* with
-//   sum_{b > b*} hist[b] < need <= sum_{b >= b*} hist[b]
+// Suffix search over hist (higher bins first), which it leaves zeroed.  Finds
+// b* with  sum_{b > b*} hist[b] < need <= sum_{b >= b*} hist[b].
 // res = {b*, sum above b*, hist[b*], total}; res[0] = kBins when total < need.
 template <int NT, int CAP>
-__device__ void hist_find_top(Smem<CAP, NT>& sm, uint32_t need) {
+__device__ __forceinline__ void hist_find_top(Smem<CAP, NT>& sm, uint32_t need) {
   constexpr int BPT = kBins / NT;
   constexpr int NW = NT / 64;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
@@ -177,24 +262,23 @@ __device__ void hist_find_top(Smem<CAP, NT>& sm, uint32_t need) {
   for (int i = 0; i < BPT; ++i) {
     h[i] = sm.hist[t * BPT + i];
     s += h[i];
+    sm.hist[t * BPT + i] = 0u;
   }
-  uint32_t x = s;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = static_cast<uint32_t>(__shfl_down(static_cast<int>(x), o));
-    if (lane + o < 64) x += y;
-  }
-  if (lane == 0) sm.wsum[w] = x;
+  const uint32_t p = wave_prefix_sum(s);   // inclusive, within the wave
+  if (lane == 63) sm.wsum[w] = p;
   if (t == 0) sm.res[0] = kBins;
   __syncthreads();
-  uint32_t add = 0;
+  uint32_t before = 0, tot = 0;
 #pragma unroll
-  for (int w2 = 0; w2 < NW; ++w2)
-    if (w2 > w) add += sm.wsum[w2];
-  const uint32_t incl = x + add;
-  const uint32_t excl = incl - s;
-  if (excl < need && need <= incl) {
-    uint32_t acc = excl;
+  for (int w2 = 0; w2 < NW; ++w2) {
+    const uint32_t ws = sm.wsum[w2];
+    tot += ws;
+    if (w2 < w) before += ws;
+  }
+  const uint32_t excl_above = tot - (before + p);   // bins owned by threads > t
+  const uint32_t incl_above = excl_above + s;
+  if (excl_above < need && need <= incl_above) {
+    uint32_t acc = excl_above;
 #pragma unroll
     for (int i = BPT - 1; i >= 0; --i) {
       if (acc + h[i] >= need) {
@@ -206,13 +290,13 @@ __device__ void hist_find_top(Smem<CAP, NT>& sm, uint32_t need) {
       acc += h[i];
     }
   }
-  if (t == 0) sm.res[3] = incl;
+  if (t == 0) sm.res[3] = tot;
   __syncthreads();
 }
 
-// In place: hist[b] <- sum_{b' < b} hist[b'].
+// In place: hist[b] <- sum_{b' < b} hist[b'].  Returns the total.
 template <int NT, int CAP>
-__device__ void hist_exclusive_scan(Smem<CAP, NT>& sm) {
+__device__ __forceinline__ uint32_t hist_exclusive_scan(Smem<CAP, NT>& sm) {
   constexpr int BPT = kBins / NT;
   constexpr int NW = NT / 64;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
@@ -223,55 +307,79 @@ __device__ void hist_exclusive_scan(Smem<CAP, NT>& sm) {
     h[i] = sm.hist[t * BPT + i];
     s += h[i];
   }
-  uint32_t x = s;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = static_cast<uint32_t>(__shfl_up(static_cast<int>(x), o));
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) sm.wsum[w] = x;
+  const uint32_t p = wave_prefix_sum(s);
+  if (lane == 63) sm.wsum[w] = p;
   __syncthreads();
-  uint32_t add = 0;
+  uint32_t before = 0, tot = 0;
 #pragma unroll
-  for (int w2 = 0; w2 < NW; ++w2)
-    if (w2 < w) add += sm.wsum[w2];
-  uint32_t run = x - s + add;
+  for (int w2 = 0; w2 < NW; ++w2) {
+    const uint32_t ws = sm.wsum[w2];
+    tot += ws;
+    if (w2 < w) before += ws;
+  }
+  uint32_t run = before + p - s;
 #pragma unroll
   for (int i = 0; i < BPT; ++i) {
     sm.hist[t * BPT + i] = run;
     run += h[i];
   }
   __syncthreads();
+  return tot;
 }
 
 template <int NT, int CAP>
-__device__ __forceinline__ void hist_clear(Smem<CAP, NT>& sm) {
+__device__ __forceinline__ void hist_zero_own(Smem<CAP, NT>& sm) {
+  constexpr int BPT = kBins / NT;
 #pragma unroll
-  for (int i = threadIdx.x; i < kBins; i += NT) sm.hist[i] = 0u;
+  for (int i = 0; i < BPT; ++i) sm.hist[threadIdx.x * BPT + i] = 0u;
 }
 
-// Among the candidates with key E and composite > T, the column I of the
+// Candidates are visited in groups of kGroup slots per thread (slot e of
+// thread t is buffer position t + e * NT): a group's LDS reads are issued
+// back to back, unconditionally at a clamped address, and waited for once.
+constexpr int kGroup = 16;
+
+template <int NT, int CAP>
+constexpr int slots_per_thread() { return (CAP + NT * kGroup - 1) / (NT * kGroup) * kGroup; }
+
+template <int NT, int CAP>
+__device__ __forceinline__ void read_group(const Smem<CAP, NT>& sm, int e0, uint32_t c,
+                                           uint32_t (&rv)[kGroup], uint32_t (&ri)[kGroup]) {
+#pragma unroll
+  for (int g = 0; g < kGroup; ++g) {
+    const uint32_t i = threadIdx.x + (e0 + g) * NT;
+    const uint32_t ic = i < CAP ? i : CAP - 1;
+    const uint32_t v = sm.val[ic], x = sm.idx[ic];
+    rv[g] = i < c ? v : kQNaN32;   // a NaN key lies above every range and never passes
+    ri[g] = x;
+  }
+}
+
+// Among the candidates with key E_key and composite > T, the column of the
 // need-th smallest column (need >= 1 and at least need such candidates).
 template <int NT, int CAP>
-__device__ uint32_t index_cut(Smem<CAP, NT>& sm, uint32_t c, uint32_t E, uint32_t need,
-                              uint64_t T, uint32_t n_cols) {
-  const int t = threadIdx.x;
+__device__ __noinline__ uint32_t index_cut(Smem<CAP, NT>& sm, uint32_t c, uint32_t E_key,
+                                           uint32_t need, uint64_t T, uint32_t n_cols) {
+  constexpr int E = slots_per_thread<NT, CAP>();
   uint32_t ibase = 0;
   uint32_t itop = n_cols > 0 ? n_cols - 1u : 0u;
   for (;;) {
-    const uint32_t span = itop - ibase;
-    const uint32_t shift = bit_length(span) > kRadixBits ? bit_length(span) - kRadixBits : 0u;
-    hist_clear(sm);
-    __syncthreads();
-    for (uint32_t i = t; i < c; i += NT) {
-      const uint32_t ci = sm.idx[i];
-      if (key_of_bits(sm.val[i]) == E && ci >= ibase && ci <= itop && comp_of(E, ci) > T)
-        atomicAdd(&sm.hist[(kBins - 1) - ((ci - ibase) >> shift)], 1u);
+    const uint32_t shift = shift_for_span(itop - ibase);
+#pragma unroll 1
+    for (int e0 = 0; e0 < E; e0 += kGroup) {
+      uint32_t rv[kGroup], ri[kGroup];
+      read_group(sm, e0, c, rv, ri);
+#pragma unroll
+      for (int g = 0; g < kGroup; ++g) {
+        const uint32_t ci = ri[g];
+        if (key_of_bits(rv[g]) == E_key && ci >= ibase && ci <= itop && comp_of(E_key, ci) > T)
+          atomicAdd(&sm.hist[(kBins - 1) - ((ci - ibase) >> shift)], 1u);
+      }
     }
     __syncthreads();
     hist_find_top(sm, need);
-    const uint32_t b = (kBins - 1) - sm.res[0];   // bin in ascending column order
-    const uint32_t below = sm.res[1], bc = sm.res[2];
+    const uint32_t b = (kBins - 1) - uniform(sm.res[0]);   // bin in ascending column order
+    const uint32_t below = uniform(sm.res[1]), bc = uniform(sm.res[2]);
     need -= below;
     ibase += b << shift;
     const uint32_t bin_top = ibase + ((1u << shift) - 1u);
@@ -283,20 +391,20 @@ __device__ uint32_t index_cut(Smem<CAP, NT>& sm, uint32_t c, uint32_t E, uint32_
 
 // Cut the candidate buffer: keep every candidate with composite > T_new, where
 // T_new >= sm.thr leaves between k and keep_max candidates (or all of them if
-// fewer than keep_max are above sm.thr).  keep_max == k gives the exact top-k.
-// Returns the new append counter index.
+// no more than keep_max are above sm.thr).  keep_max == k gives the exact
+// top-k.  Returns the new append counter index.
 template <int NT, int CAP>
-__device__ int cut_buffer(Smem<CAP, NT>& sm, int cur, uint32_t k, uint32_t keep_max,
-                          uint32_t n_cols, float hi_lane) {
-  constexpr int E = CAP / NT;
+__device__ __noinline__ int cut_buffer(Smem<CAP, NT>& sm, int cur, uint32_t k,
+                                       uint32_t keep_max, uint32_t n_cols, float hi_lane) {
+  constexpr int E = slots_per_thread<NT, CAP>();
   const int t = threadIdx.x, lane = t & 63;
-  const uint32_t hk = wave_max_u32(key_of_bits(__float_as_uint(hi_lane)));
+  const uint32_t hk = wave_max(key_of_bits(__float_as_uint(hi_lane)));
   if (lane == 0) atomicMax(&sm.hikey, hk);
   if (t == 0) sm.cnt[cur ^ 1] = 0u;
   __syncthreads();
-  const uint32_t c = sm.cnt[cur];
-  const uint64_t T = sm.thr;
-  const uint32_t hi = sm.hikey;
+  const uint32_t c = uniform(sm.cnt[cur]);
+  const uint64_t T = uniform64(sm.thr);
+  const uint32_t hi = uniform(sm.hikey);
   const uint32_t K = static_cast<uint32_t>(T >> 32);
   const uint32_t klo = static_cast<uint32_t>(T) == 0xFFFFFFFFu ? K + 1u : K;
 
@@ -305,22 +413,26 @@ __device__ int cut_buffer(Smem<CAP, NT>& sm, int cur, uint32_t k, uint32_t keep_
     uint32_t need = k, above = 0, base = klo, top = hi;
     bool first = true;
     for (;;) {
-      const uint32_t span = top - base;
-      const uint32_t shift = bit_length(span) > kRadixBits ? bit_length(span) - kRadixBits : 0u;
-      hist_clear(sm);
-      __syncthreads();
-      for (uint32_t i = t; i < c; i += NT) {
-        const uint32_t key = key_of_bits(sm.val[i]);
-        if (key >= base && key <= top && comp_of(key, sm.idx[i]) > T)
-          atomicAdd(&sm.hist[(key - base) >> shift], 1u);
+      const uint32_t shift = shift_for_span(top - base);
+#pragma unroll 1
+      for (int e0 = 0; e0 < E; e0 += kGroup) {
+        if (static_cast<uint32_t>(e0 * NT) >= c) break;   // uniform
+        uint32_t rv[kGroup], ri[kGroup];
+        read_group(sm, e0, c, rv, ri);
+#pragma unroll
+        for (int g = 0; g < kGroup; ++g) {
+          const uint32_t key = key_of_bits(rv[g]);
+          if (key >= base && key <= top && comp_of(key, ri[g]) > T)
+            atomicAdd(&sm.hist[(key - base) >> shift], 1u);
+        }
       }
       __syncthreads();
       hist_find_top(sm, need);
       if (first) {
         first = false;
-        if (sm.res[3] <= keep_max) break;   // few enough above T: only drop those at or below T
+        if (uniform(sm.res[3]) <= keep_max) break;   // few enough above T: only drop those at or below T
       }
-      const uint32_t b = sm.res[0], ab = sm.res[1], bc = sm.res[2];
+      const uint32_t b = uniform(sm.res[0]), ab = uniform(sm.res[1]), bc = uniform(sm.res[2]);
       above += ab;
       need -= ab;
       base += b << shift;
@@ -330,7 +442,7 @@ __device__ int cut_buffer(Smem<CAP, NT>& sm, int cur, uint32_t k, uint32_t keep_
         break;
       }
       if (shift == 0) {
-        const uint32_t I = index_cut(sm, c, base, need, T, n_cols);
+        const uint32_t I = index_cut<NT, CAP>(sm, c, base, need, T, n_cols);
         const uint64_t cand = comp_of(base, I) - 1u;
         newT = cand > T ? cand : T;
         break;
@@ -339,29 +451,37 @@ __device__ int cut_buffer(Smem<CAP, NT>& sm, int cur, uint32_t k, uint32_t keep_
     }
   }
 
-  // Compaction into the other counter: read everything first, then write.
+  // Compaction into the other counter, one group of slots at a time: all
+  // threads read the group, then the kept entries go to positions reserved
+  // with one LDS atomic per wave.  The write cursor never passes the number of
+  // positions read so far, so a write never lands on an unread entry.
   const int nxt = cur ^ 1;
-  uint32_t rv[E], ri[E];
+#pragma unroll 1
+  for (int e0 = 0; e0 < E; e0 += kGroup) {
+    if (static_cast<uint32_t>(e0 * NT) >= c) break;   // uniform
+    uint32_t rv[kGroup], ri[kGroup];
+    read_group(sm, e0, c, rv, ri);
+    uint32_t total = 0;
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const uint32_t i = t + e * NT;
-    rv[e] = i < c ? sm.val[i] : 0u;
-    ri[e] = i < c ? sm.idx[i] : 0u;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const uint32_t i = t + e * NT;
-    const bool keep = i < c && comp_of(key_of_bits(rv[e]), ri[e]) > newT;
-    const uint64_t m = ballot(keep);
-    if (m) {
+    for (int g = 0; g < kGroup; ++g) {
+      const bool keep = t + (e0 + g) * NT < c && comp_of(key_of_bits(rv[g]), ri[g]) > newT;
+      total += static_cast<uint32_t>(__popcll(ballot(keep)));
+    }
+    __syncthreads();
+    if (total) {
       uint32_t base = 0;
-      if (lane == 0) base = atomicAdd(&sm.cnt[nxt], static_cast<uint32_t>(__popcll(m)));
-      base = static_cast<uint32_t>(__shfl(static_cast<int>(base), 0));
-      if (keep) {
-        const uint32_t pos = base + mbcnt64(m);
-        sm.val[pos] = rv[e];
-        sm.idx[pos] = ri[e];
+      if (lane == 0) base = atomicAdd(&sm.cnt[nxt], total);
+      base = uniform(base);
+#pragma unroll
+      for (int g = 0; g < kGroup; ++g) {
+        const bool keep = t + (e0 + g) * NT < c && comp_of(key_of_bits(rv[g]), ri[g]) > newT;
+        const uint64_t m = ballot(keep);
+        if (keep) {
+          const uint32_t pos = base + mbcnt64(m);
+          sm.val[pos] = rv[g];
+          sm.idx[pos] = ri[g];
+        }
+        base += static_cast<uint32_t>(__popcll(m));
       }
     }
   }
@@ -370,11 +490,12 @@ __device__ int cut_buffer(Smem<CAP, NT>& sm, int cur, uint32_t k, uint32_t keep_
   return nxt;
 }
 
-// Filter one block held in registers and append its survivors.
+// Filter one block held in registers and append its survivors.  Returns the
+// append counter as this wave left it (0 if the wave appended nothing).
 template <bool BF16, bool RAG, int V, int NT, int CAP>
-__device__ __forceinline__ uint32_t filter_block(const uint4 (&r)[V], uint32_t blk, uint32_t L,
-                                             const Filter& F, float& hi_lane, bool& nan_lane,
-                                             Smem<CAP, NT>& sm, int cur) {
+__device__ __forceinline__ uint32_t filter_block(const u32x4 (&r)[V], uint32_t blk, uint32_t L,
+                                                 const Filter& F, float& hi_lane, bool& nan_lane,
+                                                 Smem<CAP, NT>& sm, int cur) {
   constexpr int EPV = BF16 ? 8 : 4;
   constexpr int NS = V * EPV;
   const int t = threadIdx.x, lane = t & 63;
@@ -411,130 +532,253 @@ __device__ __forceinline__ uint32_t filter_block(const uint4 (&r)[V], uint32_t b
   hi_lane = fmaxf(hi_lane, mx);
   if (!ballot(mx >= F.f)) return 0u;
 
-  bool p[NS];
-  uint64_t m[NS];
+  const bool exact = F.idx_lim != 0xFFFFFFFFu;
+  auto pass = [&](int s) -> bool {
+    return exact ? (f[s] > F.f || (f[s] == F.f && col(s) < F.idx_lim)) : f[s] >= F.f;
+  };
   uint32_t total = 0;
-  if (F.idx_lim == 0xFFFFFFFFu) {
 #pragma unroll
-    for (int s = 0; s < NS; ++s) p[s] = f[s] >= F.f;
-  } else {
-#pragma unroll
-    for (int s = 0; s < NS; ++s) p[s] = f[s] > F.f || (f[s] == F.f && col(s) < F.idx_lim);
-  }
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    m[s] = ballot(p[s]);
-    total += static_cast<uint32_t>(__popcll(m[s]));
-  }
+  for (int s = 0; s < NS; ++s) total += static_cast<uint32_t>(__popcll(ballot(pass(s))));
   if (total == 0) return 0u;
   uint32_t base = 0;
   if (lane == 0) base = atomicAdd(&sm.cnt[cur], total);
-  base = static_cast<uint32_t>(__shfl(static_cast<int>(base), 0));
+  base = uniform(base);
   const uint32_t after = base + total;
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    if (m[s]) {
-      if (p[s]) {
-        const uint32_t pos = base + mbcnt64(m[s]);
-        sm.val[pos] = __float_as_uint(f[s]);
-        sm.idx[pos] = col(s);
-      }
-      base += static_cast<uint32_t>(__popcll(m[s]));
+    const bool p = pass(s);
+    const uint64_t m = ballot(p);
+    if (p) {
+      const uint32_t pos = base + mbcnt64(m);
+      sm.val[pos] = __float_as_uint(f[s]);
+      sm.idx[pos] = col(s);
     }
+    base += static_cast<uint32_t>(__popcll(m));
   }
   return after;
 }
 
+template <int V>
+struct BlockRegs {
+  u32x4 v[V];
+};
+
+// The row's last, partial block: the same filter with every column checked
+// against L.  Out of line (once per row), block passed by value.
+template <bool BF16, int V, int NT, int CAP>
+__device__ __noinline__ uint32_t filter_ragged(BlockRegs<V> r, uint32_t blk, uint32_t L,
+                                               Filter F, float* hi_lane, bool* nan_lane,
+                                               Smem<CAP, NT>& sm, int cur) {
+  float hl = *hi_lane;
+  bool nl = *nan_lane;
+  const uint32_t after = filter_block<BF16, true, V, NT, CAP>(r.v, blk, L, F, hl, nl, sm, cur);
+  *hi_lane = hl;
+  *nan_lane = nl;
+  return after;
+}
+
+// A starting threshold from one whole block held in registers, before any of
+// it is appended: an 11-bit histogram of the block's keys over their own range
+// gives a bin edge with at least k of the block's elements at or above it.
+// That edge is a valid (monotone) threshold for the row, so the block and
+// everything after it are filtered against it instead of against -inf, and
+// the buffer never has to hold the whole first block.  Leaves hist zeroed.
+template <bool BF16, int V, int NT, int CAP>
+__device__ __noinline__ uint64_t block_threshold(BlockRegs<V> r, uint32_t k, Smem<CAP, NT>& sm) {
+  constexpr int EPV = BF16 ? 8 : 4;
+  constexpr int NS = V * EPV;
+  const int t = threadIdx.x, lane = t & 63;
+  uint32_t key[NS];
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t w = r.v[v][q];
+      if (BF16) {
+        key[v * 8 + 2 * q] = key_of_bits(w << 16);
+        key[v * 8 + 2 * q + 1] = key_of_bits(w & 0xFFFF0000u);
+      } else {
+        key[v * 4 + q] = key_of_bits(w);
+      }
+    }
+  }
+  // NaN keys fall outside [key(-inf), key(+inf)] and are left out
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const bool ok = key[s] >= 0x00800000u && key[s] <= 0xFF800000u;
+    lo = ok && key[s] < lo ? key[s] : lo;
+    hi = ok && key[s] > hi ? key[s] : hi;
+  }
+  lo = wave_min(lo);
+  hi = wave_max(hi);
+  if (t == 0) {
+    sm.res[0] = 0xFFFFFFFFu;
+    sm.res[1] = 0u;
+  }
+  __syncthreads();
+  if (lane == 0) {
+    atomicMin(&sm.res[0], lo);
+    atomicMax(&sm.res[1], hi);
+  }
+  __syncthreads();
+  lo = uniform(sm.res[0]);
+  hi = uniform(sm.res[1]);
+  if (hi < lo) {   // no ordinary value in the block
+    __syncthreads();
+    return kThrInit;
+  }
+  const uint32_t shift = shift_for_span(hi - lo);
+#pragma unroll
+  for (int s = 0; s < NS; ++s)
+    if (key[s] >= lo && key[s] <= hi) atomicAdd(&sm.hist[(key[s] - lo) >> shift], 1u);
+  __syncthreads();
+  hist_find_top(sm, k);
+  const uint32_t b = uniform(sm.res[0]);
+  if (b >= static_cast<uint32_t>(kBins)) return kThrInit;   // fewer than k ordinary values
+  return (static_cast<uint64_t>(lo + (b << shift)) << 32) - 1u;
+}
+
+// Loads of one block.  Always issued, whatever the block: a vector that would
+// start at or past L reads the row's first vector instead (its lanes are
+// discarded by the filter), so the compiler can count outstanding loads
+// exactly.
 template <bool BF16, int V, int NT>
-__device__ __forceinline__ void load_block(uint4 (&r)[V], const char* xrow, uint32_t blk,
+__device__ __forceinline__ void load_block(u32x4 (&r)[V], const char* xrow, uint32_t blk,
                                            uint32_t L) {
   constexpr int EPV = BF16 ? 8 : 4;
   constexpr int ESZ = BF16 ? 2 : 4;
   const uint32_t e0 = blk * static_cast<uint32_t>(kBlockElems) + threadIdx.x * EPV;
-  const uint32_t fill = BF16 ? 0x7FC07FC0u : kQNaN32;
-  if (blk * static_cast<uint32_t>(kBlockElems) + kBlockElems <= L) {
 #pragma unroll
-    for (int v = 0; v < V; ++v)
-      r[v] = *reinterpret_cast<const uint4*>(xrow + static_cast<size_t>(e0 + v * NT * EPV) * ESZ);
-  } else {
-#pragma unroll
-    for (int v = 0; v < V; ++v) {
-      const uint32_t e = e0 + v * NT * EPV;
-      if (e < L)
-        r[v] = *reinterpret_cast<const uint4*>(xrow + static_cast<size_t>(e) * ESZ);
-      else
-        r[v] = make_uint4(fill, fill, fill, fill);
-    }
+  for (int v = 0; v < V; ++v) {
+    uint32_t e = e0 + v * NT * EPV;
+    e = e < L ? e : 0u;
+    r[v] = __builtin_nontemporal_load(
+        reinterpret_cast<const u32x4*>(xrow + static_cast<size_t>(e) * ESZ));
   }
 }
 
-template <int NT, int CAP, int KMAX>
-__device__ __forceinline__ void write_outputs(Smem<CAP, NT>& sm, const KArgs& a, bool bf16, int row, int cur,
-                              uint32_t status) {
-  const int t = threadIdx.x, lane = t & 63;
-  const uint32_t k = a.k;
-  const int64_t out0 = static_cast<int64_t>(row) * k;
-  uint32_t m = sm.cnt[cur];
-  if (status) m = 0;
+// Sort key of a result: ascending order is output order.  By value: larger
+// value first, then lower column.  By column: the column.
+__device__ __forceinline__ uint64_t order_key(bool by_value, uint32_t v, uint32_t i) {
+  return by_value ? ((static_cast<uint64_t>(~key_of_bits(v)) << 32) | i) : i;
+}
 
-  if (!status && a.sorted != 0 && m > 1) {
-    // Group by bin, then rank inside each bin.  Bins ascend in output order.
-    const bool by_value = a.sorted == 1;
-    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
-    for (uint32_t i = t; i < m; i += NT) {
-      const uint32_t q = by_value ? key_of_bits(sm.val[i]) : sm.idx[i];
-      lo = min(lo, q);
-      hi = max(hi, q);
+// Order the m results held in val/idx[0, m).  Regions R0 = [0, KMAX) (results,
+// and the sorted output), R1 = [KMAX, 2 KMAX) and R2 = [2 KMAX, 3 KMAX)
+// (scratch).  A segment [s, e) of results is binned on its order-key range
+// (2048 bins): members of small bins are placed by an in-bin rank, large bins
+// become new segments with a narrower range (the key is unique per result, so
+// every level shrinks the range 2048-fold).  A segment keeps its offsets in
+// every region, so the regions can alternate as levels deepen.
+template <int NT, int CAP, int KMAX>
+__device__ __noinline__ void sort_results(Smem<CAP, NT>& sm, uint32_t m, bool by_value) {
+  static_assert(3 * KMAX <= CAP, "sort regions");
+  constexpr uint32_t H = 32;              // bins larger than this are split again
+  constexpr int PER = KMAX / NT;          // members per thread at most
+  const int t = threadIdx.x, lane = t & 63;
+  if (t == 0) {
+    sm.segoff[0] = 0u;                    // (start | region << 28, end)
+    sm.segoff[1] = m;
+    sm.nwork = 1u;
+  }
+  __syncthreads();
+  for (;;) {
+    const uint32_t nw = uniform(sm.nwork);
+    if (nw == 0) break;
+    const uint32_t w0 = uniform(sm.segoff[2 * (nw - 1)]), s = w0 & 0x0FFFFFFFu;
+    const uint32_t e = uniform(sm.segoff[2 * nw - 1]);
+    const uint32_t reg = w0 >> 28;
+    const uint32_t treg = reg == 1 ? 2u : 1u;
+    uint32_t* sv = sm.val + reg * KMAX;
+    uint32_t* si = sm.idx + reg * KMAX;
+    uint32_t* tv = sm.val + treg * KMAX;
+    uint32_t* ti = sm.idx + treg * KMAX;
+    const uint32_t n = e - s;
+    // members of this thread, in registers
+    uint32_t mv[PER], mi[PER];
+    uint64_t lo = ~0ull, hi = 0ull;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const uint32_t p = t + j * NT;
+      const uint32_t pc = p < n ? s + p : s;
+      mv[j] = sv[pc];
+      mi[j] = si[pc];
+      if (p < n) {
+        const uint64_t q = order_key(by_value, mv[j], mi[j]);
+        lo = q < lo ? q : lo;
+        hi = q > hi ? q : hi;
+      }
     }
-    lo = wave_min_u32(lo);
-    hi = wave_max_u32(hi);
+    lo = wave_extreme64<false>(lo);
+    hi = wave_extreme64<true>(hi);
     if (t == 0) {
-      sm.res[0] = 0xFFFFFFFFu;
-      sm.res[1] = 0u;
+      sm.rng[0] = ~0ull;
+      sm.rng[1] = 0ull;
     }
-    hist_clear(sm);
     __syncthreads();
+    if (t == 0) sm.nwork = nw - 1;   // popped (pushes come after later barriers)
     if (lane == 0) {
-      atomicMin(&sm.res[0], lo);
-      atomicMax(&sm.res[1], hi);
+      atomicMin(&sm.rng[0], static_cast<unsigned long long>(lo));
+      atomicMax(&sm.rng[1], static_cast<unsigned long long>(hi));
     }
     __syncthreads();
-    lo = sm.res[0];
-    hi = sm.res[1];
-    const uint32_t span = hi - lo;
-    const uint32_t shift = bit_length(span) > kRadixBits ? bit_length(span) - kRadixBits : 0u;
-    auto bin_of = [&](uint32_t v, uint32_t i) -> uint32_t {
-      return by_value ? (hi - key_of_bits(v)) >> shift : (i - lo) >> shift;
-    };
-    auto better = [&](uint32_t va, uint32_t ia, uint32_t vb, uint32_t ib) -> bool {
-      if (!by_value) return ia < ib;
-      const uint32_t ka = key_of_bits(va), kb = key_of_bits(vb);
-      return ka > kb || (ka == kb && ia < ib);
-    };
-    for (uint32_t i = t; i < m; i += NT) atomicAdd(&sm.hist[bin_of(sm.val[i], sm.idx[i])], 1u);
+    lo = uniform64(sm.rng[0]);
+    hi = uniform64(sm.rng[1]);
+    const uint32_t bl = bit_length64(hi - lo);
+    const uint32_t shift = bl > kRadixBits ? bl - kRadixBits : 0u;
+    auto bin_of = [&](uint64_t q) { return static_cast<uint32_t>((q - lo) >> shift); };
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+      if (t + j * NT < n) atomicAdd(&sm.hist[bin_of(order_key(by_value, mv[j], mi[j]))], 1u);
     __syncthreads();
     hist_exclusive_scan(sm);
-    uint32_t* gval = sm.val + KMAX;
-    uint32_t* gidx = sm.idx + KMAX;
-    for (uint32_t i = t; i < m; i += NT) {
-      const uint32_t v = sm.val[i], ix = sm.idx[i];
-      const uint32_t p = atomicAdd(&sm.hist[bin_of(v, ix)], 1u);
-      gval[p] = v;
-      gidx[p] = ix;
+    // group by bin into the scratch region (returning atomics, all issued at once)
+    uint32_t pos[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+      pos[j] = t + j * NT < n ? atomicAdd(&sm.hist[bin_of(order_key(by_value, mv[j], mi[j]))], 1u) : 0u;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      if (t + j * NT < n) {
+        tv[s + pos[j]] = mv[j];
+        ti[s + pos[j]] = mi[j];
+      }
+    }
+    __syncthreads();   // hist[b] now holds the end of bin b
+    for (uint32_t p = t; p < n; p += NT) {
+      const uint32_t v = tv[s + p], ix = ti[s + p];
+      const uint64_t q = order_key(by_value, v, ix);
+      const uint32_t b = bin_of(q);
+      const uint32_t bs = b ? sm.hist[b - 1] : 0u;
+      const uint32_t be = sm.hist[b];
+      if (be - bs <= H) {
+        uint32_t rank = 0;
+        for (uint32_t r = bs; r < be; ++r)
+          rank += order_key(by_value, tv[s + r], ti[s + r]) < q ? 1u : 0u;
+        sm.val[s + bs + rank] = v;
+        sm.idx[s + bs + rank] = ix;
+      } else if (p == bs) {
+        const uint32_t slot = atomicAdd(&sm.nwork, 1u);
+        sm.segoff[2 * slot] = (s + bs) | (treg << 28);
+        sm.segoff[2 * slot + 1] = s + be;
+      }
     }
     __syncthreads();
-    for (uint32_t p = t; p < m; p += NT) {
-      const uint32_t v = gval[p], ix = gidx[p];
-      const uint32_t b = bin_of(v, ix);
-      const uint32_t s = b ? sm.hist[b - 1] : 0u;
-      const uint32_t e = sm.hist[b];
-      uint32_t rank = 0;
-      for (uint32_t q = s; q < e; ++q) rank += better(gval[q], gidx[q], v, ix) ? 1u : 0u;
-      sm.val[s + rank] = v;
-      sm.idx[s + rank] = ix;
-    }
-    __syncthreads();
+    hist_zero_own(sm);
   }
+  __syncthreads();
+}
+
+template <int NT, int CAP, int KMAX>
+__device__ __forceinline__ void write_outputs(Smem<CAP, NT>& sm, const KArgs& a, bool bf16,
+                                              int row, int cur, uint32_t status) {
+  const int t = threadIdx.x;
+  const uint32_t k = a.k;
+  const int64_t out0 = static_cast<int64_t>(row) * k;
+  uint32_t m = uniform(sm.cnt[cur]);
+  if (status) m = 0;
+  if (a.sorted != 0 && m > 1) sort_results<NT, CAP, KMAX>(sm, m, a.sorted == 1);
 
   for (uint32_t j = t; j < k; j += NT) {
     uint32_t ix, v;
@@ -560,7 +804,8 @@ __device__ __forceinline__ void write_outputs(Smem<CAP, NT>& sm, const KArgs& a,
   if (t == 0) a.row_status[row] = static_cast<int32_t>(status);
 }
 
-template <bool BF16, int CLS>
+
+template <bool BF16, int CLS, bool MULTI>
 __global__ __launch_bounds__(class_threads(CLS)) void topk_kernel(KArgs a) {
   constexpr int NT = class_threads(CLS);
   constexpr int CAP = class_cap(CLS);
@@ -568,13 +813,14 @@ __global__ __launch_bounds__(class_threads(CLS)) void topk_kernel(KArgs a) {
   constexpr int EPV = BF16 ? 8 : 4;
   constexpr int ESZ = BF16 ? 2 : 4;
   constexpr int V = kBlockElems / (NT * EPV);
+  constexpr int NBUF = 4;   // ring of blocks: 3 loading while 1 is filtered
   static_assert(V >= 1 && V * NT * EPV == kBlockElems, "block geometry");
   __shared__ Smem<CAP, NT> sm;
 
   const int t = threadIdx.x, lane = t & 63;
-  const int S = a.segments;
-  const int seg = static_cast<int>(blockIdx.x) % S;
-  int row = static_cast<int>(blockIdx.x) / S;
+  const int S = MULTI ? a.segments : 1;
+  const int seg = MULTI ? static_cast<int>(blockIdx.x) % S : 0;
+  int row = MULTI ? static_cast<int>(blockIdx.x) / S : static_cast<int>(blockIdx.x);
   // Variable-length rows: schedule from the last row down (for causal
   // prefill the longest rows are last), so long rows do not trail the grid.
   if (a.end) row = a.batch - 1 - row;
@@ -590,6 +836,7 @@ __global__ __launch_bounds__(class_threads(CLS)) void topk_kernel(KArgs a) {
       L = static_cast<uint32_t>(e);
     }
   }
+  hist_zero_own(sm);
   if (t == 0) {
     sm.cnt[0] = 0u;
     sm.cnt[1] = 0u;
@@ -599,7 +846,7 @@ __global__ __launch_bounds__(class_threads(CLS)) void topk_kernel(KArgs a) {
   }
   __syncthreads();
 
-  unsigned long long* thr_g = S > 1 ? a.ws_thr + row : nullptr;
+  unsigned long long* thr_g = MULTI ? a.ws_thr + row : nullptr;
   const uint32_t k = static_cast<uint32_t>(a.k);
   const uint32_t trigger = static_cast<uint32_t>(a.trigger);
   const uint32_t slack = (trigger - k) / 4u;
@@ -615,9 +862,11 @@ __global__ __launch_bounds__(class_threads(CLS)) void topk_kernel(KArgs a) {
   const char* xrow = static_cast<const char*>(a.x) + static_cast<int64_t>(row) * a.row_stride * ESZ;
   const bool ragged_row = (L % kBlockElems) != 0;
   const uint32_t last_blk = nb - 1u;
-
-  uint4 ra[V], rb[V];
-  uint64_t g = 0;
+  // Block of this workgroup's j-th step; steps past the end re-read the last
+  // one (from L2) so that every step issues the same loads.
+  auto blk_at = [&](uint32_t j) -> uint32_t {
+    return ntl == 0 ? 0u : order(seg + (j < ntl ? j : ntl - 1u) * S);
+  };
 
   // The decision to cut must be the same in every wave, but a fast wave may
   // append for the next block before a slow wave has looked at the counter.
@@ -631,159 +880,202 @@ __global__ __launch_bounds__(class_threads(CLS)) void topk_kernel(KArgs a) {
 #pragma unroll
     for (int w2 = 0; w2 < NT / 64; ++w2) c = max(c, sm.snap[par][w2]);
     par ^= 1;
-    return c;
+    return uniform(c);
   };
 
-  auto step = [&](uint4 (&cur_r)[V], uint4 (&nxt_r)[V], uint32_t u) {
-    const uint32_t blk = order(seg + u * S);
-    if (S > 1) g = load_thr(thr_g);
-    if (u + 1 < ntl) load_block<BF16, V, NT>(nxt_r, xrow, order(seg + (u + 1) * S), L);
-    uint32_t after;
-    if (ragged_row && blk == last_blk)
-      after = filter_block<BF16, true, V, NT, CAP>(cur_r, blk, L, F, hi_lane, nan_lane, sm, cur);
-    else
-      after = filter_block<BF16, false, V, NT, CAP>(cur_r, blk, L, F, hi_lane, nan_lane, sm, cur);
-    if (S > 1 && g > thr && lane == 0) atomicMax(&sm.thr, static_cast<unsigned long long>(g));
-    const uint32_t c = count_after_step(after);
-    if (c > trigger) {
-      const uint64_t before = sm.thr;
-      cur = cut_buffer<NT, CAP>(sm, cur, k, k + slack, L, hi_lane);
-      thr = sm.thr;
-      if (S > 1 && t == 0 && thr > before) publish_thr(thr_g, thr);
-    } else if (S > 1) {
-      const uint64_t seen = sm.thr;   // may already include a later wave's raise: still a valid bound
-      thr = seen > thr ? seen : thr;
+  u32x4 r0[V], r1[V], r2[V], r3[V];   // the ring: loads of 3 blocks in flight
+  uint64_t g = 0;   // shared threshold as read one step earlier
+
+  auto step = [&](u32x4 (&cur_r)[V], u32x4 (&nxt_r)[V], uint32_t u) {
+    uint64_t g_next = 0;
+    if (MULTI) g_next = load_thr(thr_g);
+    if (ntl > 0) load_block<BF16, V, NT>(nxt_r, xrow, blk_at(u + NBUF - 1), L);
+    if (u < ntl) {
+      const uint32_t blk = blk_at(u);
+      if (u == 0 && blk * static_cast<uint32_t>(kBlockElems) + kBlockElems <= L && 2 * k <= kBlockElems) {
+        // whole first block, and at least half of it can be dropped
+        BlockRegs<V> br;
+#pragma unroll
+        for (int v = 0; v < V; ++v) br.v[v] = cur_r[v];
+        const uint64_t t0 = block_threshold<BF16, V, NT, CAP>(br, k, sm);
+        if (t0 > thr) {
+          thr = t0;
+          F = filter_of(thr);
+          if (t == 0) {
+            atomicMax(&sm.thr, static_cast<unsigned long long>(t0));
+            if (MULTI) publish_thr(thr_g, t0);
+          }
+        }
+      }
+      uint32_t after;
+      if (ragged_row && blk == last_blk) {
+        BlockRegs<V> br;
+#pragma unroll
+        for (int v = 0; v < V; ++v) br.v[v] = cur_r[v];
+        after = filter_ragged<BF16, V, NT, CAP>(br, blk, L, F, &hi_lane, &nan_lane, sm, cur);
+      } else
+        after = filter_block<BF16, false, V, NT, CAP>(cur_r, blk, L, F, hi_lane, nan_lane, sm, cur);
+      if (MULTI && g > thr && lane == 0) atomicMax(&sm.thr, static_cast<unsigned long long>(g));
+      const uint32_t c = count_after_step(after);
+      if (c > trigger) {
+        const uint64_t before = uniform64(sm.thr);
+        cur = cut_buffer<NT, CAP>(sm, cur, k, k + slack, L, hi_lane);
+        thr = uniform64(sm.thr);
+        if (MULTI && t == 0 && thr > before) publish_thr(thr_g, thr);
+      } else if (MULTI) {
+        const uint64_t seen = uniform64(sm.thr);   // may include a later wave's raise: still a valid bound
+        thr = seen > thr ? seen : thr;
+      }
+      F = filter_of(thr);
     }
-    F = filter_of(thr);
+    if (MULTI) g = g_next;
   };
 
-  if (ntl > 0) load_block<BF16, V, NT>(ra, xrow, order(seg), L);
-  uint32_t u = 0;
-  for (; u + 1 < ntl; u += 2) {
-    step(ra, rb, u);
-    step(rb, ra, u + 1);
+  if (ntl > 0) {
+    load_block<BF16, V, NT>(r0, xrow, blk_at(0), L);
+    load_block<BF16, V, NT>(r1, xrow, blk_at(1), L);
+    load_block<BF16, V, NT>(r2, xrow, blk_at(2), L);
   }
-  if (u < ntl) step(ra, rb, u);
+  for (uint32_t u = 0; u < ntl; u += NBUF) {
+    step(r0, r3, u);
+    step(r1, r0, u + 1);
+    step(r2, r1, u + 2);
+    step(r3, r2, u + 3);
+  }
 
   // NaN anywhere in this workgroup's share of [0, L).
   if (ballot(nan_lane) && lane == 0) atomicOr(&sm.flags, static_cast<uint32_t>(DS_ROW_NAN));
+  if (MULTI && t == 0) {
+    const uint64_t gl = load_thr(thr_g);
+    if (gl > sm.thr) sm.thr = gl;   // survivors at or below the shared bound are not needed
+  }
   // Exact local top-k (drops anything at or below the current threshold too).
   cur = cut_buffer<NT, CAP>(sm, cur, k, k, L, hi_lane);
 
-  if (S > 1) {
-    const uint32_t mine = sm.cnt[cur];
-    const int64_t slot = static_cast<int64_t>(row) * S + seg;
+  if (MULTI) {
+    // Hand the survivors to the row's last workgroup: each workgroup reserves
+    // a range of the row's contiguous survivor array with one atomic and fills
+    // it.  Every shared word is written and read with agent-scope atomic
+    // accesses (coherent across the XCDs' L2s by themselves), and the stores
+    // are complete before the arrival counter moves, so no L2 write-back or
+    // invalidate is needed.
+    const uint32_t mine = uniform(sm.cnt[cur]);
+    const int64_t row0 = static_cast<int64_t>(row) * S * k;
     if (t == 0) {
+      sm.res[0] = mine ? __hip_atomic_fetch_add(&a.ws_fill[row], mine, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT)
+                       : 0u;
       if (mine >= k) publish_thr(thr_g, sm.thr);
-      a.ws_cnt[slot] = mine;
-      if (sm.flags) atomicOr(&a.ws_flags[row], sm.flags);
+      if (sm.flags)
+        __hip_atomic_fetch_or(&a.ws_flags[row], sm.flags, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    uint32_t* wv = a.ws_val + slot * k;
-    uint32_t* wi = a.ws_idx + slot * k;
+    __syncthreads();
+    const uint32_t own0 = uniform(sm.res[0]);
     for (uint32_t j = t; j < mine; j += NT) {
-      wv[j] = sm.val[j];
-      wi[j] = sm.idx[j];
+      st_agent(&a.ws_val[row0 + own0 + j], sm.val[j]);
+      st_agent(&a.ws_idx[row0 + own0 + j], sm.idx[j]);
     }
-    __threadfence();
+    wait_all_memory();
     __syncthreads();
     if (t == 0) {
-      const uint32_t prev = atomicAdd(&a.ws_done[row], 1u);
+      const uint32_t prev =
+          __hip_atomic_fetch_add(&a.ws_done[row], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       sm.is_last = prev == static_cast<uint32_t>(S - 1) ? 1u : 0u;
     }
     __syncthreads();
-    if (!sm.is_last) return;
-    __threadfence();
+    if (!uniform(sm.is_last)) return;
 
-    // Last arrival: merge the other workgroups' survivors.
-    const uint64_t gfin = load_thr(thr_g);
+    // Last arrival: merge the other workgroups' survivors (its own are still in
+    // LDS, so its own range of the array is skipped).
     if (t == 0) {
+      const uint64_t gfin = load_thr(thr_g);
       if (gfin > sm.thr) sm.thr = gfin;
-      sm.flags |= __hip_atomic_load(&a.ws_flags[row], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    // The workspace must be all zero again when the call ends, whatever layout
-    // the next call uses: clear this workgroup's own survivors now, and every
-    // other slot and count as it is read below.
-    for (uint32_t j = t; j < mine; j += NT) {
-      wv[j] = 0u;
-      wi[j] = 0u;
-    }
-    // Per-segment counts -> exclusive offsets (own segment counted as 0).
-    hist_clear(sm);
-    __syncthreads();
-    for (int s2 = t; s2 < S; s2 += NT) {
-      const int64_t sl = static_cast<int64_t>(row) * S + s2;
-      sm.hist[s2] = s2 == seg ? 0u : a.ws_cnt[sl];
-      a.ws_cnt[sl] = 0u;
+      sm.flags |= ld_agent(&a.ws_flags[row]);
+      sm.res[1] = ld_agent(&a.ws_fill[row]);
     }
     __syncthreads();
-    hist_exclusive_scan(sm);   // hist[s] = first flat position of segment s
-    for (int s2 = t; s2 < S; s2 += NT) sm.segoff[s2] = sm.hist[s2];
-    const uint32_t total = sm.hist[kBins - 1];
-    __syncthreads();
-    thr = sm.thr;
+    const uint32_t total = uniform(sm.res[1]);
+    thr = uniform64(sm.thr);
     F = filter_of(thr);
-    constexpr int PER = kBlockElems / NT;
-    for (uint32_t c0 = 0; c0 < total; c0 += kBlockElems) {
-      uint32_t mv[PER], mi[PER];
+    constexpr int PER = kBlockElems / (2 * NT);
+    constexpr uint32_t CHUNK = PER * NT;
+    // Loads of one chunk; positions past the end read position 0 (a valid
+    // address) and are dropped.  Every position read is cleared, so the
+    // workspace is all zero again when the call ends.
+    auto load_chunk = [&](uint32_t c0, uint32_t (&mv)[PER], uint32_t (&mi)[PER]) {
 #pragma unroll
       for (int q = 0; q < PER; ++q) {
-        const uint32_t fpos = c0 + t + q * NT;
-        mv[q] = kQNaN32;
-        mi[q] = 0u;
-        if (fpos < total) {
-          // segment: the last one whose first position is <= fpos (empty ones share it)
-          int lo = 0, hi = S - 1;
-          while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (sm.segoff[mid] <= fpos) lo = mid; else hi = mid - 1;
-          }
-          const int64_t sl = static_cast<int64_t>(row) * S + lo;
-          const uint32_t j = fpos - sm.segoff[lo];
-          mv[q] = a.ws_val[sl * k + j];
-          mi[q] = a.ws_idx[sl * k + j];
-          a.ws_val[sl * k + j] = 0u;
-          a.ws_idx[sl * k + j] = 0u;
+        const uint32_t p = c0 + t + q * NT;
+        const int64_t addr = row0 + (p < total ? p : 0u);
+        mv[q] = ld_agent(&a.ws_val[addr]);
+        mi[q] = ld_agent(&a.ws_idx[addr]);
+      }
+    };
+    auto clear_chunk = [&](uint32_t c0) {
+#pragma unroll
+      for (int q = 0; q < PER; ++q) {
+        const uint32_t p = c0 + t + q * NT;
+        if (p < total) {
+          st_agent(&a.ws_val[row0 + p], 0u);
+          st_agent(&a.ws_idx[row0 + p], 0u);
         }
       }
-      uint64_t mm[PER];
-      bool p[PER];
+    };
+    auto merge_chunk = [&](uint32_t c0, const uint32_t (&mv)[PER], const uint32_t (&mi)[PER]) {
+      auto pass = [&](int q) -> bool {
+        const uint32_t p = c0 + t + q * NT;
+        const float fv = __uint_as_float(mv[q]);
+        return p < total && (p < own0 || p >= own0 + mine) &&
+               (fv > F.f || (fv == F.f && mi[q] < F.idx_lim));
+      };
       uint32_t tot = 0;
 #pragma unroll
       for (int q = 0; q < PER; ++q) {
-        const float fv = __uint_as_float(mv[q]);
-        p[q] = fv > F.f || (fv == F.f && mi[q] < F.idx_lim);   // the NaN fill never passes
-        if (p[q]) hi_lane = fmaxf(hi_lane, fv);
-        mm[q] = ballot(p[q]);
-        tot += static_cast<uint32_t>(__popcll(mm[q]));
+        const bool p = pass(q);
+        if (p) hi_lane = fmaxf(hi_lane, __uint_as_float(mv[q]));
+        tot += static_cast<uint32_t>(__popcll(ballot(p)));
       }
       uint32_t after = 0;
       if (tot) {
         uint32_t base = 0;
         if (lane == 0) base = atomicAdd(&sm.cnt[cur], tot);
-        base = static_cast<uint32_t>(__shfl(static_cast<int>(base), 0));
+        base = uniform(base);
         after = base + tot;
 #pragma unroll
         for (int q = 0; q < PER; ++q) {
-          if (mm[q]) {
-            if (p[q]) {
-              const uint32_t pos = base + mbcnt64(mm[q]);
-              sm.val[pos] = mv[q];
-              sm.idx[pos] = mi[q];
-            }
-            base += static_cast<uint32_t>(__popcll(mm[q]));
+          const bool p = pass(q);
+          const uint64_t mm = ballot(p);
+          if (p) {
+            const uint32_t pos = base + mbcnt64(mm);
+            sm.val[pos] = mv[q];
+            sm.idx[pos] = mi[q];
           }
+          base += static_cast<uint32_t>(__popcll(mm));
         }
       }
       if (count_after_step(after) > trigger) {
         cur = cut_buffer<NT, CAP>(sm, cur, k, k + slack, L, hi_lane);
-        F = filter_of(sm.thr);
+        F = filter_of(uniform64(sm.thr));
+      }
+    };
+    uint32_t va[PER], ia[PER], vb[PER], ib[PER];
+    if (total > 0) load_chunk(0, va, ia);
+    for (uint32_t c0 = 0; c0 < total; c0 += 2 * CHUNK) {
+      load_chunk(c0 + CHUNK, vb, ib);
+      merge_chunk(c0, va, ia);
+      clear_chunk(c0);
+      load_chunk(c0 + 2 * CHUNK, va, ia);
+      if (c0 + CHUNK < total) {
+        merge_chunk(c0 + CHUNK, vb, ib);
+        clear_chunk(c0 + CHUNK);
       }
     }
     cur = cut_buffer<NT, CAP>(sm, cur, k, k, L, hi_lane);
     if (t == 0) {
-      a.ws_done[row] = 0u;
-      a.ws_thr[row] = 0ull;
-      a.ws_flags[row] = 0u;
+      st_agent(&a.ws_done[row], 0u);
+      st_agent(&a.ws_flags[row], 0u);
+      st_agent(&a.ws_fill[row], 0u);
+      __hip_atomic_store(&a.ws_thr[row], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 
@@ -801,8 +1093,8 @@ WsLayout ws_layout(int64_t batch, int segments, int k) {
   l.thr = 0;
   l.done = up(l.thr + b * 8);
   l.flags = up(l.done + b * 4);
-  l.cnt = up(l.flags + b * 4);
-  l.val = up(l.cnt + b * s * 4);
+  l.fill = up(l.flags + b * 4);
+  l.val = up(l.fill + b * 4);
   l.idx = up(l.val + b * s * static_cast<size_t>(k) * 4);
   l.total = up(l.idx + b * s * static_cast<size_t>(k) * 4);
   return l;
@@ -812,7 +1104,10 @@ template <bool BF16, int CLS>
 static int launch_one(const KArgs& a, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.batch) * a.segments));
   const dim3 block(class_threads(CLS));
-  hipLaunchKernelGGL((topk_kernel<BF16, CLS>), grid, block, 0, stream, a);
+  if (a.segments > 1)
+    hipLaunchKernelGGL((topk_kernel<BF16, CLS, true>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((topk_kernel<BF16, CLS, false>), grid, block, 0, stream, a);
   return static_cast<int>(hipGetLastError());
 }
 
