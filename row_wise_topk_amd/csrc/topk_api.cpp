@@ -161,8 +161,7 @@ ds_status_t ds_topk_ex(const void* x, ds_dtype_t dtype, int64_t batch, int64_t n
     a.ws_done = reinterpret_cast<uint32_t*>(w + l.done);
     a.ws_flags = reinterpret_cast<uint32_t*>(w + l.flags);
     a.ws_fill = reinterpret_cast<uint32_t*>(w + l.fill);
-    a.ws_val = reinterpret_cast<uint32_t*>(w + l.val);
-    a.ws_idx = reinterpret_cast<uint32_t*>(w + l.idx);
+    a.ws_comp = reinterpret_cast<unsigned long long*>(w + l.comp);
   }
   const int err = launch_topk(a, dtype == DS_BF16 ? 1 : 0, pl.cls, stream);
   return err == 0 ? DS_OK : DS_ERR_HIP;

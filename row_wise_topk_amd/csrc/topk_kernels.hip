@@ -6,32 +6,40 @@
 // elements visited in a random order; append the values that pass T to a
 // candidate buffer; when the buffer reaches k + B2 entries, radix-select it back
 // to k and raise T.  The pages' CUDA design is prior art only; what follows is
-// laid out for CDNA4:
+// laid out for CDNA4, where a wave64 vector instruction occupies its 16-lane
+// SIMD for 4 cycles and a workgroup has few waves per SIMD, so the cost of every
+// step is close to its instruction count:
 //
 //  * one workgroup (256 or 512 lanes) streams a row, or a share of a row's
 //    blocks when several workgroups cooperate on one row;
 //  * a block is B = 4096 elements; every lane issues 16-byte loads, and the
-//    loads of the next 2-3 blocks are always in flight (a register ring whose
-//    loads are issued unconditionally, so the compiler can wait for exactly
-//    the block being filtered);
-//  * the filter runs on the raw fp32 values (bf16 is widened by a shift), with
-//    a wave-wide early-out on each lane's running maximum; survivors are
+//    loads of the next 3 blocks are always in flight (a register ring whose
+//    loads are issued unconditionally, so the compiler waits for exactly the
+//    block being filtered);
+//  * the first whole block sets T from an 11-bit histogram of its keys held in
+//    registers, so the buffer never has to hold a block admitted at -inf;
+//  * the filter compares raw fp32 values (bf16 widened by a shift) with a
+//    wave-wide early-out on each lane's running maximum; survivors are
 //    compacted into LDS with ballot / mbcnt and one LDS atomic per wave;
-//  * the cut (radix select) is an 11-bit LDS histogram over the live key range
-//    [T, max], refined only when the boundary bin is too full; exact ties on a
-//    key are cut by column with the same histogram on the column;
+//  * a candidate is one 64-bit composite in LDS, so the cut (radix select) is
+//    an 11-bit histogram over the high word in the live range [T, max], refined
+//    only when the boundary bin is too full, and keeping a candidate is one
+//    64-bit compare; exact ties on a key are cut by column the same way;
 //  * several workgroups on one row share T through a 64-bit atomicMax in
 //    device memory; the last to finish merges the others' survivors;
-//  * the epilogue orders the k results by value or by column with a histogram
-//    grouping plus an in-bin rank, and writes indices / values / status.
+//  * the epilogue orders the k results by value or by column (histogram
+//    grouping, in-bin rank, re-binning of large bins) and writes indices,
+//    values and status.
 //
 // Order and tie-break (xhh.club, "DeepSeek开源DeepSelect：比torch.topk快二十倍！",
 // Q&A on stable results): larger value first, then lower column.  A value v at
-// column i has the 64-bit composite  (key(v) << 32) | ~i,  where key() maps
-// fp32 sign-magnitude onto unsigned offset binary so that -0.0 and +0.0 share
-// one key.  The threshold T is a composite too: an element is admitted iff its
+// column i has the composite  (key(v) << 32) | ~i,  where key() maps fp32
+// sign-magnitude onto unsigned offset binary so that -0.0 and +0.0 share one
+// key.  The threshold T is a composite too: an element is admitted iff its
 // composite is > T, so T can sit between two equal values with different
 // columns.  Every published T leaves at least k composites of the row above it.
+// Output values are rebuilt from the key (exact for every non-NaN value but a
+// zero, whose sign is read back from the input).
 //
 // NaN (narracomm.com, NaN paragraph): always checked over [0, end); a NaN sets
 // a status bit for the row instead of trapping.
@@ -52,6 +60,7 @@ constexpr uint32_t kNegInf32 = 0xFF800000u;
 
 // 16 bytes of a row: one vector load per lane.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned long long u64;
 
 // ---------------------------------------------------------------- keys
 __device__ __forceinline__ uint32_t key_of_bits(uint32_t b) {
@@ -59,18 +68,20 @@ __device__ __forceinline__ uint32_t key_of_bits(uint32_t b) {
   return (b & 0x80000000u) ? kBias - mag : kBias + mag;
 }
 
-// Inverse of key_of_bits for keys of non-NaN values ([0x00800000, 0xFF800000]).
-__device__ __forceinline__ float float_of_key(uint32_t key) {
-  const uint32_t b = key >= kBias ? key - kBias : ((kBias - key) | 0x80000000u);
-  return __uint_as_float(b);
+// Inverse of key_of_bits for keys of non-NaN values ([0x00800000, 0xFF800000]);
+// the key of both zeros gives +0.0.
+__device__ __forceinline__ uint32_t bits_of_key(uint32_t key) {
+  return key >= kBias ? key - kBias : ((kBias - key) | 0x80000000u);
 }
 
-__device__ __forceinline__ uint64_t comp_of(uint32_t key, uint32_t idx) {
-  return (static_cast<uint64_t>(key) << 32) | static_cast<uint32_t>(~idx);
+__device__ __forceinline__ u64 comp_of(uint32_t key, uint32_t col) {
+  return (static_cast<u64>(key) << 32) | static_cast<uint32_t>(~col);
 }
+__device__ __forceinline__ uint32_t key_of(u64 c) { return static_cast<uint32_t>(c >> 32); }
+__device__ __forceinline__ uint32_t col_of(u64 c) { return ~static_cast<uint32_t>(c); }
 
 // T = -inf with "greater or equal": just below the key of -inf, all columns.
-constexpr uint64_t kThrInit = (static_cast<uint64_t>(0x00800000u - 1u) << 32) | 0xFFFFFFFFull;
+constexpr u64 kThrInit = (static_cast<u64>(0x00800000u - 1u) << 32) | 0xFFFFFFFFull;
 
 // The threshold in the form the filter uses: admit v iff v > f, or v == f and
 // column < idx_lim.  With idx_lim == ~0u this is simply v >= f.
@@ -79,17 +90,17 @@ struct Filter {
   uint32_t idx_lim;
 };
 
-__device__ __forceinline__ Filter filter_of(uint64_t thr) {
+__device__ __forceinline__ Filter filter_of(u64 thr) {
   const uint32_t K = static_cast<uint32_t>(thr >> 32);
   const uint32_t low = static_cast<uint32_t>(thr);
-  if (low == 0xFFFFFFFFu) return {float_of_key(K + 1u), 0xFFFFFFFFu};
-  return {float_of_key(K), ~low};
+  if (low == 0xFFFFFFFFu) return {__uint_as_float(bits_of_key(K + 1u)), 0xFFFFFFFFu};
+  return {__uint_as_float(bits_of_key(K)), ~low};
 }
 
 // ---------------------------------------------------------------- wave helpers
-__device__ __forceinline__ uint64_t ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
+__device__ __forceinline__ u64 ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
 
-__device__ __forceinline__ uint32_t mbcnt64(uint64_t m) {
+__device__ __forceinline__ uint32_t mbcnt64(u64 m) {
   return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
 }
@@ -99,13 +110,13 @@ __device__ __forceinline__ uint32_t mbcnt64(uint64_t m) {
 __device__ __forceinline__ uint32_t uniform(uint32_t v) {
   return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(v)));
 }
-__device__ __forceinline__ uint64_t uniform64(uint64_t v) {
-  return (static_cast<uint64_t>(uniform(static_cast<uint32_t>(v >> 32))) << 32) |
+__device__ __forceinline__ u64 uniform64(u64 v) {
+  return (static_cast<u64>(uniform(static_cast<uint32_t>(v >> 32))) << 32) |
          uniform(static_cast<uint32_t>(v));
 }
 
 // DPP move: lanes whose source is outside the row, or whose row is masked off,
-// receive `IDENT`.
+// receive IDENT.
 template <int CTRL, int ROW_MASK, uint32_t IDENT>
 __device__ __forceinline__ uint32_t dpp(uint32_t v) {
   return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
@@ -141,17 +152,17 @@ __device__ __forceinline__ uint32_t wave_min(uint32_t x) {
       static_cast<int>(wave_scan<OpMin, 0xFFFFFFFFu>(x, OpMin{})), 63));
 }
 
-template <int CTRL, int ROW_MASK, uint64_t IDENT>
-__device__ __forceinline__ uint64_t dpp64(uint64_t v) {
+template <int CTRL, int ROW_MASK, u64 IDENT>
+__device__ __forceinline__ u64 dpp64(u64 v) {
   const uint32_t lo = dpp<CTRL, ROW_MASK, static_cast<uint32_t>(IDENT)>(static_cast<uint32_t>(v));
   const uint32_t hi = dpp<CTRL, ROW_MASK, static_cast<uint32_t>(IDENT >> 32)>(static_cast<uint32_t>(v >> 32));
-  return (static_cast<uint64_t>(hi) << 32) | lo;
+  return (static_cast<u64>(hi) << 32) | lo;
 }
 
 template <bool MAX>
-__device__ __forceinline__ uint64_t wave_extreme64(uint64_t x) {
-  constexpr uint64_t I = MAX ? 0ull : ~0ull;
-  auto op = [](uint64_t a, uint64_t b) { return MAX ? (a > b ? a : b) : (a < b ? a : b); };
+__device__ __forceinline__ u64 wave_extreme64(u64 x) {
+  constexpr u64 I = MAX ? 0ull : ~0ull;
+  auto op = [](u64 a, u64 b) { return MAX ? (a > b ? a : b) : (a < b ? a : b); };
   x = op(x, dpp64<0x111, 0xF, I>(x));
   x = op(x, dpp64<0x112, 0xF, I>(x));
   x = op(x, dpp64<0x114, 0xF, I>(x));
@@ -160,29 +171,32 @@ __device__ __forceinline__ uint64_t wave_extreme64(uint64_t x) {
   x = op(x, dpp64<0x143, 0xC, I>(x));
   const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(x)), 63));
   const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(x >> 32)), 63));
-  return (static_cast<uint64_t>(hi) << 32) | lo;
+  return (static_cast<u64>(hi) << 32) | lo;
 }
 
 __device__ __forceinline__ uint32_t bit_length(uint32_t v) { return v ? 32u - __clz(v) : 0u; }
-__device__ __forceinline__ uint32_t bit_length64(uint64_t v) { return v ? 64u - __clzll(v) : 0u; }
+__device__ __forceinline__ uint32_t bit_length64(u64 v) { return v ? 64u - __clzll(v) : 0u; }
 
 __device__ __forceinline__ uint32_t shift_for_span(uint32_t span) {
   const uint32_t b = bit_length(span);
   return b > kRadixBits ? b - kRadixBits : 0u;
 }
 
-// Relaxed agent-scope accesses to the shared per-row threshold.
-__device__ __forceinline__ uint64_t load_thr(const unsigned long long* p) {
+// ---------------------------------------------------------------- device-memory sharing
+// Relaxed agent-scope accesses: coherent across the XCDs' L2 caches without
+// any cache write-back or invalidate.
+__device__ __forceinline__ u64 load_thr(const u64* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void publish_thr(unsigned long long* p, uint64_t v) {
-  __hip_atomic_fetch_max(p, static_cast<unsigned long long>(v), __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ void publish_thr(u64* p, u64 v) {
+  __hip_atomic_fetch_max(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void st_agent(uint32_t* p, uint32_t v) {
+template <typename W>
+__device__ __forceinline__ void st_agent(W* p, W v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ uint32_t ld_agent(const uint32_t* p) {
+template <typename W>
+__device__ __forceinline__ W ld_agent(const W* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 // Wait until every memory access this wave has issued is complete.  Used
@@ -232,20 +246,19 @@ struct BlockOrder {
 // ---------------------------------------------------------------- LDS
 template <int CAP, int NT>
 struct Smem {
-  uint32_t val[CAP];          // candidate value bits (fp32, or bf16 widened to fp32)
-  uint32_t idx[CAP];          // candidate columns
+  u64 comp[CAP];              // candidate composites
   uint32_t hist[kBins];       // zero whenever not in use
   uint32_t wsum[NT / 64];
   uint32_t res[4];
   uint32_t cnt[2];            // append counters; cur receives appends, cur^1 the next cut
   uint32_t snap[2][NT / 64];  // per-wave count after its last append, by step parity
-  uint32_t segoff[kMaxSegments];  // merge: first flat position of each segment
+  uint32_t segoff[kMaxSegments];  // epilogue sort: pending segments (start | region, end)
   uint32_t hikey;             // upper bound of every candidate key
   uint32_t flags;             // row status bits
   uint32_t is_last;
-  uint32_t nwork;             // epilogue sort: pending segments (pairs in segoff)
-  unsigned long long rng[2];  // epilogue sort: min / max order key of a segment
-  unsigned long long thr;     // the workgroup's threshold (composite)
+  uint32_t nwork;             // epilogue sort: number of pending segments
+  u64 rng[2];                 // epilogue sort: min / max order key of a segment
+  u64 thr;                    // the workgroup's threshold (composite)
 };
 
 // Suffix search over hist (higher bins first), which it leaves zeroed.  Finds
@@ -334,9 +347,12 @@ __device__ __forceinline__ void hist_zero_own(Smem<CAP, NT>& sm) {
   for (int i = 0; i < BPT; ++i) sm.hist[threadIdx.x * BPT + i] = 0u;
 }
 
+// ---------------------------------------------------------------- the cut
 // Candidates are visited in groups of kGroup slots per thread (slot e of
 // thread t is buffer position t + e * NT): a group's LDS reads are issued
 // back to back, unconditionally at a clamped address, and waited for once.
+// Slots past the count read as 0, which is below every threshold and outside
+// every key range.
 constexpr int kGroup = 16;
 
 template <int NT, int CAP>
@@ -344,14 +360,12 @@ constexpr int slots_per_thread() { return (CAP + NT * kGroup - 1) / (NT * kGroup
 
 template <int NT, int CAP>
 __device__ __forceinline__ void read_group(const Smem<CAP, NT>& sm, int e0, uint32_t c,
-                                           uint32_t (&rv)[kGroup], uint32_t (&ri)[kGroup]) {
+                                           u64 (&v)[kGroup]) {
 #pragma unroll
   for (int g = 0; g < kGroup; ++g) {
     const uint32_t i = threadIdx.x + (e0 + g) * NT;
-    const uint32_t ic = i < CAP ? i : CAP - 1;
-    const uint32_t v = sm.val[ic], x = sm.idx[ic];
-    rv[g] = i < c ? v : kQNaN32;   // a NaN key lies above every range and never passes
-    ri[g] = x;
+    const u64 x = sm.comp[i < CAP ? i : CAP - 1];
+    v[g] = i < c ? x : 0ull;
   }
 }
 
@@ -359,7 +373,7 @@ __device__ __forceinline__ void read_group(const Smem<CAP, NT>& sm, int e0, uint
 // need-th smallest column (need >= 1 and at least need such candidates).
 template <int NT, int CAP>
 __device__ __noinline__ uint32_t index_cut(Smem<CAP, NT>& sm, uint32_t c, uint32_t E_key,
-                                           uint32_t need, uint64_t T, uint32_t n_cols) {
+                                           uint32_t need, u64 T, uint32_t n_cols) {
   constexpr int E = slots_per_thread<NT, CAP>();
   uint32_t ibase = 0;
   uint32_t itop = n_cols > 0 ? n_cols - 1u : 0u;
@@ -367,13 +381,14 @@ __device__ __noinline__ uint32_t index_cut(Smem<CAP, NT>& sm, uint32_t c, uint32
     const uint32_t shift = shift_for_span(itop - ibase);
 #pragma unroll 1
     for (int e0 = 0; e0 < E; e0 += kGroup) {
-      uint32_t rv[kGroup], ri[kGroup];
-      read_group(sm, e0, c, rv, ri);
+      if (static_cast<uint32_t>(e0 * NT) >= c) break;   // uniform
+      u64 v[kGroup];
+      read_group(sm, e0, c, v);
 #pragma unroll
       for (int g = 0; g < kGroup; ++g) {
-        const uint32_t ci = ri[g];
-        if (key_of_bits(rv[g]) == E_key && ci >= ibase && ci <= itop && comp_of(E_key, ci) > T)
-          atomicAdd(&sm.hist[(kBins - 1) - ((ci - ibase) >> shift)], 1u);
+        const uint32_t ci = col_of(v[g]) - ibase;
+        if (key_of(v[g]) == E_key && ci <= itop - ibase && v[g] > T)
+          atomicAdd(&sm.hist[(kBins - 1) - (ci >> shift)], 1u);
       }
     }
     __syncthreads();
@@ -395,35 +410,44 @@ __device__ __noinline__ uint32_t index_cut(Smem<CAP, NT>& sm, uint32_t c, uint32
 // top-k.  Returns the new append counter index.
 template <int NT, int CAP>
 __device__ __noinline__ int cut_buffer(Smem<CAP, NT>& sm, int cur, uint32_t k,
-                                       uint32_t keep_max, uint32_t n_cols, float hi_lane) {
+                                       uint32_t keep_max, uint32_t n_cols, uint32_t hi_key) {
   constexpr int E = slots_per_thread<NT, CAP>();
   const int t = threadIdx.x, lane = t & 63;
-  const uint32_t hk = wave_max(key_of_bits(__float_as_uint(hi_lane)));
+  const uint32_t hk = wave_max(hi_key);
   if (lane == 0) atomicMax(&sm.hikey, hk);
   if (t == 0) sm.cnt[cur ^ 1] = 0u;
   __syncthreads();
   const uint32_t c = uniform(sm.cnt[cur]);
-  const uint64_t T = uniform64(sm.thr);
+  const u64 T = uniform64(sm.thr);
   const uint32_t hi = uniform(sm.hikey);
   const uint32_t K = static_cast<uint32_t>(T >> 32);
-  const uint32_t klo = static_cast<uint32_t>(T) == 0xFFFFFFFFu ? K + 1u : K;
+  const bool key_only = static_cast<uint32_t>(T) == 0xFFFFFFFFu;   // T = "key >= K + 1"
+  const uint32_t klo = key_only ? K + 1u : K;
 
-  uint64_t newT = T;
+  u64 newT = T;
   if (hi >= klo && c > 0) {
     uint32_t need = k, above = 0, base = klo, top = hi;
     bool first = true;
     for (;;) {
       const uint32_t shift = shift_for_span(top - base);
+      const uint32_t span = top - base;
 #pragma unroll 1
       for (int e0 = 0; e0 < E; e0 += kGroup) {
         if (static_cast<uint32_t>(e0 * NT) >= c) break;   // uniform
-        uint32_t rv[kGroup], ri[kGroup];
-        read_group(sm, e0, c, rv, ri);
+        u64 v[kGroup];
+        read_group(sm, e0, c, v);
+        if (key_only) {   // every candidate in [base, top] is above T
 #pragma unroll
-        for (int g = 0; g < kGroup; ++g) {
-          const uint32_t key = key_of_bits(rv[g]);
-          if (key >= base && key <= top && comp_of(key, ri[g]) > T)
-            atomicAdd(&sm.hist[(key - base) >> shift], 1u);
+          for (int g = 0; g < kGroup; ++g) {
+            const uint32_t d = key_of(v[g]) - base;
+            if (d <= span) atomicAdd(&sm.hist[d >> shift], 1u);
+          }
+        } else {
+#pragma unroll
+          for (int g = 0; g < kGroup; ++g) {
+            const uint32_t d = key_of(v[g]) - base;
+            if (d <= span && v[g] > T) atomicAdd(&sm.hist[d >> shift], 1u);
+          }
         }
       }
       __syncthreads();
@@ -437,13 +461,13 @@ __device__ __noinline__ int cut_buffer(Smem<CAP, NT>& sm, int cur, uint32_t k,
       need -= ab;
       base += b << shift;
       if (above + bc <= keep_max) {
-        const uint64_t cand = (static_cast<uint64_t>(base) << 32) - 1u;
+        const u64 cand = (static_cast<u64>(base) << 32) - 1u;
         newT = cand > T ? cand : T;
         break;
       }
       if (shift == 0) {
         const uint32_t I = index_cut<NT, CAP>(sm, c, base, need, T, n_cols);
-        const uint64_t cand = comp_of(base, I) - 1u;
+        const u64 cand = comp_of(base, I) - 1u;
         newT = cand > T ? cand : T;
         break;
       }
@@ -459,14 +483,11 @@ __device__ __noinline__ int cut_buffer(Smem<CAP, NT>& sm, int cur, uint32_t k,
 #pragma unroll 1
   for (int e0 = 0; e0 < E; e0 += kGroup) {
     if (static_cast<uint32_t>(e0 * NT) >= c) break;   // uniform
-    uint32_t rv[kGroup], ri[kGroup];
-    read_group(sm, e0, c, rv, ri);
+    u64 v[kGroup];
+    read_group(sm, e0, c, v);
     uint32_t total = 0;
 #pragma unroll
-    for (int g = 0; g < kGroup; ++g) {
-      const bool keep = t + (e0 + g) * NT < c && comp_of(key_of_bits(rv[g]), ri[g]) > newT;
-      total += static_cast<uint32_t>(__popcll(ballot(keep)));
-    }
+    for (int g = 0; g < kGroup; ++g) total += static_cast<uint32_t>(__popcll(ballot(v[g] > newT)));
     __syncthreads();
     if (total) {
       uint32_t base = 0;
@@ -474,13 +495,9 @@ __device__ __noinline__ int cut_buffer(Smem<CAP, NT>& sm, int cur, uint32_t k,
       base = uniform(base);
 #pragma unroll
       for (int g = 0; g < kGroup; ++g) {
-        const bool keep = t + (e0 + g) * NT < c && comp_of(key_of_bits(rv[g]), ri[g]) > newT;
-        const uint64_t m = ballot(keep);
-        if (keep) {
-          const uint32_t pos = base + mbcnt64(m);
-          sm.val[pos] = rv[g];
-          sm.idx[pos] = ri[g];
-        }
+        const bool keep = v[g] > newT;
+        const u64 m = ballot(keep);
+        if (keep) sm.comp[base + mbcnt64(m)] = v[g];
         base += static_cast<uint32_t>(__popcll(m));
       }
     }
@@ -490,6 +507,7 @@ __device__ __noinline__ int cut_buffer(Smem<CAP, NT>& sm, int cur, uint32_t k,
   return nxt;
 }
 
+// ---------------------------------------------------------------- the filter
 // Filter one block held in registers and append its survivors.  Returns the
 // append counter as this wave left it (0 if the wave appended nothing).
 template <bool BF16, bool RAG, int V, int NT, int CAP>
@@ -547,12 +565,8 @@ __device__ __forceinline__ uint32_t filter_block(const u32x4 (&r)[V], uint32_t b
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     const bool p = pass(s);
-    const uint64_t m = ballot(p);
-    if (p) {
-      const uint32_t pos = base + mbcnt64(m);
-      sm.val[pos] = __float_as_uint(f[s]);
-      sm.idx[pos] = col(s);
-    }
+    const u64 m = ballot(p);
+    if (p) sm.comp[base + mbcnt64(m)] = comp_of(key_of_bits(__float_as_uint(f[s])), col(s));
     base += static_cast<uint32_t>(__popcll(m));
   }
   return after;
@@ -584,7 +598,7 @@ __device__ __noinline__ uint32_t filter_ragged(BlockRegs<V> r, uint32_t blk, uin
 // everything after it are filtered against it instead of against -inf, and
 // the buffer never has to hold the whole first block.  Leaves hist zeroed.
 template <bool BF16, int V, int NT, int CAP>
-__device__ __noinline__ uint64_t block_threshold(BlockRegs<V> r, uint32_t k, Smem<CAP, NT>& sm) {
+__device__ __noinline__ u64 block_threshold(BlockRegs<V> r, uint32_t k, Smem<CAP, NT>& sm) {
   constexpr int EPV = BF16 ? 8 : 4;
   constexpr int NS = V * EPV;
   const int t = threadIdx.x, lane = t & 63;
@@ -606,7 +620,7 @@ __device__ __noinline__ uint64_t block_threshold(BlockRegs<V> r, uint32_t k, Sme
   // NaN keys fall outside [key(-inf), key(+inf)] and are left out
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    const bool ok = key[s] >= 0x00800000u && key[s] <= 0xFF800000u;
+    const bool ok = key[s] - 0x00800000u <= 0xFF000000u;
     lo = ok && key[s] < lo ? key[s] : lo;
     hi = ok && key[s] > hi ? key[s] : hi;
   }
@@ -629,14 +643,17 @@ __device__ __noinline__ uint64_t block_threshold(BlockRegs<V> r, uint32_t k, Sme
     return kThrInit;
   }
   const uint32_t shift = shift_for_span(hi - lo);
+  const uint32_t span = hi - lo;
 #pragma unroll
-  for (int s = 0; s < NS; ++s)
-    if (key[s] >= lo && key[s] <= hi) atomicAdd(&sm.hist[(key[s] - lo) >> shift], 1u);
+  for (int s = 0; s < NS; ++s) {
+    const uint32_t d = key[s] - lo;
+    if (d <= span) atomicAdd(&sm.hist[d >> shift], 1u);
+  }
   __syncthreads();
   hist_find_top(sm, k);
   const uint32_t b = uniform(sm.res[0]);
   if (b >= static_cast<uint32_t>(kBins)) return kThrInit;   // fewer than k ordinary values
-  return (static_cast<uint64_t>(lo + (b << shift)) << 32) - 1u;
+  return (static_cast<u64>(lo + (b << shift)) << 32) - 1u;
 }
 
 // Loads of one block.  Always issued, whatever the block: a vector that would
@@ -658,25 +675,22 @@ __device__ __forceinline__ void load_block(u32x4 (&r)[V], const char* xrow, uint
   }
 }
 
-// Sort key of a result: ascending order is output order.  By value: larger
-// value first, then lower column.  By column: the column.
-__device__ __forceinline__ uint64_t order_key(bool by_value, uint32_t v, uint32_t i) {
-  return by_value ? ((static_cast<uint64_t>(~key_of_bits(v)) << 32) | i) : i;
-}
-
-// Order the m results held in val/idx[0, m).  Regions R0 = [0, KMAX) (results,
+// ---------------------------------------------------------------- epilogue
+// Order the m results held in comp[0, m).  Regions R0 = [0, KMAX) (results,
 // and the sorted output), R1 = [KMAX, 2 KMAX) and R2 = [2 KMAX, 3 KMAX)
-// (scratch).  A segment [s, e) of results is binned on its order-key range
-// (2048 bins): members of small bins are placed by an in-bin rank, large bins
-// become new segments with a narrower range (the key is unique per result, so
-// every level shrinks the range 2048-fold).  A segment keeps its offsets in
-// every region, so the regions can alternate as levels deepen.
+// (scratch).  The sort key (ascending = output order) is ~composite by value
+// and the column by column; both are unique.  A segment [s, e) of results is
+// binned on its key range (2048 bins): members of small bins are placed by an
+// in-bin rank, large bins become new segments with a 2048-fold narrower
+// range.  A segment keeps its offsets in every region, so the regions can
+// alternate as levels deepen.
 template <int NT, int CAP, int KMAX>
 __device__ __noinline__ void sort_results(Smem<CAP, NT>& sm, uint32_t m, bool by_value) {
   static_assert(3 * KMAX <= CAP, "sort regions");
   constexpr uint32_t H = 32;              // bins larger than this are split again
   constexpr int PER = KMAX / NT;          // members per thread at most
   const int t = threadIdx.x, lane = t & 63;
+  auto order_key = [&](u64 c) -> u64 { return by_value ? ~c : static_cast<u64>(col_of(c)); };
   if (t == 0) {
     sm.segoff[0] = 0u;                    // (start | region << 28, end)
     sm.segoff[1] = m;
@@ -690,25 +704,18 @@ __device__ __noinline__ void sort_results(Smem<CAP, NT>& sm, uint32_t m, bool by
     const uint32_t e = uniform(sm.segoff[2 * nw - 1]);
     const uint32_t reg = w0 >> 28;
     const uint32_t treg = reg == 1 ? 2u : 1u;
-    uint32_t* sv = sm.val + reg * KMAX;
-    uint32_t* si = sm.idx + reg * KMAX;
-    uint32_t* tv = sm.val + treg * KMAX;
-    uint32_t* ti = sm.idx + treg * KMAX;
+    const u64* src = sm.comp + reg * KMAX;
+    u64* tmp = sm.comp + treg * KMAX;
     const uint32_t n = e - s;
-    // members of this thread, in registers
-    uint32_t mv[PER], mi[PER];
-    uint64_t lo = ~0ull, hi = 0ull;
+    u64 mv[PER];
+    u64 lo = ~0ull, hi = 0ull;
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const uint32_t p = t + j * NT;
-      const uint32_t pc = p < n ? s + p : s;
-      mv[j] = sv[pc];
-      mi[j] = si[pc];
-      if (p < n) {
-        const uint64_t q = order_key(by_value, mv[j], mi[j]);
-        lo = q < lo ? q : lo;
-        hi = q > hi ? q : hi;
-      }
+      mv[j] = src[p < n ? s + p : s];
+      const u64 q = order_key(mv[j]);
+      lo = p < n && q < lo ? q : lo;
+      hi = p < n && q > hi ? q : hi;
     }
     lo = wave_extreme64<false>(lo);
     hi = wave_extreme64<true>(hi);
@@ -719,45 +726,39 @@ __device__ __noinline__ void sort_results(Smem<CAP, NT>& sm, uint32_t m, bool by
     __syncthreads();
     if (t == 0) sm.nwork = nw - 1;   // popped (pushes come after later barriers)
     if (lane == 0) {
-      atomicMin(&sm.rng[0], static_cast<unsigned long long>(lo));
-      atomicMax(&sm.rng[1], static_cast<unsigned long long>(hi));
+      atomicMin(&sm.rng[0], lo);
+      atomicMax(&sm.rng[1], hi);
     }
     __syncthreads();
     lo = uniform64(sm.rng[0]);
     hi = uniform64(sm.rng[1]);
     const uint32_t bl = bit_length64(hi - lo);
     const uint32_t shift = bl > kRadixBits ? bl - kRadixBits : 0u;
-    auto bin_of = [&](uint64_t q) { return static_cast<uint32_t>((q - lo) >> shift); };
+    auto bin_of = [&](u64 q) { return static_cast<uint32_t>((q - lo) >> shift); };
 #pragma unroll
     for (int j = 0; j < PER; ++j)
-      if (t + j * NT < n) atomicAdd(&sm.hist[bin_of(order_key(by_value, mv[j], mi[j]))], 1u);
+      if (t + j * NT < n) atomicAdd(&sm.hist[bin_of(order_key(mv[j]))], 1u);
     __syncthreads();
     hist_exclusive_scan(sm);
     // group by bin into the scratch region (returning atomics, all issued at once)
     uint32_t pos[PER];
 #pragma unroll
     for (int j = 0; j < PER; ++j)
-      pos[j] = t + j * NT < n ? atomicAdd(&sm.hist[bin_of(order_key(by_value, mv[j], mi[j]))], 1u) : 0u;
+      pos[j] = t + j * NT < n ? atomicAdd(&sm.hist[bin_of(order_key(mv[j]))], 1u) : 0u;
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      if (t + j * NT < n) {
-        tv[s + pos[j]] = mv[j];
-        ti[s + pos[j]] = mi[j];
-      }
-    }
+    for (int j = 0; j < PER; ++j)
+      if (t + j * NT < n) tmp[s + pos[j]] = mv[j];
     __syncthreads();   // hist[b] now holds the end of bin b
     for (uint32_t p = t; p < n; p += NT) {
-      const uint32_t v = tv[s + p], ix = ti[s + p];
-      const uint64_t q = order_key(by_value, v, ix);
+      const u64 c = tmp[s + p];
+      const u64 q = order_key(c);
       const uint32_t b = bin_of(q);
       const uint32_t bs = b ? sm.hist[b - 1] : 0u;
       const uint32_t be = sm.hist[b];
       if (be - bs <= H) {
         uint32_t rank = 0;
-        for (uint32_t r = bs; r < be; ++r)
-          rank += order_key(by_value, tv[s + r], ti[s + r]) < q ? 1u : 0u;
-        sm.val[s + bs + rank] = v;
-        sm.idx[s + bs + rank] = ix;
+        for (uint32_t r = bs; r < be; ++r) rank += order_key(tmp[s + r]) < q ? 1u : 0u;
+        sm.comp[s + bs + rank] = c;
       } else if (p == bs) {
         const uint32_t slot = atomicAdd(&sm.nwork, 1u);
         sm.segoff[2 * slot] = (s + bs) | (treg << 28);
@@ -779,12 +780,20 @@ __device__ __forceinline__ void write_outputs(Smem<CAP, NT>& sm, const KArgs& a,
   uint32_t m = uniform(sm.cnt[cur]);
   if (status) m = 0;
   if (a.sorted != 0 && m > 1) sort_results<NT, CAP, KMAX>(sm, m, a.sorted == 1);
+  const char* xrow = static_cast<const char*>(a.x) + static_cast<int64_t>(row) * a.row_stride * (bf16 ? 2 : 4);
 
   for (uint32_t j = t; j < k; j += NT) {
     uint32_t ix, v;
     if (j < m) {
-      ix = sm.idx[j];
-      v = sm.val[j];
+      const u64 c = sm.comp[j];
+      ix = col_of(c);
+      const uint32_t key = key_of(c);
+      if (key == kBias) {   // a zero: its sign is only in the input
+        v = bf16 ? static_cast<uint32_t>(reinterpret_cast<const uint16_t*>(xrow)[ix]) << 16
+                 : reinterpret_cast<const uint32_t*>(xrow)[ix];
+      } else {
+        v = bits_of_key(key);
+      }
     } else {
       ix = 0xFFFFFFFFu;
       v = status ? kQNaN32 : kNegInf32;
@@ -804,7 +813,7 @@ __device__ __forceinline__ void write_outputs(Smem<CAP, NT>& sm, const KArgs& a,
   if (t == 0) a.row_status[row] = static_cast<int32_t>(status);
 }
 
-
+// ---------------------------------------------------------------- the kernel
 template <bool BF16, int CLS, bool MULTI>
 __global__ __launch_bounds__(class_threads(CLS)) void topk_kernel(KArgs a) {
   constexpr int NT = class_threads(CLS);
@@ -846,15 +855,16 @@ __global__ __launch_bounds__(class_threads(CLS)) void topk_kernel(KArgs a) {
   }
   __syncthreads();
 
-  unsigned long long* thr_g = MULTI ? a.ws_thr + row : nullptr;
+  u64* thr_g = MULTI ? reinterpret_cast<u64*>(a.ws_thr) + row : nullptr;
   const uint32_t k = static_cast<uint32_t>(a.k);
   const uint32_t trigger = static_cast<uint32_t>(a.trigger);
   const uint32_t slack = (trigger - k) / 4u;
   int cur = 0;
-  uint64_t thr = kThrInit;
+  u64 thr = kThrInit;
   Filter F = filter_of(thr);
   float hi_lane = __uint_as_float(kNegInf32);
   bool nan_lane = false;
+  auto hi_key = [&]() { return key_of_bits(__float_as_uint(hi_lane)); };
 
   const uint32_t nb = (L + kBlockElems - 1) / kBlockElems;
   const uint32_t ntl = nb > static_cast<uint32_t>(seg) ? (nb - seg + S - 1) / S : 0u;
@@ -883,11 +893,11 @@ __global__ __launch_bounds__(class_threads(CLS)) void topk_kernel(KArgs a) {
     return uniform(c);
   };
 
-  u32x4 r0[V], r1[V], r2[V], r3[V];   // the ring: loads of 3 blocks in flight
-  uint64_t g = 0;   // shared threshold as read one step earlier
+  u32x4 r0[V], r1[V], r2[V], r3[V];   // the ring
+  u64 g = 0;                          // shared threshold as read one step earlier
 
   auto step = [&](u32x4 (&cur_r)[V], u32x4 (&nxt_r)[V], uint32_t u) {
-    uint64_t g_next = 0;
+    u64 g_next = 0;
     if (MULTI) g_next = load_thr(thr_g);
     if (ntl > 0) load_block<BF16, V, NT>(nxt_r, xrow, blk_at(u + NBUF - 1), L);
     if (u < ntl) {
@@ -897,12 +907,12 @@ __global__ __launch_bounds__(class_threads(CLS)) void topk_kernel(KArgs a) {
         BlockRegs<V> br;
 #pragma unroll
         for (int v = 0; v < V; ++v) br.v[v] = cur_r[v];
-        const uint64_t t0 = block_threshold<BF16, V, NT, CAP>(br, k, sm);
+        const u64 t0 = block_threshold<BF16, V, NT, CAP>(br, k, sm);
         if (t0 > thr) {
           thr = t0;
           F = filter_of(thr);
           if (t == 0) {
-            atomicMax(&sm.thr, static_cast<unsigned long long>(t0));
+            atomicMax(&sm.thr, t0);
             if (MULTI) publish_thr(thr_g, t0);
           }
         }
@@ -913,17 +923,18 @@ __global__ __launch_bounds__(class_threads(CLS)) void topk_kernel(KArgs a) {
 #pragma unroll
         for (int v = 0; v < V; ++v) br.v[v] = cur_r[v];
         after = filter_ragged<BF16, V, NT, CAP>(br, blk, L, F, &hi_lane, &nan_lane, sm, cur);
-      } else
+      } else {
         after = filter_block<BF16, false, V, NT, CAP>(cur_r, blk, L, F, hi_lane, nan_lane, sm, cur);
-      if (MULTI && g > thr && lane == 0) atomicMax(&sm.thr, static_cast<unsigned long long>(g));
+      }
+      if (MULTI && g > thr && lane == 0) atomicMax(&sm.thr, g);
       const uint32_t c = count_after_step(after);
       if (c > trigger) {
-        const uint64_t before = uniform64(sm.thr);
-        cur = cut_buffer<NT, CAP>(sm, cur, k, k + slack, L, hi_lane);
+        const u64 before = uniform64(sm.thr);
+        cur = cut_buffer<NT, CAP>(sm, cur, k, k + slack, L, hi_key());
         thr = uniform64(sm.thr);
         if (MULTI && t == 0 && thr > before) publish_thr(thr_g, thr);
       } else if (MULTI) {
-        const uint64_t seen = uniform64(sm.thr);   // may include a later wave's raise: still a valid bound
+        const u64 seen = uniform64(sm.thr);   // may include a later wave's raise: still a valid bound
         thr = seen > thr ? seen : thr;
       }
       F = filter_of(thr);
@@ -946,21 +957,20 @@ __global__ __launch_bounds__(class_threads(CLS)) void topk_kernel(KArgs a) {
   // NaN anywhere in this workgroup's share of [0, L).
   if (ballot(nan_lane) && lane == 0) atomicOr(&sm.flags, static_cast<uint32_t>(DS_ROW_NAN));
   if (MULTI && t == 0) {
-    const uint64_t gl = load_thr(thr_g);
+    const u64 gl = load_thr(thr_g);
     if (gl > sm.thr) sm.thr = gl;   // survivors at or below the shared bound are not needed
   }
   // Exact local top-k (drops anything at or below the current threshold too).
-  cur = cut_buffer<NT, CAP>(sm, cur, k, k, L, hi_lane);
+  cur = cut_buffer<NT, CAP>(sm, cur, k, k, L, hi_key());
 
   if (MULTI) {
     // Hand the survivors to the row's last workgroup: each workgroup reserves
     // a range of the row's contiguous survivor array with one atomic and fills
     // it.  Every shared word is written and read with agent-scope atomic
-    // accesses (coherent across the XCDs' L2s by themselves), and the stores
-    // are complete before the arrival counter moves, so no L2 write-back or
-    // invalidate is needed.
+    // accesses, and the stores are complete before the arrival counter moves,
+    // so no L2 write-back or invalidate is needed.
     const uint32_t mine = uniform(sm.cnt[cur]);
-    const int64_t row0 = static_cast<int64_t>(row) * S * k;
+    u64* wsc = reinterpret_cast<u64*>(a.ws_comp) + static_cast<int64_t>(row) * S * k;
     if (t == 0) {
       sm.res[0] = mine ? __hip_atomic_fetch_add(&a.ws_fill[row], mine, __ATOMIC_RELAXED,
                                                 __HIP_MEMORY_SCOPE_AGENT)
@@ -971,10 +981,7 @@ __global__ __launch_bounds__(class_threads(CLS)) void topk_kernel(KArgs a) {
     }
     __syncthreads();
     const uint32_t own0 = uniform(sm.res[0]);
-    for (uint32_t j = t; j < mine; j += NT) {
-      st_agent(&a.ws_val[row0 + own0 + j], sm.val[j]);
-      st_agent(&a.ws_idx[row0 + own0 + j], sm.idx[j]);
-    }
+    for (uint32_t j = t; j < mine; j += NT) st_agent(&wsc[own0 + j], sm.comp[j]);
     wait_all_memory();
     __syncthreads();
     if (t == 0) {
@@ -988,94 +995,87 @@ __global__ __launch_bounds__(class_threads(CLS)) void topk_kernel(KArgs a) {
     // Last arrival: merge the other workgroups' survivors (its own are still in
     // LDS, so its own range of the array is skipped).
     if (t == 0) {
-      const uint64_t gfin = load_thr(thr_g);
+      const u64 gfin = load_thr(thr_g);
       if (gfin > sm.thr) sm.thr = gfin;
       sm.flags |= ld_agent(&a.ws_flags[row]);
       sm.res[1] = ld_agent(&a.ws_fill[row]);
     }
     __syncthreads();
     const uint32_t total = uniform(sm.res[1]);
-    thr = uniform64(sm.thr);
-    F = filter_of(thr);
+    const u64 T0 = uniform64(sm.thr);
     constexpr int PER = kBlockElems / (2 * NT);
     constexpr uint32_t CHUNK = PER * NT;
     // Loads of one chunk; positions past the end read position 0 (a valid
     // address) and are dropped.  Every position read is cleared, so the
     // workspace is all zero again when the call ends.
-    auto load_chunk = [&](uint32_t c0, uint32_t (&mv)[PER], uint32_t (&mi)[PER]) {
+    auto load_chunk = [&](uint32_t c0, u64 (&mv)[PER]) {
 #pragma unroll
       for (int q = 0; q < PER; ++q) {
         const uint32_t p = c0 + t + q * NT;
-        const int64_t addr = row0 + (p < total ? p : 0u);
-        mv[q] = ld_agent(&a.ws_val[addr]);
-        mi[q] = ld_agent(&a.ws_idx[addr]);
+        mv[q] = ld_agent(&wsc[p < total ? p : 0u]);
       }
     };
     auto clear_chunk = [&](uint32_t c0) {
 #pragma unroll
       for (int q = 0; q < PER; ++q) {
         const uint32_t p = c0 + t + q * NT;
-        if (p < total) {
-          st_agent(&a.ws_val[row0 + p], 0u);
-          st_agent(&a.ws_idx[row0 + p], 0u);
-        }
+        if (p < total) st_agent(&wsc[p], 0ull);
       }
     };
-    auto merge_chunk = [&](uint32_t c0, const uint32_t (&mv)[PER], const uint32_t (&mi)[PER]) {
+    u64 Tm = T0;
+    auto merge_chunk = [&](uint32_t c0, const u64 (&mv)[PER]) {
       auto pass = [&](int q) -> bool {
         const uint32_t p = c0 + t + q * NT;
-        const float fv = __uint_as_float(mv[q]);
-        return p < total && (p < own0 || p >= own0 + mine) &&
-               (fv > F.f || (fv == F.f && mi[q] < F.idx_lim));
+        return p < total && (p < own0 || p >= own0 + mine) && mv[q] > Tm;
       };
-      uint32_t tot = 0;
+      uint32_t tot = 0, kmax = 0;
 #pragma unroll
       for (int q = 0; q < PER; ++q) {
         const bool p = pass(q);
-        if (p) hi_lane = fmaxf(hi_lane, __uint_as_float(mv[q]));
+        kmax = p && key_of(mv[q]) > kmax ? key_of(mv[q]) : kmax;
         tot += static_cast<uint32_t>(__popcll(ballot(p)));
       }
       uint32_t after = 0;
       if (tot) {
+        const uint32_t wk = wave_max(kmax);
         uint32_t base = 0;
-        if (lane == 0) base = atomicAdd(&sm.cnt[cur], tot);
+        if (lane == 0) {
+          atomicMax(&sm.hikey, wk);
+          base = atomicAdd(&sm.cnt[cur], tot);
+        }
         base = uniform(base);
         after = base + tot;
 #pragma unroll
         for (int q = 0; q < PER; ++q) {
           const bool p = pass(q);
-          const uint64_t mm = ballot(p);
-          if (p) {
-            const uint32_t pos = base + mbcnt64(mm);
-            sm.val[pos] = mv[q];
-            sm.idx[pos] = mi[q];
-          }
+          const u64 mm = ballot(p);
+          if (p) sm.comp[base + mbcnt64(mm)] = mv[q];
           base += static_cast<uint32_t>(__popcll(mm));
         }
       }
       if (count_after_step(after) > trigger) {
-        cur = cut_buffer<NT, CAP>(sm, cur, k, k + slack, L, hi_lane);
-        F = filter_of(uniform64(sm.thr));
+        cur = cut_buffer<NT, CAP>(sm, cur, k, k + slack, L, hi_key());
+        Tm = uniform64(sm.thr);
       }
     };
-    uint32_t va[PER], ia[PER], vb[PER], ib[PER];
-    if (total > 0) load_chunk(0, va, ia);
+    u64 va[PER], vb[PER];
+    if (total > 0) load_chunk(0, va);
     for (uint32_t c0 = 0; c0 < total; c0 += 2 * CHUNK) {
-      load_chunk(c0 + CHUNK, vb, ib);
-      merge_chunk(c0, va, ia);
+      load_chunk(c0 + CHUNK, vb);
+      merge_chunk(c0, va);
       clear_chunk(c0);
-      load_chunk(c0 + 2 * CHUNK, va, ia);
+      load_chunk(c0 + 2 * CHUNK, va);
       if (c0 + CHUNK < total) {
-        merge_chunk(c0 + CHUNK, vb, ib);
+        merge_chunk(c0 + CHUNK, vb);
         clear_chunk(c0 + CHUNK);
       }
     }
-    cur = cut_buffer<NT, CAP>(sm, cur, k, k, L, hi_lane);
+    cur = cut_buffer<NT, CAP>(sm, cur, k, k, L, hi_key());
     if (t == 0) {
       st_agent(&a.ws_done[row], 0u);
       st_agent(&a.ws_flags[row], 0u);
       st_agent(&a.ws_fill[row], 0u);
-      __hip_atomic_store(&a.ws_thr[row], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      st_agent(thr_g, 0ull);
     }
   }
 
@@ -1094,9 +1094,8 @@ WsLayout ws_layout(int64_t batch, int segments, int k) {
   l.done = up(l.thr + b * 8);
   l.flags = up(l.done + b * 4);
   l.fill = up(l.flags + b * 4);
-  l.val = up(l.fill + b * 4);
-  l.idx = up(l.val + b * s * static_cast<size_t>(k) * 4);
-  l.total = up(l.idx + b * s * static_cast<size_t>(k) * 4);
+  l.comp = up(l.fill + b * 4);
+  l.total = up(l.comp + b * s * static_cast<size_t>(k) * 8);
   return l;
 }
 
