@@ -15,6 +15,11 @@ roofline     the kernel's own average duration from HIP events around every
 cpu_baseline the CPU oracle (full stable sort per row) on the host cores.
 
   python bench.py [--steps K] [--warmup W] [--config N] [--no-cpu]
+  python bench.py --calibrate-copy ...        also run a plain 256 MiB copy first
+                                              (the counter calibration kernel)
+  python bench.py --traffic-from FETCH_DIR WRITE_DIR [--config N]
+                                              write profiles/traffic.json from two
+                                              rocprofv3 --pmc runs (no GPU needed)
 """
 from __future__ import annotations
 
@@ -32,7 +37,10 @@ sys.path.insert(0, ROOT)
 METRIC = "effective HBM GB/s and µs/call for row-wise TopK (bf16 k=512, fp32 k=1024)"
 HBM_PEAK_GBPS = 8000.0
 MALL_BYTES = 256 << 20
-KERNEL_SRC = os.path.join(ROOT, "row_wise_topk_amd", "csrc", "topk_kernels.hip")
+KERNEL_SRCS = [os.path.join(ROOT, "row_wise_topk_amd", "csrc", f)
+               for f in ("topk_kernels.hip", "topk_api.cpp", "topk_internal.h")]
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+COPY_ELEMS = 64 << 20          # calibration copy: 64 Mi fp32 = 256 MiB read, 256 MiB written
 
 
 def _parse():
@@ -44,20 +52,26 @@ def _parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--no-torch", action="store_true", help="skip the torch.topk context timing")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="run a plain elementwise copy of known size before the TopK calls")
+    p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                   help="summarise two rocprofv3 --pmc output folders into profiles/traffic.json")
     return p.parse_args()
 
 
 def _kernel_hash() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in KERNEL_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def _traffic(workload_name: str):
     """Per-launch HBM bytes from the committed counter summary, if current."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
-    if not os.path.exists(path):
+    if not os.path.exists(TRAFFIC_JSON):
         return None
     try:
-        data = json.load(open(path))
+        data = json.load(open(TRAFFIC_JSON))
         rec = data.get(workload_name)
         if not rec or rec.get("kernel_sha256_16") != _kernel_hash():
             return None
@@ -66,8 +80,67 @@ def _traffic(workload_name: str):
         return None
 
 
+def _pmc_rows(folder: str, counter: str):
+    """(kernel name, value in KiB) for every dispatch in a rocprofv3 --pmc CSV."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no *counter_collection.csv under {folder}")
+    rows = []
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            if r.get("Counter_Name") == counter:
+                rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    return rows
+
+
+def _write_traffic(args):
+    """FETCH_SIZE / WRITE_SIZE per TopK launch, scaled by the copy kernel's reading."""
+    import workloads
+    w = workloads.workload(args.config)
+    copy_bytes = COPY_ELEMS * 4
+    out = {}
+    for counter, folder in (("FETCH_SIZE", args.traffic_from[0]), ("WRITE_SIZE", args.traffic_from[1])):
+        rows = _pmc_rows(folder, counter)
+        cp = [v for n, v in rows if "neg" in n.lower()]
+        tk = [v for n, v in rows if "topk_kernel" in n]
+        if not cp or not tk:
+            raise SystemExit(f"{counter}: copy dispatches {len(cp)}, topk dispatches {len(tk)}")
+        cp_kib = sorted(cp)[len(cp) // 2]
+        tk_kib = sum(tk) / len(tk)
+        factor = copy_bytes / (cp_kib * 1024.0)
+        out[counter] = {"topk_kib_per_dispatch": round(tk_kib, 1), "topk_dispatches": len(tk),
+                        "copy_kib_per_dispatch": round(cp_kib, 1), "copy_bytes": copy_bytes,
+                        "scale": round(factor, 4), "bytes_per_launch": int(tk_kib * 1024.0 * factor)}
+    data = json.load(open(TRAFFIC_JSON)) if os.path.exists(TRAFFIC_JSON) else {}
+    fetch, write = out["FETCH_SIZE"]["bytes_per_launch"], out["WRITE_SIZE"]["bytes_per_launch"]
+    data[w.name] = {
+        "kernel_sha256_16": _kernel_hash(),
+        "bytes_per_launch": fetch + write,
+        "fetch_bytes": fetch,
+        "write_bytes": write,
+        "algorithmic_input_bytes": workloads.algorithmic_bytes(w, workloads.end_ramp(w.batch, w.n_cols) if w.ragged else None),
+        "output_bytes": workloads.output_bytes(w),
+        "counters": out,
+        "commands": [
+            f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d <FETCH_DIR> -- python3 bench.py --config {w.num} --steps 5 --warmup 2 --no-cpu --no-torch --calibrate-copy",
+            f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d <WRITE_DIR> -- python3 bench.py --config {w.num} --steps 5 --warmup 2 --no-cpu --no-torch --calibrate-copy",
+            f"python3 bench.py --config {w.num} --traffic-from <FETCH_DIR> <WRITE_DIR>",
+        ],
+    }
+    os.makedirs(os.path.dirname(TRAFFIC_JSON), exist_ok=True)
+    with open(TRAFFIC_JSON, "w") as f:
+        json.dump(data, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps(data[w.name]))
+
+
 def main():
     args = _parse()
+    if args.traffic_from:
+        _write_traffic(args)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(rows shard across GPUs without any exchange; see the design notes).",
@@ -107,6 +180,14 @@ def main():
     def call(i):
         rt.topk(views[i % n_copies], w.k, end=end_t, sorted=w.sorted,
                 return_values=w.return_values, index_dtype=it, out=out)
+
+    if args.calibrate_copy:
+        src = torch.ones(COPY_ELEMS, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     for i in range(args.warmup):
         call(i)

@@ -31,6 +31,10 @@
 //   * sorted: 1 = by value (the order above), 2 = by index ascending (the
 //     pages' sorted_index), 0 = any order -- the oracle emits index order;
 //   * values are bit copies of the selected inputs.
+// The padding values, the NaN-row fill and the status codes are this
+// library's own conventions, not fixed by any page: parity unpinned for those
+// three (the tests check them only as closed forms).  Everything else is
+// pinned by brute force, library routines, hand-derived cases and invariants.
 //
 // bf16 inputs are widened exactly (the 16 bits become the top half of an
 // fp32); every comparison is done on doubles, which is exact for both dtypes.

@@ -1,4 +1,4 @@
-// Internal interface between the host API (topk_api.hip) and the kernels
+// Internal interface between the host API (topk_api.cpp) and the kernels
 // (topk_kernels.hip).  Not installed; not part of the C ABI.
 #pragma once
 
@@ -23,7 +23,7 @@ constexpr int class_b2(int c) { return c == 0 ? 1024 : c == 1 ? 3072 : class_kma
 // Buffer capacity: k + B2 candidates plus one whole block admitted at once.
 constexpr int class_cap(int c) { return class_kmax(c) + class_b2(c) + kBlockElems; }
 constexpr int class_trigger(int c) { return class_cap(c) - kBlockElems; }
-// LDS bytes per workgroup (value + index arrays, histogram, scalars).
+// LDS bytes per workgroup (candidate composites, histogram, scalars).
 constexpr int class_lds_bytes(int c) { return class_cap(c) * 8 + 2048 * 4 + 1536; }
 constexpr int class_wgs_per_cu(int c) {
   return (160 * 1024) / class_lds_bytes(c) > 0 ? (160 * 1024) / class_lds_bytes(c) : 1;

@@ -364,8 +364,15 @@ __device__ __forceinline__ void read_group(const Smem<CAP, NT>& sm, int e0, uint
 #pragma unroll
   for (int g = 0; g < kGroup; ++g) {
     const uint32_t i = threadIdx.x + (e0 + g) * NT;
-    const u64 x = sm.comp[i < CAP ? i : CAP - 1];
-    v[g] = i < c ? x : 0ull;
+    v[g] = sm.comp[i < CAP ? i : CAP - 1];
+  }
+  // All reads are issued before any result is used; without this fence the
+  // scheduler can give every read the same destination and wait for each.
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int g = 0; g < kGroup; ++g) {
+    const uint32_t i = threadIdx.x + (e0 + g) * NT;
+    v[g] = i < c ? v[g] : 0ull;
   }
 }
 
