@@ -557,13 +557,18 @@ __device__ __forceinline__ uint32_t filter_block(const u32x4 (&r)[V], uint32_t b
   hi_lane = fmaxf(hi_lane, mx);
   if (!ballot(mx >= F.f)) return 0u;
 
-  const bool exact = F.idx_lim != 0xFFFFFFFFu;
+  // Branch-free admission test (with idx_lim = ~0u it is simply f >= F.f;
+  // a NaN never passes), one wave mask per element, computed once.
   auto pass = [&](int s) -> bool {
-    return exact ? (f[s] > F.f || (f[s] == F.f && col(s) < F.idx_lim)) : f[s] >= F.f;
+    return (f[s] > F.f) | ((f[s] == F.f) & (col(s) < F.idx_lim));
   };
+  u64 m[NS];
   uint32_t total = 0;
 #pragma unroll
-  for (int s = 0; s < NS; ++s) total += static_cast<uint32_t>(__popcll(ballot(pass(s))));
+  for (int s = 0; s < NS; ++s) {
+    m[s] = ballot(pass(s));
+    total += static_cast<uint32_t>(__popcll(m[s]));
+  }
   if (total == 0) return 0u;
   uint32_t base = 0;
   if (lane == 0) base = atomicAdd(&sm.cnt[cur], total);
@@ -571,10 +576,9 @@ __device__ __forceinline__ uint32_t filter_block(const u32x4 (&r)[V], uint32_t b
   const uint32_t after = base + total;
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    const bool p = pass(s);
-    const u64 m = ballot(p);
-    if (p) sm.comp[base + mbcnt64(m)] = comp_of(key_of_bits(__float_as_uint(f[s])), col(s));
-    base += static_cast<uint32_t>(__popcll(m));
+    if ((m[s] >> lane) & 1ull)
+      sm.comp[base + mbcnt64(m[s])] = comp_of(key_of_bits(__float_as_uint(f[s])), col(s));
+    base += static_cast<uint32_t>(__popcll(m[s]));
   }
   return after;
 }
@@ -584,18 +588,24 @@ struct BlockRegs {
   u32x4 v[V];
 };
 
+struct RaggedResult {
+  uint32_t after;
+  float hi_lane;
+  uint32_t nan_lane;
+};
+
 // The row's last, partial block: the same filter with every column checked
-// against L.  Out of line (once per row), block passed by value.
+// against L.  Out of line (once per row); everything goes in and out by value,
+// so the caller's running maximum and NaN flag stay in registers (an address
+// taken would put them in scratch memory, whose loads share the counter of
+// the block loads in flight).
 template <bool BF16, int V, int NT, int CAP>
-__device__ __noinline__ uint32_t filter_ragged(BlockRegs<V> r, uint32_t blk, uint32_t L,
-                                               Filter F, float* hi_lane, bool* nan_lane,
-                                               Smem<CAP, NT>& sm, int cur) {
-  float hl = *hi_lane;
-  bool nl = *nan_lane;
-  const uint32_t after = filter_block<BF16, true, V, NT, CAP>(r.v, blk, L, F, hl, nl, sm, cur);
-  *hi_lane = hl;
-  *nan_lane = nl;
-  return after;
+__device__ __noinline__ RaggedResult filter_ragged(BlockRegs<V> r, uint32_t blk, uint32_t L,
+                                                   Filter F, float hi_lane, uint32_t nan_lane,
+                                                   Smem<CAP, NT>& sm, int cur) {
+  bool nl = nan_lane != 0;
+  const uint32_t after = filter_block<BF16, true, V, NT, CAP>(r.v, blk, L, F, hi_lane, nl, sm, cur);
+  return {after, hi_lane, nl ? 1u : 0u};
 }
 
 // A starting threshold from one whole block held in registers, before any of
@@ -900,13 +910,21 @@ __global__ __launch_bounds__(class_threads(CLS)) void topk_kernel(KArgs a) {
     return uniform(c);
   };
 
-  u32x4 r0[V], r1[V], r2[V], r3[V];   // the ring
-  u64 g = 0;                          // shared threshold as read one step earlier
+  // The ring: block j goes to r[j % 4], and the shared threshold is read into
+  // g[j % 4] just before block j's loads are issued, so waiting for a block
+  // never waits for a later load.  Steps past the workgroup's last block
+  // still issue loads (the compiler then counts outstanding loads exactly),
+  // but every lane reads the row's first vector, one cache line per wave.
+  u32x4 r0[V], r1[V], r2[V], r3[V];
+  u64 g0 = 0, g1 = 0, g2 = 0, g3 = 0;
+  auto issue = [&](u32x4 (&r)[V], u64& g, uint32_t j) {
+    if (MULTI) g = load_thr(thr_g);
+    load_block<BF16, V, NT>(r, xrow, blk_at(j), j < ntl ? L : 0u);
+  };
 
-  auto step = [&](u32x4 (&cur_r)[V], u32x4 (&nxt_r)[V], uint32_t u) {
-    u64 g_next = 0;
-    if (MULTI) g_next = load_thr(thr_g);
-    if (ntl > 0) load_block<BF16, V, NT>(nxt_r, xrow, blk_at(u + NBUF - 1), L);
+  auto step = [&](u32x4 (&cur_r)[V], u64& g, u32x4 (&nxt_r)[V], u64& g_nxt, uint32_t u) {
+    const u64 g_cur = g;
+    if (ntl > 0) issue(nxt_r, g_nxt, u + NBUF - 1);
     if (u < ntl) {
       const uint32_t blk = blk_at(u);
       if (u == 0 && blk * static_cast<uint32_t>(kBlockElems) + kBlockElems <= L && 2 * k <= kBlockElems) {
@@ -929,13 +947,19 @@ __global__ __launch_bounds__(class_threads(CLS)) void topk_kernel(KArgs a) {
         BlockRegs<V> br;
 #pragma unroll
         for (int v = 0; v < V; ++v) br.v[v] = cur_r[v];
-        after = filter_ragged<BF16, V, NT, CAP>(br, blk, L, F, &hi_lane, &nan_lane, sm, cur);
+        const RaggedResult rr =
+            filter_ragged<BF16, V, NT, CAP>(br, blk, L, F, hi_lane, nan_lane ? 1u : 0u, sm, cur);
+        after = rr.after;
+        hi_lane = rr.hi_lane;
+        nan_lane = rr.nan_lane != 0;
       } else {
         after = filter_block<BF16, false, V, NT, CAP>(cur_r, blk, L, F, hi_lane, nan_lane, sm, cur);
       }
-      if (MULTI && g > thr && lane == 0) atomicMax(&sm.thr, g);
+      if (MULTI && g_cur > thr && lane == 0) atomicMax(&sm.thr, g_cur);
       const uint32_t c = count_after_step(after);
-      if (c > trigger) {
+      // No cut after the last block: the exact cut that follows the stream
+      // takes the buffer as it is (a block never overfills it).
+      if (c > trigger && u + 1 < ntl) {
         const u64 before = uniform64(sm.thr);
         cur = cut_buffer<NT, CAP>(sm, cur, k, k + slack, L, hi_key());
         thr = uniform64(sm.thr);
@@ -946,19 +970,18 @@ __global__ __launch_bounds__(class_threads(CLS)) void topk_kernel(KArgs a) {
       }
       F = filter_of(thr);
     }
-    if (MULTI) g = g_next;
   };
 
   if (ntl > 0) {
-    load_block<BF16, V, NT>(r0, xrow, blk_at(0), L);
-    load_block<BF16, V, NT>(r1, xrow, blk_at(1), L);
-    load_block<BF16, V, NT>(r2, xrow, blk_at(2), L);
+    issue(r0, g0, 0);
+    issue(r1, g1, 1);
+    issue(r2, g2, 2);
   }
   for (uint32_t u = 0; u < ntl; u += NBUF) {
-    step(r0, r3, u);
-    step(r1, r0, u + 1);
-    step(r2, r1, u + 2);
-    step(r3, r2, u + 3);
+    step(r0, g0, r3, g3, u);
+    step(r1, g1, r0, g0, u + 1);
+    step(r2, g2, r1, g1, u + 2);
+    step(r3, g3, r2, g2, u + 3);
   }
 
   // NaN anywhere in this workgroup's share of [0, L).
