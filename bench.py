@@ -52,6 +52,8 @@ def _parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--no-torch", action="store_true", help="skip the torch.topk context timing")
+    p.add_argument("--segments", type=int, default=0,
+                   help="workgroups per row (0 = the library's automatic plan)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="run a plain elementwise copy of known size before the TopK calls")
     p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -177,9 +179,11 @@ def main():
     status = torch.empty((w.batch,), dtype=torch.int32, device=dev)
     out = (values, indices, status)
 
+    plan = rt.Plan(segments=args.segments) if args.segments else None
+
     def call(i):
         rt.topk(views[i % n_copies], w.k, end=end_t, sorted=w.sorted,
-                return_values=w.return_values, index_dtype=it, out=out)
+                return_values=w.return_values, index_dtype=it, out=out, plan=plan)
 
     if args.calibrate_copy:
         src = torch.ones(COPY_ELEMS, dtype=torch.float32, device=dev)
@@ -273,7 +277,8 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "n_cols": w.n_cols,
                    "row_stride": w.row_stride, "k": w.k, "sorted": w.sorted,
                    "return_values": w.return_values, "index_dtype": w.index_dtype,
-                   "input_copies": n_copies, "input_sha256": workloads.digest(x_np, end_np)[:16]},
+                   "input_copies": n_copies, "input_sha256": workloads.digest(x_np, end_np)[:16],
+                   "segments": args.segments or "auto"},
         "us_per_call": round(ms_per_step * 1e3, 3),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),

@@ -52,12 +52,13 @@ struct KArgs {
   uint32_t* ws_done;            // [batch]  arrivals per row
   uint32_t* ws_flags;           // [batch]  OR of row status bits
   uint32_t* ws_fill;            // [batch]  survivors written so far per row
+  unsigned long long* ws_x;     // [batch * segments]  per-workgroup merge bound
   unsigned long long* ws_comp;  // [batch * segments * k]  survivor composites, contiguous per row
 };
 
 // Workspace layout for `segments` workgroups per row (bytes, 16-B aligned parts).
 struct WsLayout {
-  size_t thr, done, flags, fill, comp, total;
+  size_t thr, done, flags, fill, x, comp, total;
 };
 WsLayout ws_layout(int64_t batch, int segments, int k);
 

@@ -249,7 +249,7 @@ struct Smem {
   u64 comp[CAP];              // candidate composites
   uint32_t hist[kBins];       // zero whenever not in use
   uint32_t wsum[NT / 64];
-  uint32_t res[4];
+  uint32_t res[5];
   uint32_t cnt[2];            // append counters; cur receives appends, cur^1 the next cut
   uint32_t snap[2][NT / 64];  // per-wave count after its last append, by step parity
   uint32_t segoff[kMaxSegments];  // epilogue sort: pending segments (start | region, end)
@@ -257,15 +257,19 @@ struct Smem {
   uint32_t flags;             // row status bits
   uint32_t is_last;
   uint32_t nwork;             // epilogue sort: number of pending segments
+  uint32_t nside;             // cut: members of a small boundary bin
   u64 rng[2];                 // epilogue sort: min / max order key of a segment
   u64 thr;                    // the workgroup's threshold (composite)
+  u64 xv;                     // a cut's second answer: a bound with >= need2 candidates above
 };
 
 // Suffix search over hist (higher bins first), which it leaves zeroed.  Finds
 // b* with  sum_{b > b*} hist[b] < need <= sum_{b >= b*} hist[b].
 // res = {b*, sum above b*, hist[b*], total}; res[0] = kBins when total < need.
+// With need2 > 0 the same search for need2 goes to res[4] (kBins if none).
 template <int NT, int CAP>
-__device__ __forceinline__ void hist_find_top(Smem<CAP, NT>& sm, uint32_t need) {
+__device__ __forceinline__ void hist_find_top(Smem<CAP, NT>& sm, uint32_t need,
+                                              uint32_t need2 = 0) {
   constexpr int BPT = kBins / NT;
   constexpr int NW = NT / 64;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
@@ -279,7 +283,10 @@ __device__ __forceinline__ void hist_find_top(Smem<CAP, NT>& sm, uint32_t need) 
   }
   const uint32_t p = wave_prefix_sum(s);   // inclusive, within the wave
   if (lane == 63) sm.wsum[w] = p;
-  if (t == 0) sm.res[0] = kBins;
+  if (t == 0) {
+    sm.res[0] = kBins;
+    sm.res[4] = kBins;
+  }
   __syncthreads();
   uint32_t before = 0, tot = 0;
 #pragma unroll
@@ -298,6 +305,17 @@ __device__ __forceinline__ void hist_find_top(Smem<CAP, NT>& sm, uint32_t need) 
         sm.res[0] = t * BPT + i;
         sm.res[1] = acc;
         sm.res[2] = h[i];
+        break;
+      }
+      acc += h[i];
+    }
+  }
+  if (need2 != 0 && excl_above < need2 && need2 <= incl_above) {
+    uint32_t acc = excl_above;
+#pragma unroll
+    for (int i = BPT - 1; i >= 0; --i) {
+      if (acc + h[i] >= need2) {
+        sm.res[4] = t * BPT + i;
         break;
       }
       acc += h[i];
@@ -394,7 +412,7 @@ __device__ __noinline__ uint32_t index_cut(Smem<CAP, NT>& sm, uint32_t c, uint32
 #pragma unroll
       for (int g = 0; g < kGroup; ++g) {
         const uint32_t ci = col_of(v[g]) - ibase;
-        if (key_of(v[g]) == E_key && ci <= itop - ibase && v[g] > T)
+        if ((key_of(v[g]) == E_key) & (ci <= itop - ibase) & (v[g] > T))
           atomicAdd(&sm.hist[(kBins - 1) - (ci >> shift)], 1u);
       }
     }
@@ -415,9 +433,12 @@ __device__ __noinline__ uint32_t index_cut(Smem<CAP, NT>& sm, uint32_t c, uint32
 // T_new >= sm.thr leaves between k and keep_max candidates (or all of them if
 // no more than keep_max are above sm.thr).  keep_max == k gives the exact
 // top-k.  Returns the new append counter index.
+// With need2 > 0 it also leaves in sm.xv a composite with at least need2 of
+// the candidates above it (0 if there are fewer than need2 above sm.thr).
 template <int NT, int CAP>
 __device__ __noinline__ int cut_buffer(Smem<CAP, NT>& sm, int cur, uint32_t k,
-                                       uint32_t keep_max, uint32_t n_cols, uint32_t hi_key) {
+                                       uint32_t keep_max, uint32_t n_cols, uint32_t hi_key,
+                                       uint32_t need2 = 0) {
   constexpr int E = slots_per_thread<NT, CAP>();
   const int t = threadIdx.x, lane = t & 63;
   const uint32_t hk = wave_max(hi_key);
@@ -432,6 +453,13 @@ __device__ __noinline__ int cut_buffer(Smem<CAP, NT>& sm, int cur, uint32_t k,
   const uint32_t klo = key_only ? K + 1u : K;
 
   u64 newT = T;
+  u64 xv = 0;
+  // Small boundary bin: its members (composite in (sb_lo, newT]) are
+  // collected during the compaction and ranked exactly; the sb_need-th
+  // largest of them is the last one kept.
+  bool small = false;
+  u64 sb_lo = 0;
+  uint32_t sb_need = 0;
   if (hi >= klo && c > 0) {
     uint32_t need = k, above = 0, base = klo, top = hi;
     bool first = true;
@@ -453,23 +481,40 @@ __device__ __noinline__ int cut_buffer(Smem<CAP, NT>& sm, int cur, uint32_t k,
 #pragma unroll
           for (int g = 0; g < kGroup; ++g) {
             const uint32_t d = key_of(v[g]) - base;
-            if (d <= span && v[g] > T) atomicAdd(&sm.hist[d >> shift], 1u);
+            if ((d <= span) & (v[g] > T)) atomicAdd(&sm.hist[d >> shift], 1u);
           }
         }
       }
       __syncthreads();
-      hist_find_top(sm, need);
+      hist_find_top(sm, need, first ? need2 : 0u);
       if (first) {
         first = false;
+        if (need2 != 0) {
+          const uint32_t b2 = uniform(sm.res[4]);
+          if (b2 < static_cast<uint32_t>(kBins)) xv = (static_cast<u64>(base + (b2 << shift)) << 32) - 1u;
+        }
         if (uniform(sm.res[3]) <= keep_max) break;   // few enough above T: only drop those at or below T
       }
       const uint32_t b = uniform(sm.res[0]), ab = uniform(sm.res[1]), bc = uniform(sm.res[2]);
       above += ab;
       need -= ab;
       base += b << shift;
+      const u64 lo_edge = (static_cast<u64>(base) << 32) - 1u;
       if (above + bc <= keep_max) {
-        const u64 cand = (static_cast<u64>(base) << 32) - 1u;
-        newT = cand > T ? cand : T;
+        newT = lo_edge > T ? lo_edge : T;
+        break;
+      }
+      if (bc <= static_cast<uint32_t>(NT)) {
+        // Keys of the bin are [base, ub]: the bin's width, capped at the top
+        // of the range this level divides (keys above it were counted in
+        // higher bins before).  ub + 1 fits in 32 bits for any non-NaN key.
+        // Everything above the bin is kept outright.
+        const uint32_t bin_hi = base + ((1u << shift) - 1u);
+        const uint32_t ub = bin_hi < top ? bin_hi : top;
+        small = true;
+        sb_lo = lo_edge > T ? lo_edge : T;
+        sb_need = need;
+        newT = (static_cast<u64>(ub + 1u) << 32) - 1u;
         break;
       }
       if (shift == 0) {
@@ -485,16 +530,22 @@ __device__ __noinline__ int cut_buffer(Smem<CAP, NT>& sm, int cur, uint32_t k,
   // Compaction into the other counter, one group of slots at a time: all
   // threads read the group, then the kept entries go to positions reserved
   // with one LDS atomic per wave.  The write cursor never passes the number of
-  // positions read so far, so a write never lands on an unread entry.
+  // positions read so far, so a write never lands on an unread entry.  The
+  // members of a small boundary bin go to the (idle, zero) histogram memory.
   const int nxt = cur ^ 1;
+  u64* side = reinterpret_cast<u64*>(sm.hist);
+  if (t == 0) sm.nside = 0u;
 #pragma unroll 1
   for (int e0 = 0; e0 < E; e0 += kGroup) {
     if (static_cast<uint32_t>(e0 * NT) >= c) break;   // uniform
     u64 v[kGroup];
     read_group(sm, e0, c, v);
-    uint32_t total = 0;
+    uint32_t total = 0, nsd = 0;
 #pragma unroll
-    for (int g = 0; g < kGroup; ++g) total += static_cast<uint32_t>(__popcll(ballot(v[g] > newT)));
+    for (int g = 0; g < kGroup; ++g) {
+      total += static_cast<uint32_t>(__popcll(ballot(v[g] > newT)));
+      if (small) nsd += static_cast<uint32_t>(__popcll(ballot((v[g] > sb_lo) & (v[g] <= newT))));
+    }
     __syncthreads();
     if (total) {
       uint32_t base = 0;
@@ -508,8 +559,45 @@ __device__ __noinline__ int cut_buffer(Smem<CAP, NT>& sm, int cur, uint32_t k,
         base += static_cast<uint32_t>(__popcll(m));
       }
     }
+    if (nsd) {
+      uint32_t base = 0;
+      if (lane == 0) base = atomicAdd(&sm.nside, nsd);
+      base = uniform(base);
+#pragma unroll
+      for (int g = 0; g < kGroup; ++g) {
+        const bool in = (v[g] > sb_lo) & (v[g] <= newT);
+        const u64 m = ballot(in);
+        if (in) side[base + mbcnt64(m)] = v[g];
+        base += static_cast<uint32_t>(__popcll(m));
+      }
+    }
   }
-  if (t == 0) sm.thr = newT;
+  if (small) {
+    // Rank the n (<= NT) members: the one with exactly sb_need - 1 larger
+    // members is the last kept (composites are distinct).
+    __syncthreads();
+    const uint32_t n = uniform(sm.nside);
+    const u64 mine = side[t < static_cast<int>(n) ? t : 0];
+    uint32_t r = 0;
+#pragma unroll 4
+    for (uint32_t j = 0; j < n; ++j) r += side[j] > mine ? 1u : 0u;
+    if (t < static_cast<int>(n) && r + 1u == sb_need) sm.rng[0] = mine;
+    __syncthreads();
+    const u64 kth = uniform64(sm.rng[0]);
+    const bool keep = (t < static_cast<int>(n)) & (mine >= kth);
+    const u64 m = ballot(keep);
+    uint32_t base = 0;
+    if (lane == 0 && m) base = atomicAdd(&sm.cnt[nxt], static_cast<uint32_t>(__popcll(m)));
+    base = uniform(base);
+    if (keep) sm.comp[base + mbcnt64(m)] = mine;
+    newT = kth - 1u;
+    __syncthreads();
+    for (uint32_t j = t; j < 2u * n; j += NT) sm.hist[j] = 0u;
+  }
+  if (t == 0) {
+    sm.thr = newT;
+    sm.xv = xv;
+  }
   __syncthreads();
   return nxt;
 }
@@ -544,7 +632,7 @@ __device__ __forceinline__ uint32_t filter_block(const u32x4 (&r)[V], uint32_t b
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       const bool valid = col(s) < L;
-      nan_lane |= valid && (f[s] != f[s]);
+      nan_lane |= valid & (f[s] != f[s]);
       if (!valid) f[s] = __uint_as_float(kQNaN32);
     }
   } else {
@@ -609,68 +697,90 @@ __device__ __noinline__ RaggedResult filter_ragged(BlockRegs<V> r, uint32_t blk,
 }
 
 // A starting threshold from one whole block held in registers, before any of
-// it is appended: an 11-bit histogram of the block's keys over their own range
-// gives a bin edge with at least k of the block's elements at or above it.
-// That edge is a valid (monotone) threshold for the row, so the block and
-// everything after it are filtered against it instead of against -inf, and
-// the buffer never has to hold the whole first block.  Leaves hist zeroed.
+// it is appended.  The block's values are binned linearly between their
+// finite minimum and maximum (2048 bins; -inf and +inf clamp to the end
+// bins, NaN is left out).  Linear bins spread the usual bell-shaped scores
+// over many bins, so the LDS atomics rarely collide, where bins on the key
+// bits would pile most of a binade into a few.  The suffix search finds the
+// bin b* with at least k elements in bins >= b*; since the binning is
+// monotone, the smallest key among those elements is a threshold with at
+// least k of the block's elements at or above it -- a valid (monotone)
+// starting point for the row.  Leaves hist zeroed.
 template <bool BF16, int V, int NT, int CAP>
 __device__ __noinline__ u64 block_threshold(BlockRegs<V> r, uint32_t k, Smem<CAP, NT>& sm) {
   constexpr int EPV = BF16 ? 8 : 4;
   constexpr int NS = V * EPV;
   const int t = threadIdx.x, lane = t & 63;
-  uint32_t key[NS];
-  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+  float f[NS];
 #pragma unroll
   for (int v = 0; v < V; ++v) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const uint32_t w = r.v[v][q];
       if (BF16) {
-        key[v * 8 + 2 * q] = key_of_bits(w << 16);
-        key[v * 8 + 2 * q + 1] = key_of_bits(w & 0xFFFF0000u);
+        f[v * 8 + 2 * q] = __uint_as_float(w << 16);
+        f[v * 8 + 2 * q + 1] = __uint_as_float(w & 0xFFFF0000u);
       } else {
-        key[v * 4 + q] = key_of_bits(w);
+        f[v * 4 + q] = __uint_as_float(w);
       }
     }
   }
-  // NaN keys fall outside [key(-inf), key(+inf)] and are left out
+  // finite range, through the order-preserving keys
+  uint32_t klo = 0xFFFFFFFFu, khi = 0u;
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    const bool ok = key[s] - 0x00800000u <= 0xFF000000u;
-    lo = ok && key[s] < lo ? key[s] : lo;
-    hi = ok && key[s] > hi ? key[s] : hi;
+    const uint32_t key = key_of_bits(__float_as_uint(f[s]));
+    const bool fin = __builtin_fabsf(f[s]) <= 3.402823466e38f;
+    klo = fin & (key < klo) ? key : klo;
+    khi = fin & (key > khi) ? key : khi;
   }
-  lo = wave_min(lo);
-  hi = wave_max(hi);
+  klo = wave_min(klo);
+  khi = wave_max(khi);
   if (t == 0) {
     sm.res[0] = 0xFFFFFFFFu;
     sm.res[1] = 0u;
   }
   __syncthreads();
   if (lane == 0) {
-    atomicMin(&sm.res[0], lo);
-    atomicMax(&sm.res[1], hi);
+    atomicMin(&sm.res[0], klo);
+    atomicMax(&sm.res[1], khi);
   }
   __syncthreads();
-  lo = uniform(sm.res[0]);
-  hi = uniform(sm.res[1]);
-  if (hi < lo) {   // no ordinary value in the block
+  klo = uniform(sm.res[0]);
+  khi = uniform(sm.res[1]);
+  if (khi < klo) {   // no finite value in the block
     __syncthreads();
     return kThrInit;
   }
-  const uint32_t shift = shift_for_span(hi - lo);
-  const uint32_t span = hi - lo;
+  const float lo = __uint_as_float(bits_of_key(klo));
+  const float hi = __uint_as_float(bits_of_key(khi));
+  const float span = hi - lo;   // may be +inf for extreme ranges: then scale 0, one bin
+  const float scale = span > 0.0f ? static_cast<float>(kBins - 1) / span : 0.0f;
+  auto bin_of = [&](float x) -> uint32_t {
+    // fmaxf / fminf drop a NaN product (inf * 0) in favour of the bound
+    const float y = __builtin_fminf(__builtin_fmaxf((x - lo) * scale, 0.0f),
+                                    static_cast<float>(kBins - 1));
+    return static_cast<uint32_t>(y);
+  };
 #pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    const uint32_t d = key[s] - lo;
-    if (d <= span) atomicAdd(&sm.hist[d >> shift], 1u);
-  }
+  for (int s = 0; s < NS; ++s)
+    if (f[s] == f[s]) atomicAdd(&sm.hist[bin_of(f[s])], 1u);
   __syncthreads();
   hist_find_top(sm, k);
   const uint32_t b = uniform(sm.res[0]);
-  if (b >= static_cast<uint32_t>(kBins)) return kThrInit;   // fewer than k ordinary values
-  return (static_cast<u64>(lo + (b << shift)) << 32) - 1u;
+  if (b >= static_cast<uint32_t>(kBins)) return kThrInit;   // fewer than k non-NaN values
+  uint32_t tk = 0xFFFFFFFFu;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const uint32_t key = key_of_bits(__float_as_uint(f[s]));
+    tk = (f[s] == f[s]) & (bin_of(f[s]) >= b) & (key < tk) ? key : tk;
+  }
+  tk = wave_min(tk);
+  if (t == 0) sm.res[2] = 0xFFFFFFFFu;
+  __syncthreads();
+  if (lane == 0) atomicMin(&sm.res[2], tk);
+  __syncthreads();
+  return (static_cast<u64>(uniform(sm.res[2])) << 32) - 1u;
 }
 
 // Loads of one block.  Always issued, whatever the block: a vector that would
@@ -731,8 +841,8 @@ __device__ __noinline__ void sort_results(Smem<CAP, NT>& sm, uint32_t m, bool by
       const uint32_t p = t + j * NT;
       mv[j] = src[p < n ? s + p : s];
       const u64 q = order_key(mv[j]);
-      lo = p < n && q < lo ? q : lo;
-      hi = p < n && q > hi ? q : hi;
+      lo = (p < n) & (q < lo) ? q : lo;
+      hi = (p < n) & (q > hi) ? q : hi;
     }
     lo = wave_extreme64<false>(lo);
     hi = wave_extreme64<true>(hi);
@@ -991,7 +1101,12 @@ __global__ __launch_bounds__(class_threads(CLS)) void topk_kernel(KArgs a) {
     if (gl > sm.thr) sm.thr = gl;   // survivors at or below the shared bound are not needed
   }
   // Exact local top-k (drops anything at or below the current threshold too).
-  cur = cut_buffer<NT, CAP>(sm, cur, k, k, L, hi_key());
+  // With several workgroups on the row, the cut also finds the bound x_seg
+  // with at least ceil(k / S) of this workgroup's survivors above it: the
+  // smallest x_seg over the row then has at least k survivors above it, so
+  // the merge can drop everything at or below it.
+  cur = cut_buffer<NT, CAP>(sm, cur, k, k, L, hi_key(),
+                            MULTI ? (k + static_cast<uint32_t>(S) - 1u) / static_cast<uint32_t>(S) : 0u);
 
   if (MULTI) {
     // Hand the survivors to the row's last workgroup: each workgroup reserves
@@ -1006,6 +1121,7 @@ __global__ __launch_bounds__(class_threads(CLS)) void topk_kernel(KArgs a) {
                                                 __HIP_MEMORY_SCOPE_AGENT)
                        : 0u;
       if (mine >= k) publish_thr(thr_g, sm.thr);
+      st_agent(&a.ws_x[static_cast<int64_t>(row) * S + seg], sm.xv);
       if (sm.flags)
         __hip_atomic_fetch_or(&a.ws_flags[row], sm.flags, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -1023,17 +1139,31 @@ __global__ __launch_bounds__(class_threads(CLS)) void topk_kernel(KArgs a) {
     if (!uniform(sm.is_last)) return;
 
     // Last arrival: merge the other workgroups' survivors (its own are still in
-    // LDS, so its own range of the array is skipped).
+    // LDS, so its own range of the array is skipped).  Start from the largest
+    // of the shared threshold and min_seg x_seg (0 if any workgroup had fewer
+    // than ceil(k / S) survivors).
+    u64 xs = ~0ull;
+    if (t < S) {
+      u64* xp = &a.ws_x[static_cast<int64_t>(row) * S + t];
+      xs = ld_agent(xp);
+      st_agent(xp, 0ull);
+    }
+    xs = wave_extreme64<false>(xs);
     if (t == 0) {
+      sm.rng[0] = ~0ull;
       const u64 gfin = load_thr(thr_g);
       if (gfin > sm.thr) sm.thr = gfin;
       sm.flags |= ld_agent(&a.ws_flags[row]);
       sm.res[1] = ld_agent(&a.ws_fill[row]);
     }
     __syncthreads();
+    if (lane == 0) atomicMin(&sm.rng[0], xs);
+    __syncthreads();
+    if (t == 0 && sm.rng[0] > sm.thr) sm.thr = sm.rng[0];
+    __syncthreads();
     const uint32_t total = uniform(sm.res[1]);
     const u64 T0 = uniform64(sm.thr);
-    constexpr int PER = kBlockElems / (2 * NT);
+    constexpr int PER = kBlockElems / NT;
     constexpr uint32_t CHUNK = PER * NT;
     // Loads of one chunk; positions past the end read position 0 (a valid
     // address) and are dropped.  Every position read is cleared, so the
@@ -1056,14 +1186,17 @@ __global__ __launch_bounds__(class_threads(CLS)) void topk_kernel(KArgs a) {
     auto merge_chunk = [&](uint32_t c0, const u64 (&mv)[PER]) {
       auto pass = [&](int q) -> bool {
         const uint32_t p = c0 + t + q * NT;
-        return p < total && (p < own0 || p >= own0 + mine) && mv[q] > Tm;
+        return (p < total) & ((p < own0) | (p >= own0 + mine)) & (mv[q] > Tm);
       };
+      u64 mm[PER];
       uint32_t tot = 0, kmax = 0;
 #pragma unroll
       for (int q = 0; q < PER; ++q) {
         const bool p = pass(q);
-        kmax = p && key_of(mv[q]) > kmax ? key_of(mv[q]) : kmax;
-        tot += static_cast<uint32_t>(__popcll(ballot(p)));
+        const uint32_t kq = p ? key_of(mv[q]) : 0u;
+        kmax = kq > kmax ? kq : kmax;
+        mm[q] = ballot(p);
+        tot += static_cast<uint32_t>(__popcll(mm[q]));
       }
       uint32_t after = 0;
       if (tot) {
@@ -1077,10 +1210,8 @@ __global__ __launch_bounds__(class_threads(CLS)) void topk_kernel(KArgs a) {
         after = base + tot;
 #pragma unroll
         for (int q = 0; q < PER; ++q) {
-          const bool p = pass(q);
-          const u64 mm = ballot(p);
-          if (p) sm.comp[base + mbcnt64(mm)] = mv[q];
-          base += static_cast<uint32_t>(__popcll(mm));
+          if ((mm[q] >> lane) & 1ull) sm.comp[base + mbcnt64(mm[q])] = mv[q];
+          base += static_cast<uint32_t>(__popcll(mm[q]));
         }
       }
       if (count_after_step(after) > trigger) {
@@ -1124,7 +1255,8 @@ WsLayout ws_layout(int64_t batch, int segments, int k) {
   l.done = up(l.thr + b * 8);
   l.flags = up(l.done + b * 4);
   l.fill = up(l.flags + b * 4);
-  l.comp = up(l.fill + b * 4);
+  l.x = up(l.fill + b * 4);
+  l.comp = up(l.x + b * s * 8);
   l.total = up(l.comp + b * s * static_cast<size_t>(k) * 8);
   return l;
 }
