@@ -252,7 +252,7 @@ struct Smem {
   uint32_t res[5];
   uint32_t cnt[2];            // append counters; cur receives appends, cur^1 the next cut
   uint32_t snap[2][NT / 64];  // per-wave count after its last append, by step parity
-  uint32_t segoff[kMaxSegments];  // epilogue sort: pending segments (start | region, end)
+  uint32_t segoff[4 * 128];   // epilogue sort: pending segments (4 words each)
   uint32_t hikey;             // upper bound of every candidate key
   uint32_t flags;             // row status bits
   uint32_t is_last;
@@ -429,6 +429,105 @@ __device__ __noinline__ uint32_t index_cut(Smem<CAP, NT>& sm, uint32_t c, uint32
   }
 }
 
+// Compaction into counter `nxt`, one group of slots at a time: all threads
+// read the group, then the kept entries (composite > keep_above) go to
+// positions reserved with one LDS atomic per wave.  The write cursor never
+// passes the number of positions read so far, so a write never lands on an
+// unread entry.  With SIDE, the members of a small boundary bin
+// (side_lo < composite <= keep_above) go to the idle, zero histogram memory,
+// counted in sm.nside.
+template <int NT, int CAP, bool SIDE>
+__device__ __forceinline__ void compact_buffer(Smem<CAP, NT>& sm, uint32_t c, int nxt,
+                                               u64 keep_above, u64 side_lo) {
+  constexpr int E = slots_per_thread<NT, CAP>();
+  const int lane = threadIdx.x & 63;
+  u64* side = reinterpret_cast<u64*>(sm.hist);
+  if (SIDE && threadIdx.x == 0) sm.nside = 0u;
+#pragma unroll 1
+  for (int e0 = 0; e0 < E; e0 += kGroup) {
+    if (static_cast<uint32_t>(e0 * NT) >= c) break;   // uniform
+    u64 v[kGroup];
+    read_group(sm, e0, c, v);
+    u64 mk[kGroup], ms[kGroup];
+    uint32_t total = 0, nsd = 0;
+#pragma unroll
+    for (int g = 0; g < kGroup; ++g) {
+      mk[g] = ballot(v[g] > keep_above);
+      total += static_cast<uint32_t>(__popcll(mk[g]));
+      if (SIDE) {
+        ms[g] = ballot((v[g] > side_lo) & (v[g] <= keep_above));
+        nsd += static_cast<uint32_t>(__popcll(ms[g]));
+      }
+    }
+    __syncthreads();
+    if (total) {
+      uint32_t base = 0;
+      if (lane == 0) base = atomicAdd(&sm.cnt[nxt], total);
+      base = uniform(base);
+#pragma unroll
+      for (int g = 0; g < kGroup; ++g) {
+        if ((mk[g] >> lane) & 1ull) sm.comp[base + mbcnt64(mk[g])] = v[g];
+        base += static_cast<uint32_t>(__popcll(mk[g]));
+      }
+    }
+    if (SIDE && nsd) {
+      uint32_t base = 0;
+      if (lane == 0) base = atomicAdd(&sm.nside, nsd);
+      base = uniform(base);
+#pragma unroll
+      for (int g = 0; g < kGroup; ++g) {
+        if ((ms[g] >> lane) & 1ull) side[base + mbcnt64(ms[g])] = v[g];
+        base += static_cast<uint32_t>(__popcll(ms[g]));
+      }
+    }
+  }
+}
+
+constexpr uint32_t kSmallBin = 64;   // largest boundary bin ranked directly
+
+// The n = sm.nside (<= kSmallBin) members of a small boundary bin sit in the
+// histogram memory as composites.  Each wave counts, for every member, how
+// many members of its share are larger; the member with exactly need - 1
+// larger members is the last one kept (composites are distinct).  Kept
+// members are appended to counter `nxt`.  Returns the new threshold and
+// leaves the histogram memory zeroed.
+template <int NT, int CAP>
+__device__ __noinline__ u64 resolve_small_bin(Smem<CAP, NT>& sm, int nxt, uint32_t need) {
+  constexpr int NW = NT / 64;
+  constexpr uint32_t PART = (kSmallBin + NW - 1) / NW;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  u64* side = reinterpret_cast<u64*>(sm.hist);
+  uint32_t* rank = sm.hist + 2 * kSmallBin;   // kSmallBin counters, zero
+  __syncthreads();
+  const uint32_t n = uniform(sm.nside);
+  const u64 mine = side[static_cast<uint32_t>(lane) < n ? lane : 0];
+  u64 other[PART];
+#pragma unroll
+  for (uint32_t j = 0; j < PART; ++j) {
+    const uint32_t q = w * PART + j;
+    other[j] = side[q < n ? q : 0];
+  }
+  uint32_t r = 0;
+#pragma unroll
+  for (uint32_t j = 0; j < PART; ++j) r += ((w * PART + j < n) & (other[j] > mine)) ? 1u : 0u;
+  if (static_cast<uint32_t>(lane) < n && r) atomicAdd(&rank[lane], r);
+  __syncthreads();
+  if (w == 0 && static_cast<uint32_t>(lane) < n && rank[lane] + 1u == need) sm.rng[0] = mine;
+  __syncthreads();
+  const u64 kth = uniform64(sm.rng[0]);
+  if (w == 0) {
+    const bool keep = (static_cast<uint32_t>(lane) < n) & (mine >= kth);
+    const u64 m = ballot(keep);
+    uint32_t base = 0;
+    if (lane == 0 && m) base = atomicAdd(&sm.cnt[nxt], static_cast<uint32_t>(__popcll(m)));
+    base = uniform(base);
+    if (keep) sm.comp[base + mbcnt64(m)] = mine;
+  }
+  __syncthreads();
+  for (uint32_t j = t; j < 3 * kSmallBin; j += NT) sm.hist[j] = 0u;
+  return kth - 1u;
+}
+
 // Cut the candidate buffer: keep every candidate with composite > T_new, where
 // T_new >= sm.thr leaves between k and keep_max candidates (or all of them if
 // no more than keep_max are above sm.thr).  keep_max == k gives the exact
@@ -504,7 +603,7 @@ __device__ __noinline__ int cut_buffer(Smem<CAP, NT>& sm, int cur, uint32_t k,
         newT = lo_edge > T ? lo_edge : T;
         break;
       }
-      if (bc <= static_cast<uint32_t>(NT)) {
+      if (bc <= kSmallBin) {
         // Keys of the bin are [base, ub]: the bin's width, capped at the top
         // of the range this level divides (keys above it were counted in
         // higher bins before).  ub + 1 fits in 32 bits for any non-NaN key.
@@ -527,72 +626,12 @@ __device__ __noinline__ int cut_buffer(Smem<CAP, NT>& sm, int cur, uint32_t k,
     }
   }
 
-  // Compaction into the other counter, one group of slots at a time: all
-  // threads read the group, then the kept entries go to positions reserved
-  // with one LDS atomic per wave.  The write cursor never passes the number of
-  // positions read so far, so a write never lands on an unread entry.  The
-  // members of a small boundary bin go to the (idle, zero) histogram memory.
   const int nxt = cur ^ 1;
-  u64* side = reinterpret_cast<u64*>(sm.hist);
-  if (t == 0) sm.nside = 0u;
-#pragma unroll 1
-  for (int e0 = 0; e0 < E; e0 += kGroup) {
-    if (static_cast<uint32_t>(e0 * NT) >= c) break;   // uniform
-    u64 v[kGroup];
-    read_group(sm, e0, c, v);
-    uint32_t total = 0, nsd = 0;
-#pragma unroll
-    for (int g = 0; g < kGroup; ++g) {
-      total += static_cast<uint32_t>(__popcll(ballot(v[g] > newT)));
-      if (small) nsd += static_cast<uint32_t>(__popcll(ballot((v[g] > sb_lo) & (v[g] <= newT))));
-    }
-    __syncthreads();
-    if (total) {
-      uint32_t base = 0;
-      if (lane == 0) base = atomicAdd(&sm.cnt[nxt], total);
-      base = uniform(base);
-#pragma unroll
-      for (int g = 0; g < kGroup; ++g) {
-        const bool keep = v[g] > newT;
-        const u64 m = ballot(keep);
-        if (keep) sm.comp[base + mbcnt64(m)] = v[g];
-        base += static_cast<uint32_t>(__popcll(m));
-      }
-    }
-    if (nsd) {
-      uint32_t base = 0;
-      if (lane == 0) base = atomicAdd(&sm.nside, nsd);
-      base = uniform(base);
-#pragma unroll
-      for (int g = 0; g < kGroup; ++g) {
-        const bool in = (v[g] > sb_lo) & (v[g] <= newT);
-        const u64 m = ballot(in);
-        if (in) side[base + mbcnt64(m)] = v[g];
-        base += static_cast<uint32_t>(__popcll(m));
-      }
-    }
-  }
   if (small) {
-    // Rank the n (<= NT) members: the one with exactly sb_need - 1 larger
-    // members is the last kept (composites are distinct).
-    __syncthreads();
-    const uint32_t n = uniform(sm.nside);
-    const u64 mine = side[t < static_cast<int>(n) ? t : 0];
-    uint32_t r = 0;
-#pragma unroll 4
-    for (uint32_t j = 0; j < n; ++j) r += side[j] > mine ? 1u : 0u;
-    if (t < static_cast<int>(n) && r + 1u == sb_need) sm.rng[0] = mine;
-    __syncthreads();
-    const u64 kth = uniform64(sm.rng[0]);
-    const bool keep = (t < static_cast<int>(n)) & (mine >= kth);
-    const u64 m = ballot(keep);
-    uint32_t base = 0;
-    if (lane == 0 && m) base = atomicAdd(&sm.cnt[nxt], static_cast<uint32_t>(__popcll(m)));
-    base = uniform(base);
-    if (keep) sm.comp[base + mbcnt64(m)] = mine;
-    newT = kth - 1u;
-    __syncthreads();
-    for (uint32_t j = t; j < 2u * n; j += NT) sm.hist[j] = 0u;
+    compact_buffer<NT, CAP, true>(sm, c, nxt, newT, sb_lo);
+    newT = resolve_small_bin<NT, CAP>(sm, nxt, sb_need);
+  } else {
+    compact_buffer<NT, CAP, false>(sm, c, nxt, newT, 0ull);
   }
   if (t == 0) {
     sm.thr = newT;
@@ -803,110 +842,165 @@ __device__ __forceinline__ void load_block(u32x4 (&r)[V], const char* xrow, uint
 }
 
 // ---------------------------------------------------------------- epilogue
-// Order the m results held in comp[0, m).  Regions R0 = [0, KMAX) (results,
-// and the sorted output), R1 = [KMAX, 2 KMAX) and R2 = [2 KMAX, 3 KMAX)
-// (scratch).  The sort key (ascending = output order) is ~composite by value
-// and the column by column; both are unique.  A segment [s, e) of results is
-// binned on its key range (2048 bins): members of small bins are placed by an
-// in-bin rank, large bins become new segments with a 2048-fold narrower
-// range.  A segment keeps its offsets in every region, so the regions can
-// alternate as levels deepen.
+// Order the m results held in comp[0, m) (m <= KMAX).  The sort key
+// (ascending = output order) is ~composite by value and the column by
+// column; both are unique.  Every thread keeps the same elements in registers
+// throughout and only their final positions are worked out, level by level:
+//  * a level bins every still-unplaced element within its segment (a run of
+//    final positions whose keys lie in [lo, lo + 2^bits)); the 2048 bins are
+//    shared out among the segments in proportion to their sizes;
+//  * a scan over the bins gives each bin its run of final positions, and the
+//    elements are grouped there in a scratch region;
+//  * an element in a bin of at most 32 is placed by its rank within the bin;
+//    a larger bin becomes a segment of the next level, binned on the exact
+//    minimum and maximum of its own keys (so a run of equal values, whose keys
+//    differ only in the column, spreads out at once).
+// Regions: R0 = comp[0, KMAX) receives the sorted output, R1 = comp[KMAX,
+// 2 KMAX) holds the grouped elements, and after R1 come two segment tables
+// (this level's and the next), 4 words of 64 bits per segment.
+constexpr int kSortSegs = 128;   // > 4096 / 33, the most segments a level can make
+
 template <int NT, int CAP, int KMAX>
-__device__ __noinline__ void sort_results(Smem<CAP, NT>& sm, uint32_t m, bool by_value) {
-  static_assert(3 * KMAX <= CAP, "sort regions");
+__device__ __noinline__ void sort_results(Smem<CAP, NT>& sm, uint32_t m, bool by_value,
+                                          u64 key_lo, uint32_t span_bits) {
+  static_assert(2 * KMAX + 2 * 4 * kSortSegs <= CAP, "sort regions");
   constexpr uint32_t H = 32;              // bins larger than this are split again
-  constexpr int PER = KMAX / NT;          // members per thread at most
-  const int t = threadIdx.x, lane = t & 63;
+  constexpr int PER = KMAX / NT;          // elements per thread at most
+  constexpr int RB = 8;                   // in-bin rank: members read per round
+  constexpr uint32_t kDone = 0xFFFFu;
+  const int t = threadIdx.x;
+  u64* out = sm.comp;
+  u64* grp = sm.comp + KMAX;
+  // table entry: [0] lo, [1] start | base << 13 | shift << 25, [2] min, [3] max
+  u64* tab[2] = {sm.comp + 2 * KMAX, sm.comp + 2 * KMAX + 4 * kSortSegs};
   auto order_key = [&](u64 c) -> u64 { return by_value ? ~c : static_cast<u64>(col_of(c)); };
-  if (t == 0) {
-    sm.segoff[0] = 0u;                    // (start | region << 28, end)
-    sm.segoff[1] = m;
-    sm.nwork = 1u;
+
+  u64 c[PER];
+  uint32_t seg[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const uint32_t p = t + j * NT;
+    c[j] = out[p < m ? p : 0];
+    seg[j] = p < m ? 0u : kDone;
   }
-  __syncthreads();
+  if (t == 0) {
+    tab[0][0] = key_lo;
+    tab[0][1] = static_cast<u64>(span_bits > kRadixBits ? span_bits - kRadixBits : 0u) << 25;
+  }
+  __syncthreads();   // everything is in registers: R0 may be written
+  int cur = 0;
   for (;;) {
-    const uint32_t nw = uniform(sm.nwork);
-    if (nw == 0) break;
-    const uint32_t w0 = uniform(sm.segoff[2 * (nw - 1)]), s = w0 & 0x0FFFFFFFu;
-    const uint32_t e = uniform(sm.segoff[2 * nw - 1]);
-    const uint32_t reg = w0 >> 28;
-    const uint32_t treg = reg == 1 ? 2u : 1u;
-    const u64* src = sm.comp + reg * KMAX;
-    u64* tmp = sm.comp + treg * KMAX;
-    const uint32_t n = e - s;
-    u64 mv[PER];
-    u64 lo = ~0ull, hi = 0ull;
+    const u64* tc = tab[cur];
+    u64* tn = tab[cur ^ 1];
+    uint32_t bin[PER], start[PER], base[PER];
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
-      const uint32_t p = t + j * NT;
-      mv[j] = src[p < n ? s + p : s];
-      const u64 q = order_key(mv[j]);
-      lo = (p < n) & (q < lo) ? q : lo;
-      hi = (p < n) & (q > hi) ? q : hi;
+      const uint32_t sj = seg[j] == kDone ? 0u : seg[j];
+      const u64 lo = tc[4 * sj];
+      const uint32_t pk = static_cast<uint32_t>(tc[4 * sj + 1]);
+      start[j] = pk & 0x1FFFu;
+      base[j] = (pk >> 13) & 0xFFFu;
+      bin[j] = base[j] + static_cast<uint32_t>((order_key(c[j]) - lo) >> (pk >> 25));
+      if (seg[j] != kDone) atomicAdd(&sm.hist[bin[j]], 1u);
     }
-    lo = wave_extreme64<false>(lo);
-    hi = wave_extreme64<true>(hi);
-    if (t == 0) {
-      sm.rng[0] = ~0ull;
-      sm.rng[1] = 0ull;
+    if (t == 0) sm.nwork = 0u;
+    __syncthreads();
+    uint32_t cnt[PER], first[PER], b0[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) cnt[j] = sm.hist[bin[j]];
+    hist_exclusive_scan(sm);   // writes only after a barrier, so the reads above see counts
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      b0[j] = sm.hist[base[j]];
+      first[j] = start[j] + (sm.hist[bin[j]] - b0[j]);   // final position of the bin
     }
     __syncthreads();
-    if (t == 0) sm.nwork = nw - 1;   // popped (pushes come after later barriers)
-    if (lane == 0) {
-      atomicMin(&sm.rng[0], lo);
-      atomicMax(&sm.rng[1], hi);
-    }
-    __syncthreads();
-    lo = uniform64(sm.rng[0]);
-    hi = uniform64(sm.rng[1]);
-    const uint32_t bl = bit_length64(hi - lo);
-    const uint32_t shift = bl > kRadixBits ? bl - kRadixBits : 0u;
-    auto bin_of = [&](u64 q) { return static_cast<uint32_t>((q - lo) >> shift); };
 #pragma unroll
-    for (int j = 0; j < PER; ++j)
-      if (t + j * NT < n) atomicAdd(&sm.hist[bin_of(order_key(mv[j]))], 1u);
-    __syncthreads();
-    hist_exclusive_scan(sm);
-    // group by bin into the scratch region (returning atomics, all issued at once)
-    uint32_t pos[PER];
-#pragma unroll
-    for (int j = 0; j < PER; ++j)
-      pos[j] = t + j * NT < n ? atomicAdd(&sm.hist[bin_of(order_key(mv[j]))], 1u) : 0u;
-#pragma unroll
-    for (int j = 0; j < PER; ++j)
-      if (t + j * NT < n) tmp[s + pos[j]] = mv[j];
-    __syncthreads();   // hist[b] now holds the end of bin b
-    for (uint32_t p = t; p < n; p += NT) {
-      const u64 c = tmp[s + p];
-      const u64 q = order_key(c);
-      const uint32_t b = bin_of(q);
-      const uint32_t bs = b ? sm.hist[b - 1] : 0u;
-      const uint32_t be = sm.hist[b];
-      if (be - bs <= H) {
-        uint32_t rank = 0;
-        for (uint32_t r = bs; r < be; ++r) rank += order_key(tmp[s + r]) < q ? 1u : 0u;
-        sm.comp[s + bs + rank] = c;
-      } else if (p == bs) {
-        const uint32_t slot = atomicAdd(&sm.nwork, 1u);
-        sm.segoff[2 * slot] = (s + bs) | (treg << 28);
-        sm.segoff[2 * slot + 1] = s + be;
+    for (int j = 0; j < PER; ++j) {
+      if (seg[j] != kDone) {
+        const uint32_t slot = atomicAdd(&sm.hist[bin[j]], 1u);
+        grp[start[j] + (slot - b0[j])] = c[j];
       }
     }
     __syncthreads();
+    // place the members of small bins; the first member of a large bin
+    // registers it as a segment of the next level
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      if (seg[j] == kDone) continue;
+      if (cnt[j] <= H) {
+        uint32_t rank = 0;
+        if (cnt[j] > 1) {
+          const u64 q = order_key(c[j]);
+          const uint32_t be = first[j] + cnt[j];
+          for (uint32_t r0 = first[j]; r0 < be; r0 += RB) {
+            u64 o[RB];
+#pragma unroll
+            for (int i = 0; i < RB; ++i) o[i] = grp[r0 + i < be ? r0 + i : first[j]];
+#pragma unroll
+            for (int i = 0; i < RB; ++i) rank += ((r0 + i < be) & (order_key(o[i]) < q)) ? 1u : 0u;
+          }
+        }
+        out[first[j] + rank] = c[j];
+        seg[j] = kDone;
+      } else if (grp[first[j]] == c[j]) {
+        const uint32_t id = atomicAdd(&sm.nwork, 1u);
+        tn[4 * id + 2] = ~0ull;
+        tn[4 * id + 3] = 0ull;
+        sm.hist[bin[j]] = id;   // read back by the bin's members
+      }
+    }
+    __syncthreads();
+    const uint32_t nseg = uniform(sm.nwork);
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      if (seg[j] == kDone) continue;
+      seg[j] = sm.hist[bin[j]];
+      const u64 q = order_key(c[j]);
+      atomicMin(&tn[4 * seg[j] + 2], q);
+      atomicMax(&tn[4 * seg[j] + 3], q);
+    }
+    __syncthreads();
     hist_zero_own(sm);
+    if (nseg == 0) break;
+    // the first member of each new segment fills in its entry
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      if (seg[j] == kDone || grp[first[j]] != c[j]) continue;
+      const u64 mn = tn[4 * seg[j] + 2], mx = tn[4 * seg[j] + 3];
+      const uint32_t s0 = first[j], s1 = first[j] + cnt[j];
+      const uint32_t b_lo = static_cast<uint32_t>((static_cast<u64>(s0) * kBins) / m);
+      const uint32_t b_hi = static_cast<uint32_t>((static_cast<u64>(s1) * kBins) / m);
+      const uint32_t bits = bit_length64(mx - mn);
+      const uint32_t nbits = 31u - static_cast<uint32_t>(__clz(b_hi - b_lo));
+      const uint32_t sh = bits > nbits ? bits - nbits : 0u;
+      tn[4 * seg[j]] = mn;
+      tn[4 * seg[j] + 1] = static_cast<u64>(s0 | (b_lo << 13) | (sh << 25));
+    }
+    __syncthreads();   // the histogram and the next table are ready
+    cur ^= 1;
   }
-  __syncthreads();
 }
 
 template <int NT, int CAP, int KMAX>
 __device__ __forceinline__ void write_outputs(Smem<CAP, NT>& sm, const KArgs& a, bool bf16,
-                                              int row, int cur, uint32_t status) {
+                                              int row, int cur, uint32_t status, uint32_t L) {
   const int t = threadIdx.x;
   const uint32_t k = a.k;
   const int64_t out0 = static_cast<int64_t>(row) * k;
   uint32_t m = uniform(sm.cnt[cur]);
   if (status) m = 0;
-  if (a.sorted != 0 && m > 1) sort_results<NT, CAP, KMAX>(sm, m, a.sorted == 1);
+  if (a.sorted != 0 && m > 1) {
+    // Bounds of the sort keys: every result is above the threshold and has a
+    // key no larger than hikey; columns are below L.
+    if (a.sorted == 1) {
+      const u64 lo = static_cast<u64>(~uniform(sm.hikey)) << 32;
+      const u64 hi = ~uniform64(sm.thr) - 1u;
+      sort_results<NT, CAP, KMAX>(sm, m, true, lo, bit_length64(hi - lo));
+    } else {
+      sort_results<NT, CAP, KMAX>(sm, m, false, 0ull, bit_length(L - 1u));
+    }
+  }
   const char* xrow = static_cast<const char*>(a.x) + static_cast<int64_t>(row) * a.row_stride * (bf16 ? 2 : 4);
 
   for (uint32_t j = t; j < k; j += NT) {
@@ -1241,7 +1335,7 @@ __global__ __launch_bounds__(class_threads(CLS)) void topk_kernel(KArgs a) {
   }
 
   status |= sm.flags;
-  write_outputs<NT, CAP, KMAX>(sm, a, BF16, row, cur, status);
+  write_outputs<NT, CAP, KMAX>(sm, a, BF16, row, cur, status, L);
 }
 
 }  // namespace
