@@ -557,6 +557,7 @@ __device__ __noinline__ int cut_buffer(Smem<CAP, NT>& sm, int cur, uint32_t k,
   // collected during the compaction and ranked exactly; the sb_need-th
   // largest of them is the last one kept.
   bool small = false;
+  bool keep_all = false;   // every candidate is above T and kept: no compaction
   u64 sb_lo = 0;
   uint32_t sb_need = 0;
   if (hi >= klo && c > 0) {
@@ -592,7 +593,11 @@ __device__ __noinline__ int cut_buffer(Smem<CAP, NT>& sm, int cur, uint32_t k,
           const uint32_t b2 = uniform(sm.res[4]);
           if (b2 < static_cast<uint32_t>(kBins)) xv = (static_cast<u64>(base + (b2 << shift)) << 32) - 1u;
         }
-        if (uniform(sm.res[3]) <= keep_max) break;   // few enough above T: only drop those at or below T
+        const uint32_t above_T = uniform(sm.res[3]);
+        if (above_T <= keep_max) {   // few enough above T: only drop those at or below T
+          keep_all = above_T == c;
+          break;
+        }
       }
       const uint32_t b = uniform(sm.res[0]), ab = uniform(sm.res[1]), bc = uniform(sm.res[2]);
       above += ab;
@@ -626,8 +631,10 @@ __device__ __noinline__ int cut_buffer(Smem<CAP, NT>& sm, int cur, uint32_t k,
     }
   }
 
-  const int nxt = cur ^ 1;
-  if (small) {
+  int nxt = cur ^ 1;
+  if (keep_all) {
+    nxt = cur;
+  } else if (small) {
     compact_buffer<NT, CAP, true>(sm, c, nxt, newT, sb_lo);
     newT = resolve_small_bin<NT, CAP>(sm, nxt, sb_need);
   } else {
@@ -820,6 +827,61 @@ __device__ __noinline__ u64 block_threshold(BlockRegs<V> r, uint32_t k, Smem<CAP
   if (lane == 0) atomicMin(&sm.res[2], tk);
   __syncthreads();
   return (static_cast<u64>(uniform(sm.res[2])) << 32) - 1u;
+}
+
+// A second, tighter start over the first (up to) three whole blocks in the
+// ring, once a one-block threshold T (a key bound: admit key >= K1) is known.
+// The keys > K1 of those blocks are histogrammed on their own range
+// (K1, max]; keys equal to K1 are left out, so a run of equal values at the
+// bottom (exact zeros, say) costs no atomics on one hot counter.  A bin edge
+// with at least k of these elements at or above it is again a valid threshold
+// for the row.  Returns T if no such edge improves on it.  Leaves hist zeroed.
+template <bool BF16, int V, int NT, int CAP>
+__device__ __forceinline__ u64 ring_threshold(const BlockRegs<V>& b0, const BlockRegs<V>& b1,
+                                              const BlockRegs<V>& b2, uint32_t whole, u64 T,
+                                              uint32_t k, Smem<CAP, NT>& sm) {
+  constexpr int EPV = BF16 ? 8 : 4;
+  constexpr int NS = V * EPV;
+  const int t = threadIdx.x, lane = t & 63;
+  const uint32_t K1 = static_cast<uint32_t>(T >> 32) + 1u;
+  constexpr uint32_t kKeyMax = 0xFF800000u;   // key of +inf; NaN keys lie above
+  auto key_at = [&](const BlockRegs<V>& b, int s) -> uint32_t {
+    const uint32_t w = b.v[BF16 ? s / 8 : s / 4][BF16 ? (s % 8) / 2 : s % 4];
+    return key_of_bits(BF16 ? ((s & 1) ? (w & 0xFFFF0000u) : (w << 16)) : w);
+  };
+  auto each = [&](auto&& fn) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      if (whole & 1u) fn(key_at(b0, s));
+      if (whole & 2u) fn(key_at(b1, s));
+      if (whole & 4u) fn(key_at(b2, s));
+    }
+  };
+  uint32_t mx = 0;
+  each([&](uint32_t key) { mx = (key <= kKeyMax) & (key > mx) ? key : mx; });
+  mx = wave_max(mx);
+  if (t == 0) sm.res[0] = 0u;
+  __syncthreads();
+  if (lane == 0) atomicMax(&sm.res[0], mx);
+  __syncthreads();
+  mx = uniform(sm.res[0]);
+  if (mx <= K1) {   // nothing above K1 to tighten with
+    __syncthreads();
+    return T;
+  }
+  const uint32_t lo = K1 + 1u;
+  const uint32_t span = mx - lo;
+  const uint32_t shift = shift_for_span(span);
+  each([&](uint32_t key) {
+    const uint32_t d = key - lo;
+    if (d <= span) atomicAdd(&sm.hist[d >> shift], 1u);
+  });
+  __syncthreads();
+  hist_find_top(sm, k);
+  const uint32_t b = uniform(sm.res[0]);
+  if (b >= static_cast<uint32_t>(kBins)) return T;   // the k-th lies at K1 or below
+  const u64 T2 = (static_cast<u64>(lo + (b << shift)) << 32) - 1u;
+  return T2 > T ? T2 : T;
 }
 
 // Loads of one block.  Always issued, whatever the block: a vector that would
@@ -1136,7 +1198,23 @@ __global__ __launch_bounds__(class_threads(CLS)) void topk_kernel(KArgs a) {
         BlockRegs<V> br;
 #pragma unroll
         for (int v = 0; v < V; ++v) br.v[v] = cur_r[v];
-        const u64 t0 = block_threshold<BF16, V, NT, CAP>(br, k, sm);
+        u64 t0 = block_threshold<BF16, V, NT, CAP>(br, k, sm);
+        if (!MULTI && ntl >= 2 && t0 != kThrInit) {
+          // One workgroup streams the whole row: tighten over the whole blocks
+          // already in the ring, which saves cuts later in a long stream.
+          uint32_t whole = 0;
+#pragma unroll
+          for (uint32_t j = 0; j < 3; ++j)
+            if (j < ntl && blk_at(j) * static_cast<uint32_t>(kBlockElems) + kBlockElems <= L)
+              whole |= 1u << j;
+          BlockRegs<V> a1, a2;
+#pragma unroll
+          for (int v = 0; v < V; ++v) {
+            a1.v[v] = r1[v];
+            a2.v[v] = r2[v];
+          }
+          t0 = ring_threshold<BF16, V, NT, CAP>(br, a1, a2, whole, t0, k, sm);
+        }
         if (t0 > thr) {
           thr = t0;
           F = filter_of(thr);
