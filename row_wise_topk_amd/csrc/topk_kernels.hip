@@ -247,7 +247,7 @@ struct BlockOrder {
 template <int CAP, int NT>
 struct Smem {
   u64 comp[CAP];              // candidate composites
-  uint32_t hist[kBins];       // zero whenever not in use
+  alignas(16) uint32_t hist[kBins];   // zero whenever not in use
   uint32_t wsum[NT / 64];
   uint32_t res[5];
   uint32_t cnt[2];            // append counters; cur receives appends, cur^1 the next cut
@@ -263,6 +263,35 @@ struct Smem {
   u64 xv;                     // a cut's second answer: a bound with >= need2 candidates above
 };
 
+// A thread's own run of BPT consecutive bins, read and written 16 bytes at a
+// time (BPT is a multiple of 4): one wide access instead of BPT narrow ones
+// that would all fall on a few LDS banks.
+template <int BPT, int NT, int CAP>
+__device__ __forceinline__ void own_bins_read(const Smem<CAP, NT>& sm, uint32_t (&h)[BPT]) {
+  static_assert(BPT % 4 == 0, "bins per thread");
+  const u32x4* p = reinterpret_cast<const u32x4*>(sm.hist + threadIdx.x * BPT);
+#pragma unroll
+  for (int i = 0; i < BPT / 4; ++i) {
+    const u32x4 v = p[i];
+    h[4 * i] = v.x;
+    h[4 * i + 1] = v.y;
+    h[4 * i + 2] = v.z;
+    h[4 * i + 3] = v.w;
+  }
+}
+template <int BPT, int NT, int CAP>
+__device__ __forceinline__ void own_bins_write(Smem<CAP, NT>& sm, const uint32_t (&h)[BPT]) {
+  u32x4* p = reinterpret_cast<u32x4*>(sm.hist + threadIdx.x * BPT);
+#pragma unroll
+  for (int i = 0; i < BPT / 4; ++i) p[i] = u32x4{h[4 * i], h[4 * i + 1], h[4 * i + 2], h[4 * i + 3]};
+}
+template <int BPT, int NT, int CAP>
+__device__ __forceinline__ void own_bins_zero(Smem<CAP, NT>& sm) {
+  u32x4* p = reinterpret_cast<u32x4*>(sm.hist + threadIdx.x * BPT);
+#pragma unroll
+  for (int i = 0; i < BPT / 4; ++i) p[i] = u32x4{0u, 0u, 0u, 0u};
+}
+
 // Suffix search over hist (higher bins first), which it leaves zeroed.  Finds
 // b* with  sum_{b > b*} hist[b] < need <= sum_{b >= b*} hist[b].
 // res = {b*, sum above b*, hist[b*], total}; res[0] = kBins when total < need.
@@ -274,13 +303,11 @@ __device__ __forceinline__ void hist_find_top(Smem<CAP, NT>& sm, uint32_t need,
   constexpr int NW = NT / 64;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   uint32_t h[BPT];
+  own_bins_read<BPT>(sm, h);
+  own_bins_zero<BPT>(sm);
   uint32_t s = 0;
 #pragma unroll
-  for (int i = 0; i < BPT; ++i) {
-    h[i] = sm.hist[t * BPT + i];
-    s += h[i];
-    sm.hist[t * BPT + i] = 0u;
-  }
+  for (int i = 0; i < BPT; ++i) s += h[i];
   const uint32_t p = wave_prefix_sum(s);   // inclusive, within the wave
   if (lane == 63) sm.wsum[w] = p;
   if (t == 0) {
@@ -332,12 +359,10 @@ __device__ __forceinline__ uint32_t hist_exclusive_scan(Smem<CAP, NT>& sm) {
   constexpr int NW = NT / 64;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   uint32_t h[BPT];
+  own_bins_read<BPT>(sm, h);
   uint32_t s = 0;
 #pragma unroll
-  for (int i = 0; i < BPT; ++i) {
-    h[i] = sm.hist[t * BPT + i];
-    s += h[i];
-  }
+  for (int i = 0; i < BPT; ++i) s += h[i];
   const uint32_t p = wave_prefix_sum(s);
   if (lane == 63) sm.wsum[w] = p;
   __syncthreads();
@@ -349,20 +374,20 @@ __device__ __forceinline__ uint32_t hist_exclusive_scan(Smem<CAP, NT>& sm) {
     if (w2 < w) before += ws;
   }
   uint32_t run = before + p - s;
+  uint32_t o[BPT];
 #pragma unroll
   for (int i = 0; i < BPT; ++i) {
-    sm.hist[t * BPT + i] = run;
+    o[i] = run;
     run += h[i];
   }
+  own_bins_write<BPT>(sm, o);
   __syncthreads();
   return tot;
 }
 
 template <int NT, int CAP>
 __device__ __forceinline__ void hist_zero_own(Smem<CAP, NT>& sm) {
-  constexpr int BPT = kBins / NT;
-#pragma unroll
-  for (int i = 0; i < BPT; ++i) sm.hist[threadIdx.x * BPT + i] = 0u;
+  own_bins_zero<kBins / NT>(sm);
 }
 
 // ---------------------------------------------------------------- the cut
