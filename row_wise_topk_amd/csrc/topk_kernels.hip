@@ -1339,13 +1339,28 @@ __global__ __launch_bounds__(class_threads(CLS)) void topk_kernel(KArgs a) {
     // LDS, so its own range of the array is skipped).  Start from the largest
     // of the shared threshold and min_seg x_seg (0 if any workgroup had fewer
     // than ceil(k / S) survivors).
+    // Every load goes out at once: the bounds, the row's counters and the
+    // first two chunks of survivors.  The chunks need no count first: the
+    // row's array is zero past its fill, and zero is never above a threshold.
+    constexpr int PER = kBlockElems / NT;
+    constexpr uint32_t CHUNK = PER * NT;
+    const uint32_t area = static_cast<uint32_t>(S) * k;
+    // Loads of one chunk; positions past the array read position 0 (a valid
+    // address) and are dropped.  Every position read below the fill is
+    // cleared, so the workspace is all zero again when the call ends.
+    auto load_chunk = [&](uint32_t c0, u64 (&mv)[PER]) {
+#pragma unroll
+      for (int q = 0; q < PER; ++q) {
+        const uint32_t p = c0 + t + q * NT;
+        mv[q] = ld_agent(&wsc[p < area ? p : 0u]);
+      }
+    };
     u64 xs = ~0ull;
-    if (t < S) {
-      u64* xp = &a.ws_x[static_cast<int64_t>(row) * S + t];
-      xs = ld_agent(xp);
-      st_agent(xp, 0ull);
-    }
-    xs = wave_extreme64<false>(xs);
+    u64* xp = &a.ws_x[static_cast<int64_t>(row) * S + (t < S ? t : 0)];
+    if (t < S) xs = ld_agent(xp);
+    u64 va[PER], vb[PER];
+    load_chunk(0, va);
+    load_chunk(CHUNK, vb);
     if (t == 0) {
       sm.rng[0] = ~0ull;
       const u64 gfin = load_thr(thr_g);
@@ -1353,6 +1368,8 @@ __global__ __launch_bounds__(class_threads(CLS)) void topk_kernel(KArgs a) {
       sm.flags |= ld_agent(&a.ws_flags[row]);
       sm.res[1] = ld_agent(&a.ws_fill[row]);
     }
+    if (t < S) st_agent(xp, 0ull);
+    xs = wave_extreme64<false>(xs);
     __syncthreads();
     if (lane == 0) atomicMin(&sm.rng[0], xs);
     __syncthreads();
@@ -1360,18 +1377,6 @@ __global__ __launch_bounds__(class_threads(CLS)) void topk_kernel(KArgs a) {
     __syncthreads();
     const uint32_t total = uniform(sm.res[1]);
     const u64 T0 = uniform64(sm.thr);
-    constexpr int PER = kBlockElems / NT;
-    constexpr uint32_t CHUNK = PER * NT;
-    // Loads of one chunk; positions past the end read position 0 (a valid
-    // address) and are dropped.  Every position read is cleared, so the
-    // workspace is all zero again when the call ends.
-    auto load_chunk = [&](uint32_t c0, u64 (&mv)[PER]) {
-#pragma unroll
-      for (int q = 0; q < PER; ++q) {
-        const uint32_t p = c0 + t + q * NT;
-        mv[q] = ld_agent(&wsc[p < total ? p : 0u]);
-      }
-    };
     auto clear_chunk = [&](uint32_t c0) {
 #pragma unroll
       for (int q = 0; q < PER; ++q) {
@@ -1416,17 +1421,15 @@ __global__ __launch_bounds__(class_threads(CLS)) void topk_kernel(KArgs a) {
         Tm = uniform64(sm.thr);
       }
     };
-    u64 va[PER], vb[PER];
-    if (total > 0) load_chunk(0, va);
     for (uint32_t c0 = 0; c0 < total; c0 += 2 * CHUNK) {
-      load_chunk(c0 + CHUNK, vb);
       merge_chunk(c0, va);
       clear_chunk(c0);
-      load_chunk(c0 + 2 * CHUNK, va);
+      if (c0 + 2 * CHUNK < total) load_chunk(c0 + 2 * CHUNK, va);
       if (c0 + CHUNK < total) {
         merge_chunk(c0 + CHUNK, vb);
         clear_chunk(c0 + CHUNK);
       }
+      if (c0 + 3 * CHUNK < total) load_chunk(c0 + 3 * CHUNK, vb);
     }
     cur = cut_buffer<NT, CAP>(sm, cur, k, k, L, hi_key());
     if (t == 0) {
