@@ -391,21 +391,36 @@ __device__ __forceinline__ void hist_zero_own(Smem<CAP, NT>& sm) {
 }
 
 // ---------------------------------------------------------------- the cut
-// Candidates are visited in groups of kGroup slots per thread (slot e of
-// thread t is buffer position t + e * NT): a group's LDS reads are issued
-// back to back, unconditionally at a clamped address, and waited for once.
-// Slots past the count read as 0, which is below every threshold and outside
-// every key range.
+// Candidates are visited in groups of G slots per thread (slot e of thread t
+// is buffer position t + e * NT): a group's LDS reads are issued back to
+// back, unconditionally at a clamped address, and waited for once.  Slots
+// past the count read as 0, which is below every threshold and outside every
+// key range.  Whole groups of 16 are followed by one last group of 4, 8 or 16
+// slots, whichever covers the rest, so a short buffer is not read 16 deep.
 constexpr int kGroup = 16;
 
-template <int NT, int CAP>
-constexpr int slots_per_thread() { return (CAP + NT * kGroup - 1) / (NT * kGroup) * kGroup; }
+template <int G>
+struct GroupSize {
+  static constexpr int value = G;
+};
 
-template <int NT, int CAP>
-__device__ __forceinline__ void read_group(const Smem<CAP, NT>& sm, int e0, uint32_t c,
-                                           u64 (&v)[kGroup]) {
+template <int NT, typename Body>
+__device__ __forceinline__ void for_groups(uint32_t c, Body&& body) {
+  const uint32_t slots = (c + NT - 1) / NT;   // uniform
+  uint32_t e0 = 0;
+#pragma unroll 1
+  for (; e0 + kGroup < slots; e0 += kGroup) body(GroupSize<kGroup>{}, e0);
+  const uint32_t rest = slots - e0;
+  if (rest > 8) body(GroupSize<16>{}, e0);
+  else if (rest > 4) body(GroupSize<8>{}, e0);
+  else if (rest > 0) body(GroupSize<4>{}, e0);
+}
+
+template <int G, int NT, int CAP>
+__device__ __forceinline__ void read_group(const Smem<CAP, NT>& sm, uint32_t e0, uint32_t c,
+                                           u64 (&v)[G]) {
 #pragma unroll
-  for (int g = 0; g < kGroup; ++g) {
+  for (int g = 0; g < G; ++g) {
     const uint32_t i = threadIdx.x + (e0 + g) * NT;
     v[g] = sm.comp[i < CAP ? i : CAP - 1];
   }
@@ -413,7 +428,7 @@ __device__ __forceinline__ void read_group(const Smem<CAP, NT>& sm, int e0, uint
   // scheduler can give every read the same destination and wait for each.
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int g = 0; g < kGroup; ++g) {
+  for (int g = 0; g < G; ++g) {
     const uint32_t i = threadIdx.x + (e0 + g) * NT;
     v[g] = i < c ? v[g] : 0ull;
   }
@@ -424,23 +439,21 @@ __device__ __forceinline__ void read_group(const Smem<CAP, NT>& sm, int e0, uint
 template <int NT, int CAP>
 __device__ __noinline__ uint32_t index_cut(Smem<CAP, NT>& sm, uint32_t c, uint32_t E_key,
                                            uint32_t need, u64 T, uint32_t n_cols) {
-  constexpr int E = slots_per_thread<NT, CAP>();
   uint32_t ibase = 0;
   uint32_t itop = n_cols > 0 ? n_cols - 1u : 0u;
   for (;;) {
     const uint32_t shift = shift_for_span(itop - ibase);
-#pragma unroll 1
-    for (int e0 = 0; e0 < E; e0 += kGroup) {
-      if (static_cast<uint32_t>(e0 * NT) >= c) break;   // uniform
-      u64 v[kGroup];
-      read_group(sm, e0, c, v);
+    for_groups<NT>(c, [&](auto gs, uint32_t e0) {
+      constexpr int G = decltype(gs)::value;
+      u64 v[G];
+      read_group<G>(sm, e0, c, v);
 #pragma unroll
-      for (int g = 0; g < kGroup; ++g) {
+      for (int g = 0; g < G; ++g) {
         const uint32_t ci = col_of(v[g]) - ibase;
         if ((key_of(v[g]) == E_key) & (ci <= itop - ibase) & (v[g] > T))
           atomicAdd(&sm.hist[(kBins - 1) - (ci >> shift)], 1u);
       }
-    }
+    });
     __syncthreads();
     hist_find_top(sm, need);
     const uint32_t b = (kBins - 1) - uniform(sm.res[0]);   // bin in ascending column order
@@ -464,19 +477,17 @@ __device__ __noinline__ uint32_t index_cut(Smem<CAP, NT>& sm, uint32_t c, uint32
 template <int NT, int CAP, bool SIDE>
 __device__ __forceinline__ void compact_buffer(Smem<CAP, NT>& sm, uint32_t c, int nxt,
                                                u64 keep_above, u64 side_lo) {
-  constexpr int E = slots_per_thread<NT, CAP>();
   const int lane = threadIdx.x & 63;
   u64* side = reinterpret_cast<u64*>(sm.hist);
   if (SIDE && threadIdx.x == 0) sm.nside = 0u;
-#pragma unroll 1
-  for (int e0 = 0; e0 < E; e0 += kGroup) {
-    if (static_cast<uint32_t>(e0 * NT) >= c) break;   // uniform
-    u64 v[kGroup];
-    read_group(sm, e0, c, v);
-    u64 mk[kGroup], ms[kGroup];
+  for_groups<NT>(c, [&](auto gs, uint32_t e0) {
+    constexpr int G = decltype(gs)::value;
+    u64 v[G];
+    read_group<G>(sm, e0, c, v);
+    u64 mk[G], ms[G];
     uint32_t total = 0, nsd = 0;
 #pragma unroll
-    for (int g = 0; g < kGroup; ++g) {
+    for (int g = 0; g < G; ++g) {
       mk[g] = ballot(v[g] > keep_above);
       total += static_cast<uint32_t>(__popcll(mk[g]));
       if (SIDE) {
@@ -490,7 +501,7 @@ __device__ __forceinline__ void compact_buffer(Smem<CAP, NT>& sm, uint32_t c, in
       if (lane == 0) base = atomicAdd(&sm.cnt[nxt], total);
       base = uniform(base);
 #pragma unroll
-      for (int g = 0; g < kGroup; ++g) {
+      for (int g = 0; g < G; ++g) {
         if ((mk[g] >> lane) & 1ull) sm.comp[base + mbcnt64(mk[g])] = v[g];
         base += static_cast<uint32_t>(__popcll(mk[g]));
       }
@@ -500,12 +511,12 @@ __device__ __forceinline__ void compact_buffer(Smem<CAP, NT>& sm, uint32_t c, in
       if (lane == 0) base = atomicAdd(&sm.nside, nsd);
       base = uniform(base);
 #pragma unroll
-      for (int g = 0; g < kGroup; ++g) {
+      for (int g = 0; g < G; ++g) {
         if ((ms[g] >> lane) & 1ull) side[base + mbcnt64(ms[g])] = v[g];
         base += static_cast<uint32_t>(__popcll(ms[g]));
       }
     }
-  }
+  });
 }
 
 constexpr uint32_t kSmallBin = 64;   // largest boundary bin ranked directly
@@ -563,7 +574,6 @@ template <int NT, int CAP>
 __device__ __noinline__ int cut_buffer(Smem<CAP, NT>& sm, int cur, uint32_t k,
                                        uint32_t keep_max, uint32_t n_cols, uint32_t hi_key,
                                        uint32_t need2 = 0) {
-  constexpr int E = slots_per_thread<NT, CAP>();
   const int t = threadIdx.x, lane = t & 63;
   const uint32_t hk = wave_max(hi_key);
   if (lane == 0) atomicMax(&sm.hikey, hk);
@@ -591,25 +601,24 @@ __device__ __noinline__ int cut_buffer(Smem<CAP, NT>& sm, int cur, uint32_t k,
     for (;;) {
       const uint32_t shift = shift_for_span(top - base);
       const uint32_t span = top - base;
-#pragma unroll 1
-      for (int e0 = 0; e0 < E; e0 += kGroup) {
-        if (static_cast<uint32_t>(e0 * NT) >= c) break;   // uniform
-        u64 v[kGroup];
-        read_group(sm, e0, c, v);
+      for_groups<NT>(c, [&](auto gs, uint32_t e0) {
+        constexpr int G = decltype(gs)::value;
+        u64 v[G];
+        read_group<G>(sm, e0, c, v);
         if (key_only) {   // every candidate in [base, top] is above T
 #pragma unroll
-          for (int g = 0; g < kGroup; ++g) {
+          for (int g = 0; g < G; ++g) {
             const uint32_t d = key_of(v[g]) - base;
             if (d <= span) atomicAdd(&sm.hist[d >> shift], 1u);
           }
         } else {
 #pragma unroll
-          for (int g = 0; g < kGroup; ++g) {
+          for (int g = 0; g < G; ++g) {
             const uint32_t d = key_of(v[g]) - base;
             if ((d <= span) & (v[g] > T)) atomicAdd(&sm.hist[d >> shift], 1u);
           }
         }
-      }
+      });
       __syncthreads();
       hist_find_top(sm, need, first ? need2 : 0u);
       if (first) {
@@ -1335,8 +1344,7 @@ __global__ __launch_bounds__(class_threads(CLS)) void topk_kernel(KArgs a) {
     __syncthreads();
     if (!uniform(sm.is_last)) return;
 
-    // Last arrival: merge the other workgroups' survivors (its own are still in
-    // LDS, so its own range of the array is skipped).  Start from the largest
+    // Last arrival: merge every workgroup's survivors.  Start from the largest
     // of the shared threshold and min_seg x_seg (0 if any workgroup had fewer
     // than ceil(k / S) survivors).
     // Every load goes out at once: the bounds, the row's counters and the
@@ -1377,6 +1385,10 @@ __global__ __launch_bounds__(class_threads(CLS)) void topk_kernel(KArgs a) {
     __syncthreads();
     const uint32_t total = uniform(sm.res[1]);
     const u64 T0 = uniform64(sm.thr);
+    // Its own candidates come back from the array with everyone else's,
+    // filtered by the same bound, so the LDS buffer starts empty.
+    if (t == 0) sm.cnt[cur] = 0u;
+    __syncthreads();
     auto clear_chunk = [&](uint32_t c0) {
 #pragma unroll
       for (int q = 0; q < PER; ++q) {
@@ -1388,7 +1400,7 @@ __global__ __launch_bounds__(class_threads(CLS)) void topk_kernel(KArgs a) {
     auto merge_chunk = [&](uint32_t c0, const u64 (&mv)[PER]) {
       auto pass = [&](int q) -> bool {
         const uint32_t p = c0 + t + q * NT;
-        return (p < total) & ((p < own0) | (p >= own0 + mine)) & (mv[q] > Tm);
+        return (p < total) & (mv[q] > Tm);
       };
       u64 mm[PER];
       uint32_t tot = 0, kmax = 0;
