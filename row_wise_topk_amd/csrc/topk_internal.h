@@ -53,7 +53,7 @@ struct KArgs {
   uint32_t* ws_flags;           // [batch]  OR of row status bits
   uint32_t* ws_fill;            // [batch]  survivors written so far per row
   unsigned long long* ws_x;     // [batch * segments]  per-workgroup merge bound
-  unsigned long long* ws_comp;  // [batch * segments * k]  survivor composites, contiguous per row
+  unsigned long long* ws_comp;  // [batch * segments * (k + 64)]  candidate composites, contiguous per row
 };
 
 // Workspace layout for `segments` workgroups per row (bytes, 16-B aligned parts).

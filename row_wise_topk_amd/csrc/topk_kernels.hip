@@ -258,6 +258,7 @@ struct Smem {
   uint32_t is_last;
   uint32_t nwork;             // epilogue sort: number of pending segments
   uint32_t nside;             // cut: members of a small boundary bin
+  uint32_t kept;              // cut: candidates above the new threshold
   u64 rng[2];                 // epilogue sort: min / max order key of a segment
   u64 thr;                    // the workgroup's threshold (composite)
   u64 xv;                     // a cut's second answer: a bound with >= need2 candidates above
@@ -570,16 +571,20 @@ __device__ __noinline__ u64 resolve_small_bin(Smem<CAP, NT>& sm, int nxt, uint32
 // top-k.  Returns the new append counter index.
 // With need2 > 0 it also leaves in sm.xv a composite with at least need2 of
 // the candidates above it (0 if there are fewer than need2 above sm.thr).
+// sm.kept receives the number of candidates above the new threshold.  With
+// find_only the buffer is left as it is (the caller reads it filtered by
+// sm.thr); keep_max must then be at least k + kSmallBin, so that a boundary
+// bin small enough to rank is always kept whole.
 template <int NT, int CAP>
 __device__ __noinline__ int cut_buffer(Smem<CAP, NT>& sm, int cur, uint32_t k,
                                        uint32_t keep_max, uint32_t n_cols, uint32_t hi_key,
-                                       uint32_t need2 = 0) {
+                                       uint32_t need2 = 0, bool find_only = false) {
   const int t = threadIdx.x, lane = t & 63;
   const uint32_t hk = wave_max(hi_key);
   if (lane == 0) atomicMax(&sm.hikey, hk);
   if (t == 0) sm.cnt[cur ^ 1] = 0u;
   __syncthreads();
-  const uint32_t c = uniform(sm.cnt[cur]);
+  const uint32_t c = min(uniform(sm.cnt[cur]), static_cast<uint32_t>(CAP));
   const u64 T = uniform64(sm.thr);
   const uint32_t hi = uniform(sm.hikey);
   const uint32_t K = static_cast<uint32_t>(T >> 32);
@@ -588,6 +593,7 @@ __device__ __noinline__ int cut_buffer(Smem<CAP, NT>& sm, int cur, uint32_t k,
 
   u64 newT = T;
   u64 xv = 0;
+  uint32_t kept = 0;
   // Small boundary bin: its members (composite in (sb_lo, newT]) are
   // collected during the compaction and ranked exactly; the sb_need-th
   // largest of them is the last one kept.
@@ -630,6 +636,7 @@ __device__ __noinline__ int cut_buffer(Smem<CAP, NT>& sm, int cur, uint32_t k,
         const uint32_t above_T = uniform(sm.res[3]);
         if (above_T <= keep_max) {   // few enough above T: only drop those at or below T
           keep_all = above_T == c;
+          kept = above_T;
           break;
         }
       }
@@ -640,6 +647,7 @@ __device__ __noinline__ int cut_buffer(Smem<CAP, NT>& sm, int cur, uint32_t k,
       const u64 lo_edge = (static_cast<u64>(base) << 32) - 1u;
       if (above + bc <= keep_max) {
         newT = lo_edge > T ? lo_edge : T;
+        kept = above + bc;
         break;
       }
       if (bc <= kSmallBin) {
@@ -652,6 +660,7 @@ __device__ __noinline__ int cut_buffer(Smem<CAP, NT>& sm, int cur, uint32_t k,
         small = true;
         sb_lo = lo_edge > T ? lo_edge : T;
         sb_need = need;
+        kept = above + need;
         newT = (static_cast<u64>(ub + 1u) << 32) - 1u;
         break;
       }
@@ -659,6 +668,7 @@ __device__ __noinline__ int cut_buffer(Smem<CAP, NT>& sm, int cur, uint32_t k,
         const uint32_t I = index_cut<NT, CAP>(sm, c, base, need, T, n_cols);
         const u64 cand = comp_of(base, I) - 1u;
         newT = cand > T ? cand : T;
+        kept = above + need;
         break;
       }
       top = base + ((1u << shift) - 1u);
@@ -666,7 +676,7 @@ __device__ __noinline__ int cut_buffer(Smem<CAP, NT>& sm, int cur, uint32_t k,
   }
 
   int nxt = cur ^ 1;
-  if (keep_all) {
+  if (keep_all || find_only) {
     nxt = cur;
   } else if (small) {
     compact_buffer<NT, CAP, true>(sm, c, nxt, newT, sb_lo);
@@ -677,6 +687,7 @@ __device__ __noinline__ int cut_buffer(Smem<CAP, NT>& sm, int cur, uint32_t k,
   if (t == 0) {
     sm.thr = newT;
     sm.xv = xv;
+    sm.kept = kept;
   }
   __syncthreads();
   return nxt;
@@ -985,7 +996,10 @@ __device__ __noinline__ void sort_results(Smem<CAP, NT>& sm, uint32_t m, bool by
   }
   __syncthreads();   // everything is in registers: R0 may be written
   int cur = 0;
-  for (;;) {
+  // Distinct keys need at most ~22 levels (each narrows a segment's range at
+  // least 8-fold); the cap only guards against a corrupted buffer.
+#pragma unroll 1
+  for (int level = 0; level < 64; ++level) {
     const u64* tc = tab[cur];
     u64* tn = tab[cur ^ 1];
     uint32_t bin[PER], start[PER], base[PER];
@@ -1084,7 +1098,7 @@ __device__ __forceinline__ void write_outputs(Smem<CAP, NT>& sm, const KArgs& a,
   const int t = threadIdx.x;
   const uint32_t k = a.k;
   const int64_t out0 = static_cast<int64_t>(row) * k;
-  uint32_t m = uniform(sm.cnt[cur]);
+  uint32_t m = min(uniform(sm.cnt[cur]), k);
   if (status) m = 0;
   if (a.sorted != 0 && m > 1) {
     // Bounds of the sort keys: every result is above the threshold and has a
@@ -1306,13 +1320,16 @@ __global__ __launch_bounds__(class_threads(CLS)) void topk_kernel(KArgs a) {
     const u64 gl = load_thr(thr_g);
     if (gl > sm.thr) sm.thr = gl;   // survivors at or below the shared bound are not needed
   }
-  // Exact local top-k (drops anything at or below the current threshold too).
-  // With several workgroups on the row, the cut also finds the bound x_seg
-  // with at least ceil(k / S) of this workgroup's survivors above it: the
-  // smallest x_seg over the row then has at least k survivors above it, so
-  // the merge can drop everything at or below it.
-  cur = cut_buffer<NT, CAP>(sm, cur, k, k, L, hi_key(),
-                            MULTI ? (k + static_cast<uint32_t>(S) - 1u) / static_cast<uint32_t>(S) : 0u);
+  // One workgroup on the row: the exact top-k.  Several: only the threshold
+  // that leaves between k and k + kSmallBin candidates (the merge makes the
+  // row's one exact cut), and the bound x_seg with at least ceil(k / S) of
+  // this workgroup's candidates above it: the smallest x_seg over the row has
+  // at least k candidates above it, so the merge drops everything at or
+  // below it.  The buffer is not compacted: the hand-over below reads it
+  // filtered by the threshold.
+  cur = cut_buffer<NT, CAP>(sm, cur, k, MULTI ? k + kSmallBin : k, L, hi_key(),
+                            MULTI ? (k + static_cast<uint32_t>(S) - 1u) / static_cast<uint32_t>(S) : 0u,
+                            MULTI);
 
   if (MULTI) {
     // Hand the survivors to the row's last workgroup: each workgroup reserves
@@ -1320,20 +1337,48 @@ __global__ __launch_bounds__(class_threads(CLS)) void topk_kernel(KArgs a) {
     // it.  Every shared word is written and read with agent-scope atomic
     // accesses, and the stores are complete before the arrival counter moves,
     // so no L2 write-back or invalidate is needed.
-    const uint32_t mine = uniform(sm.cnt[cur]);
-    u64* wsc = reinterpret_cast<u64*>(a.ws_comp) + static_cast<int64_t>(row) * S * k;
+    const uint32_t c = uniform(sm.cnt[cur]);
+    const uint32_t mine = uniform(sm.kept);   // at most k + kSmallBin
+    const u64 Tk = uniform64(sm.thr);
+    u64* wsc = reinterpret_cast<u64*>(a.ws_comp) + static_cast<int64_t>(row) * S * (k + kSmallBin);
     if (t == 0) {
       sm.res[0] = mine ? __hip_atomic_fetch_add(&a.ws_fill[row], mine, __ATOMIC_RELAXED,
                                                 __HIP_MEMORY_SCOPE_AGENT)
                        : 0u;
-      if (mine >= k) publish_thr(thr_g, sm.thr);
+      sm.cnt[cur ^ 1] = 0u;
+      if (mine >= k) publish_thr(thr_g, Tk);
       st_agent(&a.ws_x[static_cast<int64_t>(row) * S + seg], sm.xv);
       if (sm.flags)
         __hip_atomic_fetch_or(&a.ws_flags[row], sm.flags, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
     const uint32_t own0 = uniform(sm.res[0]);
-    for (uint32_t j = t; j < mine; j += NT) st_agent(&wsc[own0 + j], sm.comp[j]);
+    // Every candidate above the threshold goes to the reserved range, at an
+    // offset taken with one LDS atomic per wave and group (never past the
+    // range, whatever the count).
+    for_groups<NT>(c, [&](auto gs, uint32_t e0) {
+      constexpr int G = decltype(gs)::value;
+      u64 v[G];
+      read_group<G>(sm, e0, c, v);
+      u64 mk[G];
+      uint32_t tot = 0;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        mk[g] = ballot(v[g] > Tk);
+        tot += static_cast<uint32_t>(__popcll(mk[g]));
+      }
+      if (tot) {
+        uint32_t base = 0;
+        if (lane == 0) base = atomicAdd(&sm.cnt[cur ^ 1], tot);
+        base = uniform(base);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const uint32_t pos = base + mbcnt64(mk[g]);
+          if (((mk[g] >> lane) & 1ull) & (pos < mine)) st_agent(&wsc[own0 + pos], v[g]);
+          base += static_cast<uint32_t>(__popcll(mk[g]));
+        }
+      }
+    });
     wait_all_memory();
     __syncthreads();
     if (t == 0) {
@@ -1350,9 +1395,18 @@ __global__ __launch_bounds__(class_threads(CLS)) void topk_kernel(KArgs a) {
     // Every load goes out at once: the bounds, the row's counters and the
     // first two chunks of survivors.  The chunks need no count first: the
     // row's array is zero past its fill, and zero is never above a threshold.
-    constexpr int PER = kBlockElems / NT;
+    // Two chunks hold the survivors of up to 8 workgroups at the class's
+    // largest k (within a register budget of 16 per thread per chunk), so the
+    // merge usually waits for one round trip only.  A chunk must also fit in
+    // the buffer after a cut (at most k + slack candidates remain).
+    constexpr int PER_FIT = (8 * (KMAX + static_cast<int>(kSmallBin)) + 2 * NT - 1) / (2 * NT);
+    constexpr int PER_ROOM = (CAP - (3 * KMAX + class_trigger(CLS)) / 4) / NT;
+    constexpr int PER_A = PER_FIT > 16 ? 16 : PER_FIT;
+    constexpr int PER_B = PER_A > PER_ROOM ? PER_ROOM : PER_A;
+    constexpr int PER = PER_B < 4 ? 4 : PER_B;
+    static_assert(PER * NT + (3 * KMAX + class_trigger(CLS)) / 4 <= CAP, "merge chunk room");
     constexpr uint32_t CHUNK = PER * NT;
-    const uint32_t area = static_cast<uint32_t>(S) * k;
+    const uint32_t area = static_cast<uint32_t>(S) * (k + kSmallBin);
     // Loads of one chunk; positions past the array read position 0 (a valid
     // address) and are dropped.  Every position read below the fill is
     // cleared, so the workspace is all zero again when the call ends.
@@ -1383,7 +1437,7 @@ __global__ __launch_bounds__(class_threads(CLS)) void topk_kernel(KArgs a) {
     __syncthreads();
     if (t == 0 && sm.rng[0] > sm.thr) sm.thr = sm.rng[0];
     __syncthreads();
-    const uint32_t total = uniform(sm.res[1]);
+    const uint32_t total = min(uniform(sm.res[1]), area);
     const u64 T0 = uniform64(sm.thr);
     // Its own candidates come back from the array with everyone else's,
     // filtered by the same bound, so the LDS buffer starts empty.
@@ -1412,25 +1466,38 @@ __global__ __launch_bounds__(class_threads(CLS)) void topk_kernel(KArgs a) {
         mm[q] = ballot(p);
         tot += static_cast<uint32_t>(__popcll(mm[q]));
       }
-      uint32_t after = 0;
-      if (tot) {
-        const uint32_t wk = wave_max(kmax);
-        uint32_t base = 0;
-        if (lane == 0) {
-          atomicMax(&sm.hikey, wk);
-          base = atomicAdd(&sm.cnt[cur], tot);
-        }
-        base = uniform(base);
-        after = base + tot;
-#pragma unroll
-        for (int q = 0; q < PER; ++q) {
-          if ((mm[q] >> lane) & 1ull) sm.comp[base + mbcnt64(mm[q])] = mv[q];
-          base += static_cast<uint32_t>(__popcll(mm[q]));
-        }
+      // The chunk's total is known before anything is appended: if it would
+      // not fit, cut first and filter the chunk again with the raised bound.
+      const uint32_t wk = wave_max(kmax);
+      if (lane == 0) {
+        sm.snap[par][t >> 6] = tot;
+        atomicMax(&sm.hikey, wk);
       }
-      if (count_after_step(after) > trigger) {
+      __syncthreads();
+      uint32_t sum = 0;
+#pragma unroll
+      for (int w2 = 0; w2 < NT / 64; ++w2) sum += sm.snap[par][w2];
+      par ^= 1;
+      if (uniform(sm.cnt[cur]) + uniform(sum) > static_cast<uint32_t>(CAP)) {
         cur = cut_buffer<NT, CAP>(sm, cur, k, k + slack, L, hi_key());
         Tm = uniform64(sm.thr);
+        tot = 0;
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+          mm[q] = ballot(pass(q));
+          tot += static_cast<uint32_t>(__popcll(mm[q]));
+        }
+      }
+      if (tot) {
+        uint32_t base = 0;
+        if (lane == 0) base = atomicAdd(&sm.cnt[cur], tot);
+        base = uniform(base);
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+          const uint32_t pos = base + mbcnt64(mm[q]);
+          if (((mm[q] >> lane) & 1ull) & (pos < static_cast<uint32_t>(CAP))) sm.comp[pos] = mv[q];
+          base += static_cast<uint32_t>(__popcll(mm[q]));
+        }
       }
     };
     for (uint32_t c0 = 0; c0 < total; c0 += 2 * CHUNK) {
@@ -1469,7 +1536,7 @@ WsLayout ws_layout(int64_t batch, int segments, int k) {
   l.fill = up(l.flags + b * 4);
   l.x = up(l.fill + b * 4);
   l.comp = up(l.x + b * s * 8);
-  l.total = up(l.comp + b * s * static_cast<size_t>(k) * 8);
+  l.total = up(l.comp + b * s * (static_cast<size_t>(k) + kSmallBin) * 8);
   return l;
 }
 
