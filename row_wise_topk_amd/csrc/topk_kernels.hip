@@ -949,7 +949,7 @@ __device__ __forceinline__ void load_block(u32x4 (&r)[V], const char* xrow, uint
 }
 
 // ---------------------------------------------------------------- epilogue
-// Order the m results held in comp[0, m) (m <= KMAX).  The sort key
+// Order the m results held in comp[0, m) (m <= MMAX).  The sort key
 // (ascending = output order) is ~composite by value and the column by
 // column; both are unique.  Every thread keeps the same elements in registers
 // throughout and only their final positions are worked out, level by level:
@@ -962,24 +962,24 @@ __device__ __forceinline__ void load_block(u32x4 (&r)[V], const char* xrow, uint
 //    a larger bin becomes a segment of the next level, binned on the exact
 //    minimum and maximum of its own keys (so a run of equal values, whose keys
 //    differ only in the column, spreads out at once).
-// Regions: R0 = comp[0, KMAX) receives the sorted output, R1 = comp[KMAX,
-// 2 KMAX) holds the grouped elements, and after R1 come two segment tables
+// Regions: R0 = comp[0, MMAX) receives the sorted output, R1 = comp[MMAX,
+// 2 MMAX) holds the grouped elements, and after R1 come two segment tables
 // (this level's and the next), 4 words of 64 bits per segment.
 constexpr int kSortSegs = 128;   // > 4096 / 33, the most segments a level can make
 
-template <int NT, int CAP, int KMAX>
+template <int NT, int CAP, int MMAX>
 __device__ __noinline__ void sort_results(Smem<CAP, NT>& sm, uint32_t m, bool by_value,
                                           u64 key_lo, uint32_t span_bits) {
-  static_assert(2 * KMAX + 2 * 4 * kSortSegs <= CAP, "sort regions");
+  static_assert(2 * MMAX + 2 * 4 * kSortSegs <= CAP, "sort regions");
   constexpr uint32_t H = 32;              // bins larger than this are split again
-  constexpr int PER = KMAX / NT;          // elements per thread at most
+  constexpr int PER = MMAX / NT;          // elements per thread at most
   constexpr int RB = 8;                   // in-bin rank: members read per round
   constexpr uint32_t kDone = 0xFFFFu;
   const int t = threadIdx.x;
   u64* out = sm.comp;
-  u64* grp = sm.comp + KMAX;
+  u64* grp = sm.comp + MMAX;
   // table entry: [0] lo, [1] start | base << 13 | shift << 25, [2] min, [3] max
-  u64* tab[2] = {sm.comp + 2 * KMAX, sm.comp + 2 * KMAX + 4 * kSortSegs};
+  u64* tab[2] = {sm.comp + 2 * MMAX, sm.comp + 2 * MMAX + 4 * kSortSegs};
   auto order_key = [&](u64 c) -> u64 { return by_value ? ~c : static_cast<u64>(col_of(c)); };
 
   u64 c[PER];
@@ -1092,13 +1092,16 @@ __device__ __noinline__ void sort_results(Smem<CAP, NT>& sm, uint32_t m, bool by
   }
 }
 
-template <int NT, int CAP, int KMAX>
+// The buffer holds m candidates: exactly the top min(k, L) after an exact
+// cut, or (value order only) every candidate above the threshold, at most
+// MMAX of them, of which the sort puts the top k first.
+template <int NT, int CAP, int MMAX>
 __device__ __forceinline__ void write_outputs(Smem<CAP, NT>& sm, const KArgs& a, bool bf16,
                                               int row, int cur, uint32_t status, uint32_t L) {
   const int t = threadIdx.x;
   const uint32_t k = a.k;
   const int64_t out0 = static_cast<int64_t>(row) * k;
-  uint32_t m = min(uniform(sm.cnt[cur]), k);
+  uint32_t m = min(uniform(sm.cnt[cur]), a.sorted == 1 ? static_cast<uint32_t>(MMAX) : k);
   if (status) m = 0;
   if (a.sorted != 0 && m > 1) {
     // Bounds of the sort keys: every result is above the threshold and has a
@@ -1106,11 +1109,12 @@ __device__ __forceinline__ void write_outputs(Smem<CAP, NT>& sm, const KArgs& a,
     if (a.sorted == 1) {
       const u64 lo = static_cast<u64>(~uniform(sm.hikey)) << 32;
       const u64 hi = ~uniform64(sm.thr) - 1u;
-      sort_results<NT, CAP, KMAX>(sm, m, true, lo, bit_length64(hi - lo));
+      sort_results<NT, CAP, MMAX>(sm, m, true, lo, bit_length64(hi - lo));
     } else {
-      sort_results<NT, CAP, KMAX>(sm, m, false, 0ull, bit_length(L - 1u));
+      sort_results<NT, CAP, MMAX>(sm, m, false, 0ull, bit_length(L - 1u));
     }
   }
+  m = min(m, k);
   const char* xrow = static_cast<const char*>(a.x) + static_cast<int64_t>(row) * a.row_stride * (bf16 ? 2 : 4);
 
   for (uint32_t j = t; j < k; j += NT) {
@@ -1146,10 +1150,14 @@ __device__ __forceinline__ void write_outputs(Smem<CAP, NT>& sm, const KArgs& a,
 
 // ---------------------------------------------------------------- the kernel
 template <bool BF16, int CLS, bool MULTI>
-__global__ __launch_bounds__(class_threads(CLS)) void topk_kernel(KArgs a) {
+__global__ __launch_bounds__(class_threads(CLS), 2) void topk_kernel(KArgs a) {
   constexpr int NT = class_threads(CLS);
   constexpr int CAP = class_cap(CLS);
   constexpr int KMAX = class_kmax(CLS);
+  // A value sort takes up to SORT_CAP candidates, so for value order the
+  // exact cut is skipped whenever all candidates above the threshold fit:
+  // the sort puts the top k first.
+  constexpr int SORT_CAP = CLS <= 1 ? 2 * KMAX : KMAX;
   constexpr int EPV = BF16 ? 8 : 4;
   constexpr int ESZ = BF16 ? 2 : 4;
   constexpr int V = kBlockElems / (NT * EPV);
@@ -1158,6 +1166,7 @@ __global__ __launch_bounds__(class_threads(CLS)) void topk_kernel(KArgs a) {
   __shared__ Smem<CAP, NT> sm;
 
   const int t = threadIdx.x, lane = t & 63;
+  const uint32_t wid = uniform(static_cast<uint32_t>(t) >> 6);   // wave index, in a scalar register
   const int S = MULTI ? a.segments : 1;
   const int seg = MULTI ? static_cast<int>(blockIdx.x) % S : 0;
   int row = MULTI ? static_cast<int>(blockIdx.x) / S : static_cast<int>(blockIdx.x);
@@ -1215,7 +1224,7 @@ __global__ __launch_bounds__(class_threads(CLS)) void topk_kernel(KArgs a) {
   // by step parity; the maximum over the waves is the count after the block.
   int par = 0;
   auto count_after_step = [&](uint32_t after) -> uint32_t {
-    if (lane == 0) sm.snap[par][t >> 6] = after;
+    if (lane == 0) sm.snap[par][wid] = after;
     __syncthreads();
     uint32_t c = 0;
 #pragma unroll
@@ -1327,9 +1336,15 @@ __global__ __launch_bounds__(class_threads(CLS)) void topk_kernel(KArgs a) {
   // at least k candidates above it, so the merge drops everything at or
   // below it.  The buffer is not compacted: the hand-over below reads it
   // filtered by the threshold.
-  cur = cut_buffer<NT, CAP>(sm, cur, k, MULTI ? k + kSmallBin : k, L, hi_key(),
-                            MULTI ? (k + static_cast<uint32_t>(S) - 1u) / static_cast<uint32_t>(S) : 0u,
-                            MULTI);
+  if (!MULTI) {   // hikey bounds every candidate's key, cut or no cut
+    const uint32_t hk = wave_max(hi_key());
+    if (lane == 0) atomicMax(&sm.hikey, hk);
+    __syncthreads();
+  }
+  if (MULTI || a.sorted != 1 || uniform(sm.cnt[cur]) > static_cast<uint32_t>(SORT_CAP))
+    cur = cut_buffer<NT, CAP>(sm, cur, k, MULTI ? k + kSmallBin : k, L, hi_key(),
+                              MULTI ? (k + static_cast<uint32_t>(S) - 1u) / static_cast<uint32_t>(S) : 0u,
+                              MULTI);
 
   if (MULTI) {
     // Hand the survivors to the row's last workgroup: each workgroup reserves
@@ -1396,12 +1411,12 @@ __global__ __launch_bounds__(class_threads(CLS)) void topk_kernel(KArgs a) {
     // first two chunks of survivors.  The chunks need no count first: the
     // row's array is zero past its fill, and zero is never above a threshold.
     // Two chunks hold the survivors of up to 8 workgroups at the class's
-    // largest k (within a register budget of 16 per thread per chunk), so the
+    // largest k (within a register budget of 17 per thread per chunk), so the
     // merge usually waits for one round trip only.  A chunk must also fit in
     // the buffer after a cut (at most k + slack candidates remain).
     constexpr int PER_FIT = (8 * (KMAX + static_cast<int>(kSmallBin)) + 2 * NT - 1) / (2 * NT);
     constexpr int PER_ROOM = (CAP - (3 * KMAX + class_trigger(CLS)) / 4) / NT;
-    constexpr int PER_A = PER_FIT > 16 ? 16 : PER_FIT;
+    constexpr int PER_A = PER_FIT > 17 ? 17 : PER_FIT;
     constexpr int PER_B = PER_A > PER_ROOM ? PER_ROOM : PER_A;
     constexpr int PER = PER_B < 4 ? 4 : PER_B;
     static_assert(PER * NT + (3 * KMAX + class_trigger(CLS)) / 4 <= CAP, "merge chunk room");
@@ -1470,7 +1485,7 @@ __global__ __launch_bounds__(class_threads(CLS)) void topk_kernel(KArgs a) {
       // not fit, cut first and filter the chunk again with the raised bound.
       const uint32_t wk = wave_max(kmax);
       if (lane == 0) {
-        sm.snap[par][t >> 6] = tot;
+        sm.snap[par][wid] = tot;
         atomicMax(&sm.hikey, wk);
       }
       __syncthreads();
@@ -1510,7 +1525,9 @@ __global__ __launch_bounds__(class_threads(CLS)) void topk_kernel(KArgs a) {
       }
       if (c0 + 3 * CHUNK < total) load_chunk(c0 + 3 * CHUNK, vb);
     }
-    cur = cut_buffer<NT, CAP>(sm, cur, k, k, L, hi_key());
+    __syncthreads();   // every append is counted
+    if (a.sorted != 1 || uniform(sm.cnt[cur]) > static_cast<uint32_t>(SORT_CAP))
+      cur = cut_buffer<NT, CAP>(sm, cur, k, k, L, hi_key());
     if (t == 0) {
       st_agent(&a.ws_done[row], 0u);
       st_agent(&a.ws_flags[row], 0u);
@@ -1520,7 +1537,7 @@ __global__ __launch_bounds__(class_threads(CLS)) void topk_kernel(KArgs a) {
   }
 
   status |= sm.flags;
-  write_outputs<NT, CAP, KMAX>(sm, a, BF16, row, cur, status, L);
+  write_outputs<NT, CAP, SORT_CAP>(sm, a, BF16, row, cur, status, L);
 }
 
 }  // namespace
