@@ -13,6 +13,13 @@ roofline     the kernel's own average duration from HIP events around every
              WRITE_SIZE per launch) comes from the committed rocprofv3 counter
              summary when the kernel source still matches it.
 cpu_baseline the CPU oracle (full stable sort per row) on the host cores.
+read_ceiling the same input bytes read by a kernel with the same grid, block
+             order and loads that does nothing else (ds_read_ceiling): the
+             achievable ceiling of this access pattern, and value's fraction
+             of it.
+return_values_ab
+             µs per call with and without the values output (the pages note
+             that skipping the values is faster).
 
   python bench.py [--steps K] [--warmup W] [--config N] [--no-cpu]
   python bench.py --calibrate-copy ...        also run a plain 256 MiB copy first
@@ -227,6 +234,34 @@ def main():
     achieved = alg_bytes / (kernel_ms * 1e-3) / 1e9
     traffic = _traffic(w.name)
 
+    def timed(fn, reps):
+        for i in range(min(args.warmup, 5)):
+            fn(i)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(reps):
+            fn(i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / reps
+
+    # Read ceiling: the same bytes, blocks, workgroups and loads, and nothing else.
+    sink = torch.zeros((1,), dtype=torch.int32, device=dev)
+    ceil_us = timed(lambda i: rt.read_ceiling(views[i % n_copies], w.k, end=end_t, plan=plan,
+                                              sink=sink), args.steps)
+    ceil_gbps = alg_bytes / (ceil_us * 1e-6) / 1e9
+
+    # The same calls with the values output switched the other way.
+    alt = not w.return_values
+    alt_vals = torch.empty((w.batch, w.k), dtype=base.dtype, device=dev) if alt else None
+    alt_us = timed(lambda i: rt.topk(views[i % n_copies], w.k, end=end_t, sorted=w.sorted,
+                                     return_values=alt, index_dtype=it,
+                                     out=(alt_vals, indices, status), plan=plan), args.steps)
+    us_call = ms_per_step * 1e3
+    ab = {"with_values_us": round(alt_us if alt else us_call, 3),
+          "without_values_us": round(us_call if alt else alt_us, 3)}
+
     torch_us = None
     if not args.no_torch:
         xs = views[0]
@@ -285,6 +320,9 @@ def main():
                      "traffic": traffic, "kernel_us_mean": round(kernel_ms * 1e3, 3),
                      "kernel_us_median": round(kernel_med_ms * 1e3, 3),
                      "algorithmic_bytes": alg_bytes},
+        "read_ceiling": {"us_per_call": round(ceil_us, 3), "GBps": round(ceil_gbps, 2),
+                         "frac_of_ceiling": round(value / ceil_gbps, 4)},
+        "return_values_ab": ab,
         "effective_GBps_with_outputs": round((alg_bytes + out_bytes) / (ms_per_step * 1e-3) / 1e9, 2),
         "torch_topk_us": None if torch_us is None else round(torch_us, 2),
         "cpu_baseline": cpu,

@@ -172,6 +172,26 @@ int64_t ds_topk_stride_requirement(ds_dtype_t dtype);
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* ds_topk_status_string(ds_status_t status);
 
+/*
+ * Measurement aid, not part of the selection.  The pages rate a TopK by its
+ * effective bandwidth, the input bytes it must read over its time [XH,
+ * "torch.topk 的性能痛点"].  This call reads exactly the bytes ds_topk_ex
+ * would read for the same arguments -- each valid element x[i, 0:L) once,
+ * in the same blocks, block order, workgroups and 16-byte loads -- and does
+ * nothing else, so its time is the read ceiling of that access pattern.
+ *   x, dtype, batch, n_cols, row_stride, end, k, plan   as for ds_topk_ex
+ *                (k and plan fix the workgroup layout only).
+ *   sink         device pointer to one uint32_t, 4-B aligned; the kernel
+ *                writes it only in the rare case that the folded data equals
+ *                a fixed constant, so its content means nothing.
+ *   stream       HIP stream the single kernel launch is queued on.
+ * Returns DS_OK, the argument error ds_topk_ex would return for these
+ * arguments (DS_ERR_NULL also for a NULL sink), or DS_ERR_HIP.
+ */
+ds_status_t ds_read_ceiling(const void* x, ds_dtype_t dtype, int64_t batch, int64_t n_cols,
+                            int64_t row_stride, const int32_t* end, int32_t k,
+                            const ds_topk_plan_t* plan, uint32_t* sink, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -7,7 +7,8 @@ and the current stream.
 
 Raw entry points carry the C names and arguments (``ds_topk``, ``ds_topk_ex``,
 ``ds_topk_validate``, ``ds_topk_workspace_size``, ``ds_topk_workspace_size_ex``,
-``ds_topk_stride_requirement``, ``ds_topk_status_string``).  :func:`topk` is the
+``ds_topk_stride_requirement``, ``ds_topk_status_string``, and the measurement
+aid ``ds_read_ceiling``).  :func:`topk` is the
 tensor-level call, the counterpart of ``deep_select.topk(x, topk, sorted_index,
 indices_type, return_value)`` described on xhh.club, "DeepSeek开源DeepSelect：
 比torch.topk快二十倍！" (Q&A), with a per-row ``end`` as described on
@@ -69,6 +70,9 @@ _lib.ds_topk_stride_requirement.argtypes = [ctypes.c_int]
 _lib.ds_topk_stride_requirement.restype = ctypes.c_int64
 _lib.ds_topk_status_string.argtypes = [ctypes.c_int]
 _lib.ds_topk_status_string.restype = ctypes.c_char_p
+_lib.ds_read_ceiling.argtypes = [_vp, ctypes.c_int, _i64, _i64, _i64, _vp, _i32,
+                                ctypes.POINTER(Plan), _vp, _vp]
+_lib.ds_read_ceiling.restype = ctypes.c_int
 
 
 def exported_names() -> list[str]:
@@ -124,6 +128,11 @@ def ds_topk_stride_requirement(dtype) -> int:
 
 def ds_topk_status_string(status) -> str:
     return _lib.ds_topk_status_string(status).decode()
+
+
+def ds_read_ceiling(x, dtype, batch, n_cols, row_stride, end, k, plan, sink, stream) -> int:
+    return _lib.ds_read_ceiling(x, dtype, batch, n_cols, row_stride, end, k, _plan_ptr(plan),
+                                sink, stream)
 
 
 # ---------------------------------------------------------------- tensor-level call
@@ -204,6 +213,26 @@ def topk(x: torch.Tensor, k: int, *, end: torch.Tensor | None = None, sorted: in
     if rc != DS_OK:
         raise TopkError(rc)
     return values, indices, status
+
+
+def read_ceiling(x: torch.Tensor, k: int, *, end: torch.Tensor | None = None,
+                 n_cols: int | None = None, plan=None, sink: torch.Tensor | None = None) -> None:
+    """Queue the read-ceiling kernel on the current stream: the bytes
+    :func:`topk` would read for the same arguments, read the same way, and
+    nothing else (a measurement aid; see ``ds_read_ceiling``)."""
+    if x.dim() != 2 or not x.is_cuda or x.dtype not in _DT:
+        raise ValueError("x must be a 2-D float32 / bfloat16 CUDA tensor")
+    batch = x.shape[0]
+    n_cols = x.shape[1] if n_cols is None else int(n_cols)
+    row_stride = x.stride(0) if batch > 1 else max(x.stride(0), x.shape[1])
+    if sink is None:
+        sink = torch.empty((1,), dtype=torch.int32, device=x.device)
+    stream = torch.cuda.current_stream(x.device).cuda_stream
+    rc = ds_read_ceiling(x.data_ptr(), _DT[x.dtype], batch, n_cols, row_stride,
+                         end.data_ptr() if end is not None else None, int(k), plan,
+                         sink.data_ptr(), stream)
+    if rc != DS_OK:
+        raise TopkError(rc)
 
 
 def pad_rows(x: torch.Tensor) -> torch.Tensor:

@@ -190,6 +190,33 @@ size_t ds_topk_workspace_size(ds_dtype_t dtype, int64_t batch, int64_t n_cols, i
   return ds_topk_workspace_size_ex(dtype, batch, n_cols, k, nullptr);
 }
 
+ds_status_t ds_read_ceiling(const void* x, ds_dtype_t dtype, int64_t batch, int64_t n_cols,
+                            int64_t row_stride, const int32_t* end, int32_t k,
+                            const ds_topk_plan_t* plan, uint32_t* sink, hipStream_t stream) {
+  ds_status_t st = check_scalars(dtype, batch, n_cols, row_stride, k, 1, DS_INT32);
+  if (st != DS_OK) return st;
+  Plan pl;
+  st = resolve_plan(batch, n_cols, k, plan, &pl);
+  if (st != DS_OK || batch == 0) return st;
+  if (!sink || (n_cols > 0 && !x)) return DS_ERR_NULL;
+  if ((x && misaligned(x, 16)) || (row_stride * elem_size(dtype)) % 16 != 0) return DS_ERR_ALIGN;
+  if (misaligned(sink, 4) || (end && misaligned(end, 4))) return DS_ERR_ALIGN;
+  if (batch * static_cast<int64_t>(pl.segments) > INT32_MAX) return DS_ERR_SHAPE;
+  KArgs a{};
+  a.x = x;
+  a.row_stride = row_stride;
+  a.n_cols = static_cast<int32_t>(n_cols);
+  a.batch = static_cast<int32_t>(batch);
+  a.end = end;
+  a.k = k;
+  a.segments = pl.segments;
+  a.perm_seed = pl.seed;
+  a.in_order = pl.in_order;
+  a.trigger = pl.trigger;
+  const int err = launch_read(a, dtype == DS_BF16 ? 1 : 0, pl.cls, sink, stream);
+  return err == 0 ? DS_OK : DS_ERR_HIP;
+}
+
 int64_t ds_topk_stride_requirement(ds_dtype_t dtype) {
   if (dtype == DS_FP32) return 4;
   if (dtype == DS_BF16) return 8;

@@ -66,4 +66,8 @@ WsLayout ws_layout(int64_t batch, int segments, int k);
 // hipError_t of the launch.
 int launch_topk(const KArgs& a, int dtype, int cls, hipStream_t stream);
 
+// Queue the read-ceiling kernel (same grid and loads as launch_topk, no
+// selection).  Returns the hipError_t of the launch.
+int launch_read(const KArgs& a, int dtype, int cls, uint32_t* sink, hipStream_t stream);
+
 }  // namespace dstk

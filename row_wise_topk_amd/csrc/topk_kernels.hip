@@ -1540,6 +1540,57 @@ __global__ __launch_bounds__(class_threads(CLS), 2) void topk_kernel(KArgs a) {
   write_outputs<NT, CAP, SORT_CAP>(sm, a, BF16, row, cur, status, L);
 }
 
+// ---------------------------------------------------------------- read ceiling
+// A measurement aid, not part of the selection: the TopK stream's grid, block
+// order and 16-byte loads (a ring of four blocks, three in flight), with the
+// data only folded into one word per lane.  The word is stored only if it
+// equals a constant, so no load can be dropped.  Its time is the read ceiling
+// of this access pattern on the same input.
+template <bool BF16, int NT>
+__global__ __launch_bounds__(NT, 2) void read_kernel(KArgs a, uint32_t* sink) {
+  constexpr int EPV = BF16 ? 8 : 4;
+  constexpr int ESZ = BF16 ? 2 : 4;
+  constexpr int V = kBlockElems / (NT * EPV);
+  const int S = a.segments;
+  const int seg = static_cast<int>(blockIdx.x) % S;
+  const int row = static_cast<int>(blockIdx.x) / S;
+  uint32_t L = static_cast<uint32_t>(a.n_cols);
+  if (a.end) {
+    const int32_t e = a.end[row];
+    L = (e < 0 || e > a.n_cols) ? 0u : static_cast<uint32_t>(e);
+  }
+  const uint32_t nb = (L + kBlockElems - 1) / kBlockElems;
+  const uint32_t ntl = nb > static_cast<uint32_t>(seg) ? (nb - seg + S - 1) / S : 0u;
+  const BlockOrder order(nb, a.perm_seed, static_cast<uint32_t>(row), a.in_order != 0);
+  const char* xrow = static_cast<const char*>(a.x) + static_cast<int64_t>(row) * a.row_stride * ESZ;
+  auto ld = [&](u32x4 (&r)[V], uint32_t j) {
+    const uint32_t blk = ntl == 0 ? 0u : order(seg + (j < ntl ? j : ntl - 1u) * S);
+    load_block<BF16, V, NT>(r, xrow, blk, j < ntl ? L : 0u);
+  };
+  uint32_t acc = 0;
+  auto use = [&](const u32x4 (&r)[V]) {
+#pragma unroll
+    for (int v = 0; v < V; ++v) acc += (r[v].x ^ r[v].y) + (r[v].z ^ r[v].w);
+  };
+  u32x4 r0[V], r1[V], r2[V], r3[V];
+  if (ntl > 0) {
+    ld(r0, 0);
+    ld(r1, 1);
+    ld(r2, 2);
+  }
+  for (uint32_t u = 0; u < ntl; u += 4) {
+    ld(r3, u + 3);
+    use(r0);
+    ld(r0, u + 4);
+    use(r1);
+    ld(r1, u + 5);
+    use(r2);
+    ld(r2, u + 6);
+    use(r3);
+  }
+  if (acc == 0x9E3779B9u) sink[0] = acc;
+}
+
 }  // namespace
 
 WsLayout ws_layout(int64_t batch, int segments, int k) {
@@ -1565,6 +1616,19 @@ static int launch_one(const KArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((topk_kernel<BF16, CLS, true>), grid, block, 0, stream, a);
   else
     hipLaunchKernelGGL((topk_kernel<BF16, CLS, false>), grid, block, 0, stream, a);
+  return static_cast<int>(hipGetLastError());
+}
+
+int launch_read(const KArgs& a, int dtype, int cls, uint32_t* sink, hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.batch) * a.segments));
+  const int nt = class_threads(cls);
+  if (dtype == 0) {
+    if (nt == 512) hipLaunchKernelGGL((read_kernel<false, 512>), grid, dim3(512), 0, stream, a, sink);
+    else hipLaunchKernelGGL((read_kernel<false, 256>), grid, dim3(256), 0, stream, a, sink);
+  } else {
+    if (nt == 512) hipLaunchKernelGGL((read_kernel<true, 512>), grid, dim3(512), 0, stream, a, sink);
+    else hipLaunchKernelGGL((read_kernel<true, 256>), grid, dim3(256), 0, stream, a, sink);
+  }
   return static_cast<int>(hipGetLastError());
 }
 

@@ -23,7 +23,7 @@ def test_every_declared_symbol_is_exported():
     names = rt.exported_names()
     assert {"ds_topk", "ds_topk_ex", "ds_topk_validate", "ds_topk_workspace_size",
             "ds_topk_workspace_size_ex", "ds_topk_stride_requirement",
-            "ds_topk_status_string"} <= set(names)
+            "ds_topk_status_string", "ds_read_ceiling"} <= set(names)
     lib = ctypes.CDLL(rt.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -128,6 +128,29 @@ def test_invalid_call_returns_before_launch():
     rc = rt.ds_topk_ex(A16, rt.DS_FP32, 0, 1000, 1000, None, 5, 1, 1, rt.DS_INT32, None, None,
                        None, None, 0, None, None)
     assert rc == ERR["DS_OK"]   # batch == 0: nothing to do
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"sink": None}, "DS_ERR_NULL"),
+    ({"x": None}, "DS_ERR_NULL"),
+    ({"sink": A16b + 2}, "DS_ERR_ALIGN"),
+    ({"x": A16 + 4}, "DS_ERR_ALIGN"),
+    ({"row_stride": 1002}, "DS_ERR_ALIGN"),
+    ({"end": A16 + 2}, "DS_ERR_ALIGN"),
+    ({"k": 0}, "DS_ERR_K_RANGE"),
+    ({"dtype": 3}, "DS_ERR_DTYPE"),
+    ({"row_stride": 996}, "DS_ERR_SHAPE"),
+    ({"plan": {"segments": 300}}, "DS_ERR_PLAN"),
+    ({"batch": 0, "x": None, "sink": None}, "DS_OK"),
+])
+def test_read_ceiling_argument_errors(kw, code):
+    # Every case returns before a launch (batch == 0 launches nothing).
+    a = dict(x=A16, dtype=rt.DS_FP32, batch=4, n_cols=1000, row_stride=1000, end=None, k=10,
+             plan=None, sink=A16b, stream=None)
+    a.update(kw)
+    rc = rt.ds_read_ceiling(a["x"], a["dtype"], a["batch"], a["n_cols"], a["row_stride"],
+                            a["end"], a["k"], a["plan"], a["sink"], a["stream"])
+    assert rc == ERR[code]
 
 
 def test_product_path_has_no_oracle_or_fallback():
