@@ -787,7 +787,7 @@ __device__ __noinline__ RaggedResult filter_ragged(BlockRegs<V> r, uint32_t blk,
   return {after, hi_lane, nl ? 1u : 0u};
 }
 
-// A starting threshold from one whole block held in registers, before any of
+// Starting thresholds from one whole block held in registers, before any of
 // it is appended.  The block's values are binned linearly between their
 // finite minimum and maximum (2048 bins; -inf and +inf clamp to the end
 // bins, NaN is left out).  Linear bins spread the usual bell-shaped scores
@@ -796,9 +796,16 @@ __device__ __noinline__ RaggedResult filter_ragged(BlockRegs<V> r, uint32_t blk,
 // bin b* with at least k elements in bins >= b*; since the binning is
 // monotone, the smallest key among those elements is a threshold with at
 // least k of the block's elements at or above it -- a valid (monotone)
-// starting point for the row.  Leaves hist zeroed.
+// starting point for the row (t0).  With need2 > 0 the same search for
+// need2 gives t2, with at least need2 of the block's elements at or above it:
+// only an estimate for the row, which the caller must verify.  Leaves hist
+// zeroed and res[3] = 0 (a free counter).
+struct ThrPair {
+  u64 t0, t2;
+};
 template <bool BF16, int V, int NT, int CAP>
-__device__ __noinline__ u64 block_threshold(BlockRegs<V> r, uint32_t k, Smem<CAP, NT>& sm) {
+__device__ __noinline__ ThrPair block_threshold(BlockRegs<V> r, uint32_t k, uint32_t need2,
+                                                Smem<CAP, NT>& sm) {
   constexpr int EPV = BF16 ? 8 : 4;
   constexpr int NS = V * EPV;
   const int t = threadIdx.x, lane = t & 63;
@@ -841,7 +848,7 @@ __device__ __noinline__ u64 block_threshold(BlockRegs<V> r, uint32_t k, Smem<CAP
   khi = uniform(sm.res[1]);
   if (khi < klo) {   // no finite value in the block
     __syncthreads();
-    return kThrInit;
+    return {kThrInit, kThrInit};
   }
   const float lo = __uint_as_float(bits_of_key(klo));
   const float hi = __uint_as_float(bits_of_key(khi));
@@ -857,77 +864,36 @@ __device__ __noinline__ u64 block_threshold(BlockRegs<V> r, uint32_t k, Smem<CAP
   for (int s = 0; s < NS; ++s)
     if (f[s] == f[s]) atomicAdd(&sm.hist[bin_of(f[s])], 1u);
   __syncthreads();
-  hist_find_top(sm, k);
+  hist_find_top(sm, k, need2);
   const uint32_t b = uniform(sm.res[0]);
-  if (b >= static_cast<uint32_t>(kBins)) return kThrInit;   // fewer than k non-NaN values
-  uint32_t tk = 0xFFFFFFFFu;
+  const uint32_t b2 = need2 ? uniform(sm.res[4]) : static_cast<uint32_t>(kBins);
+  if (b >= static_cast<uint32_t>(kBins)) return {kThrInit, kThrInit};   // fewer than k non-NaN values
+  uint32_t tk = 0xFFFFFFFFu, tk2 = 0xFFFFFFFFu;
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     const uint32_t key = key_of_bits(__float_as_uint(f[s]));
-    tk = (f[s] == f[s]) & (bin_of(f[s]) >= b) & (key < tk) ? key : tk;
+    const uint32_t bn = bin_of(f[s]);
+    tk = (f[s] == f[s]) & (bn >= b) & (key < tk) ? key : tk;
+    tk2 = (f[s] == f[s]) & (bn >= b2) & (key < tk2) ? key : tk2;
   }
   tk = wave_min(tk);
-  if (t == 0) sm.res[2] = 0xFFFFFFFFu;
+  tk2 = wave_min(tk2);
+  if (t == 0) {
+    sm.res[2] = 0xFFFFFFFFu;
+    sm.res[3] = 0u;
+    sm.res[4] = 0xFFFFFFFFu;
+  }
   __syncthreads();
-  if (lane == 0) atomicMin(&sm.res[2], tk);
+  if (lane == 0) {
+    atomicMin(&sm.res[2], tk);
+    atomicMin(&sm.res[4], tk2);
+  }
   __syncthreads();
-  return (static_cast<u64>(uniform(sm.res[2])) << 32) - 1u;
+  const u64 t0 = (static_cast<u64>(uniform(sm.res[2])) << 32) - 1u;
+  const uint32_t k2 = uniform(sm.res[4]);
+  return {t0, k2 == 0xFFFFFFFFu ? kThrInit : (static_cast<u64>(k2) << 32) - 1u};
 }
 
-// A second, tighter start over the first (up to) three whole blocks in the
-// ring, once a one-block threshold T (a key bound: admit key >= K1) is known.
-// The keys > K1 of those blocks are histogrammed on their own range
-// (K1, max]; keys equal to K1 are left out, so a run of equal values at the
-// bottom (exact zeros, say) costs no atomics on one hot counter.  A bin edge
-// with at least k of these elements at or above it is again a valid threshold
-// for the row.  Returns T if no such edge improves on it.  Leaves hist zeroed.
-template <bool BF16, int V, int NT, int CAP>
-__device__ __forceinline__ u64 ring_threshold(const BlockRegs<V>& b0, const BlockRegs<V>& b1,
-                                              const BlockRegs<V>& b2, uint32_t whole, u64 T,
-                                              uint32_t k, Smem<CAP, NT>& sm) {
-  constexpr int EPV = BF16 ? 8 : 4;
-  constexpr int NS = V * EPV;
-  const int t = threadIdx.x, lane = t & 63;
-  const uint32_t K1 = static_cast<uint32_t>(T >> 32) + 1u;
-  constexpr uint32_t kKeyMax = 0xFF800000u;   // key of +inf; NaN keys lie above
-  auto key_at = [&](const BlockRegs<V>& b, int s) -> uint32_t {
-    const uint32_t w = b.v[BF16 ? s / 8 : s / 4][BF16 ? (s % 8) / 2 : s % 4];
-    return key_of_bits(BF16 ? ((s & 1) ? (w & 0xFFFF0000u) : (w << 16)) : w);
-  };
-  auto each = [&](auto&& fn) {
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      if (whole & 1u) fn(key_at(b0, s));
-      if (whole & 2u) fn(key_at(b1, s));
-      if (whole & 4u) fn(key_at(b2, s));
-    }
-  };
-  uint32_t mx = 0;
-  each([&](uint32_t key) { mx = (key <= kKeyMax) & (key > mx) ? key : mx; });
-  mx = wave_max(mx);
-  if (t == 0) sm.res[0] = 0u;
-  __syncthreads();
-  if (lane == 0) atomicMax(&sm.res[0], mx);
-  __syncthreads();
-  mx = uniform(sm.res[0]);
-  if (mx <= K1) {   // nothing above K1 to tighten with
-    __syncthreads();
-    return T;
-  }
-  const uint32_t lo = K1 + 1u;
-  const uint32_t span = mx - lo;
-  const uint32_t shift = shift_for_span(span);
-  each([&](uint32_t key) {
-    const uint32_t d = key - lo;
-    if (d <= span) atomicAdd(&sm.hist[d >> shift], 1u);
-  });
-  __syncthreads();
-  hist_find_top(sm, k);
-  const uint32_t b = uniform(sm.res[0]);
-  if (b >= static_cast<uint32_t>(kBins)) return T;   // the k-th lies at K1 or below
-  const u64 T2 = (static_cast<u64>(lo + (b << shift)) << 32) - 1u;
-  return T2 > T ? T2 : T;
-}
 
 // Loads of one block.  Always issued, whatever the block: a vector that would
 // start at or past L reads the row's first vector instead (its lanes are
@@ -978,8 +944,11 @@ __device__ __noinline__ void sort_results(Smem<CAP, NT>& sm, uint32_t m, bool by
   const int t = threadIdx.x;
   u64* out = sm.comp;
   u64* grp = sm.comp + MMAX;
-  // table entry: [0] lo, [1] start | base << 13 | shift << 25, [2] min, [3] max
-  u64* tab[2] = {sm.comp + 2 * MMAX, sm.comp + 2 * MMAX + 4 * kSortSegs};
+  // Two segment tables after R1, addressed by offset into comp: a pointer
+  // picked at run time from an array would lose its LDS address space and
+  // turn every table access into a flat one.  Entry: [0] lo, [1] start |
+  // base << 13 | shift << 25, [2] min, [3] max.
+  constexpr uint32_t kTab0 = 2 * MMAX, kTab1 = 2 * MMAX + 4 * kSortSegs;
   auto order_key = [&](u64 c) -> u64 { return by_value ? ~c : static_cast<u64>(col_of(c)); };
 
   u64 c[PER];
@@ -991,8 +960,8 @@ __device__ __noinline__ void sort_results(Smem<CAP, NT>& sm, uint32_t m, bool by
     seg[j] = p < m ? 0u : kDone;
   }
   if (t == 0) {
-    tab[0][0] = key_lo;
-    tab[0][1] = static_cast<u64>(span_bits > kRadixBits ? span_bits - kRadixBits : 0u) << 25;
+    sm.comp[kTab0] = key_lo;
+    sm.comp[kTab0 + 1] = static_cast<u64>(span_bits > kRadixBits ? span_bits - kRadixBits : 0u) << 25;
   }
   __syncthreads();   // everything is in registers: R0 may be written
   int cur = 0;
@@ -1000,14 +969,14 @@ __device__ __noinline__ void sort_results(Smem<CAP, NT>& sm, uint32_t m, bool by
   // least 8-fold); the cap only guards against a corrupted buffer.
 #pragma unroll 1
   for (int level = 0; level < 64; ++level) {
-    const u64* tc = tab[cur];
-    u64* tn = tab[cur ^ 1];
+    const uint32_t tc = cur ? kTab1 : kTab0;   // this level's table
+    const uint32_t tn = cur ? kTab0 : kTab1;   // the next level's
     uint32_t bin[PER], start[PER], base[PER];
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const uint32_t sj = seg[j] == kDone ? 0u : seg[j];
-      const u64 lo = tc[4 * sj];
-      const uint32_t pk = static_cast<uint32_t>(tc[4 * sj + 1]);
+      const u64 lo = sm.comp[tc + 4 * sj];
+      const uint32_t pk = static_cast<uint32_t>(sm.comp[tc + 4 * sj + 1]);
       start[j] = pk & 0x1FFFu;
       base[j] = (pk >> 13) & 0xFFFu;
       bin[j] = base[j] + static_cast<uint32_t>((order_key(c[j]) - lo) >> (pk >> 25));
@@ -1055,8 +1024,8 @@ __device__ __noinline__ void sort_results(Smem<CAP, NT>& sm, uint32_t m, bool by
         seg[j] = kDone;
       } else if (grp[first[j]] == c[j]) {
         const uint32_t id = atomicAdd(&sm.nwork, 1u);
-        tn[4 * id + 2] = ~0ull;
-        tn[4 * id + 3] = 0ull;
+        sm.comp[tn + 4 * id + 2] = ~0ull;
+        sm.comp[tn + 4 * id + 3] = 0ull;
         sm.hist[bin[j]] = id;   // read back by the bin's members
       }
     }
@@ -1067,8 +1036,8 @@ __device__ __noinline__ void sort_results(Smem<CAP, NT>& sm, uint32_t m, bool by
       if (seg[j] == kDone) continue;
       seg[j] = sm.hist[bin[j]];
       const u64 q = order_key(c[j]);
-      atomicMin(&tn[4 * seg[j] + 2], q);
-      atomicMax(&tn[4 * seg[j] + 3], q);
+      atomicMin(&sm.comp[tn + 4 * seg[j] + 2], q);
+      atomicMax(&sm.comp[tn + 4 * seg[j] + 3], q);
     }
     __syncthreads();
     hist_zero_own(sm);
@@ -1077,15 +1046,15 @@ __device__ __noinline__ void sort_results(Smem<CAP, NT>& sm, uint32_t m, bool by
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       if (seg[j] == kDone || grp[first[j]] != c[j]) continue;
-      const u64 mn = tn[4 * seg[j] + 2], mx = tn[4 * seg[j] + 3];
+      const u64 mn = sm.comp[tn + 4 * seg[j] + 2], mx = sm.comp[tn + 4 * seg[j] + 3];
       const uint32_t s0 = first[j], s1 = first[j] + cnt[j];
       const uint32_t b_lo = static_cast<uint32_t>((static_cast<u64>(s0) * kBins) / m);
       const uint32_t b_hi = static_cast<uint32_t>((static_cast<u64>(s1) * kBins) / m);
       const uint32_t bits = bit_length64(mx - mn);
       const uint32_t nbits = 31u - static_cast<uint32_t>(__clz(b_hi - b_lo));
       const uint32_t sh = bits > nbits ? bits - nbits : 0u;
-      tn[4 * seg[j]] = mn;
-      tn[4 * seg[j] + 1] = static_cast<u64>(s0 | (b_lo << 13) | (sh << 25));
+      sm.comp[tn + 4 * seg[j]] = mn;
+      sm.comp[tn + 4 * seg[j] + 1] = static_cast<u64>(s0 | (b_lo << 13) | (sh << 25));
     }
     __syncthreads();   // the histogram and the next table are ready
     cur ^= 1;
@@ -1255,22 +1224,48 @@ __global__ __launch_bounds__(class_threads(CLS), 2) void topk_kernel(KArgs a) {
         BlockRegs<V> br;
 #pragma unroll
         for (int v = 0; v < V; ++v) br.v[v] = cur_r[v];
-        u64 t0 = block_threshold<BF16, V, NT, CAP>(br, k, sm);
-        if (!MULTI && ntl >= 2 && t0 != kThrInit) {
-          // One workgroup streams the whole row: tighten over the whole blocks
-          // already in the ring, which saves cuts later in a long stream.
-          uint32_t whole = 0;
+        // One workgroup streams the whole row: the whole blocks already in the
+        // ring (up to three) can vouch for a tighter start, which saves cuts
+        // later in a long stream.  t2 estimates, from the first block alone
+        // and with 10% to spare, the edge with k of those blocks' elements at
+        // or above it; a plain count over them confirms it before it is used.
+        uint32_t whole = 0;
+        if (!MULTI) {
 #pragma unroll
           for (uint32_t j = 0; j < 3; ++j)
             if (j < ntl && blk_at(j) * static_cast<uint32_t>(kBlockElems) + kBlockElems <= L)
               whole |= 1u << j;
-          BlockRegs<V> a1, a2;
+        }
+        const uint32_t nw = static_cast<uint32_t>(__popc(whole));
+        const uint32_t need2 = nw >= 2u ? (11u * k + 10u * nw - 1u) / (10u * nw) : 0u;
+        const ThrPair tp = block_threshold<BF16, V, NT, CAP>(br, k, need2, sm);
+        u64 t0 = tp.t0;
+        if (need2 != 0u && t0 != kThrInit && tp.t2 > t0) {
+          const uint32_t tk2 = static_cast<uint32_t>(tp.t2 >> 32) + 1u;
+          uint32_t n = 0;
+          auto count_in = [&](const u32x4 (&rr)[V]) {
 #pragma unroll
-          for (int v = 0; v < V; ++v) {
-            a1.v[v] = r1[v];
-            a2.v[v] = r2[v];
-          }
-          t0 = ring_threshold<BF16, V, NT, CAP>(br, a1, a2, whole, t0, k, sm);
+            for (int v = 0; v < V; ++v) {
+              const uint32_t w[4] = {rr[v].x, rr[v].y, rr[v].z, rr[v].w};
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+#pragma unroll
+                for (int h = 0; h < (BF16 ? 2 : 1); ++h) {
+                  const uint32_t bits = BF16 ? (h ? (w[q] & 0xFFFF0000u) : (w[q] << 16)) : w[q];
+                  const bool ok = ((bits & 0x7FFFFFFFu) <= 0x7F800000u) & (key_of_bits(bits) >= tk2);
+                  n += ok ? 1u : 0u;
+                }
+              }
+            }
+          };
+          count_in(cur_r);
+          if (whole & 2u) count_in(r1);
+          if (whole & 4u) count_in(r2);
+          const uint32_t wt = static_cast<uint32_t>(
+              __builtin_amdgcn_readlane(static_cast<int>(wave_prefix_sum(n)), 63));
+          if (lane == 0) atomicAdd(&sm.res[3], wt);
+          __syncthreads();
+          if (uniform(sm.res[3]) >= k) t0 = tp.t2;
         }
         if (t0 > thr) {
           thr = t0;
