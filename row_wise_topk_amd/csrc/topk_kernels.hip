@@ -1224,18 +1224,17 @@ __global__ __launch_bounds__(class_threads(CLS), 2) void topk_kernel(KArgs a) {
         BlockRegs<V> br;
 #pragma unroll
         for (int v = 0; v < V; ++v) br.v[v] = cur_r[v];
-        // One workgroup streams the whole row: the whole blocks already in the
-        // ring (up to three) can vouch for a tighter start, which saves cuts
-        // later in a long stream.  t2 estimates, from the first block alone
-        // and with 10% to spare, the edge with k of those blocks' elements at
-        // or above it; a plain count over them confirms it before it is used.
+        // The whole blocks already in the ring (up to three) can vouch for a
+        // tighter start, which saves appends and cuts later.  t2 estimates,
+        // from the first block alone and with 10% to spare, the edge with k
+        // of those blocks' elements at or above it; a plain count over them
+        // confirms it before it is used.  They are elements of the row, so
+        // the edge is valid for the whole row, shared or not.
         uint32_t whole = 0;
-        if (!MULTI) {
 #pragma unroll
-          for (uint32_t j = 0; j < 3; ++j)
-            if (j < ntl && blk_at(j) * static_cast<uint32_t>(kBlockElems) + kBlockElems <= L)
-              whole |= 1u << j;
-        }
+        for (uint32_t j = 0; j < 3; ++j)
+          if (j < ntl && blk_at(j) * static_cast<uint32_t>(kBlockElems) + kBlockElems <= L)
+            whole |= 1u << j;
         const uint32_t nw = static_cast<uint32_t>(__popc(whole));
         const uint32_t need2 = nw >= 2u ? (11u * k + 10u * nw - 1u) / (10u * nw) : 0u;
         const ThrPair tp = block_threshold<BF16, V, NT, CAP>(br, k, need2, sm);
