@@ -931,13 +931,17 @@ __device__ __forceinline__ void load_block(u32x4 (&r)[V], const char* xrow, uint
 // Regions: R0 = comp[0, MMAX) receives the sorted output, R1 = comp[MMAX,
 // 2 MMAX) holds the grouped elements, and after R1 come two segment tables
 // (this level's and the next), 4 words of 64 bits per segment.
-constexpr int kSortSegs = 128;   // > 4096 / 33, the most segments a level can make
+constexpr int kSortSegs = 512;   // > 4096 / 9, the most segments a level can make
+// A level ranks bins of up to 32 members directly, unless the ranking work of
+// its bins of 9..32 members (the sum of their squared sizes) exceeds what
+// another level costs: then those bins are split again too (runs of equal
+// values make such bins, and the next level spreads them by column at once).
+constexpr uint32_t kSplitWork = 6000;
 
 template <int NT, int CAP, int MMAX>
 __device__ __noinline__ void sort_results(Smem<CAP, NT>& sm, uint32_t m, bool by_value,
                                           u64 key_lo, uint32_t span_bits) {
   static_assert(2 * MMAX + 2 * 4 * kSortSegs <= CAP, "sort regions");
-  constexpr uint32_t H = 32;              // bins larger than this are split again
   constexpr int PER = MMAX / NT;          // elements per thread at most
   constexpr int RB = 8;                   // in-bin rank: members read per round
   constexpr uint32_t kDone = 0xFFFFu;
@@ -982,12 +986,26 @@ __device__ __noinline__ void sort_results(Smem<CAP, NT>& sm, uint32_t m, bool by
       bin[j] = base[j] + static_cast<uint32_t>((order_key(c[j]) - lo) >> (pk >> 25));
       if (seg[j] != kDone) atomicAdd(&sm.hist[bin[j]], 1u);
     }
-    if (t == 0) sm.nwork = 0u;
+    if (t == 0) {
+      sm.nwork = 0u;
+      sm.res[4] = 0u;
+    }
     __syncthreads();
     uint32_t cnt[PER], first[PER], b0[PER];
 #pragma unroll
     for (int j = 0; j < PER; ++j) cnt[j] = sm.hist[bin[j]];
+    {
+      constexpr int BPT = kBins / NT;
+      uint32_t hb[BPT];
+      own_bins_read<BPT>(sm, hb);
+      uint32_t w2 = 0;
+#pragma unroll
+      for (int i = 0; i < BPT; ++i) w2 += (hb[i] > 8u) & (hb[i] <= 32u) ? hb[i] * hb[i] : 0u;
+      w2 = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(wave_prefix_sum(w2)), 63));
+      if ((t & 63) == 0 && w2) atomicAdd(&sm.res[4], w2);
+    }
     hist_exclusive_scan(sm);   // writes only after a barrier, so the reads above see counts
+    const uint32_t H = uniform(sm.res[4]) > kSplitWork ? 8u : 32u;   // bins above H split again
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       b0[j] = sm.hist[base[j]];
