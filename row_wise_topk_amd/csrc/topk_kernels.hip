@@ -252,7 +252,6 @@ struct Smem {
   uint32_t res[5];
   uint32_t cnt[2];            // append counters; cur receives appends, cur^1 the next cut
   uint32_t snap[2][NT / 64];  // per-wave count after its last append, by step parity
-  uint32_t segoff[4 * 128];   // epilogue sort: pending segments (4 words each)
   uint32_t hikey;             // upper bound of every candidate key
   uint32_t flags;             // row status bits
   uint32_t is_last;

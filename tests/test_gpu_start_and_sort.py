@@ -1,0 +1,78 @@
+"""GPU parity for two data-dependent choices inside the kernel.
+
+The start threshold over the whole ring blocks is an estimate from the first
+block, confirmed by a count over those blocks; rows whose first block is not
+like the next two make the count reject it (the row then starts from the
+first block's own bound), on one workgroup per row and on shared rows.
+
+The epilogue sort ranks small bins directly but splits bins of 9..32 members
+again when ranking them would cost more than another level; bf16 rows with a
+few dozen copies of each value among the results take that path, rows with
+small tie groups the other.  Either way the result is the oracle's, bit for
+bit.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import workloads
+from tests.gpu_util import BF16, FP32, check_case
+
+pytestmark = pytest.mark.gpu
+
+B = 4096   # elements per block
+
+
+def _blocky_rows(nblocks: int, big_every: int, seed: int, batch: int = 3) -> np.ndarray:
+    """Rows of nblocks whole blocks: block b holds 100 + U[0,1) when b is a
+    multiple of big_every, else U[0,1)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = rng.random((batch, nblocks * B), dtype=np.float32)
+    for b in range(0, nblocks, big_every):
+        x[:, b * B:(b + 1) * B] += np.float32(100.0)
+    return x
+
+
+@pytest.mark.parametrize("plan", [
+    {"segments": 1, "in_order": 1},   # ring 0,1,2: big, small, small -> estimate rejected
+    {"segments": 2, "in_order": 1},   # one workgroup rejects, the other confirms
+    {"segments": 3, "in_order": 1},
+    {"segments": 1},                  # random order: either outcome
+])
+@pytest.mark.parametrize("k", [1024, 2048])
+def test_start_estimate_rejected_or_confirmed_fp32(plan, k):
+    x = _blocky_rows(16, 4, seed=31 + k)
+    check_case(x, FP32, x.shape[1], k, 1, True, "int32", plan=plan,
+               name=f"blocky fp32 k={k} {plan}")
+
+
+@pytest.mark.parametrize("plan", [{"segments": 1, "in_order": 1}, {"segments": 2, "in_order": 1}])
+def test_start_estimate_rejected_bf16(plan):
+    x = workloads.to_bf16_bits(_blocky_rows(12, 3, seed=41))
+    check_case(x, BF16, x.shape[1], 512, 0, False, "int32", plan=plan,
+               name=f"blocky bf16 k=512 {plan}")
+    check_case(x, BF16, x.shape[1], 512, 1, True, "int64", plan=plan,
+               name=f"blocky bf16 k=512 sorted {plan}")
+
+
+def _levels_bf16(batch: int, n: int, levels: int, seed: int) -> np.ndarray:
+    """bf16 rows (as bits) taking `levels` consecutive bf16 codes from 1.0 up,
+    so `levels` distinct values, each about n / levels times."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    lv = rng.integers(0, levels, size=(batch, n))
+    return (0x3F80 + lv).astype(np.uint16)
+
+
+@pytest.mark.parametrize("levels,k", [
+    (2048, 2048),   # about 32 copies of each value among the results: bins split again
+    (8192, 1024),   # about 8 copies: bins ranked directly
+    (64, 512),      # about 1024 copies: bins larger than any rank limit
+])
+@pytest.mark.parametrize("segments", [1, 4])
+def test_sort_with_tie_groups(levels, k, segments):
+    x = _levels_bf16(4, 65536, levels, seed=levels + k)
+    check_case(x, BF16, 65536, k, 1, True, "int32", plan={"segments": segments},
+               name=f"ties levels={levels} k={k} S={segments}")
+    check_case(x, BF16, 65536, k, 2, False, "int32", plan={"segments": segments},
+               name=f"ties by column levels={levels} k={k} S={segments}")
