@@ -735,17 +735,23 @@ __device__ __forceinline__ uint32_t filter_block(const u32x4 (&r)[V], uint32_t b
   hi_lane = fmaxf(hi_lane, mx);
   if (!ballot(mx >= F.f)) return 0u;
 
-  // Branch-free admission test (with idx_lim = ~0u it is simply f >= F.f;
-  // a NaN never passes), one wave mask per element, computed once.
-  auto pass = [&](int s) -> bool {
-    return (f[s] > F.f) | ((f[s] == F.f) & (col(s) < F.idx_lim));
-  };
+  // Admission test, one wave mask per element, computed once: f >= F.f when
+  // the threshold is a key bound (idx_lim = ~0u, the usual case), else
+  // branch-free f > F.f or f == F.f at a lower column.  A NaN never passes.
   u64 m[NS];
   uint32_t total = 0;
+  if (F.idx_lim == 0xFFFFFFFFu) {
 #pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    m[s] = ballot(pass(s));
-    total += static_cast<uint32_t>(__popcll(m[s]));
+    for (int s = 0; s < NS; ++s) {
+      m[s] = ballot(f[s] >= F.f);
+      total += static_cast<uint32_t>(__popcll(m[s]));
+    }
+  } else {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      m[s] = ballot((f[s] > F.f) | ((f[s] == F.f) & (col(s) < F.idx_lim)));
+      total += static_cast<uint32_t>(__popcll(m[s]));
+    }
   }
   if (total == 0) return 0u;
   uint32_t base = 0;
