@@ -31,7 +31,7 @@ def build(verbose: bool = False, extra: list[str] | None = None) -> str:
     a_obj = os.path.join(bdir, "topk_api.o")
     _run([HIPCC, *COMMON, *DEVICE, *extra, "-c", os.path.join(CSRC, "topk_kernels.hip"),
           "-o", k_obj], verbose)
-    _run([HIPCC, *COMMON, *DEVICE, "-x", "hip", "-c", os.path.join(CSRC, "topk_api.cpp"),
+    _run([HIPCC, *COMMON, *DEVICE, *extra, "-x", "hip", "-c", os.path.join(CSRC, "topk_api.cpp"),
           "-o", a_obj], verbose)
     tmp = LIB + ".tmp"
     _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", k_obj, a_obj, "-o", tmp], verbose)

@@ -162,6 +162,7 @@ ds_status_t ds_topk_ex(const void* x, ds_dtype_t dtype, int64_t batch, int64_t n
     a.ws_flags = reinterpret_cast<uint32_t*>(w + l.flags);
     a.ws_fill = reinterpret_cast<uint32_t*>(w + l.fill);
     a.ws_x = reinterpret_cast<unsigned long long*>(w + l.x);
+    a.ws_spec = reinterpret_cast<unsigned long long*>(w + l.spec);
     a.ws_comp = reinterpret_cast<unsigned long long*>(w + l.comp);
   }
   const int err = launch_topk(a, dtype == DS_BF16 ? 1 : 0, pl.cls, stream);

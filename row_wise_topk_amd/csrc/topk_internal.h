@@ -17,7 +17,10 @@ constexpr int kMaxSegments = 256;
 // k classes: each has its own buffer capacity, threads per workgroup and trigger.
 constexpr int kNumClasses = 4;
 constexpr int class_kmax(int c) { return c == 0 ? 256 : c == 1 ? 1024 : c == 2 ? 2048 : 4096; }
-constexpr int class_threads(int c) { return c == 3 ? 512 : 256; }
+#ifndef DS_NT_LOW
+#define DS_NT_LOW 256
+#endif
+constexpr int class_threads(int c) { return c == 3 ? 512 : DS_NT_LOW; }
 // B2 (extra candidates collected before a cut) per class.
 constexpr int class_b2(int c) { return c == 0 ? 1024 : c == 1 ? 3072 : class_kmax(c); }
 // Buffer capacity: k + B2 candidates plus one whole block admitted at once.
@@ -25,8 +28,16 @@ constexpr int class_cap(int c) { return class_kmax(c) + class_b2(c) + kBlockElem
 constexpr int class_trigger(int c) { return class_cap(c) - kBlockElems; }
 // LDS bytes per workgroup (candidate composites, histogram, scalars).
 constexpr int class_lds_bytes(int c) { return class_cap(c) * 8 + 2048 * 4 + 1536; }
+// The kernels are built for two waves per SIMD (up to 256 VGPRs a lane), so
+// a CU (4 SIMDs) holds 8 waves: 2 workgroups of 256 threads or 1 of 512.
+constexpr int kWavesPerSimd = 2;
+// Workgroups of class c resident on one CU: the smaller of the LDS and the
+// register limits.
 constexpr int class_wgs_per_cu(int c) {
-  return (160 * 1024) / class_lds_bytes(c) > 0 ? (160 * 1024) / class_lds_bytes(c) : 1;
+  const int lds = (160 * 1024) / class_lds_bytes(c);
+  const int regs = kWavesPerSimd * 4 * 64 / class_threads(c);
+  const int w = lds < regs ? lds : regs;
+  return w > 0 ? w : 1;
 }
 inline int class_of_k(int k) { return k <= 256 ? 0 : k <= 1024 ? 1 : k <= 2048 ? 2 : 3; }
 
@@ -53,12 +64,13 @@ struct KArgs {
   uint32_t* ws_flags;           // [batch]  OR of row status bits
   uint32_t* ws_fill;            // [batch]  survivors written so far per row
   unsigned long long* ws_x;     // [batch * segments]  per-workgroup merge bound
+  unsigned long long* ws_spec;  // [batch]  largest estimated start used on the row (0: none)
   unsigned long long* ws_comp;  // [batch * segments * (k + 64)]  candidate composites, contiguous per row
 };
 
 // Workspace layout for `segments` workgroups per row (bytes, 16-B aligned parts).
 struct WsLayout {
-  size_t thr, done, flags, fill, x, comp, total;
+  size_t thr, done, flags, fill, x, spec, comp, total;
 };
 WsLayout ws_layout(int64_t batch, int segments, int k);
 

@@ -46,6 +46,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "ds_topk.h"
 #include "topk_internal.h"
 
@@ -261,6 +263,8 @@ struct Smem {
   u64 rng[2];                 // epilogue sort: min / max order key of a segment
   u64 thr;                    // the workgroup's threshold (composite)
   u64 xv;                     // a cut's second answer: a bound with >= need2 candidates above
+  u64 specmax;                // merge: the largest estimated start used on the row (0: none)
+  u64 tvalid;                 // merge: the largest bound known to leave k of the row above it
 };
 
 // A thread's own run of BPT consecutive bins, read and written 16 bytes at a
@@ -717,7 +721,7 @@ __device__ __forceinline__ uint32_t filter_block(const u32x4 (&r)[V], uint32_t b
     }
   }
   const uint32_t base_idx = blk * static_cast<uint32_t>(kBlockElems) + t * EPV;
-  auto col = [&](int s) { return base_idx + (s / EPV) * (NT * EPV) + (s % EPV); };
+  auto col = [&](int s) { return base_idx + static_cast<uint32_t>((s / EPV) * (NT * EPV) + (s % EPV)); };
   if (RAG) {
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
@@ -729,42 +733,59 @@ __device__ __forceinline__ uint32_t filter_block(const u32x4 (&r)[V], uint32_t b
 #pragma unroll
     for (int s = 0; s < NS; s += 2) nan_lane |= __builtin_isunordered(f[s], f[s + 1]);
   }
+  // The threshold is the same in every lane; reading it into scalar registers
+  // lets the compiler see that, so the per-element wave masks below stay
+  // scalar and each store reuses its compare as the execution mask.
+  const float ff = __uint_as_float(uniform(__float_as_uint(F.f)));
+  const uint32_t lim = uniform(F.idx_lim);
   float mx = f[0];
 #pragma unroll
   for (int s = 1; s < NS; ++s) mx = fmaxf(mx, f[s]);
   hi_lane = fmaxf(hi_lane, mx);
-  if (!ballot(mx >= F.f)) return 0u;
+  if (!ballot(mx >= ff)) return 0u;
 
-  // Admission test, one wave mask per element, computed once: f >= F.f when
-  // the threshold is a key bound (idx_lim = ~0u, the usual case), else
-  // branch-free f > F.f or f == F.f at a lower column.  A NaN never passes.
-  u64 m[NS];
-  uint32_t total = 0;
-  if (F.idx_lim == 0xFFFFFFFFu) {
+  // Admission test: f >= ff when the threshold is a key bound (lim = ~0u, the
+  // usual case), else branch-free f > ff or f == ff at a lower column.  A NaN
+  // never passes.  The wave masks give the block's total and each store's
+  // position; the test itself is repeated as each store's execution mask.
+  const uint32_t ncol0 = ~base_idx;   // ~col(s) = ncol0 - (col(s) - base_idx)
+  auto run = [&](auto key_only, auto positive) -> uint32_t {
+    auto pass = [&](int s) -> bool {
+      if (decltype(key_only)::value) return f[s] >= ff;
+      return (f[s] > ff) | ((f[s] == ff) & (col(s) < lim));
+    };
+    u64 m[NS];
+    uint32_t total = 0;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      m[s] = ballot(f[s] >= F.f);
+      m[s] = ballot(pass(s));
       total += static_cast<uint32_t>(__popcll(m[s]));
     }
-  } else {
+    if (total == 0) return 0u;
+    uint32_t base = 0;
+    if (lane == 0) base = atomicAdd(&sm.cnt[cur], total);
+    base = uniform(base);
+    const uint32_t after = base + total;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      m[s] = ballot((f[s] > F.f) | ((f[s] == F.f) & (col(s) < F.idx_lim)));
-      total += static_cast<uint32_t>(__popcll(m[s]));
+      if (pass(s)) {
+        const uint32_t bits = __float_as_uint(f[s]);
+        // Above a positive threshold every admitted value is positive, and
+        // the key of a positive value is its bit pattern with the top bit set.
+        const uint32_t key = decltype(positive)::value ? (bits | kBias) : key_of_bits(bits);
+        const uint32_t pos = __builtin_amdgcn_mbcnt_hi(
+            static_cast<uint32_t>(m[s] >> 32), __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m[s]), base));
+        const uint32_t off = static_cast<uint32_t>((s / EPV) * (NT * EPV) + (s % EPV));
+        sm.comp[pos] = (static_cast<u64>(key) << 32) | (ncol0 - off);
+      }
+      base += static_cast<uint32_t>(__popcll(m[s]));
     }
-  }
-  if (total == 0) return 0u;
-  uint32_t base = 0;
-  if (lane == 0) base = atomicAdd(&sm.cnt[cur], total);
-  base = uniform(base);
-  const uint32_t after = base + total;
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    if ((m[s] >> lane) & 1ull)
-      sm.comp[base + mbcnt64(m[s])] = comp_of(key_of_bits(__float_as_uint(f[s])), col(s));
-    base += static_cast<uint32_t>(__popcll(m[s]));
-  }
-  return after;
+    return after;
+  };
+  const bool positive = ff > 0.0f;
+  if (lim == 0xFFFFFFFFu)
+    return positive ? run(std::true_type{}, std::true_type{}) : run(std::true_type{}, std::false_type{});
+  return positive ? run(std::false_type{}, std::true_type{}) : run(std::false_type{}, std::false_type{});
 }
 
 template <int V>
@@ -834,8 +855,8 @@ __device__ __noinline__ ThrPair block_threshold(BlockRegs<V> r, uint32_t k, uint
   for (int s = 0; s < NS; ++s) {
     const uint32_t key = key_of_bits(__float_as_uint(f[s]));
     const bool fin = __builtin_fabsf(f[s]) <= 3.402823466e38f;
-    klo = fin & (key < klo) ? key : klo;
-    khi = fin & (key > khi) ? key : khi;
+    klo = (fin & (key < klo)) ? key : klo;
+    khi = (fin & (key > khi)) ? key : khi;
   }
   klo = wave_min(klo);
   khi = wave_max(khi);
@@ -878,8 +899,8 @@ __device__ __noinline__ ThrPair block_threshold(BlockRegs<V> r, uint32_t k, uint
   for (int s = 0; s < NS; ++s) {
     const uint32_t key = key_of_bits(__float_as_uint(f[s]));
     const uint32_t bn = bin_of(f[s]);
-    tk = (f[s] == f[s]) & (bn >= b) & (key < tk) ? key : tk;
-    tk2 = (f[s] == f[s]) & (bn >= b2) & (key < tk2) ? key : tk2;
+    tk = ((f[s] == f[s]) & (bn >= b) & (key < tk)) ? key : tk;
+    tk2 = ((f[s] == f[s]) & (bn >= b2) & (key < tk2)) ? key : tk2;
   }
   tk = wave_min(tk);
   tk2 = wave_min(tk2);
@@ -936,6 +957,9 @@ __device__ __forceinline__ void load_block(u32x4 (&r)[V], const char* xrow, uint
 // Regions: R0 = comp[0, MMAX) receives the sorted output, R1 = comp[MMAX,
 // 2 MMAX) holds the grouped elements, and after R1 come two segment tables
 // (this level's and the next), 4 words of 64 bits per segment.
+// Longest share (in blocks) of a shared row that may start from an estimate.
+constexpr uint32_t kSpecSteps = 16;
+
 constexpr int kSortSegs = 512;   // > 4096 / 9, the most segments a level can make
 // A level ranks bins of up to 32 members directly, unless the ranking work of
 // its bins of 9..32 members (the sum of their squared sizes) exceeds what
@@ -1005,7 +1029,7 @@ __device__ __noinline__ void sort_results(Smem<CAP, NT>& sm, uint32_t m, bool by
       own_bins_read<BPT>(sm, hb);
       uint32_t w2 = 0;
 #pragma unroll
-      for (int i = 0; i < BPT; ++i) w2 += (hb[i] > 8u) & (hb[i] <= 32u) ? hb[i] * hb[i] : 0u;
+      for (int i = 0; i < BPT; ++i) w2 += ((hb[i] > 8u) & (hb[i] <= 32u)) ? hb[i] * hb[i] : 0u;
       w2 = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(wave_prefix_sum(w2)), 63));
       if ((t & 63) == 0 && w2) atomicAdd(&sm.res[4], w2);
     }
@@ -1142,7 +1166,7 @@ __device__ __forceinline__ void write_outputs(Smem<CAP, NT>& sm, const KArgs& a,
 
 // ---------------------------------------------------------------- the kernel
 template <bool BF16, int CLS, bool MULTI>
-__global__ __launch_bounds__(class_threads(CLS), 2) void topk_kernel(KArgs a) {
+__global__ __launch_bounds__(class_threads(CLS), kWavesPerSimd) void topk_kernel(KArgs a) {
   constexpr int NT = class_threads(CLS);
   constexpr int CAP = class_cap(CLS);
   constexpr int KMAX = class_kmax(CLS);
@@ -1188,6 +1212,7 @@ __global__ __launch_bounds__(class_threads(CLS), 2) void topk_kernel(KArgs a) {
   __syncthreads();
 
   u64* thr_g = MULTI ? reinterpret_cast<u64*>(a.ws_thr) + row : nullptr;
+  u64* spec_g = MULTI ? reinterpret_cast<u64*>(a.ws_spec) + row : nullptr;
   const uint32_t k = static_cast<uint32_t>(a.k);
   const uint32_t trigger = static_cast<uint32_t>(a.trigger);
   const uint32_t slack = (trigger - k) / 4u;
@@ -1253,17 +1278,33 @@ __global__ __launch_bounds__(class_threads(CLS), 2) void topk_kernel(KArgs a) {
         // of those blocks' elements at or above it; a plain count over them
         // confirms it before it is used.  They are elements of the row, so
         // the edge is valid for the whole row, shared or not.
+        //
+        // A workgroup with a short share of a shared row goes further: t2 is
+        // then an estimate of the edge with 2k of the row's L elements at or
+        // above it (the 2kB/L-th largest of the first block).  It is used if
+        // the ring's count scales to at least 1.5k for the row, and it is
+        // recorded for the row: the merge checks at the end that no element
+        // of the top k lay at or below it, and reads the row again if one
+        // may have.
         uint32_t whole = 0;
 #pragma unroll
         for (uint32_t j = 0; j < 3; ++j)
           if (j < ntl && blk_at(j) * static_cast<uint32_t>(kBlockElems) + kBlockElems <= L)
             whole |= 1u << j;
         const uint32_t nw = static_cast<uint32_t>(__popc(whole));
-        const uint32_t need2 = nw >= 2u ? (11u * k + 10u * nw - 1u) / (10u * nw) : 0u;
+        const uint32_t nspec =
+            (MULTI && ntl <= kSpecSteps && nw >= 2u)
+                ? static_cast<uint32_t>((2ull * k * kBlockElems + L - 1u) / L)
+                : k;
+        const bool spec = nspec < k;
+        const uint32_t need2 =
+            spec ? nspec : (nw >= 2u ? (11u * k + 10u * nw - 1u) / (10u * nw) : 0u);
         const ThrPair tp = block_threshold<BF16, V, NT, CAP>(br, k, need2, sm);
-        u64 t0 = tp.t0;
-        if (need2 != 0u && t0 != kThrInit && tp.t2 > t0) {
-          const uint32_t tk2 = static_cast<uint32_t>(tp.t2 >> 32) + 1u;
+        u64 t0 = uniform64(tp.t0);   // the same in every lane: keep it scalar
+        const u64 t2 = uniform64(tp.t2);
+        u64 tloc = t0;               // this workgroup's start
+        if (need2 != 0u && t0 != kThrInit && t2 > t0) {
+          const uint32_t tk2 = static_cast<uint32_t>(t2 >> 32) + 1u;
           uint32_t n = 0;
           auto count_in = [&](const u32x4 (&rr)[V]) {
 #pragma unroll
@@ -1287,14 +1328,24 @@ __global__ __launch_bounds__(class_threads(CLS), 2) void topk_kernel(KArgs a) {
               __builtin_amdgcn_readlane(static_cast<int>(wave_prefix_sum(n)), 63));
           if (lane == 0) atomicAdd(&sm.res[3], wt);
           __syncthreads();
-          if (uniform(sm.res[3]) >= k) t0 = tp.t2;
+          const uint32_t ring = uniform(sm.res[3]);
+          if (ring >= k) {
+            t0 = t2;   // k of the row's elements at or above it: valid
+            tloc = t2;
+          } else if (spec && 2ull * ring * nb >= 3ull * k * nw) {
+            tloc = t2;   // an estimate, checked by the merge
+          }
         }
-        if (t0 > thr) {
-          thr = t0;
+        if (tloc > thr) {
+          thr = tloc;
           F = filter_of(thr);
           if (t == 0) {
-            atomicMax(&sm.thr, t0);
-            if (MULTI) publish_thr(thr_g, t0);
+            atomicMax(&sm.thr, tloc);
+            if (MULTI) {
+              publish_thr(thr_g, t0);   // only a valid bound is shared
+              if (tloc != t0)
+                __hip_atomic_fetch_max(spec_g, tloc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
           }
         }
       }
@@ -1414,6 +1465,7 @@ __global__ __launch_bounds__(class_threads(CLS), 2) void topk_kernel(KArgs a) {
     wait_all_memory();
     __syncthreads();
     if (t == 0) {
+      sm.rng[0] = ~0ull;   // the merge's minimum over the bounds x_seg
       const uint32_t prev =
           __hip_atomic_fetch_add(&a.ws_done[row], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       sm.is_last = prev == static_cast<uint32_t>(S - 1) ? 1u : 0u;
@@ -1424,16 +1476,18 @@ __global__ __launch_bounds__(class_threads(CLS), 2) void topk_kernel(KArgs a) {
     // Last arrival: merge every workgroup's survivors.  Start from the largest
     // of the shared threshold and min_seg x_seg (0 if any workgroup had fewer
     // than ceil(k / S) survivors).
-    // Every load goes out at once: the bounds, the row's counters and the
-    // first two chunks of survivors.  The chunks need no count first: the
-    // row's array is zero past its fill, and zero is never above a threshold.
-    // Two chunks hold the survivors of up to 8 workgroups at the class's
-    // largest k (within a register budget of 17 per thread per chunk), so the
-    // merge usually waits for one round trip only.  A chunk must also fit in
-    // the buffer after a cut (at most k + slack candidates remain).
+    // Every load goes out at once: the row's counters and bounds first (so
+    // that using them waits for nothing else), then the first two chunks of
+    // survivors.  The chunks need no count first: the row's array is zero
+    // past its fill, and zero is never above a threshold.  A chunk is at most
+    // 9 survivors per thread: two chunks hold the 2k or so survivors that
+    // workgroups starting from an estimate hand over, in one round trip, and
+    // the registers stay clear of the spills whose reloads would wait for
+    // every load and store in flight.  A chunk must also fit in the buffer
+    // after a cut (at most k + slack candidates remain).
     constexpr int PER_FIT = (8 * (KMAX + static_cast<int>(kSmallBin)) + 2 * NT - 1) / (2 * NT);
     constexpr int PER_ROOM = (CAP - (3 * KMAX + class_trigger(CLS)) / 4) / NT;
-    constexpr int PER_A = PER_FIT > 17 ? 17 : PER_FIT;
+    constexpr int PER_A = PER_FIT > 9 ? 9 : PER_FIT;
     constexpr int PER_B = PER_A > PER_ROOM ? PER_ROOM : PER_A;
     constexpr int PER = PER_B < 4 ? 4 : PER_B;
     static_assert(PER * NT + (3 * KMAX + class_trigger(CLS)) / 4 <= CAP, "merge chunk room");
@@ -1449,32 +1503,42 @@ __global__ __launch_bounds__(class_threads(CLS), 2) void topk_kernel(KArgs a) {
         mv[q] = ld_agent(&wsc[p < area ? p : 0u]);
       }
     };
+    u64 gfin = 0, spm = 0;
+    uint32_t fl = 0, fill = 0;
+    if (t == 0) {
+      gfin = load_thr(thr_g);
+      spm = ld_agent(spec_g);
+      fl = ld_agent(&a.ws_flags[row]);
+      fill = ld_agent(&a.ws_fill[row]);
+    }
     u64 xs = ~0ull;
     u64* xp = &a.ws_x[static_cast<int64_t>(row) * S + (t < S ? t : 0)];
     if (t < S) xs = ld_agent(xp);
     u64 va[PER], vb[PER];
     load_chunk(0, va);
     load_chunk(CHUNK, vb);
-    if (t == 0) {
-      sm.rng[0] = ~0ull;
-      const u64 gfin = load_thr(thr_g);
-      if (gfin > sm.thr) sm.thr = gfin;
-      sm.flags |= ld_agent(&a.ws_flags[row]);
-      sm.res[1] = ld_agent(&a.ws_fill[row]);
-    }
     if (t < S) st_agent(xp, 0ull);
     xs = wave_extreme64<false>(xs);
-    __syncthreads();
-    if (lane == 0) atomicMin(&sm.rng[0], xs);
-    __syncthreads();
-    if (t == 0 && sm.rng[0] > sm.thr) sm.thr = sm.rng[0];
+    if (lane == 0 && t < S) atomicMin(&sm.rng[0], xs);   // rng[0] was set before the arrival count
+    if (t == 0) {
+      if (gfin > sm.thr) sm.thr = gfin;
+      sm.tvalid = gfin;
+      sm.specmax = spm;
+      sm.flags |= fl;
+      sm.res[1] = fill;
+      // Its own candidates come back from the array with everyone else's,
+      // filtered by the same bound, so the LDS buffer starts empty.
+      sm.cnt[cur] = 0u;
+    }
     __syncthreads();
     const uint32_t total = min(uniform(sm.res[1]), area);
-    const u64 T0 = uniform64(sm.thr);
-    // Its own candidates come back from the array with everyone else's,
-    // filtered by the same bound, so the LDS buffer starts empty.
-    if (t == 0) sm.cnt[cur] = 0u;
-    __syncthreads();
+    const u64 xmin = uniform64(sm.rng[0]);
+    u64 T0 = uniform64(sm.thr);
+    T0 = xmin > T0 ? xmin : T0;
+    if (t == 0) {   // read again only after the next barrier
+      sm.thr = T0;
+      if (xmin > sm.tvalid) sm.tvalid = xmin;
+    }
     auto clear_chunk = [&](uint32_t c0) {
 #pragma unroll
       for (int q = 0; q < PER; ++q) {
@@ -1483,6 +1547,12 @@ __global__ __launch_bounds__(class_threads(CLS), 2) void topk_kernel(KArgs a) {
       }
     };
     u64 Tm = T0;
+    // Appended candidates above the row's largest estimated start (checked
+    // after the merge).  A cut inside the merge can only drop candidates at
+    // or below its new bound, and keeps k above it: if that bound is below
+    // the estimate the count stays exact, else the check passes either way.
+    const u64 specmax = uniform64(sm.specmax);
+    uint32_t n_above = 0;
     auto merge_chunk = [&](uint32_t c0, const u64 (&mv)[PER]) {
       auto pass = [&](int q) -> bool {
         const uint32_t p = c0 + t + q * NT;
@@ -1527,7 +1597,9 @@ __global__ __launch_bounds__(class_threads(CLS), 2) void topk_kernel(KArgs a) {
 #pragma unroll
         for (int q = 0; q < PER; ++q) {
           const uint32_t pos = base + mbcnt64(mm[q]);
-          if (((mm[q] >> lane) & 1ull) & (pos < static_cast<uint32_t>(CAP))) sm.comp[pos] = mv[q];
+          const bool mine = (mm[q] >> lane) & 1ull;
+          if (mine & (pos < static_cast<uint32_t>(CAP))) sm.comp[pos] = mv[q];
+          n_above += (mine & (mv[q] > specmax)) ? 1u : 0u;
           base += static_cast<uint32_t>(__popcll(mm[q]));
         }
       }
@@ -1542,10 +1614,60 @@ __global__ __launch_bounds__(class_threads(CLS), 2) void topk_kernel(KArgs a) {
       }
       if (c0 + 3 * CHUNK < total) load_chunk(c0 + 3 * CHUNK, vb);
     }
+    n_above = static_cast<uint32_t>(
+        __builtin_amdgcn_readlane(static_cast<int>(wave_prefix_sum(n_above)), 63));
+    if (lane == 0) sm.snap[par][wid] = n_above;
     __syncthreads();   // every append is counted
+    uint32_t above = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < NT / 64; ++w2) above += sm.snap[par][w2];
+    par ^= 1;
+
+    // An estimated start dropped, unseen, whatever lay at or below it.  That
+    // lost nothing iff at least k merged candidates lie above the row's
+    // largest estimate (then so does the row's k-th largest).  Otherwise the
+    // row is read again, whole and in order, from the largest valid bound.
+    if (specmax != 0ull) {
+      if (uniform(above) < k && uniform(sm.flags) == 0u) {
+        if (t == 0) {
+          sm.cnt[cur] = 0u;
+          sm.thr = sm.tvalid;
+        }
+        __syncthreads();
+        thr = uniform64(sm.thr);
+        F = filter_of(thr);
+        for (uint32_t b = 0; b < nb; ++b) {
+          u32x4 rb[V];
+          load_block<BF16, V, NT>(rb, xrow, b, L);
+          uint32_t after;
+          if (ragged_row && b == last_blk) {
+            BlockRegs<V> br;
+#pragma unroll
+            for (int v = 0; v < V; ++v) br.v[v] = rb[v];
+            const RaggedResult rr =
+                filter_ragged<BF16, V, NT, CAP>(br, b, L, F, hi_lane, nan_lane ? 1u : 0u, sm, cur);
+            after = rr.after;
+            hi_lane = rr.hi_lane;
+            nan_lane = rr.nan_lane != 0;
+          } else {
+            after = filter_block<BF16, false, V, NT, CAP>(rb, b, L, F, hi_lane, nan_lane, sm, cur);
+          }
+          const uint32_t c2 = count_after_step(after);
+          if (c2 > trigger && b + 1 < nb) {
+            cur = cut_buffer<NT, CAP>(sm, cur, k, k + slack, L, hi_key());
+            thr = uniform64(sm.thr);
+            F = filter_of(thr);
+          }
+        }
+        const uint32_t hk = wave_max(hi_key());   // every candidate key, for the sort
+        if (lane == 0) atomicMax(&sm.hikey, hk);
+        __syncthreads();
+      }
+    }
     if (a.sorted != 1 || uniform(sm.cnt[cur]) > static_cast<uint32_t>(SORT_CAP))
       cur = cut_buffer<NT, CAP>(sm, cur, k, k, L, hi_key());
     if (t == 0) {
+      st_agent(spec_g, 0ull);
       st_agent(&a.ws_done[row], 0u);
       st_agent(&a.ws_flags[row], 0u);
       st_agent(&a.ws_fill[row], 0u);
@@ -1620,7 +1742,8 @@ WsLayout ws_layout(int64_t batch, int segments, int k) {
   l.flags = up(l.done + b * 4);
   l.fill = up(l.flags + b * 4);
   l.x = up(l.fill + b * 4);
-  l.comp = up(l.x + b * s * 8);
+  l.spec = up(l.x + b * s * 8);
+  l.comp = up(l.spec + b * 8);
   l.total = up(l.comp + b * s * (static_cast<size_t>(k) + kSmallBin) * 8);
   return l;
 }

@@ -5,6 +5,14 @@ block, confirmed by a count over those blocks; rows whose first block is not
 like the next two make the count reject it (the row then starts from the
 first block's own bound), on one workgroup per row and on shared rows.
 
+A workgroup with a short share of a shared row may instead start from an
+estimate of the row's 2k-th largest value, read from its first block and
+accepted when the ring's count agrees; the merge then checks that at least k
+merged candidates lie above the row's largest estimate, and reads the whole
+row again when not.  Rows whose first workgroup sees only large values in its
+ring make that check fail (the row is read again); rows whose first block
+alone is large make the ring refuse the estimate.
+
 The epilogue sort ranks small bins directly but splits bins of 9..32 members
 again when ranking them would cost more than another level; bf16 rows with a
 few dozen copies of each value among the results take that path, rows with
@@ -54,6 +62,72 @@ def test_start_estimate_rejected_bf16(plan):
                name=f"blocky bf16 k=512 {plan}")
     check_case(x, BF16, x.shape[1], 512, 1, True, "int64", plan=plan,
                name=f"blocky bf16 k=512 sorted {plan}")
+
+
+def _hot_blocks(nblocks: int, hot, seed: int, batch: int = 3) -> np.ndarray:
+    """Rows of nblocks whole blocks of U[0,1), plus 100 in the blocks `hot`."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = rng.random((batch, nblocks * B), dtype=np.float32)
+    for b in hot:
+        x[:, b * B:(b + 1) * B] += np.float32(100.0)
+    return x
+
+
+# In block order, workgroup 0 of S reads blocks 0, S, 2S, ... and its ring holds
+# the first three.  All three large: its estimate (the 2kB/L-th largest of block
+# 0, about the 65th at k = 1024 and 32 blocks) is accepted, but only about 200
+# elements of the row lie above it, so the merge reads the row again.
+@pytest.mark.parametrize("segments", [4, 8])
+@pytest.mark.parametrize("k", [512, 1024])
+def test_start_estimate_fails_merge_check_fp32(segments, k):
+    x = _hot_blocks(32, (0, segments, 2 * segments), seed=53 + segments + k)
+    plan = {"segments": segments, "in_order": 1}
+    check_case(x, FP32, x.shape[1], k, 1, True, "int64", plan=plan,
+               name=f"hot ring fp32 k={k} S={segments}")
+    check_case(x, FP32, x.shape[1], k, 0, False, "int32", plan=plan,
+               name=f"hot ring fp32 unsorted k={k} S={segments}")
+    check_case(x, FP32, x.shape[1], k, 2, False, "int32", plan=plan,
+               name=f"hot ring fp32 by column k={k} S={segments}")
+
+
+def test_start_estimate_fails_merge_check_ragged_and_end():
+    """The row read again ends in a partial block (n_cols and end)."""
+    x = _hot_blocks(32, (0, 8, 16), seed=59)
+    n = x.shape[1] - 1000
+    plan = {"segments": 8, "in_order": 1}
+    check_case(x[:, :n].copy(), FP32, n, 1024, 1, True, "int32", plan=plan,
+               name="hot ring fp32 ragged")
+    end = np.array([n, x.shape[1], x.shape[1] - 4096 - 7], dtype=np.int32)
+    check_case(x, FP32, x.shape[1], 1024, 1, True, "int32", end=end, plan=plan,
+               name="hot ring fp32 end")
+
+
+def test_start_estimate_fails_merge_check_bf16():
+    # 1 + U[0,1) in the large blocks and U[0,1)/4 elsewhere: bf16 keeps 128
+    # levels in [1, 2), fine enough for the estimate to sit above the k-th
+    rng = np.random.Generator(np.random.PCG64(61))
+    x = rng.random((3, 32 * B), dtype=np.float32) * np.float32(0.25)
+    for b in (0, 4, 8):
+        x[:, b * B:(b + 1) * B] = np.float32(1.0) + rng.random((3, B), dtype=np.float32)
+    x = workloads.to_bf16_bits(x)
+    plan = {"segments": 4, "in_order": 1}
+    check_case(x, BF16, x.shape[1], 512, 0, False, "int32", plan=plan,
+               name="hot ring bf16 k=512")
+    check_case(x, BF16, x.shape[1], 512, 1, True, "int32", plan=plan,
+               name="hot ring bf16 k=512 sorted")
+
+
+# Only block 0 large: the ring's count (about 65 in three blocks) scales to
+# far fewer than 1.5k for the row, so workgroup 0 starts from block 0's own
+# k-th largest, a valid bound.
+@pytest.mark.parametrize("dtype", [FP32, BF16])
+def test_start_estimate_refused_by_ring(dtype):
+    x = _hot_blocks(32, (0,), seed=67)
+    if dtype == BF16:
+        x = workloads.to_bf16_bits(x)
+    plan = {"segments": 8, "in_order": 1}
+    check_case(x, dtype, x.shape[1], 1024, 1, True, "int32", plan=plan,
+               name=f"hot block 0 {'bf16' if dtype else 'fp32'}")
 
 
 def _levels_bf16(batch: int, n: int, levels: int, seed: int) -> np.ndarray:
