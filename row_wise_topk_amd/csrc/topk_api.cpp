@@ -34,24 +34,35 @@ bool misaligned(const void* p, uintptr_t a) {
   return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0;
 }
 
-int auto_segments(int64_t batch, int64_t n_cols, int cls) {
+// Workgroups per row: enough to fill every CU's workgroup slots, at least two
+// blocks each.  Shared fp32 rows use 512-thread workgroups, one per CU, so
+// they are planned for that.
+int auto_segments(int64_t batch, int64_t n_cols, int cls, int dtype) {
   const int64_t nb = (n_cols + kBlockElems - 1) / kBlockElems;
   if (batch <= 0 || nb <= 1) return 1;
-  const int64_t target = static_cast<int64_t>(kNumCU) * class_wgs_per_cu(cls);
-  int64_t s = (target + batch - 1) / batch;
-  const int64_t most = (nb + 1) / 2;   // at least two blocks per workgroup
-  if (s > most) s = most;
-  if (s > kMaxSegments) s = kMaxSegments;
-  if (s < 1) s = 1;
+  auto plan_for = [&](int nt) {
+    const int64_t target = static_cast<int64_t>(kNumCU) * wgs_per_cu(cls, nt);
+    int64_t s = (target + batch - 1) / batch;
+    const int64_t most = (nb + 1) / 2;   // at least two blocks per workgroup
+    if (s > most) s = most;
+    if (s > kMaxSegments) s = kMaxSegments;
+    if (s < 1) s = 1;
+    return s;
+  };
+  int64_t s = plan_for(kernel_threads(cls, dtype, false));
+  if (s > 1 && kernel_threads(cls, dtype, true) != kernel_threads(cls, dtype, false)) {
+    const int64_t s2 = plan_for(kernel_threads(cls, dtype, true));
+    if (s2 > 1) s = s2;
+  }
   return static_cast<int>(s);
 }
 
 // Fills `out`; returns DS_ERR_PLAN for an out-of-range override.
-ds_status_t resolve_plan(int64_t batch, int64_t n_cols, int32_t k, const ds_topk_plan_t* p,
-                         Plan* out) {
+ds_status_t resolve_plan(int64_t batch, int64_t n_cols, int32_t k, ds_dtype_t dtype,
+                         const ds_topk_plan_t* p, Plan* out) {
   Plan pl{};
   pl.cls = class_of_k(k);
-  pl.segments = auto_segments(batch, n_cols, pl.cls);
+  pl.segments = auto_segments(batch, n_cols, pl.cls, dtype == DS_BF16 ? 1 : 0);
   pl.seed = 0x5EEDu;
   pl.in_order = 0;
   pl.trigger = class_trigger(pl.cls);
@@ -93,7 +104,7 @@ ds_status_t validate(const void* x, ds_dtype_t dtype, int64_t batch, int64_t n_c
                      size_t workspace_bytes, const ds_topk_plan_t* plan, Plan* pl) {
   ds_status_t st = check_scalars(dtype, batch, n_cols, row_stride, k, sorted, index_dtype);
   if (st != DS_OK) return st;
-  st = resolve_plan(batch, n_cols, k, plan, pl);
+  st = resolve_plan(batch, n_cols, k, dtype, plan, pl);
   if (st != DS_OK) return st;
   if (batch == 0) return DS_OK;
   if (!indices || !row_status || (return_values && !values) || (n_cols > 0 && !x))
@@ -183,7 +194,7 @@ size_t ds_topk_workspace_size_ex(ds_dtype_t dtype, int64_t batch, int64_t n_cols
                                  const ds_topk_plan_t* plan) {
   if (check_scalars(dtype, batch, n_cols, n_cols, k, 1, DS_INT32) != DS_OK) return 0;
   Plan pl;
-  if (resolve_plan(batch, n_cols, k, plan, &pl) != DS_OK) return 0;
+  if (resolve_plan(batch, n_cols, k, dtype, plan, &pl) != DS_OK) return 0;
   return workspace_bytes_for(batch, pl.segments, k);
 }
 
@@ -197,7 +208,7 @@ ds_status_t ds_read_ceiling(const void* x, ds_dtype_t dtype, int64_t batch, int6
   ds_status_t st = check_scalars(dtype, batch, n_cols, row_stride, k, 1, DS_INT32);
   if (st != DS_OK) return st;
   Plan pl;
-  st = resolve_plan(batch, n_cols, k, plan, &pl);
+  st = resolve_plan(batch, n_cols, k, dtype, plan, &pl);
   if (st != DS_OK || batch == 0) return st;
   if (!sink || (n_cols > 0 && !x)) return DS_ERR_NULL;
   if ((x && misaligned(x, 16)) || (row_stride * elem_size(dtype)) % 16 != 0) return DS_ERR_ALIGN;

@@ -17,10 +17,15 @@ constexpr int kMaxSegments = 256;
 // k classes: each has its own buffer capacity, threads per workgroup and trigger.
 constexpr int kNumClasses = 4;
 constexpr int class_kmax(int c) { return c == 0 ? 256 : c == 1 ? 1024 : c == 2 ? 2048 : 4096; }
-#ifndef DS_NT_LOW
-#define DS_NT_LOW 256
-#endif
-constexpr int class_threads(int c) { return c == 3 ? 512 : DS_NT_LOW; }
+// Threads per workgroup: 512 for the largest k class, and for fp32 rows
+// shared by several workgroups (a 16-byte-per-lane block of 512 threads
+// keeps 48 KB in flight per CU, as two workgroups of 256 do; the post-stream
+// passes of the one workgroup per CU then run on twice the waves).  256
+// otherwise: bf16 blocks are half the bytes, and rows with one workgroup
+// each want two workgroups per CU.
+constexpr int kernel_threads(int c, int dtype, bool multi) {
+  return (c == 3 || (dtype == 0 && multi)) ? 512 : 256;
+}
 // B2 (extra candidates collected before a cut) per class.
 constexpr int class_b2(int c) { return c == 0 ? 1024 : c == 1 ? 3072 : class_kmax(c); }
 // Buffer capacity: k + B2 candidates plus one whole block admitted at once.
@@ -31,11 +36,11 @@ constexpr int class_lds_bytes(int c) { return class_cap(c) * 8 + 2048 * 4 + 1536
 // The kernels are built for two waves per SIMD (up to 256 VGPRs a lane), so
 // a CU (4 SIMDs) holds 8 waves: 2 workgroups of 256 threads or 1 of 512.
 constexpr int kWavesPerSimd = 2;
-// Workgroups of class c resident on one CU: the smaller of the LDS and the
-// register limits.
-constexpr int class_wgs_per_cu(int c) {
+// Workgroups of class c with nt threads resident on one CU: the smaller of
+// the LDS and the register limits.
+constexpr int wgs_per_cu(int c, int nt) {
   const int lds = (160 * 1024) / class_lds_bytes(c);
-  const int regs = kWavesPerSimd * 4 * 64 / class_threads(c);
+  const int regs = kWavesPerSimd * 4 * 64 / nt;
   const int w = lds < regs ? lds : regs;
   return w > 0 ? w : 1;
 }

@@ -1166,8 +1166,9 @@ __device__ __forceinline__ void write_outputs(Smem<CAP, NT>& sm, const KArgs& a,
 
 // ---------------------------------------------------------------- the kernel
 template <bool BF16, int CLS, bool MULTI>
-__global__ __launch_bounds__(class_threads(CLS), kWavesPerSimd) void topk_kernel(KArgs a) {
-  constexpr int NT = class_threads(CLS);
+__global__ __launch_bounds__(kernel_threads(CLS, BF16 ? 1 : 0, MULTI), kWavesPerSimd) void topk_kernel(
+    KArgs a) {
+  constexpr int NT = kernel_threads(CLS, BF16 ? 1 : 0, MULTI);
   constexpr int CAP = class_cap(CLS);
   constexpr int KMAX = class_kmax(CLS);
   // A value sort takes up to SORT_CAP candidates, so for value order the
@@ -1751,17 +1752,18 @@ WsLayout ws_layout(int64_t batch, int segments, int k) {
 template <bool BF16, int CLS>
 static int launch_one(const KArgs& a, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.batch) * a.segments));
-  const dim3 block(class_threads(CLS));
   if (a.segments > 1)
-    hipLaunchKernelGGL((topk_kernel<BF16, CLS, true>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((topk_kernel<BF16, CLS, true>), grid, dim3(kernel_threads(CLS, BF16 ? 1 : 0, true)),
+                       0, stream, a);
   else
-    hipLaunchKernelGGL((topk_kernel<BF16, CLS, false>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((topk_kernel<BF16, CLS, false>), grid,
+                       dim3(kernel_threads(CLS, BF16 ? 1 : 0, false)), 0, stream, a);
   return static_cast<int>(hipGetLastError());
 }
 
 int launch_read(const KArgs& a, int dtype, int cls, uint32_t* sink, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.batch) * a.segments));
-  const int nt = class_threads(cls);
+  const int nt = kernel_threads(cls, dtype, a.segments > 1);
   if (dtype == 0) {
     if (nt == 512) hipLaunchKernelGGL((read_kernel<false, 512>), grid, dim3(512), 0, stream, a, sink);
     else hipLaunchKernelGGL((read_kernel<false, 256>), grid, dim3(256), 0, stream, a, sink);
