@@ -1268,30 +1268,45 @@ __global__ __launch_bounds__(kernel_threads(CLS, BF16 ? 1 : 0, MULTI), kWavesPer
     if (ntl > 0) issue(nxt_r, g_nxt, u + NBUF - 1);
     if (u < ntl) {
       const uint32_t blk = blk_at(u);
-      if (u == 0 && blk * static_cast<uint32_t>(kBlockElems) + kBlockElems <= L && 2 * k <= kBlockElems) {
-        // whole first block, and at least half of it can be dropped
-        BlockRegs<V> br;
+      // The whole blocks among the first three (bit j: block j).
+      uint32_t whole = 0;
+      if (u == 0) {
 #pragma unroll
-        for (int v = 0; v < V; ++v) br.v[v] = cur_r[v];
+        for (uint32_t j = 0; j < 3; ++j)
+          if (j < ntl && blk_at(j) * static_cast<uint32_t>(kBlockElems) + kBlockElems <= L)
+            whole |= 1u << j;
+      }
+      if (u == 0 && (whole & 3u) != 0u && 2 * k <= kBlockElems) {
+        // The start comes from the first whole block in the ring, where at
+        // least half of a block can be dropped: block 0, or block 1 when
+        // block 0 is the row's partial last block (then filtered from it).
+        BlockRegs<V> br;
+        if (whole & 1u) {
+#pragma unroll
+          for (int v = 0; v < V; ++v) br.v[v] = cur_r[v];
+        } else {
+          // The empty asm keeps this a branch: as a select between the two
+          // copies, every workgroup would wait for block 1 first.
+#pragma unroll
+          for (int v = 0; v < V; ++v) {
+            br.v[v] = r1[v];
+            asm volatile("" : "+v"(br.v[v].x), "+v"(br.v[v].y), "+v"(br.v[v].z), "+v"(br.v[v].w));
+          }
+        }
         // The whole blocks already in the ring (up to three) can vouch for a
         // tighter start, which saves appends and cuts later.  t2 estimates,
-        // from the first block alone and with 10% to spare, the edge with k
+        // from that block alone and with 10% to spare, the edge with k
         // of those blocks' elements at or above it; a plain count over them
         // confirms it before it is used.  They are elements of the row, so
         // the edge is valid for the whole row, shared or not.
         //
         // A workgroup with a short share of a shared row goes further: t2 is
         // then an estimate of the edge with 2k of the row's L elements at or
-        // above it (the 2kB/L-th largest of the first block).  It is used if
+        // above it (the 2kB/L-th largest of that block).  It is used if
         // the ring's count scales to at least 1.5k for the row, and it is
         // recorded for the row: the merge checks at the end that no element
         // of the top k lay at or below it, and reads the row again if one
         // may have.
-        uint32_t whole = 0;
-#pragma unroll
-        for (uint32_t j = 0; j < 3; ++j)
-          if (j < ntl && blk_at(j) * static_cast<uint32_t>(kBlockElems) + kBlockElems <= L)
-            whole |= 1u << j;
         const uint32_t nw = static_cast<uint32_t>(__popc(whole));
         const uint32_t nspec =
             (MULTI && ntl <= kSpecSteps && nw >= 2u)
@@ -1322,7 +1337,7 @@ __global__ __launch_bounds__(kernel_threads(CLS, BF16 ? 1 : 0, MULTI), kWavesPer
               }
             }
           };
-          count_in(cur_r);
+          if (whole & 1u) count_in(cur_r);
           if (whole & 2u) count_in(r1);
           if (whole & 4u) count_in(r2);
           const uint32_t wt = static_cast<uint32_t>(
