@@ -263,6 +263,7 @@ struct Smem {
   u64 rng[2];                 // epilogue sort: min / max order key of a segment
   u64 thr;                    // the workgroup's threshold (composite)
   u64 xv;                     // a cut's second answer: a bound with >= need2 candidates above
+  uint32_t bt[5];             // first-block start: min key, max key, t0 key, t2 key, ring count
   u64 specmax;                // merge: the largest estimated start used on the row (0: none)
   u64 tvalid;                 // merge: the largest bound known to leave k of the row above it
 };
@@ -825,7 +826,8 @@ __device__ __noinline__ RaggedResult filter_ragged(BlockRegs<V> r, uint32_t blk,
 // starting point for the row (t0).  With need2 > 0 the same search for
 // need2 gives t2, with at least need2 of the block's elements at or above it:
 // only an estimate for the row, which the caller must verify.  Leaves hist
-// zeroed and res[3] = 0 (a free counter).
+// zeroed.  Its reductions use bt[0..3], set at the kernel's start (it runs
+// at most once per workgroup).
 struct ThrPair {
   u64 t0, t2;
 };
@@ -860,18 +862,13 @@ __device__ __noinline__ ThrPair block_threshold(BlockRegs<V> r, uint32_t k, uint
   }
   klo = wave_min(klo);
   khi = wave_max(khi);
-  if (t == 0) {
-    sm.res[0] = 0xFFFFFFFFu;
-    sm.res[1] = 0u;
+  if (lane == 0) {   // bt[] was set at the kernel's start
+    atomicMin(&sm.bt[0], klo);
+    atomicMax(&sm.bt[1], khi);
   }
   __syncthreads();
-  if (lane == 0) {
-    atomicMin(&sm.res[0], klo);
-    atomicMax(&sm.res[1], khi);
-  }
-  __syncthreads();
-  klo = uniform(sm.res[0]);
-  khi = uniform(sm.res[1]);
+  klo = uniform(sm.bt[0]);
+  khi = uniform(sm.bt[1]);
   if (khi < klo) {   // no finite value in the block
     __syncthreads();
     return {kThrInit, kThrInit};
@@ -904,19 +901,13 @@ __device__ __noinline__ ThrPair block_threshold(BlockRegs<V> r, uint32_t k, uint
   }
   tk = wave_min(tk);
   tk2 = wave_min(tk2);
-  if (t == 0) {
-    sm.res[2] = 0xFFFFFFFFu;
-    sm.res[3] = 0u;
-    sm.res[4] = 0xFFFFFFFFu;
-  }
-  __syncthreads();
   if (lane == 0) {
-    atomicMin(&sm.res[2], tk);
-    atomicMin(&sm.res[4], tk2);
+    atomicMin(&sm.bt[2], tk);
+    atomicMin(&sm.bt[3], tk2);
   }
   __syncthreads();
-  const u64 t0 = (static_cast<u64>(uniform(sm.res[2])) << 32) - 1u;
-  const uint32_t k2 = uniform(sm.res[4]);
+  const u64 t0 = (static_cast<u64>(uniform(sm.bt[2])) << 32) - 1u;
+  const uint32_t k2 = uniform(sm.bt[3]);
   return {t0, k2 == 0xFFFFFFFFu ? kThrInit : (static_cast<u64>(k2) << 32) - 1u};
 }
 
@@ -1209,6 +1200,11 @@ __global__ __launch_bounds__(kernel_threads(CLS, BF16 ? 1 : 0, MULTI), kWavesPer
     sm.hikey = 0u;
     sm.flags = 0u;
     sm.thr = kThrInit;
+    sm.bt[0] = 0xFFFFFFFFu;   // the start's reductions, used once, start here
+    sm.bt[1] = 0u;
+    sm.bt[2] = 0xFFFFFFFFu;
+    sm.bt[3] = 0xFFFFFFFFu;
+    sm.bt[4] = 0u;
   }
   __syncthreads();
 
@@ -1342,9 +1338,9 @@ __global__ __launch_bounds__(kernel_threads(CLS, BF16 ? 1 : 0, MULTI), kWavesPer
           if (whole & 4u) count_in(r2);
           const uint32_t wt = static_cast<uint32_t>(
               __builtin_amdgcn_readlane(static_cast<int>(wave_prefix_sum(n)), 63));
-          if (lane == 0) atomicAdd(&sm.res[3], wt);
+          if (lane == 0) atomicAdd(&sm.bt[4], wt);
           __syncthreads();
-          const uint32_t ring = uniform(sm.res[3]);
+          const uint32_t ring = uniform(sm.bt[4]);
           if (ring >= k) {
             t0 = t2;   // k of the row's elements at or above it: valid
             tloc = t2;
