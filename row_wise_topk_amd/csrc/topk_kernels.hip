@@ -1237,6 +1237,7 @@ __global__ __launch_bounds__(kernel_threads(CLS, BF16 ? 1 : 0, MULTI), kWavesPer
   // So each wave records the count its own append produced, in a slot chosen
   // by step parity; the maximum over the waves is the count after the block.
   int par = 0;
+  bool spec_used = false;   // this workgroup started from an estimate
   auto count_after_step = [&](uint32_t after) -> uint32_t {
     if (lane == 0) sm.snap[par][wid] = after;
     __syncthreads();
@@ -1296,16 +1297,17 @@ __global__ __launch_bounds__(kernel_threads(CLS, BF16 ? 1 : 0, MULTI), kWavesPer
         // confirms it before it is used.  They are elements of the row, so
         // the edge is valid for the whole row, shared or not.
         //
-        // A workgroup with a short share of a shared row goes further: t2 is
-        // then an estimate of the edge with 2k of the row's L elements at or
-        // above it (the 2kB/L-th largest of that block).  It is used if
-        // the ring's count scales to at least 1.5k for the row, and it is
-        // recorded for the row: the merge checks at the end that no element
-        // of the top k lay at or below it, and reads the row again if one
-        // may have.
+        // A workgroup with a short share (a whole row or part of one) goes
+        // further: t2 is then an estimate of the edge with 2k of the row's L
+        // elements at or above it (the 2kB/L-th largest of that block).  It
+        // is used if the ring's count scales to at least 1.5k for the row,
+        // and checked at the end: by the merge for a shared row (the estimate
+        // is recorded for the row), by the final count for a whole row.  A
+        // failed check means one of the top k may lie at or below it, and the
+        // row is read again from a valid bound.
         const uint32_t nw = static_cast<uint32_t>(__popc(whole));
         const uint32_t nspec =
-            (MULTI && ntl <= kSpecSteps && nw >= 2u)
+            (ntl <= kSpecSteps && nw >= 2u)
                 ? static_cast<uint32_t>((2ull * k * kBlockElems + L - 1u) / L)
                 : k;
         const bool spec = nspec < k;
@@ -1348,6 +1350,8 @@ __global__ __launch_bounds__(kernel_threads(CLS, BF16 ? 1 : 0, MULTI), kWavesPer
             tloc = t2;   // an estimate, checked by the merge
           }
         }
+        spec_used = tloc != t0;
+        if (!MULTI && t == 0) sm.tvalid = t0;   // where a re-read starts
         if (tloc > thr) {
           thr = tloc;
           F = filter_of(thr);
@@ -1403,8 +1407,55 @@ __global__ __launch_bounds__(kernel_threads(CLS, BF16 ? 1 : 0, MULTI), kWavesPer
     step(r3, g3, r2, g2, u + 3);
   }
 
+  // The whole row read again, in order, from the largest valid bound
+  // (sm.tvalid), with the usual filter and cuts: for an estimated start that
+  // may have dropped one of the top k.
+  auto reread_row = [&]() {
+    if (t == 0) {
+      sm.cnt[cur] = 0u;
+      sm.thr = sm.tvalid;
+    }
+    __syncthreads();
+    thr = uniform64(sm.thr);
+    F = filter_of(thr);
+    for (uint32_t b = 0; b < nb; ++b) {
+      u32x4 rb[V];
+      load_block<BF16, V, NT>(rb, xrow, b, L);
+      uint32_t after;
+      if (ragged_row && b == last_blk) {
+        BlockRegs<V> br;
+#pragma unroll
+        for (int v = 0; v < V; ++v) br.v[v] = rb[v];
+        const RaggedResult rr =
+            filter_ragged<BF16, V, NT, CAP>(br, b, L, F, hi_lane, nan_lane ? 1u : 0u, sm, cur);
+        after = rr.after;
+        hi_lane = rr.hi_lane;
+        nan_lane = rr.nan_lane != 0;
+      } else {
+        after = filter_block<BF16, false, V, NT, CAP>(rb, b, L, F, hi_lane, nan_lane, sm, cur);
+      }
+      const uint32_t c2 = count_after_step(after);
+      if (c2 > trigger && b + 1 < nb) {
+        cur = cut_buffer<NT, CAP>(sm, cur, k, k + slack, L, hi_key());
+        thr = uniform64(sm.thr);
+        F = filter_of(thr);
+      }
+    }
+    const uint32_t hk = wave_max(hi_key());   // every candidate key, for the sort
+    if (lane == 0) atomicMax(&sm.hikey, hk);
+    __syncthreads();
+  };
+
   // NaN anywhere in this workgroup's share of [0, L).
   if (ballot(nan_lane) && lane == 0) atomicOr(&sm.flags, static_cast<uint32_t>(DS_ROW_NAN));
+  // A workgroup that owns its row and started from an estimate holds every
+  // element above the estimate; with at least k of them (or after a cut,
+  // which keeps k) none of the top k was dropped.  Otherwise it reads the row
+  // again from t0.
+  if (!MULTI && spec_used) {
+    __syncthreads();   // the NaN flags are in
+    if (uniform(sm.cnt[cur]) < k && uniform(sm.flags) == 0u) reread_row();
+  }
   if (MULTI && t == 0) {
     const u64 gl = load_thr(thr_g);
     if (gl > sm.thr) sm.thr = gl;   // survivors at or below the shared bound are not needed
@@ -1640,41 +1691,7 @@ __global__ __launch_bounds__(kernel_threads(CLS, BF16 ? 1 : 0, MULTI), kWavesPer
     // largest estimate (then so does the row's k-th largest).  Otherwise the
     // row is read again, whole and in order, from the largest valid bound.
     if (specmax != 0ull) {
-      if (uniform(above) < k && uniform(sm.flags) == 0u) {
-        if (t == 0) {
-          sm.cnt[cur] = 0u;
-          sm.thr = sm.tvalid;
-        }
-        __syncthreads();
-        thr = uniform64(sm.thr);
-        F = filter_of(thr);
-        for (uint32_t b = 0; b < nb; ++b) {
-          u32x4 rb[V];
-          load_block<BF16, V, NT>(rb, xrow, b, L);
-          uint32_t after;
-          if (ragged_row && b == last_blk) {
-            BlockRegs<V> br;
-#pragma unroll
-            for (int v = 0; v < V; ++v) br.v[v] = rb[v];
-            const RaggedResult rr =
-                filter_ragged<BF16, V, NT, CAP>(br, b, L, F, hi_lane, nan_lane ? 1u : 0u, sm, cur);
-            after = rr.after;
-            hi_lane = rr.hi_lane;
-            nan_lane = rr.nan_lane != 0;
-          } else {
-            after = filter_block<BF16, false, V, NT, CAP>(rb, b, L, F, hi_lane, nan_lane, sm, cur);
-          }
-          const uint32_t c2 = count_after_step(after);
-          if (c2 > trigger && b + 1 < nb) {
-            cur = cut_buffer<NT, CAP>(sm, cur, k, k + slack, L, hi_key());
-            thr = uniform64(sm.thr);
-            F = filter_of(thr);
-          }
-        }
-        const uint32_t hk = wave_max(hi_key());   // every candidate key, for the sort
-        if (lane == 0) atomicMax(&sm.hikey, hk);
-        __syncthreads();
-      }
+      if (uniform(above) < k && uniform(sm.flags) == 0u) reread_row();
     }
     if (a.sorted != 1 || uniform(sm.cnt[cur]) > static_cast<uint32_t>(SORT_CAP))
       cur = cut_buffer<NT, CAP>(sm, cur, k, k, L, hi_key());

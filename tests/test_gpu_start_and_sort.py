@@ -5,13 +5,14 @@ block, confirmed by a count over those blocks; rows whose first block is not
 like the next two make the count reject it (the row then starts from the
 first block's own bound), on one workgroup per row and on shared rows.
 
-A workgroup with a short share of a shared row may instead start from an
-estimate of the row's 2k-th largest value, read from its first block and
-accepted when the ring's count agrees; the merge then checks that at least k
-merged candidates lie above the row's largest estimate, and reads the whole
-row again when not.  Rows whose first workgroup sees only large values in its
-ring make that check fail (the row is read again); rows whose first block
-alone is large make the ring refuse the estimate.
+A workgroup with a short share of a row may instead start from an estimate
+of the row's 2k-th largest value, read from its first block and accepted
+when the ring's count agrees.  On a shared row the merge then checks that at
+least k merged candidates lie above the row's largest estimate; on a row
+with one workgroup the stream must end with at least k candidates.  Either
+way the row is read again when the check fails.  Rows whose (first)
+workgroup sees only large values in its ring make the check fail; rows whose
+first block alone is large make the ring refuse the estimate.
 
 The epilogue sort ranks small bins directly but splits bins of 9..32 members
 again when ranking them would cost more than another level; bf16 rows with a
@@ -115,6 +116,36 @@ def test_start_estimate_fails_merge_check_bf16():
                name="hot ring bf16 k=512")
     check_case(x, BF16, x.shape[1], 512, 1, True, "int32", plan=plan,
                name="hot ring bf16 k=512 sorted")
+
+
+# One workgroup per row: the ring (blocks 0, 1, 2 in block order) all large,
+# the rest small.  The estimate (the 2kB/L-th largest of block 0) is accepted,
+# but fewer than k elements of the row lie above it, so the workgroup ends
+# its stream with fewer than k candidates and reads the row again from t0.
+@pytest.mark.parametrize("k", [1024, 2048])
+def test_start_estimate_fails_final_count_one_workgroup(k):
+    x = _hot_blocks(16, (0, 1, 2), seed=71 + k)
+    plan = {"segments": 1, "in_order": 1}
+    check_case(x, FP32, x.shape[1], k, 1, True, "int32", plan=plan,
+               name=f"hot ring one wg fp32 k={k}")
+    check_case(x, FP32, x.shape[1], k, 0, False, "int64", plan=plan,
+               name=f"hot ring one wg fp32 unsorted k={k}")
+    n = x.shape[1] - 1000   # the re-read ends in a partial block
+    check_case(x[:, :n].copy(), FP32, n, k, 1, True, "int32", plan=plan,
+               name=f"hot ring one wg fp32 ragged k={k}")
+
+
+def test_start_estimate_fails_final_count_one_workgroup_bf16():
+    rng = np.random.Generator(np.random.PCG64(73))
+    x = rng.random((3, 16 * B), dtype=np.float32) * np.float32(0.25)
+    for b in (0, 1, 2):
+        x[:, b * B:(b + 1) * B] = np.float32(1.0) + rng.random((3, B), dtype=np.float32)
+    x = workloads.to_bf16_bits(x)
+    plan = {"segments": 1, "in_order": 1}
+    check_case(x, BF16, x.shape[1], 2048, 1, True, "int32", plan=plan,
+               name="hot ring one wg bf16 k=2048")
+    check_case(x, BF16, x.shape[1], 1024, 2, False, "int32", plan=plan,
+               name="hot ring one wg bf16 by column k=1024")
 
 
 # Only block 0 large: the ring's count (about 65 in three blocks) scales to
