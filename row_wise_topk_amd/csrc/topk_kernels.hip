@@ -16,8 +16,11 @@
 //    loads of the next 3 blocks are always in flight (a register ring whose
 //    loads are issued unconditionally, so the compiler waits for exactly the
 //    block being filtered);
-//  * the first whole block sets T from an 11-bit histogram of its keys held in
-//    registers, so the buffer never has to hold a block admitted at -inf;
+//  * the first whole block sets T from an 11-bit histogram of its values held
+//    in registers, so the buffer never has to hold a block admitted at -inf;
+//    a workgroup with a short share of a shared row starts from an estimate
+//    of the row's 2k-th value instead, which the merge checks (and, should
+//    it fail, the merger reads the row again from a valid bound);
 //  * the filter compares raw fp32 values (bf16 widened by a shift) with a
 //    wave-wide early-out on each lane's running maximum; survivors are
 //    compacted into LDS with ballot / mbcnt and one LDS atomic per wave;
@@ -26,7 +29,8 @@
 //    only when the boundary bin is too full, and keeping a candidate is one
 //    64-bit compare; exact ties on a key are cut by column the same way;
 //  * several workgroups on one row share T through a 64-bit atomicMax in
-//    device memory; the last to finish merges the others' survivors;
+//    device memory; the last to finish merges the others' survivors (fp32
+//    rows shared this way run 512-lane workgroups, one per CU);
 //  * the epilogue orders the k results by value or by column (histogram
 //    grouping, in-bin rank, re-binning of large bins) and writes indices,
 //    values and status.
@@ -1069,6 +1073,9 @@ __device__ __noinline__ void sort_results(Smem<CAP, NT>& sm, uint32_t m, bool by
     }
     __syncthreads();
     const uint32_t nseg = uniform(sm.nwork);
+    // Every element placed: done.  The histogram is left as it is (the sort
+    // is its last user in the kernel).
+    if (nseg == 0) break;
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       if (seg[j] == kDone) continue;
@@ -1079,7 +1086,6 @@ __device__ __noinline__ void sort_results(Smem<CAP, NT>& sm, uint32_t m, bool by
     }
     __syncthreads();
     hist_zero_own(sm);
-    if (nseg == 0) break;
     // the first member of each new segment fills in its entry
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
