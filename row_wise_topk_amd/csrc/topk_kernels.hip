@@ -1462,7 +1462,12 @@ __global__ __launch_bounds__(kernel_threads(CLS, BF16 ? 1 : 0, MULTI), kWavesPer
     __syncthreads();   // the NaN flags are in
     if (uniform(sm.cnt[cur]) < k && uniform(sm.flags) == 0u) reread_row();
   }
-  if (MULTI && t == 0) {
+  // A shared row's buffer that already fits the hand-over needs no cut, only
+  // the bound x_w; it is found from a 256-bin histogram that every wave
+  // scans for itself (two barriers instead of a cut's five).
+  const uint32_t c_end = min(uniform(sm.cnt[cur]), static_cast<uint32_t>(CAP));
+  const bool x_only = MULTI && c_end <= k + static_cast<uint32_t>(kSmallBin);
+  if (MULTI && !x_only && t == 0) {
     const u64 gl = load_thr(thr_g);
     if (gl > sm.thr) sm.thr = gl;   // survivors at or below the shared bound are not needed
   }
@@ -1478,10 +1483,62 @@ __global__ __launch_bounds__(kernel_threads(CLS, BF16 ? 1 : 0, MULTI), kWavesPer
     if (lane == 0) atomicMax(&sm.hikey, hk);
     __syncthreads();
   }
-  if (MULTI || a.sorted != 1 || uniform(sm.cnt[cur]) > static_cast<uint32_t>(SORT_CAP))
+  uint32_t mine = 0;   // shared rows: candidates above the threshold
+  u64 x_w = 0;         // and the bound they vouch for
+  if (x_only) {
+    const uint32_t need_w = (k + static_cast<uint32_t>(S) - 1u) / static_cast<uint32_t>(S);
+    const u64 T = uniform64(sm.thr);
+    const uint32_t K = static_cast<uint32_t>(T >> 32);
+    const uint32_t klo = static_cast<uint32_t>(T) == 0xFFFFFFFFu ? K + 1u : K;
+    const uint32_t hk = wave_max(hi_key());
+    uint32_t n = 0;
+    for (uint32_t i = t; i < c_end; i += NT) n += sm.comp[i] > T ? 1u : 0u;
+    n = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(wave_prefix_sum(n)), 63));
+    if (lane == 0) {
+      sm.snap[par][wid] = n;
+      atomicMax(&sm.hikey, hk);
+    }
+    __syncthreads();   // also: every wave's NaN flag is in
+#pragma unroll
+    for (int w2 = 0; w2 < NT / 64; ++w2) mine += sm.snap[par][w2];
+    par ^= 1;
+    mine = uniform(mine);
+    const uint32_t hi = uniform(sm.hikey);
+    if (mine >= need_w && hi >= klo) {
+      const uint32_t sh = bit_length(hi - klo) > 8u ? bit_length(hi - klo) - 8u : 0u;
+      for (uint32_t i = t; i < c_end; i += NT) {
+        const u64 v = sm.comp[i];
+        if (v > T) atomicAdd(&sm.hist[(key_of(v) - klo) >> sh], 1u);
+      }
+      __syncthreads();
+      // Bins 4 lane .. 4 lane + 3 per lane; the suffix count from the top
+      // finds the bin b with >= need_w candidates in bins >= b.
+      const u32x4 hb = reinterpret_cast<const u32x4*>(sm.hist)[lane];
+      const uint32_t s4 = hb.x + hb.y + hb.z + hb.w;
+      const uint32_t incl = wave_prefix_sum(s4);
+      const uint32_t total = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(incl), 63));
+      const uint32_t above = total - incl;   // bins of the lanes above this one
+      const u64 hit = ballot((above < need_w) & (above + s4 >= need_w));
+      const int hl = static_cast<int>(__ffsll(static_cast<long long>(hit))) - 1;   // one lane
+      uint32_t b = 4u * static_cast<uint32_t>(lane) + 3u, acc = above;
+      const uint32_t h4[4] = {hb.x, hb.y, hb.z, hb.w};
+#pragma unroll
+      for (int i = 3; i >= 0; --i) {
+        if (acc < need_w) b = 4u * static_cast<uint32_t>(lane) + static_cast<uint32_t>(i);
+        acc += h4[i];
+      }
+      b = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(b), hl));
+      x_w = (static_cast<u64>(klo + (b << sh)) << 32) - 1u;
+    }
+  } else if (MULTI || a.sorted != 1 || uniform(sm.cnt[cur]) > static_cast<uint32_t>(SORT_CAP)) {
     cur = cut_buffer<NT, CAP>(sm, cur, k, MULTI ? k + kSmallBin : k, L, hi_key(),
                               MULTI ? (k + static_cast<uint32_t>(S) - 1u) / static_cast<uint32_t>(S) : 0u,
                               MULTI);
+    if (MULTI) {
+      mine = uniform(sm.kept);   // at most k + kSmallBin
+      x_w = uniform64(sm.xv);
+    }
+  }
 
   if (MULTI) {
     // Hand the survivors to the row's last workgroup: each workgroup reserves
@@ -1490,7 +1547,6 @@ __global__ __launch_bounds__(kernel_threads(CLS, BF16 ? 1 : 0, MULTI), kWavesPer
     // accesses, and the stores are complete before the arrival counter moves,
     // so no L2 write-back or invalidate is needed.
     const uint32_t c = uniform(sm.cnt[cur]);
-    const uint32_t mine = uniform(sm.kept);   // at most k + kSmallBin
     const u64 Tk = uniform64(sm.thr);
     u64* wsc = reinterpret_cast<u64*>(a.ws_comp) + static_cast<int64_t>(row) * S * (k + kSmallBin);
     if (t == 0) {
@@ -1499,11 +1555,13 @@ __global__ __launch_bounds__(kernel_threads(CLS, BF16 ? 1 : 0, MULTI), kWavesPer
                        : 0u;
       sm.cnt[cur ^ 1] = 0u;
       if (mine >= k) publish_thr(thr_g, Tk);
-      st_agent(&a.ws_x[static_cast<int64_t>(row) * S + seg], sm.xv);
+      st_agent(&a.ws_x[static_cast<int64_t>(row) * S + seg], x_w);
       if (sm.flags)
         __hip_atomic_fetch_or(&a.ws_flags[row], sm.flags, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
+    if (x_only)   // the 256 bins x_w used go back to zero (every wave has read them)
+      for (uint32_t i = t; i < 256u; i += NT) sm.hist[i] = 0u;
     const uint32_t own0 = uniform(sm.res[0]);
     // Every candidate above the threshold goes to the reserved range, at an
     // offset taken with one LDS atomic per wave and group (never past the
