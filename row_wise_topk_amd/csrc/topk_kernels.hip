@@ -1541,18 +1541,33 @@ __global__ __launch_bounds__(kernel_threads(CLS, BF16 ? 1 : 0, MULTI), kWavesPer
   }
 
   if (MULTI) {
-    // Hand the survivors to the row's last workgroup: each workgroup reserves
-    // a range of the row's contiguous survivor array with one atomic and fills
-    // it.  Every shared word is written and read with agent-scope atomic
-    // accesses, and the stores are complete before the arrival counter moves,
-    // so no L2 write-back or invalidate is needed.
+    // Hand the survivors to the row's last workgroup.  When the row's whole
+    // survivor array (k + kSmallBin slots per workgroup) fits the merge's
+    // first two chunks, each workgroup fills its own slots from the start:
+    // the array is all zero between calls and zero is never above a
+    // threshold, so the merge reads every slot and no count is needed.
+    // Otherwise each workgroup reserves a range of the row's contiguous
+    // array with one atomic and fills it, and the merge reads up to the
+    // row's fill.  Every shared word is written and read with agent-scope
+    // atomic accesses, and the stores are complete before the arrival
+    // counter moves, so no L2 write-back or invalidate is needed.
+    constexpr int PER_FIT = (8 * (KMAX + static_cast<int>(kSmallBin)) + 2 * NT - 1) / (2 * NT);
+    constexpr int PER_ROOM = (CAP - (3 * KMAX + class_trigger(CLS)) / 4) / NT;
+    constexpr int PER_A = PER_FIT > 9 ? 9 : PER_FIT;
+    constexpr int PER_B = PER_A > PER_ROOM ? PER_ROOM : PER_A;
+    constexpr int PER = PER_B < 4 ? 4 : PER_B;
+    static_assert(PER * NT + (3 * KMAX + class_trigger(CLS)) / 4 <= CAP, "merge chunk room");
+    constexpr uint32_t CHUNK = PER * NT;
+    const uint32_t area = static_cast<uint32_t>(S) * (k + kSmallBin);
+    const bool fixed_slots = area <= 2u * CHUNK;
     const uint32_t c = uniform(sm.cnt[cur]);
     const u64 Tk = uniform64(sm.thr);
     u64* wsc = reinterpret_cast<u64*>(a.ws_comp) + static_cast<int64_t>(row) * S * (k + kSmallBin);
     if (t == 0) {
-      sm.res[0] = mine ? __hip_atomic_fetch_add(&a.ws_fill[row], mine, __ATOMIC_RELAXED,
-                                                __HIP_MEMORY_SCOPE_AGENT)
-                       : 0u;
+      if (!fixed_slots)
+        sm.res[0] = mine ? __hip_atomic_fetch_add(&a.ws_fill[row], mine, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT)
+                         : 0u;
       sm.cnt[cur ^ 1] = 0u;
       if (mine >= k) publish_thr(thr_g, Tk);
       st_agent(&a.ws_x[static_cast<int64_t>(row) * S + seg], x_w);
@@ -1562,9 +1577,10 @@ __global__ __launch_bounds__(kernel_threads(CLS, BF16 ? 1 : 0, MULTI), kWavesPer
     __syncthreads();
     if (x_only)   // the 256 bins x_w used go back to zero (every wave has read them)
       for (uint32_t i = t; i < 256u; i += NT) sm.hist[i] = 0u;
-    const uint32_t own0 = uniform(sm.res[0]);
-    // Every candidate above the threshold goes to the reserved range, at an
-    // offset taken with one LDS atomic per wave and group (never past the
+    const uint32_t own0 = fixed_slots ? static_cast<uint32_t>(seg) * (k + static_cast<uint32_t>(kSmallBin))
+                                      : uniform(sm.res[0]);
+    // Every candidate above the threshold goes to the workgroup's range, at
+    // an offset taken with one LDS atomic per wave and group (never past the
     // range, whatever the count).
     for_groups<NT>(c, [&](auto gs, uint32_t e0) {
       constexpr int G = decltype(gs)::value;
@@ -1605,24 +1621,17 @@ __global__ __launch_bounds__(kernel_threads(CLS, BF16 ? 1 : 0, MULTI), kWavesPer
     // than ceil(k / S) survivors).
     // Every load goes out at once: the row's counters and bounds first (so
     // that using them waits for nothing else), then the first two chunks of
-    // survivors.  The chunks need no count first: the row's array is zero
-    // past its fill, and zero is never above a threshold.  A chunk is at most
-    // 9 survivors per thread: two chunks hold the 2k or so survivors that
-    // workgroups starting from an estimate hand over, in one round trip, and
-    // the registers stay clear of the spills whose reloads would wait for
-    // every load and store in flight.  A chunk must also fit in the buffer
-    // after a cut (at most k + slack candidates remain).
-    constexpr int PER_FIT = (8 * (KMAX + static_cast<int>(kSmallBin)) + 2 * NT - 1) / (2 * NT);
-    constexpr int PER_ROOM = (CAP - (3 * KMAX + class_trigger(CLS)) / 4) / NT;
-    constexpr int PER_A = PER_FIT > 9 ? 9 : PER_FIT;
-    constexpr int PER_B = PER_A > PER_ROOM ? PER_ROOM : PER_A;
-    constexpr int PER = PER_B < 4 ? 4 : PER_B;
-    static_assert(PER * NT + (3 * KMAX + class_trigger(CLS)) / 4 <= CAP, "merge chunk room");
-    constexpr uint32_t CHUNK = PER * NT;
-    const uint32_t area = static_cast<uint32_t>(S) * (k + kSmallBin);
+    // survivor slots.  The slots need no count: unused ones are zero, and
+    // zero is never above a threshold.  A chunk is at most 9 slots per
+    // thread: two chunks hold the slots of up to 4 workgroups at k near the
+    // class's largest (all of them, for the sampler and indexer shapes) in
+    // one round trip, and the registers stay clear of the spills whose
+    // reloads would wait for every load and store in flight.  A chunk must
+    // also fit in the buffer after a cut (at most k + slack candidates
+    // remain).
     // Loads of one chunk; positions past the array read position 0 (a valid
-    // address) and are dropped.  Every position read below the fill is
-    // cleared, so the workspace is all zero again when the call ends.
+    // address) and are dropped.  Every used position read is cleared, so the
+    // workspace is all zero again when the call ends.
     auto load_chunk = [&](uint32_t c0, u64 (&mv)[PER]) {
 #pragma unroll
       for (int q = 0; q < PER; ++q) {
@@ -1636,7 +1645,7 @@ __global__ __launch_bounds__(kernel_threads(CLS, BF16 ? 1 : 0, MULTI), kWavesPer
       gfin = load_thr(thr_g);
       spm = ld_agent(spec_g);
       fl = ld_agent(&a.ws_flags[row]);
-      fill = ld_agent(&a.ws_fill[row]);
+      if (!fixed_slots) fill = ld_agent(&a.ws_fill[row]);
     }
     u64 xs = ~0ull;
     u64* xp = &a.ws_x[static_cast<int64_t>(row) * S + (t < S ? t : 0)];
@@ -1658,7 +1667,7 @@ __global__ __launch_bounds__(kernel_threads(CLS, BF16 ? 1 : 0, MULTI), kWavesPer
       sm.cnt[cur] = 0u;
     }
     __syncthreads();
-    const uint32_t total = min(uniform(sm.res[1]), area);
+    const uint32_t total = fixed_slots ? area : min(uniform(sm.res[1]), area);
     const u64 xmin = uniform64(sm.rng[0]);
     u64 T0 = uniform64(sm.thr);
     T0 = xmin > T0 ? xmin : T0;
@@ -1666,11 +1675,11 @@ __global__ __launch_bounds__(kernel_threads(CLS, BF16 ? 1 : 0, MULTI), kWavesPer
       sm.thr = T0;
       if (xmin > sm.tvalid) sm.tvalid = xmin;
     }
-    auto clear_chunk = [&](uint32_t c0) {
+    auto clear_chunk = [&](uint32_t c0, const u64 (&mv)[PER]) {   // every used position
 #pragma unroll
       for (int q = 0; q < PER; ++q) {
         const uint32_t p = c0 + t + q * NT;
-        if (p < total) st_agent(&wsc[p], 0ull);
+        if ((p < total) & (!fixed_slots | (mv[q] != 0ull))) st_agent(&wsc[p], 0ull);
       }
     };
     u64 Tm = T0;
@@ -1733,11 +1742,11 @@ __global__ __launch_bounds__(kernel_threads(CLS, BF16 ? 1 : 0, MULTI), kWavesPer
     };
     for (uint32_t c0 = 0; c0 < total; c0 += 2 * CHUNK) {
       merge_chunk(c0, va);
-      clear_chunk(c0);
+      clear_chunk(c0, va);
       if (c0 + 2 * CHUNK < total) load_chunk(c0 + 2 * CHUNK, va);
       if (c0 + CHUNK < total) {
         merge_chunk(c0 + CHUNK, vb);
-        clear_chunk(c0 + CHUNK);
+        clear_chunk(c0 + CHUNK, vb);
       }
       if (c0 + 3 * CHUNK < total) load_chunk(c0 + 3 * CHUNK, vb);
     }
