@@ -1371,6 +1371,30 @@ __global__ __launch_bounds__(kernel_threads(CLS, BF16 ? 1 : 0, MULTI), kWavesPer
           }
         }
       }
+      if constexpr (2 * KMAX > kBlockElems) {
+        // k above half a block: one block cannot drop enough, but three whole
+        // ring blocks (3 B >= 2 k) can.  Their k-th largest value is a valid
+        // start (k elements of the row at or above it).
+        if (u == 0 && whole == 7u && 2u * k <= 3u * static_cast<uint32_t>(kBlockElems)) {
+          BlockRegs<3 * V> b3;
+#pragma unroll
+          for (int v = 0; v < V; ++v) {
+            b3.v[v] = cur_r[v];
+            b3.v[V + v] = r1[v];
+            b3.v[2 * V + v] = r2[v];
+          }
+          const u64 t3 = uniform64(block_threshold<BF16, 3 * V, NT, CAP>(b3, k, 0u, sm).t0);
+          if (t == 0) sm.tvalid = t3;
+          if (t3 > thr) {
+            thr = t3;
+            F = filter_of(thr);
+            if (t == 0) {
+              atomicMax(&sm.thr, t3);
+              if (MULTI) publish_thr(thr_g, t3);
+            }
+          }
+        }
+      }
       uint32_t after;
       if (ragged_row && blk == last_blk) {
         BlockRegs<V> br;

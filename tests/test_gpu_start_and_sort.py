@@ -161,6 +161,25 @@ def test_start_estimate_refused_by_ring(dtype):
                name=f"hot block 0 {'bf16' if dtype else 'fp32'}")
 
 
+# k above half a block: the start is the k-th largest of the first three
+# whole blocks (a valid bound), for one workgroup per row and for shares of
+# four blocks; normal rows and rows whose ring blocks are all large.
+@pytest.mark.parametrize("k", [2049, 3000, 4096])
+@pytest.mark.parametrize("dtype", [FP32, BF16])
+@pytest.mark.parametrize("segments", [1, 4])
+def test_three_block_start_large_k(k, dtype, segments):
+    rng = np.random.Generator(np.random.PCG64(k + segments))
+    f = rng.standard_normal((3, 16 * B)).astype(np.float32)
+    x = workloads.to_bf16_bits(f) if dtype == BF16 else f
+    plan = {"segments": segments}
+    check_case(x, dtype, 16 * B, k, 1, True, "int32", plan=plan,
+               name=f"three-block start k={k} S={segments}")
+    h = _hot_blocks(16, (0, segments, 2 * segments), seed=k)
+    h = workloads.to_bf16_bits(h) if dtype == BF16 else h
+    check_case(h, dtype, 16 * B, k, 0, False, "int32", plan={"segments": segments, "in_order": 1},
+               name=f"three-block start, large ring k={k} S={segments}")
+
+
 def _levels_bf16(batch: int, n: int, levels: int, seed: int) -> np.ndarray:
     """bf16 rows (as bits) taking `levels` consecutive bf16 codes from 1.0 up,
     so `levels` distinct values, each about n / levels times."""
