@@ -836,8 +836,8 @@ struct ThrPair {
   u64 t0, t2;
 };
 template <bool BF16, int V, int NT, int CAP>
-__device__ __noinline__ ThrPair block_threshold(BlockRegs<V> r, uint32_t k, uint32_t need2,
-                                                Smem<CAP, NT>& sm) {
+__device__ __forceinline__ ThrPair block_threshold_body(const BlockRegs<V>& r, uint32_t k,
+                                                        uint32_t need2, Smem<CAP, NT>& sm) {
   constexpr int EPV = BF16 ? 8 : 4;
   constexpr int NS = V * EPV;
   const int t = threadIdx.x, lane = t & 63;
@@ -913,6 +913,14 @@ __device__ __noinline__ ThrPair block_threshold(BlockRegs<V> r, uint32_t k, uint
   const u64 t0 = (static_cast<u64>(uniform(sm.bt[2])) << 32) - 1u;
   const uint32_t k2 = uniform(sm.bt[3]);
   return {t0, k2 == 0xFFFFFFFFu ? kThrInit : (static_cast<u64>(k2) << 32) - 1u};
+}
+// Out of line for one block (once per workgroup, and small enough to pass in
+// registers); several blocks are passed to the body inline instead, since
+// their registers would go through scratch memory as arguments.
+template <bool BF16, int V, int NT, int CAP>
+__device__ __noinline__ ThrPair block_threshold(BlockRegs<V> r, uint32_t k, uint32_t need2,
+                                                Smem<CAP, NT>& sm) {
+  return block_threshold_body<BF16, V, NT, CAP>(r, k, need2, sm);
 }
 
 
@@ -1383,7 +1391,7 @@ __global__ __launch_bounds__(kernel_threads(CLS, BF16 ? 1 : 0, MULTI), kWavesPer
             b3.v[V + v] = r1[v];
             b3.v[2 * V + v] = r2[v];
           }
-          const u64 t3 = uniform64(block_threshold<BF16, 3 * V, NT, CAP>(b3, k, 0u, sm).t0);
+          const u64 t3 = uniform64(block_threshold_body<BF16, 3 * V, NT, CAP>(b3, k, 0u, sm).t0);
           if (t == 0) sm.tvalid = t3;
           if (t3 > thr) {
             thr = t3;
