@@ -818,8 +818,9 @@ __device__ __noinline__ RaggedResult filter_ragged(BlockRegs<V> r, uint32_t blk,
   return {after, hi_lane, nl ? 1u : 0u};
 }
 
-// Starting thresholds from one whole block held in registers, before any of
-// it is appended.  The block's values are binned linearly between their
+// Starting thresholds from whole blocks held in registers, before any of
+// them is appended (used for the three-block start of k above half a block;
+// one block uses the per-wave version below).  The values are binned linearly between their
 // finite minimum and maximum (2048 bins; -inf and +inf clamp to the end
 // bins, NaN is left out).  Linear bins spread the usual bell-shaped scores
 // over many bins, so the LDS atomics rarely collide, where bins on the key
@@ -914,14 +915,135 @@ __device__ __forceinline__ ThrPair block_threshold_body(const BlockRegs<V>& r, u
   const uint32_t k2 = uniform(sm.bt[3]);
   return {t0, k2 == 0xFFFFFFFFu ? kThrInit : (static_cast<u64>(k2) << 32) - 1u};
 }
-// Out of line for one block (once per workgroup, and small enough to pass in
-// registers); several blocks are passed to the body inline instead, since
-// their registers would go through scratch memory as arguments.
+// The same starting thresholds with one barrier, for one block: each of the
+// NW waves bins
+// its own values linearly between their finite minimum and maximum, into
+// its own 256 bins (hist[256 w, 256 w + 256)), and finds with a wave scan
+// the edge with ceil(k / NW) of its values at or above it.  Every wave thus
+// vouches for ceil(k / NW) values above its edge, so the smallest edge over
+// the waves has NW ceil(k / NW) >= k values of the block(s) at or above it:
+// t0, a valid start.  The waves' edges for ceil(need2 / NW) are combined by
+// their lower median into the estimate t2 (the caller verifies it).  A wave
+// with fewer than ceil(k / NW) finite values vouches for nothing, and then
+// t0 = kThrInit.  Leaves hist zeroed.  Binning each wave's values on its
+// own also keeps a rare outlier from stretching every bin: it widens one
+// wave's bins, and the median passes over that wave's estimate.
 template <bool BF16, int V, int NT, int CAP>
-__device__ __noinline__ ThrPair block_threshold(BlockRegs<V> r, uint32_t k, uint32_t need2,
-                                                Smem<CAP, NT>& sm) {
-  return block_threshold_body<BF16, V, NT, CAP>(r, k, need2, sm);
+__device__ __forceinline__ ThrPair wave_threshold(const BlockRegs<V>& r, uint32_t k, uint32_t need2,
+                                                  Smem<CAP, NT>& sm) {
+  constexpr int EPV = BF16 ? 8 : 4;
+  constexpr int NS = V * EPV;
+  constexpr int NW = NT / 64;
+  constexpr uint32_t kWaveBins = 256;
+  static_assert(NW * kWaveBins <= kBins, "per-wave bins");
+  const int t = threadIdx.x, lane = t & 63;
+  const uint32_t w = static_cast<uint32_t>(t) >> 6;
+  const uint32_t kw = (k + NW - 1u) / NW;
+  const uint32_t nw2 = need2 ? (need2 + NW - 1u) / NW : 0u;
+  float f[NS];
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t x = r.v[v][q];
+      if (BF16) {
+        f[v * 8 + 2 * q] = __uint_as_float(x << 16);
+        f[v * 8 + 2 * q + 1] = __uint_as_float(x & 0xFFFF0000u);
+      } else {
+        f[v * 4 + q] = __uint_as_float(x);
+      }
+    }
+  }
+  uint32_t klo = 0xFFFFFFFFu, khi = 0u;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const uint32_t key = key_of_bits(__float_as_uint(f[s]));
+    const bool fin = __builtin_fabsf(f[s]) <= 3.402823466e38f;
+    klo = (fin & (key < klo)) ? key : klo;
+    khi = (fin & (key > khi)) ? key : khi;
+  }
+  klo = wave_min(klo);
+  khi = wave_max(khi);
+  uint32_t e0 = 0, e2 = 0xFFFFFFFFu;   // this wave's edges (keys); 0: vouches for nothing
+  uint32_t* hw = sm.hist + w * kWaveBins;
+  if (khi >= klo) {
+    const float lo = __uint_as_float(bits_of_key(klo));
+    const float hi = __uint_as_float(bits_of_key(khi));
+    const float span = hi - lo;
+    const float scale = span > 0.0f ? static_cast<float>(kWaveBins - 1) / span : 0.0f;
+    auto bin_of = [&](float x) -> uint32_t {
+      const float y = __builtin_fminf(__builtin_fmaxf((x - lo) * scale, 0.0f),
+                                      static_cast<float>(kWaveBins - 1));
+      return static_cast<uint32_t>(y);
+    };
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      if (f[s] == f[s]) atomicAdd(&hw[bin_of(f[s])], 1u);
+    // Bins 4 lane .. 4 lane + 3 of this wave; suffix counts from the top.
+    // One wave's LDS accesses complete in the order issued, so its reads see
+    // all of its atomics: no barrier, only no reordering by the compiler.
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    const u32x4 hb = reinterpret_cast<const u32x4*>(hw)[lane];
+    reinterpret_cast<u32x4*>(hw)[lane] = u32x4{0u, 0u, 0u, 0u};
+    const uint32_t h4[4] = {hb.x, hb.y, hb.z, hb.w};
+    const uint32_t s4 = hb.x + hb.y + hb.z + hb.w;
+    const uint32_t incl = wave_prefix_sum(s4);
+    const uint32_t total = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(incl), 63));
+    const uint32_t above = total - incl;   // in the bins of higher lanes
+    auto edge_bin = [&](uint32_t need) -> uint32_t {   // highest b with >= need in bins >= b
+      uint32_t b = 0xFFFFFFFFu, acc = above;
+#pragma unroll
+      for (int i = 3; i >= 0; --i) {
+        if ((acc < need) & (acc + h4[i] >= need)) b = 4u * static_cast<uint32_t>(lane) + static_cast<uint32_t>(i);
+        acc += h4[i];
+      }
+      return wave_min(b);   // exactly one lane has it; 0xFFFFFFFF if total < need
+    };
+    const uint32_t b0 = edge_bin(kw);
+    const uint32_t b2 = nw2 ? edge_bin(nw2) : 0xFFFFFFFFu;
+    uint32_t m0 = 0xFFFFFFFFu, m2 = 0xFFFFFFFFu;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const uint32_t key = key_of_bits(__float_as_uint(f[s]));
+      const uint32_t bn = bin_of(f[s]);
+      const bool ok = f[s] == f[s];
+      m0 = (ok & (bn >= b0) & (key < m0)) ? key : m0;
+      m2 = (ok & (bn >= b2) & (key < m2)) ? key : m2;
+    }
+    m0 = wave_min(m0);
+    m2 = wave_min(m2);
+    if (b0 != 0xFFFFFFFFu) e0 = m0;
+    if (b2 != 0xFFFFFFFFu) e2 = m2;
+  }
+  if (lane == 0) {
+    sm.wsum[w] = e0;
+    sm.snap[0][w] = e2;   // reused: no step has run yet
+  }
+  __syncthreads();
+  uint32_t lo0 = 0xFFFFFFFFu;
+  uint32_t e2s[NW];
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    const uint32_t a0 = sm.wsum[i];
+    lo0 = a0 < lo0 ? a0 : lo0;
+    e2s[i] = sm.snap[0][i];
+  }
+  // lower median of the waves' estimates (a small sorting network)
+#pragma unroll
+  for (int i = 0; i < NW; ++i)
+#pragma unroll
+    for (int j = 0; j + 1 < NW - i; ++j) {
+      const uint32_t x = e2s[j], y = e2s[j + 1];
+      e2s[j] = x < y ? x : y;
+      e2s[j + 1] = x < y ? y : x;
+    }
+  const uint32_t med = e2s[(NW - 1) / 2];
+  __syncthreads();   // wsum and snap are free again
+  const u64 t0 = lo0 == 0u || lo0 == 0xFFFFFFFFu ? kThrInit : (static_cast<u64>(lo0) << 32) - 1u;
+  const u64 t2 = (!nw2 || med == 0xFFFFFFFFu || med == 0u) ? kThrInit : (static_cast<u64>(med) << 32) - 1u;
+  return {t0, t2};
 }
+
 
 
 // Loads of one block.  Always issued, whatever the block: a vector that would
@@ -1327,7 +1449,7 @@ __global__ __launch_bounds__(kernel_threads(CLS, BF16 ? 1 : 0, MULTI), kWavesPer
         const bool spec = nspec < k;
         const uint32_t need2 =
             spec ? nspec : (nw >= 2u ? (11u * k + 10u * nw - 1u) / (10u * nw) : 0u);
-        const ThrPair tp = block_threshold<BF16, V, NT, CAP>(br, k, need2, sm);
+        const ThrPair tp = wave_threshold<BF16, V, NT, CAP>(br, k, need2, sm);
         u64 t0 = uniform64(tp.t0);   // the same in every lane: keep it scalar
         const u64 t2 = uniform64(tp.t2);
         u64 tloc = t0;               // this workgroup's start
@@ -1391,6 +1513,8 @@ __global__ __launch_bounds__(kernel_threads(CLS, BF16 ? 1 : 0, MULTI), kWavesPer
             b3.v[V + v] = r1[v];
             b3.v[2 * V + v] = r2[v];
           }
+          // (the block-wide histogram: its k-th value is tighter than the
+          // smallest of the waves' edges, and no estimate is needed here)
           const u64 t3 = uniform64(block_threshold_body<BF16, 3 * V, NT, CAP>(b3, k, 0u, sm).t0);
           if (t == 0) sm.tvalid = t3;
           if (t3 > thr) {
