@@ -529,6 +529,14 @@ __device__ __forceinline__ void compact_buffer(Smem<CAP, NT>& sm, uint32_t c, in
 }
 
 constexpr uint32_t kSmallBin = 64;   // largest boundary bin ranked directly
+#ifndef SMALL_CUT_G
+#define SMALL_CUT_G 4
+#endif
+// small_cut: candidates per thread, within the buffer's room
+constexpr int small_cut_g(int cap, int nt) {
+  return SMALL_CUT_G * nt + static_cast<int>(kSmallBin) <= cap ? SMALL_CUT_G
+                                                               : (cap - static_cast<int>(kSmallBin)) / nt;
+}
 
 // The n = sm.nside (<= kSmallBin) members of a small boundary bin sit in the
 // histogram memory as composites.  Each wave counts, for every member, how
@@ -696,6 +704,150 @@ __device__ __noinline__ int cut_buffer(Smem<CAP, NT>& sm, int cur, uint32_t k,
     sm.thr = newT;
     sm.xv = xv;
     sm.kept = kept;
+  }
+  __syncthreads();
+  return nxt;
+}
+
+// The exact top-k of a buffer of at most G * NT candidates (k of those above
+// sm.thr are kept, the rest dropped), in four barriers where cut_buffer needs
+// about nine.  Every thread holds its G candidates in registers, so the
+// compaction may overwrite the buffer in place.  One histogram of 256 bins
+// over [lowest key above sm.thr, sm.hikey], which every wave scans for
+// itself, finds the boundary bin; everything above it is kept, and the bin's
+// members (at most kSmallBin) are ranked by one wave, which keeps the top
+// ones.  A larger boundary bin, or no more than k candidates above sm.thr,
+// falls back to cut_buffer.  sm.hikey must bound every candidate's key.
+template <int G, int NT, int CAP>
+__device__ __noinline__ int small_cut(Smem<CAP, NT>& sm, int cur, uint32_t k, uint32_t n_cols,
+                                      uint32_t hi_key) {
+  static_assert(G * NT + static_cast<int>(kSmallBin) <= CAP, "small cut room");
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int nxt = cur ^ 1;
+  const uint32_t c = min(uniform(sm.cnt[cur]), static_cast<uint32_t>(CAP));
+  const u64 T = uniform64(sm.thr);
+  const uint32_t hi = uniform(sm.hikey);
+  const uint32_t K = static_cast<uint32_t>(T >> 32);
+  const uint32_t klo = static_cast<uint32_t>(T) == 0xFFFFFFFFu ? K + 1u : K;   // lowest key above T
+  const uint32_t span = hi - klo;
+  const uint32_t sh = bit_length(span) > 8u ? bit_length(span) - 8u : 0u;
+  auto bin_of = [&](u64 v) -> uint32_t {
+    const uint32_t d = key_of(v) - klo;
+    return (d < span ? d : span) >> sh;
+  };
+  u64 v[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const uint32_t i = static_cast<uint32_t>(t + g * NT);
+    v[g] = i < c ? sm.comp[i] : 0ull;
+    v[g] = v[g] > T ? v[g] : 0ull;   // 0 is never above T
+  }
+  const bool usable = (hi >= klo) & (c > k);
+  if (usable) {
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+      if (v[g] != 0ull) atomicAdd(&sm.hist[bin_of(v[g])], 1u);
+  }
+  if (t == 0) {
+    sm.cnt[nxt] = 0u;
+    sm.nside = 0u;
+  }
+  __syncthreads();
+  // Bins 4 lane .. 4 lane + 3 per lane, suffix counts from the top: the bin b
+  // with fewer than k candidates above it and at least k at or above it.
+  uint32_t b = 0, ab = 0, bc = 0;
+  bool found = false;
+  if (usable) {
+    const u32x4 hb = reinterpret_cast<const u32x4*>(sm.hist)[lane];
+    const uint32_t h4[4] = {hb.x, hb.y, hb.z, hb.w};
+    const uint32_t s4 = hb.x + hb.y + hb.z + hb.w;
+    const uint32_t incl = wave_prefix_sum(s4);
+    const uint32_t total = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(incl), 63));
+    const uint32_t above = total - incl;
+    const u64 hit = ballot((above < k) & (above + s4 >= k));
+    if (hit) {
+      const int hl = static_cast<int>(__ffsll(static_cast<long long>(hit))) - 1;
+      uint32_t lb = 0, lab = 0, lbc = 0, acc = above;
+#pragma unroll
+      for (int i = 3; i >= 0; --i) {
+        if ((acc < k) & (acc + h4[i] >= k)) {
+          lb = 4u * static_cast<uint32_t>(lane) + static_cast<uint32_t>(i);
+          lab = acc;
+          lbc = h4[i];
+        }
+        acc += h4[i];
+      }
+      b = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(lb), hl));
+      ab = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(lab), hl));
+      bc = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(lbc), hl));
+      found = bc <= kSmallBin;
+    }
+  }
+  if (!found) {   // nothing written yet: clear the bins and cut the general way
+    __syncthreads();
+    for (uint32_t j = t; j < 256u; j += NT) sm.hist[j] = 0u;
+    return cut_buffer<NT, CAP>(sm, cur, k, k, n_cols, hi_key);
+  }
+  const uint32_t need = k - ab;   // 1 <= need <= bc
+  const bool whole = need == bc;  // the boundary bin is kept whole
+  u64* side = sm.comp + (CAP - static_cast<int>(kSmallBin));
+  {
+    u64 mk[G], ms[G];
+    uint32_t nk = 0, ns = 0;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const uint32_t bn = bin_of(v[g]);
+      const bool live = v[g] != 0ull;
+      mk[g] = ballot(live & ((bn > b) | (whole & (bn == b))));
+      ms[g] = ballot(live & !whole & (bn == b));
+      nk += static_cast<uint32_t>(__popcll(mk[g]));
+      ns += static_cast<uint32_t>(__popcll(ms[g]));
+    }
+    uint32_t kb = 0, sb = 0;
+    if (lane == 0) {
+      if (nk) kb = atomicAdd(&sm.cnt[nxt], nk);
+      if (ns) sb = atomicAdd(&sm.nside, ns);
+    }
+    kb = uniform(kb);
+    sb = uniform(sb);
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      if ((mk[g] >> lane) & 1ull) sm.comp[kb + mbcnt64(mk[g])] = v[g];
+      if ((ms[g] >> lane) & 1ull) side[sb + mbcnt64(ms[g])] = v[g];
+      kb += static_cast<uint32_t>(__popcll(mk[g]));
+      sb += static_cast<uint32_t>(__popcll(ms[g]));
+    }
+  }
+  if (whole && t == 0) {
+    const u64 lo_edge = (static_cast<u64>(klo + (b << sh)) << 32) - 1u;
+    sm.thr = lo_edge > T ? lo_edge : T;
+  }
+  __syncthreads();   // every wave has scanned the bins and appended
+  for (uint32_t j = t; j < 256u; j += NT) sm.hist[j] = 0u;
+  if (!whole && w == 0) {
+    // Composites are distinct: the member with need - 1 larger members is the
+    // last one kept.
+    const uint32_t n = bc;
+    const u64 mine = static_cast<uint32_t>(lane) < n ? side[lane] : 0ull;
+    uint32_t r = 0;
+    for (uint32_t j = 0; j < n; ++j) r += side[j] > mine ? 1u : 0u;
+    const bool in = static_cast<uint32_t>(lane) < n;
+    const u64 m = ballot(in & (r < need));
+    uint32_t base = 0;
+    if (lane == 0) base = atomicAdd(&sm.cnt[nxt], static_cast<uint32_t>(__popcll(m)));
+    base = uniform(base);
+    if ((m >> lane) & 1ull) sm.comp[base + mbcnt64(m)] = mine;
+    const u64 last = ballot(in & (r + 1u == need));
+    const int ll = static_cast<int>(__ffsll(static_cast<long long>(last))) - 1;
+    const u64 kth = static_cast<u64>(static_cast<uint32_t>(__builtin_amdgcn_readlane(
+                        static_cast<int>(static_cast<uint32_t>(mine >> 32)), ll)))
+                        << 32 |
+                    static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(mine)), ll));
+    if (lane == 0) sm.thr = kth - 1u;
+  }
+  if (t == 0) {
+    sm.kept = k;
+    sm.xv = 0ull;
   }
   __syncthreads();
   return nxt;
@@ -1434,17 +1586,22 @@ __global__ __launch_bounds__(kernel_threads(CLS, BF16 ? 1 : 0, MULTI), kWavesPer
         // the edge is valid for the whole row, shared or not.
         //
         // A workgroup with a short share (a whole row or part of one) goes
-        // further: t2 is then an estimate of the edge with 2k of the row's L
-        // elements at or above it (the 2kB/L-th largest of that block).  It
+        // further: t2 is then an estimate of the edge with fk of the row's L
+        // elements at or above it (the fkB/L-th largest of that block).  It
         // is used if the ring's count scales to at least 1.5k for the row,
         // and checked at the end: by the merge for a shared row (the estimate
         // is recorded for the row), by the final count for a whole row.  A
         // failed check means one of the top k may lie at or below it, and the
-        // row is read again from a valid bound.
+        // row is read again from a valid bound.  f is 3 on a shared row whose
+        // results need no sort, else 2: the wider margin makes a refused
+        // estimate (whose workgroup then lags the row) rarer, and costs more
+        // survivors at the end, which the sort pays for per candidate and
+        // the merge's exact cut hardly at all.
         const uint32_t nw = static_cast<uint32_t>(__popc(whole));
+        const uint32_t fold = (MULTI && a.sorted != 1) ? 3u : 2u;
         const uint32_t nspec =
             (ntl <= kSpecSteps && nw >= 2u)
-                ? static_cast<uint32_t>((2ull * k * kBlockElems + L - 1u) / L)
+                ? static_cast<uint32_t>((static_cast<u64>(fold) * k * kBlockElems + L - 1u) / L)
                 : k;
         const bool spec = nspec < k;
         const uint32_t need2 =
@@ -1922,8 +2079,12 @@ __global__ __launch_bounds__(kernel_threads(CLS, BF16 ? 1 : 0, MULTI), kWavesPer
     if (specmax != 0ull) {
       if (uniform(above) < k && uniform(sm.flags) == 0u) reread_row();
     }
-    if (a.sorted != 1 || uniform(sm.cnt[cur]) > static_cast<uint32_t>(SORT_CAP))
-      cur = cut_buffer<NT, CAP>(sm, cur, k, k, L, hi_key());
+    if (a.sorted != 1 || uniform(sm.cnt[cur]) > static_cast<uint32_t>(SORT_CAP)) {
+      if (uniform(sm.cnt[cur]) <= static_cast<uint32_t>(small_cut_g(CAP, NT) * NT))
+        cur = small_cut<small_cut_g(CAP, NT), NT, CAP>(sm, cur, k, L, hi_key());
+      else
+        cur = cut_buffer<NT, CAP>(sm, cur, k, k, L, hi_key());
+    }
     if (t == 0) {
       st_agent(spec_g, 0ull);
       st_agent(&a.ws_done[row], 0u);

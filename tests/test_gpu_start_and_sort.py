@@ -200,3 +200,28 @@ def test_sort_with_tie_groups(levels, k, segments):
                name=f"ties levels={levels} k={k} S={segments}")
     check_case(x, BF16, 65536, k, 2, False, "int32", plan={"segments": segments},
                name=f"ties by column levels={levels} k={k} S={segments}")
+
+
+# The merge's exact cut of a small buffer (at most a few per thread): one
+# histogram finds the boundary bin, whose members are ranked directly, or
+# kept whole when all of them are needed; a boundary bin of more than 64
+# members (heavy bf16 ties) goes the general way.  Unsorted results on
+# shared rows take it; rows barely longer than k leave the merge no more
+# than k candidates.
+@pytest.mark.parametrize("segments", [2, 4])
+@pytest.mark.parametrize("k", [64, 512])
+def test_merge_small_cut(segments, k):
+    rng = np.random.Generator(np.random.PCG64(101 + k + segments))
+    f = rng.standard_normal((4, 16 * B)).astype(np.float32)
+    plan = {"segments": segments}
+    check_case(f, FP32, 16 * B, k, 0, True, "int32", plan=plan,
+               name=f"small cut fp32 k={k} S={segments}")
+    check_case(workloads.to_bf16_bits(f), BF16, 16 * B, k, 0, True, "int32", plan=plan,
+               name=f"small cut bf16 k={k} S={segments}")
+    for levels in (64, 8192):   # tie groups of about 1000 and about 8 values
+        x = _levels_bf16(4, 16 * B, levels, seed=levels + k)
+        check_case(x, BF16, 16 * B, k, 0, False, "int32", plan=plan,
+                   name=f"small cut ties levels={levels} k={k} S={segments}")
+    end = np.array([k + 1, k + 70, 2 * B + 5, 16 * B], dtype=np.int32)
+    check_case(f, FP32, 16 * B, k, 0, True, "int64", end=end, plan=plan,
+               name=f"small cut short rows k={k} S={segments}")
