@@ -88,6 +88,7 @@ __device__ __forceinline__ uint32_t col_of(u64 c) { return ~static_cast<uint32_t
 
 // T = -inf with "greater or equal": just below the key of -inf, all columns.
 constexpr u64 kThrInit = (static_cast<u64>(0x00800000u - 1u) << 32) | 0xFFFFFFFFull;
+constexpr uint32_t kNegInfKey = 0x00800000u;   // key of -inf, the lowest of any non-NaN value
 
 // The threshold in the form the filter uses: admit v iff v > f, or v == f and
 // column < idx_lim.  With idx_lim == ~0u this is simply v >= f.
@@ -1071,7 +1072,8 @@ __device__ __forceinline__ ThrPair block_threshold_body(const BlockRegs<V>& r, u
 // NW waves bins
 // its own values linearly between their finite minimum and maximum, into
 // its own 256 bins (hist[256 w, 256 w + 256)), and finds with a wave scan
-// the edge with ceil(k / NW) of its values at or above it.  Every wave thus
+// the highest bin b with ceil(k / NW) of its values in bins >= b; its edge is
+// a value that bins below b (so lies below all of them).  Every wave thus
 // vouches for ceil(k / NW) values above its edge, so the smallest edge over
 // the waves has NW ceil(k / NW) >= k values of the block(s) at or above it:
 // t0, a valid start.  The waves' edges for ceil(need2 / NW) are combined by
@@ -1107,15 +1109,18 @@ __device__ __forceinline__ ThrPair wave_threshold(const BlockRegs<V>& r, uint32_
     }
   }
   uint32_t klo = 0xFFFFFFFFu, khi = 0u;
+  bool ninf = false;   // a -inf, which bin 0 holds below klo
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     const uint32_t key = key_of_bits(__float_as_uint(f[s]));
     const bool fin = __builtin_fabsf(f[s]) <= 3.402823466e38f;
     klo = (fin & (key < klo)) ? key : klo;
     khi = (fin & (key > khi)) ? key : khi;
+    ninf |= key == kNegInfKey;
   }
   klo = wave_min(klo);
   khi = wave_max(khi);
+  const bool any_ninf = ballot(ninf) != 0ull;
   uint32_t e0 = 0, e2 = 0xFFFFFFFFu;   // this wave's edges (keys); 0: vouches for nothing
   uint32_t* hw = sm.hist + w * kWaveBins;
   if (khi >= klo) {
@@ -1153,32 +1158,33 @@ __device__ __forceinline__ ThrPair wave_threshold(const BlockRegs<V>& r, uint32_
     };
     const uint32_t b0 = edge_bin(kw);
     const uint32_t b2 = nw2 ? edge_bin(nw2) : 0xFFFFFFFFu;
-    uint32_t m0 = 0xFFFFFFFFu, m2 = 0xFFFFFFFFu;
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const uint32_t key = key_of_bits(__float_as_uint(f[s]));
-      const uint32_t bn = bin_of(f[s]);
-      const bool ok = f[s] == f[s];
-      m0 = (ok & (bn >= b0) & (key < m0)) ? key : m0;
-      m2 = (ok & (bn >= b2) & (key < m2)) ? key : m2;
-    }
-    m0 = wave_min(m0);
-    m2 = wave_min(m2);
-    if (b0 != 0xFFFFFFFFu) e0 = m0;
-    if (b2 != 0xFFFFFFFFu) e2 = m2;
+    // A key at or below every member of bins >= b.  For b > 0: the middle
+    // of bin b - 1, confirmed by binning it (bin_of never decreases as x
+    // grows, so any x binned at b or above is strictly greater than a value
+    // binned below b, and so is its key).  Bin 0 holds every non-NaN value:
+    // the smallest finite key, or that of -inf if the wave holds one.  A
+    // middle that does not bin below b gives the lowest key.
+    auto below_bin = [&](uint32_t b) -> uint32_t {
+      if (b == 0u) return any_ninf ? kNegInfKey : klo;
+      const float mid = lo + (static_cast<float>(b) - 0.5f) * (span / static_cast<float>(kWaveBins - 1));
+      return bin_of(mid) < b ? key_of_bits(__float_as_uint(mid)) : kNegInfKey;
+    };
+    if (b0 != 0xFFFFFFFFu) e0 = below_bin(b0);
+    if (b2 != 0xFFFFFFFFu) e2 = below_bin(b2);
   }
   if (lane == 0) {
     sm.wsum[w] = e0;
     sm.snap[0][w] = e2;   // reused: no step has run yet
   }
   __syncthreads();
+  // The same in every lane: combined in scalar registers.
   uint32_t lo0 = 0xFFFFFFFFu;
   uint32_t e2s[NW];
 #pragma unroll
   for (int i = 0; i < NW; ++i) {
-    const uint32_t a0 = sm.wsum[i];
+    const uint32_t a0 = uniform(sm.wsum[i]);
     lo0 = a0 < lo0 ? a0 : lo0;
-    e2s[i] = sm.snap[0][i];
+    e2s[i] = uniform(sm.snap[0][i]);
   }
   // lower median of the waves' estimates (a small sorting network)
 #pragma unroll
