@@ -1255,7 +1255,7 @@ __device__ __noinline__ void sort_results(Smem<CAP, NT>& sm, uint32_t m, bool by
                                           u64 key_lo, uint32_t span_bits) {
   static_assert(2 * MMAX + 2 * 4 * kSortSegs <= CAP, "sort regions");
   constexpr int PER = MMAX / NT;          // elements per thread at most
-  constexpr int RB = 8;                   // in-bin rank: members read per round
+  constexpr int RB = 4;                   // in-bin rank: members read per round
   constexpr uint32_t kDone = 0xFFFFu;
   const int t = threadIdx.x;
   u64* out = sm.comp;
