@@ -1781,11 +1781,14 @@ __global__ __launch_bounds__(kernel_threads(CLS, BF16 ? 1 : 0, MULTI), kWavesPer
     __syncthreads();   // the NaN flags are in
     if (uniform(sm.cnt[cur]) < k && uniform(sm.flags) == 0u) reread_row();
   }
-  // A shared row's buffer that already fits the hand-over needs no cut, only
-  // the bound x_w; it is found from a 256-bin histogram that every wave
-  // scans for itself (two barriers instead of a cut's five).
+  // A shared row's small buffer needs no cut, only the bound x_w and, when
+  // it holds more than the hand-over's k + kSmallBin slots, a bin edge with
+  // between k and k + kSmallBin candidates above it.  Both come from a
+  // 256-bin histogram that every wave scans for itself (two barriers instead
+  // of a cut's five); a boundary bin too large for the slots falls back to
+  // the cut.
   const uint32_t c_end = min(uniform(sm.cnt[cur]), static_cast<uint32_t>(CAP));
-  const bool x_only = MULTI && c_end <= k + static_cast<uint32_t>(kSmallBin);
+  const bool x_only = MULTI && c_end <= static_cast<uint32_t>(small_cut_g(CAP, NT) * NT);
   if (MULTI && !x_only && t == 0) {
     const u64 gl = load_thr(thr_g);
     if (gl > sm.thr) sm.thr = gl;   // survivors at or below the shared bound are not needed
@@ -1804,6 +1807,8 @@ __global__ __launch_bounds__(kernel_threads(CLS, BF16 ? 1 : 0, MULTI), kWavesPer
   }
   uint32_t mine = 0;   // shared rows: candidates above the threshold
   u64 x_w = 0;         // and the bound they vouch for
+  u64 t_keep = 0;      // x_only: the threshold the hand-over filters by
+  bool cut = !x_only && (MULTI || a.sorted != 1 || uniform(sm.cnt[cur]) > static_cast<uint32_t>(SORT_CAP));
   if (x_only) {
     const uint32_t need_w = (k + static_cast<uint32_t>(S) - 1u) / static_cast<uint32_t>(S);
     const u64 T = uniform64(sm.thr);
@@ -1822,6 +1827,7 @@ __global__ __launch_bounds__(kernel_threads(CLS, BF16 ? 1 : 0, MULTI), kWavesPer
     for (int w2 = 0; w2 < NT / 64; ++w2) mine += sm.snap[par][w2];
     par ^= 1;
     mine = uniform(mine);
+    t_keep = T;
     const uint32_t hi = uniform(sm.hikey);
     if (mine >= need_w && hi >= klo) {
       const uint32_t sh = bit_length(hi - klo) > 8u ? bit_length(hi - klo) - 8u : 0u;
@@ -1848,8 +1854,38 @@ __global__ __launch_bounds__(kernel_threads(CLS, BF16 ? 1 : 0, MULTI), kWavesPer
       }
       b = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(b), hl));
       x_w = (static_cast<u64>(klo + (b << sh)) << 32) - 1u;
+      if (mine > k + static_cast<uint32_t>(kSmallBin)) {
+        // The bin bk with fewer than k candidates above it and at least k
+        // at or above it; its lower edge keeps the candidates of bins >= bk.
+        const u64 kh = ballot((above < k) & (above + s4 >= k));
+        const int kl = static_cast<int>(__ffsll(static_cast<long long>(kh))) - 1;   // one lane
+        uint32_t bk = 0, in_k = 0;
+        acc = above;
+#pragma unroll
+        for (int i = 3; i >= 0; --i) {
+          if ((acc < k) & (acc + h4[i] >= k)) {
+            bk = 4u * static_cast<uint32_t>(lane) + static_cast<uint32_t>(i);
+            in_k = acc + h4[i];
+          }
+          acc += h4[i];
+        }
+        bk = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(bk), kl));
+        in_k = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(in_k), kl));
+        if (in_k <= k + static_cast<uint32_t>(kSmallBin)) {
+          const u64 edge = (static_cast<u64>(klo + (bk << sh)) << 32) - 1u;
+          t_keep = edge > T ? edge : T;
+          mine = in_k;
+        } else {
+          cut = true;
+        }
+      }
     }
-  } else if (MULTI || a.sorted != 1 || uniform(sm.cnt[cur]) > static_cast<uint32_t>(SORT_CAP)) {
+    if (cut) {   // every wave has scanned the bins: clear them for the cut
+      __syncthreads();
+      for (uint32_t j = t; j < 256u; j += NT) sm.hist[j] = 0u;
+    }
+  }
+  if (cut) {
     cur = cut_buffer<NT, CAP>(sm, cur, k, MULTI ? k + kSmallBin : k, L, hi_key(),
                               MULTI ? (k + static_cast<uint32_t>(S) - 1u) / static_cast<uint32_t>(S) : 0u,
                               MULTI);
@@ -1880,7 +1916,7 @@ __global__ __launch_bounds__(kernel_threads(CLS, BF16 ? 1 : 0, MULTI), kWavesPer
     const uint32_t area = static_cast<uint32_t>(S) * (k + kSmallBin);
     const bool fixed_slots = area <= 2u * CHUNK;
     const uint32_t c = uniform(sm.cnt[cur]);
-    const u64 Tk = uniform64(sm.thr);
+    const u64 Tk = (x_only && !cut) ? t_keep : uniform64(sm.thr);
     u64* wsc = reinterpret_cast<u64*>(a.ws_comp) + static_cast<int64_t>(row) * S * (k + kSmallBin);
     if (t == 0) {
       if (!fixed_slots)
@@ -1888,6 +1924,7 @@ __global__ __launch_bounds__(kernel_threads(CLS, BF16 ? 1 : 0, MULTI), kWavesPer
                                                   __HIP_MEMORY_SCOPE_AGENT)
                          : 0u;
       sm.cnt[cur ^ 1] = 0u;
+      sm.thr = Tk;   // read again only after the barrier below
       if (mine >= k) publish_thr(thr_g, Tk);
       st_agent(&a.ws_x[static_cast<int64_t>(row) * S + seg], x_w);
       if (sm.flags)

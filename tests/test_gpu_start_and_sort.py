@@ -225,3 +225,26 @@ def test_merge_small_cut(segments, k):
     end = np.array([k + 1, k + 70, 2 * B + 5, 16 * B], dtype=np.int32)
     check_case(f, FP32, 16 * B, k, 0, True, "int64", end=end, plan=plan,
                name=f"small cut short rows k={k} S={segments}")
+
+
+# A shared row's workgroup whose buffer ends between k + 64 and four
+# candidates per thread takes its hand-over threshold from the same 256-bin
+# histogram as its bound x_w (the edge of the bin holding the k-th
+# candidate), or cuts the general way when that bin would overfill the
+# hand-over.  Workgroup 1 of 4 (blocks 1, 5, 9, 13 in order) estimates its
+# start from a normal block 1 while its other blocks sit 0.5 higher, so it
+# ends with roughly 650-900 candidates; bf16 ties exercise the fallback.
+@pytest.mark.parametrize("sorted_mode", [0, 1])
+@pytest.mark.parametrize("dtype", [FP32, BF16])
+def test_local_bin_edge_threshold(sorted_mode, dtype):
+    rng = np.random.Generator(np.random.PCG64(211 + sorted_mode))
+    f = rng.standard_normal((4, 16 * B)).astype(np.float32)
+    for b in (5, 9, 13):
+        f[:, b * B:(b + 1) * B] += np.float32(0.5)
+    x = workloads.to_bf16_bits(f) if dtype == BF16 else f
+    plan = {"segments": 4, "in_order": 1}
+    check_case(x, dtype, 16 * B, 512, sorted_mode, True, "int32", plan=plan,
+               name=f"local bin edge {'bf16' if dtype else 'fp32'} sorted={sorted_mode}")
+    levels = _levels_bf16(4, 16 * B, 256, seed=7 + sorted_mode)
+    check_case(levels, BF16, 16 * B, 512, sorted_mode, False, "int32", plan=plan,
+               name=f"local bin edge ties sorted={sorted_mode}")
