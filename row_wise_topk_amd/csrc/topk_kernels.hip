@@ -1594,20 +1594,23 @@ __global__ __launch_bounds__(kernel_threads(CLS, BF16 ? 1 : 0, MULTI), kWavesPer
         // A workgroup with a short share (a whole row or part of one) goes
         // further: t2 is then an estimate of the edge with fk of the row's L
         // elements at or above it (the fkB/L-th largest of that block).  It
-        // is used if the ring's count scales to at least 1.5k for the row,
-        // and checked at the end: by the merge for a shared row (the estimate
-        // is recorded for the row), by the final count for a whole row.  A
-        // failed check means one of the top k may lie at or below it, and the
-        // row is read again from a valid bound.  f is 3 on a shared row whose
-        // results need no sort, else 2: the wider margin makes a refused
-        // estimate (whose workgroup then lags the row) rarer, and costs more
-        // survivors at the end, which the sort pays for per candidate and
-        // the merge's exact cut hardly at all.
+        // is used if the ring's count scales to at least 0.75 min(f, 2) k for
+        // the row, and checked at the end: by the merge for a shared row (the
+        // estimate is recorded for the row), by the final count for a whole
+        // row.  A failed check means one of the top k may lie at or below
+        // it, and the row is read again from a valid bound.  f is 3 on a
+        // shared row whose results need no sort, 2 on other shared rows: the
+        // wider margin makes a refused estimate (whose workgroup then lags
+        // the row) rarer, and costs more survivors at the end, which the
+        // sort pays for per candidate and the merge's exact cut hardly at
+        // all.  A whole row has no other workgroup to lag behind, and its
+        // exact cut pays for every extra candidate: f is 1.5 there.
         const uint32_t nw = static_cast<uint32_t>(__popc(whole));
-        const uint32_t fold = (MULTI && a.sorted != 1) ? 3u : 2u;
+        const uint32_t fold4 = MULTI ? (a.sorted != 1 ? 12u : 8u) : 6u;   // f in quarters
         const uint32_t nspec =
             (ntl <= kSpecSteps && nw >= 2u)
-                ? static_cast<uint32_t>((static_cast<u64>(fold) * k * kBlockElems + L - 1u) / L)
+                ? static_cast<uint32_t>((static_cast<u64>(fold4) * k * kBlockElems + 4ull * L - 1u) /
+                                        (4ull * L))
                 : k;
         const bool spec = nspec < k;
         const uint32_t need2 =
@@ -1645,7 +1648,7 @@ __global__ __launch_bounds__(kernel_threads(CLS, BF16 ? 1 : 0, MULTI), kWavesPer
           if (ring >= k) {
             t0 = t2;   // k of the row's elements at or above it: valid
             tloc = t2;
-          } else if (spec && 2ull * ring * nb >= 3ull * k * nw) {
+          } else if (spec && 16ull * ring * nb >= 3ull * (fold4 < 8u ? fold4 : 8u) * k * nw) {
             tloc = t2;   // an estimate, checked by the merge
           }
         }

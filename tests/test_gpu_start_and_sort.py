@@ -6,8 +6,8 @@ like the next two make the count reject it (the row then starts from the
 first block's own bound), on one workgroup per row and on shared rows.
 
 A workgroup with a short share of a row may instead start from an estimate
-of the row's 2k-th largest value, read from its first block and accepted
-when the ring's count agrees.  On a shared row the merge then checks that at
+of the row's fk-th largest value (f = 1.5, 2 or 3 by shape), read from its
+first block and accepted when the ring's count agrees.  On a shared row the merge then checks that at
 least k merged candidates lie above the row's largest estimate; on a row
 with one workgroup the stream must end with at least k candidates.  Either
 way the row is read again when the check fails.  Rows whose (first)
