@@ -16,11 +16,12 @@
 //    loads of the next 3 blocks are always in flight (a register ring whose
 //    loads are issued unconditionally, so the compiler waits for exactly the
 //    block being filtered);
-//  * the first whole block sets T from an 11-bit histogram of its values held
-//    in registers, so the buffer never has to hold a block admitted at -inf;
-//    a workgroup with a short share of a shared row starts from an estimate
-//    of the row's 2k-th value instead, which the merge checks (and, should
-//    it fail, the merger reads the row again from a valid bound);
+//  * the first whole block sets T from histograms of its values held in
+//    registers (one per wave), so the buffer never has to hold a block
+//    admitted at -inf; a workgroup with a short share of a row starts from
+//    an estimate of the row's 1.5k-th to 3k-th value instead, checked by the
+//    merge or by the final count (should it fail, the row is read again from
+//    a valid bound);
 //  * the filter compares raw fp32 values (bf16 widened by a shift) with a
 //    wave-wide early-out on each lane's running maximum; survivors are
 //    compacted into LDS with ballot / mbcnt and one LDS atomic per wave;
@@ -1810,7 +1811,7 @@ __global__ __launch_bounds__(kernel_threads(CLS, BF16 ? 1 : 0, MULTI), kWavesPer
   }
   uint32_t mine = 0;   // shared rows: candidates above the threshold
   u64 x_w = 0;         // and the bound they vouch for
-  u64 t_keep = 0;      // x_only: the threshold the hand-over filters by
+  u64 t_keep = 0;      // small buffer: the threshold the hand-over filters by
   bool cut = !x_only && (MULTI || a.sorted != 1 || uniform(sm.cnt[cur]) > static_cast<uint32_t>(SORT_CAP));
   if (x_only) {
     const uint32_t need_w = (k + static_cast<uint32_t>(S) - 1u) / static_cast<uint32_t>(S);
