@@ -1621,7 +1621,11 @@ __global__ __launch_bounds__(kernel_threads(CLS, BF16 ? 1 : 0, MULTI), kWavesPer
         const u64 t2 = uniform64(tp.t2);
         u64 tloc = t0;               // this workgroup's start
         if (need2 != 0u && t0 != kThrInit && t2 > t0) {
+          // Elements with key >= tk2 are the values >= the value of key tk2
+          // (keys order like the values, both zeros share one key, and a NaN
+          // compares false): one float compare per element.
           const uint32_t tk2 = static_cast<uint32_t>(t2 >> 32) + 1u;
+          const float tf = __uint_as_float(uniform(bits_of_key(tk2)));
           uint32_t n = 0;
           auto count_in = [&](const u32x4 (&rr)[V]) {
 #pragma unroll
@@ -1632,8 +1636,7 @@ __global__ __launch_bounds__(kernel_threads(CLS, BF16 ? 1 : 0, MULTI), kWavesPer
 #pragma unroll
                 for (int h = 0; h < (BF16 ? 2 : 1); ++h) {
                   const uint32_t bits = BF16 ? (h ? (w[q] & 0xFFFF0000u) : (w[q] << 16)) : w[q];
-                  const bool ok = ((bits & 0x7FFFFFFFu) <= 0x7F800000u) & (key_of_bits(bits) >= tk2);
-                  n += ok ? 1u : 0u;
+                  n += __uint_as_float(bits) >= tf ? 1u : 0u;
                 }
               }
             }
