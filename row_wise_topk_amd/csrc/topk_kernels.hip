@@ -1050,24 +1050,19 @@ __device__ __forceinline__ ThrPair block_threshold_body(const BlockRegs<V>& r, u
   const uint32_t b = uniform(sm.res[0]);
   const uint32_t b2 = need2 ? uniform(sm.res[4]) : static_cast<uint32_t>(kBins);
   if (b >= static_cast<uint32_t>(kBins)) return {kThrInit, kThrInit};   // fewer than k non-NaN values
-  uint32_t tk = 0xFFFFFFFFu, tk2 = 0xFFFFFFFFu;
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    const uint32_t key = key_of_bits(__float_as_uint(f[s]));
-    const uint32_t bn = bin_of(f[s]);
-    tk = ((f[s] == f[s]) & (bn >= b) & (key < tk)) ? key : tk;
-    tk2 = ((f[s] == f[s]) & (bn >= b2) & (key < tk2)) ? key : tk2;
-  }
-  tk = wave_min(tk);
-  tk2 = wave_min(tk2);
-  if (lane == 0) {
-    atomicMin(&sm.bt[2], tk);
-    atomicMin(&sm.bt[3], tk2);
-  }
-  __syncthreads();
-  const u64 t0 = (static_cast<u64>(uniform(sm.bt[2])) << 32) - 1u;
-  const uint32_t k2 = uniform(sm.bt[3]);
-  return {t0, k2 == 0xFFFFFFFFu ? kThrInit : (static_cast<u64>(k2) << 32) - 1u};
+  // A key at or below every member of bins >= bb: the middle of bin bb - 1,
+  // confirmed by binning it (bin_of never decreases as x grows, so every
+  // value binned at bb or above is strictly greater).  Bin 0 holds every
+  // non-NaN value (and -inf), as does a middle that does not bin below bb:
+  // the lowest key.
+  auto below_bin = [&](uint32_t bb) -> uint32_t {
+    if (bb == 0u) return kNegInfKey;
+    const float mid = lo + (static_cast<float>(bb) - 0.5f) * (span / static_cast<float>(kBins - 1));
+    return bin_of(mid) < bb ? key_of_bits(__float_as_uint(mid)) : kNegInfKey;
+  };
+  const u64 t0 = (static_cast<u64>(below_bin(b)) << 32) - 1u;
+  const u64 t2 = b2 < static_cast<uint32_t>(kBins) ? (static_cast<u64>(below_bin(b2)) << 32) - 1u : kThrInit;
+  return {t0, t2};
 }
 // The same starting thresholds with one barrier, for one block: each of the
 // NW waves bins
