@@ -721,8 +721,8 @@ __device__ __noinline__ int cut_buffer(Smem<CAP, NT>& sm, int cur, uint32_t k,
 // ones.  A larger boundary bin, or no more than k candidates above sm.thr,
 // falls back to cut_buffer.  sm.hikey must bound every candidate's key.
 template <int G, int NT, int CAP>
-__device__ __noinline__ int small_cut(Smem<CAP, NT>& sm, int cur, uint32_t k, uint32_t n_cols,
-                                      uint32_t hi_key) {
+__device__ __forceinline__ int small_cut(Smem<CAP, NT>& sm, int cur, uint32_t k, uint32_t n_cols,
+                                         uint32_t hi_key) {
   static_assert(G * NT + static_cast<int>(kSmallBin) <= CAP, "small cut room");
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int nxt = cur ^ 1;
@@ -853,6 +853,14 @@ __device__ __noinline__ int small_cut(Smem<CAP, NT>& sm, int cur, uint32_t k, ui
   }
   __syncthreads();
   return nxt;
+}
+// The same out of line.  The merge inlines the cut for k <= 1024, where
+// nearly every shared row's buffer fits it; for larger k the inlined body
+// would only add code to the kernel around a cut that rarely applies.
+template <int G, int NT, int CAP>
+__device__ __noinline__ int small_cut_call(Smem<CAP, NT>& sm, int cur, uint32_t k, uint32_t n_cols,
+                                           uint32_t hi_key) {
+  return small_cut<G, NT, CAP>(sm, cur, k, n_cols, hi_key);
 }
 
 // ---------------------------------------------------------------- the filter
@@ -2125,10 +2133,14 @@ __global__ __launch_bounds__(kernel_threads(CLS, BF16 ? 1 : 0, MULTI), kWavesPer
       if (uniform(above) < k && uniform(sm.flags) == 0u) reread_row();
     }
     if (a.sorted != 1 || uniform(sm.cnt[cur]) > static_cast<uint32_t>(SORT_CAP)) {
-      if (uniform(sm.cnt[cur]) <= static_cast<uint32_t>(small_cut_g(CAP, NT) * NT))
-        cur = small_cut<small_cut_g(CAP, NT), NT, CAP>(sm, cur, k, L, hi_key());
-      else
+      if (uniform(sm.cnt[cur]) <= static_cast<uint32_t>(small_cut_g(CAP, NT) * NT)) {
+        if constexpr (CLS <= 1)
+          cur = small_cut<small_cut_g(CAP, NT), NT, CAP>(sm, cur, k, L, hi_key());
+        else
+          cur = small_cut_call<small_cut_g(CAP, NT), NT, CAP>(sm, cur, k, L, hi_key());
+      } else {
         cur = cut_buffer<NT, CAP>(sm, cur, k, k, L, hi_key());
+      }
     }
     if (t == 0) {
       st_agent(spec_g, 0ull);
