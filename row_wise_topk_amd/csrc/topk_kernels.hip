@@ -1018,17 +1018,17 @@ __device__ __forceinline__ ThrPair block_threshold_body(const BlockRegs<V>& r, u
       }
     }
   }
-  // finite range, through the order-preserving keys
-  uint32_t klo = 0xFFFFFFFFu, khi = 0u;
+  // finite range in floats, turned into the order-preserving keys once per
+  // lane (a lane with no finite value gives +inf / -inf, which lose)
+  float flo = __uint_as_float(0x7F800000u), fhi = __uint_as_float(kNegInf32);
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    const uint32_t key = key_of_bits(__float_as_uint(f[s]));
     const bool fin = __builtin_fabsf(f[s]) <= 3.402823466e38f;
-    klo = (fin & (key < klo)) ? key : klo;
-    khi = (fin & (key > khi)) ? key : khi;
+    flo = fin ? __builtin_fminf(flo, f[s]) : flo;
+    fhi = fin ? __builtin_fmaxf(fhi, f[s]) : fhi;
   }
-  klo = wave_min(klo);
-  khi = wave_max(khi);
+  uint32_t klo = wave_min(key_of_bits(__float_as_uint(flo)));
+  uint32_t khi = wave_max(key_of_bits(__float_as_uint(fhi)));
   if (lane == 0) {   // bt[] was set at the kernel's start
     atomicMin(&sm.bt[0], klo);
     atomicMax(&sm.bt[1], khi);
@@ -1112,18 +1112,20 @@ __device__ __forceinline__ ThrPair wave_threshold(const BlockRegs<V>& r, uint32_
       }
     }
   }
-  uint32_t klo = 0xFFFFFFFFu, khi = 0u;
+  // The finite range in floats, turned into keys once per lane (keys order
+  // like the values; both zeros share one key).
+  float flo = __uint_as_float(0x7F800000u), fhi = __uint_as_float(kNegInf32);
   bool ninf = false;   // a -inf, which bin 0 holds below klo
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    const uint32_t key = key_of_bits(__float_as_uint(f[s]));
     const bool fin = __builtin_fabsf(f[s]) <= 3.402823466e38f;
-    klo = (fin & (key < klo)) ? key : klo;
-    khi = (fin & (key > khi)) ? key : khi;
-    ninf |= key == kNegInfKey;
+    flo = fin ? __builtin_fminf(flo, f[s]) : flo;
+    fhi = fin ? __builtin_fmaxf(fhi, f[s]) : fhi;
+    ninf |= f[s] == __uint_as_float(kNegInf32);
   }
-  klo = wave_min(klo);
-  khi = wave_max(khi);
+  // No finite value in a lane: its +inf / -inf keys lose every min / max.
+  uint32_t klo = wave_min(key_of_bits(__float_as_uint(flo)));
+  uint32_t khi = wave_max(key_of_bits(__float_as_uint(fhi)));
   const bool any_ninf = ballot(ninf) != 0ull;
   uint32_t e0 = 0, e2 = 0xFFFFFFFFu;   // this wave's edges (keys); 0: vouches for nothing
   uint32_t* hw = sm.hist + w * kWaveBins;
