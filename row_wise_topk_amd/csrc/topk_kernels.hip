@@ -981,19 +981,20 @@ __device__ __noinline__ RaggedResult filter_ragged(BlockRegs<V> r, uint32_t blk,
 }
 
 // Starting thresholds from whole blocks held in registers, before any of
-// them is appended (used for the three-block start of k above half a block;
-// one block uses the per-wave version below).  The values are binned linearly between their
-// finite minimum and maximum (2048 bins; -inf and +inf clamp to the end
-// bins, NaN is left out).  Linear bins spread the usual bell-shaped scores
-// over many bins, so the LDS atomics rarely collide, where bins on the key
-// bits would pile most of a binade into a few.  The suffix search finds the
-// bin b* with at least k elements in bins >= b*; since the binning is
-// monotone, the smallest key among those elements is a threshold with at
-// least k of the block's elements at or above it -- a valid (monotone)
-// starting point for the row (t0).  With need2 > 0 the same search for
-// need2 gives t2, with at least need2 of the block's elements at or above it:
+// them is appended (used for the three-block start of k above half a
+// block; one block uses the per-wave version below).  The values are binned
+// linearly between their finite minimum and maximum (2048 bins; -inf and
+// +inf clamp to the end bins, NaN is left out).  Linear bins spread the
+// usual bell-shaped scores over many bins, so the LDS atomics rarely
+// collide, where bins on the key bits would pile most of a binade into a
+// few.  The suffix search finds the bin b* with at least k elements in bins
+// >= b*; since the binning never decreases with the value, a value that
+// bins below b* lies below all of those elements, and its key is a
+// threshold with at least k of the blocks' elements above it -- a valid
+// (monotone) starting point for the row (t0).  With need2 > 0 the same
+// search for need2 gives t2, with at least need2 of the elements above it:
 // only an estimate for the row, which the caller must verify.  Leaves hist
-// zeroed.  Its reductions use bt[0..3], set at the kernel's start (it runs
+// zeroed.  Its reductions use bt[0..1], set at the kernel's start (it runs
 // at most once per workgroup).
 struct ThrPair {
   u64 t0, t2;
