@@ -248,3 +248,23 @@ def test_local_bin_edge_threshold(sorted_mode, dtype):
     levels = _levels_bf16(4, 16 * B, 256, seed=7 + sorted_mode)
     check_case(levels, BF16, 16 * B, 512, sorted_mode, False, "int32", plan=plan,
                name=f"local bin edge ties sorted={sorted_mode}")
+
+
+# Rows that are mostly zeros of both signs (and a few -inf), so the start's
+# edges and the ring's count land on zero: the count compares values
+# against the value of the edge's key, and both zeros share one key, so
+# -0.0 and +0.0 must count alike; -inf must never count above a finite edge.
+@pytest.mark.parametrize("segments", [1, 2])
+@pytest.mark.parametrize("sorted_mode", [0, 1])
+@pytest.mark.parametrize("dtype", [FP32, BF16])
+def test_start_on_signed_zeros(segments, sorted_mode, dtype):
+    rng = np.random.Generator(np.random.PCG64(307 + 2 * segments + sorted_mode))
+    n = 8 * B
+    f = np.where(rng.random((3, n)) < 0.5, np.float32(0.0), np.float32(-0.0)).astype(np.float32)
+    pos = rng.random((3, n)) < 0.03
+    f[pos] = np.abs(rng.standard_normal(int(pos.sum()))).astype(np.float32) + np.float32(0.5)
+    f[rng.random((3, n)) < 0.01] = -np.inf
+    x = workloads.to_bf16_bits(f) if dtype == BF16 else f
+    for k in (256, 1024, 2048):
+        check_case(x, dtype, n, k, sorted_mode, True, "int32", plan={"segments": segments},
+                   name=f"signed zeros k={k} S={segments} sorted={sorted_mode}")
