@@ -14,7 +14,10 @@ paragraph) and the Lightning Indexer path (bf16 scores, k tuned for 512, per-row
 ``end`` for variable-length rows -- aifluxnews.com, section
 "PyTorch 接口与 CUDA 环境要求"), plus a small fp32 case and an adversarial
 ascending-by-index case for the randomised block order (narracomm.com, method
-paragraph).
+paragraph).  A sixth is the pages' torch.topk pathology case: the top 1000 of
+a billion floats in one row (xhh.club, "DeepSeek开源DeepSelect", section
+"torch.topk 的性能痛点与版本波动"); its values are i.i.d. N(0, 1), the
+plainest reading of an unstated distribution.
 """
 from __future__ import annotations
 
@@ -28,7 +31,7 @@ FP32, BF16 = 0, 1
 
 @dataclass(frozen=True)
 class Workload:
-    num: int              # 1..5
+    num: int              # 1..6
     name: str
     dtype: int            # FP32 / BF16
     batch: int
@@ -55,6 +58,8 @@ WORKLOADS = {
                 2048, 1, True, "int32", True),
     5: Workload(5, "ascending fp32 8x16777216 k=4096", FP32, 8, 16777216, 16777216, 4096, 1,
                 True, "int32", False),
+    6: Workload(6, "huge row fp32 1x1000000000 k=1000", FP32, 1, 1_000_000_000, 1_000_000_000,
+                1000, 1, True, "int64", False),
 }
 
 
@@ -109,6 +114,8 @@ def make_input(w: Workload, seed: int | None = None, poison_tail: bool = False):
         noise = np.float32(1e-3) * rng.random((b, n), dtype=np.float32)
         v = ramp[None, :] + noise
         del noise
+    elif w.num == 6:
+        v = rng.standard_normal((b, n), dtype=np.float32)
     else:
         raise ValueError(w.num)
 
@@ -117,6 +124,8 @@ def make_input(w: Workload, seed: int | None = None, poison_tail: bool = False):
         nan_bits = np.uint16(0x7FC0)
         out = np.full((b, w.row_stride), nan_bits, dtype=np.uint16)
         out[:, :n] = bits
+    elif w.row_stride == n:   # no padding: the rows as drawn (a 4 GB row is not copied)
+        out = v
     else:
         out = np.full((b, w.row_stride), np.float32(np.nan), dtype=np.float32)
         out[:, :n] = v
