@@ -1550,14 +1550,17 @@ __global__ __launch_bounds__(kernel_threads(CLS, BF16 ? 1 : 0, MULTI), kWavesPer
   };
 
   // The ring: block j goes to r[j % 4], and the shared threshold is read into
-  // g[j % 4] just before block j's loads are issued, so waiting for a block
-  // never waits for a later load.  Steps past the workgroup's last block
+  // g0 just before the loads of every fourth block are issued, so waiting
+  // for a block never waits for a later load.  Steps past the workgroup's last block
   // still issue loads (the compiler then counts outstanding loads exactly),
   // but every lane reads the row's first vector, one cache line per wave.
   u32x4 r0[V], r1[V], r2[V], r3[V];
   u64 g0 = 0, g1 = 0, g2 = 0, g3 = 0;
+  // The shared threshold is read once per turn of the ring (with the blocks
+  // that go to r0): every workgroup of a shared row reads the same word, up
+  // to 256 of them on one row, and a bound read late only admits more.
   auto issue = [&](u32x4 (&r)[V], u64& g, uint32_t j) {
-    if (MULTI) g = load_thr(thr_g);
+    if (MULTI && (j & 3u) == 0u) g = load_thr(thr_g);
     load_block<BF16, V, NT>(r, xrow, blk_at(j), j < ntl ? L : 0u);
   };
 
