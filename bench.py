@@ -283,9 +283,9 @@ def main():
         cores = len(os.sched_getaffinity(0))
         used = min(cores, w.batch)
         idx_np = np.int64 if w.index_dtype == "int64" else np.int32
-        # The oracle sorts every row whole: a row of more than 2^26 elements is
+        # The oracle sorts every row whole: a row longer than 2^24 elements is
         # timed on its first 2^24 columns instead (a bounded sample).
-        cols = w.n_cols if w.batch * w.n_cols <= (1 << 26) else (1 << 24)
+        cols = min(w.n_cols, 1 << 24)
         s_bytes = alg_bytes if cols == w.n_cols else w.batch * cols * w.elem_bytes
         reps, t0 = 0, time.perf_counter()
         while True:
