@@ -76,6 +76,9 @@ typedef enum {
 #define DS_TOPK_MAX_K 4096            /* [NC coverage]: topk must be 4096 or less   */
 #define DS_ROW_NAN 1                  /* row_status bit: a NaN in x[i, 0:L)          */
 #define DS_ROW_BAD_END 2              /* row_status bit: end[i] < 0 or end[i] > n_cols */
+#define DS_ROW_INTERNAL 4             /* row_status bit: a consistency check inside the
+                                         kernel failed (never expected); the row is
+                                         written as -1 / qNaN instead of looping on */
 
 /*
  * ds_topk -- top-k of every row of a 2-D array [IT "DeepSelect" section; NC
@@ -125,17 +128,30 @@ ds_status_t ds_topk(const void* x, ds_dtype_t dtype, int64_t batch, int64_t n_co
  * automatic plan.  [NC method]: blocks are visited in a random order and B,
  * B2 are tuning parameters.
  *   segments     workgroups that share one row (0 = automatic, else 1..256).
+ *                With the chunk kernels any value above 1 means one
+ *                workgroup per chunk of the row (at most 256 chunks).
  *   perm_seed    seed of the per-row block permutation (any value).
  *   in_order     1 = visit blocks in address order instead.
  *   flush_at     candidate count that triggers a cut back to k (0 = automatic;
- *                else k+1 .. the buffer's fixed trigger for this k class).
+ *                else k+1 .. the buffer's fixed trigger for this k class; the
+ *                chunk kernels raise it to at least k + 2048).
+ *   kernel       DS_KERNEL_AUTO (0), DS_KERNEL_STREAM (1): one or more
+ *                workgroups stream a row block by block (long rows), or
+ *                DS_KERNEL_CHUNK (2): a workgroup holds 32 KiB of a row in
+ *                registers at a time (rows of up to 64 chunks: 524,288 fp32 or
+ *                1,048,576 bf16 values).
  */
 typedef struct {
   int32_t segments;
   uint32_t perm_seed;
   int32_t in_order;
   int32_t flush_at;
+  int32_t kernel;
 } ds_topk_plan_t;
+
+#define DS_KERNEL_AUTO 0
+#define DS_KERNEL_STREAM 1
+#define DS_KERNEL_CHUNK 2
 
 /* ds_topk with an explicit plan (plan may be NULL = automatic).  Same
  * arguments, ownership and errors as ds_topk, plus DS_ERR_PLAN. */

@@ -35,7 +35,8 @@ DS_FP32, DS_BF16 = 0, 1
 DS_INT32, DS_INT64 = 0, 1
 DS_UNSORTED, DS_SORTED_VALUE, DS_SORTED_INDEX = 0, 1, 2
 DS_OK = 0
-DS_ROW_NAN, DS_ROW_BAD_END = 1, 2
+DS_ROW_NAN, DS_ROW_BAD_END, DS_ROW_INTERNAL = 1, 2, 4
+DS_KERNEL_AUTO, DS_KERNEL_STREAM, DS_KERNEL_CHUNK = 0, 1, 2
 DS_TOPK_MAX_K = 4096
 STATUS_NAMES = ["DS_OK", "DS_ERR_NULL", "DS_ERR_DTYPE", "DS_ERR_INDEX_DTYPE", "DS_ERR_K_RANGE",
                 "DS_ERR_SHAPE", "DS_ERR_ALIGN", "DS_ERR_SORTED_MODE", "DS_ERR_WORKSPACE",
@@ -43,9 +44,10 @@ STATUS_NAMES = ["DS_OK", "DS_ERR_NULL", "DS_ERR_DTYPE", "DS_ERR_INDEX_DTYPE", "D
 
 
 class Plan(ctypes.Structure):
-    """ds_topk_plan_t: segments, perm_seed, in_order, flush_at (0 = automatic)."""
+    """ds_topk_plan_t: segments, perm_seed, in_order, flush_at, kernel (0 = automatic)."""
     _fields_ = [("segments", ctypes.c_int32), ("perm_seed", ctypes.c_uint32),
-                ("in_order", ctypes.c_int32), ("flush_at", ctypes.c_int32)]
+                ("in_order", ctypes.c_int32), ("flush_at", ctypes.c_int32),
+                ("kernel", ctypes.c_int32)]
 
 
 if not os.path.exists(LIB_PATH):
@@ -87,7 +89,8 @@ def _plan_ptr(plan):
     if isinstance(plan, Plan):
         return ctypes.pointer(plan)
     p = Plan(int(plan.get("segments", 0)), int(plan.get("perm_seed", 0x5EED)) & 0xFFFFFFFF,
-             int(plan.get("in_order", 0)), int(plan.get("flush_at", 0)))
+             int(plan.get("in_order", 0)), int(plan.get("flush_at", 0)),
+             int(plan.get("kernel", 0)))
     return ctypes.pointer(p)
 
 

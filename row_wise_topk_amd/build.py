@@ -28,13 +28,16 @@ def build(verbose: bool = False, extra: list[str] | None = None) -> str:
     bdir = os.path.join(PKG, "_build")
     os.makedirs(bdir, exist_ok=True)
     k_obj = os.path.join(bdir, "topk_kernels.o")
+    c_obj = os.path.join(bdir, "chunk_kernels.o")
     a_obj = os.path.join(bdir, "topk_api.o")
     _run([HIPCC, *COMMON, *DEVICE, *extra, "-c", os.path.join(CSRC, "topk_kernels.hip"),
           "-o", k_obj], verbose)
+    _run([HIPCC, *COMMON, *DEVICE, *extra, "-c", os.path.join(CSRC, "chunk_kernels.hip"),
+          "-o", c_obj], verbose)
     _run([HIPCC, *COMMON, *DEVICE, *extra, "-x", "hip", "-c", os.path.join(CSRC, "topk_api.cpp"),
           "-o", a_obj], verbose)
     tmp = LIB + ".tmp"
-    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", k_obj, a_obj, "-o", tmp], verbose)
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", k_obj, c_obj, a_obj, "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 

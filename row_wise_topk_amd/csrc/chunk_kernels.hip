@@ -1,0 +1,1210 @@
+// Row-wise TopK for MI355X (gfx950, wave64): the chunk kernels.
+//
+// Method (narracomm.com, "DeepSeek releases DeepSelect, a TopK kernel for
+// sparse attention and sampling", method paragraph): a threshold T that never
+// falls, the row read once in contiguous blocks, the values that pass T
+// appended to a candidate buffer, and a radix select that cuts the buffer back
+// to k and raises T when it fills.  These kernels serve rows of up to a few
+// hundred thousand elements (the sampler and Lightning Indexer shapes), where
+// the cost is not the stream but the serial chain of a workgroup's steps; they
+// are laid out to keep that chain short on CDNA4:
+//
+//  * a chunk is 8 16-byte loads per lane of a 256-lane workgroup (8192 fp32 or
+//    16384 bf16 values, 32 KiB), all issued at once and held in registers; a
+//    workgroup takes either one chunk of a row (a row split into one
+//    workgroup per chunk, when the batch alone cannot fill the chip) or a
+//    whole row, chunk by chunk with the next chunk's loads in flight;
+//  * the first chunk sets T before anything is appended.  A workgroup that
+//    holds a whole row sets the row's exact start (at least min(k, L) of its
+//    values pass); otherwise T is an estimate, at least m values of the chunk
+//    pass it, with m the chunk's expected share of the top k plus a margin of
+//    six standard deviations.  An estimate is checked once the row is
+//    complete: if fewer than min(k, L) candidates passed, the row is read
+//    again from a valid bound;
+//  * T comes from a 256-bin histogram anchored at the chunk's largest value,
+//    one bin per bf16 value (1/128 octave for fp32), over either every value
+//    in the window or, when m is small, only each lane's largest value (at
+//    least m values lie at or above the m-th largest lane maximum);
+//  * a chunk is filtered in two passes over the registers: a count (so that
+//    every wave knows where its candidates go) and a write, where a slot no
+//    lane of the wave keeps costs one compare;
+//  * a candidate is the 64-bit composite (key(v) << 32) | ~column, so one
+//    unsigned compare orders candidates exactly as the output (larger value
+//    first, then lower column: xhh.club, "DeepSeek开源DeepSelect：比torch.topk快二十倍！",
+//    Q&A on stable results).  key() maps fp32 sign-magnitude onto offset
+//    binary, so -0.0 and +0.0 share a key; a zero's sign is read back from the
+//    input when it is written out.  A threshold is a composite too: a
+//    candidate passes iff its composite is >= T;
+//  * the cut is an MSD radix select over the composites' live range (11-bit
+//    LDS histograms, at most six levels), which ranks a boundary bin of at
+//    most 64 members directly; it keeps exactly the requested count;
+//  * a split row hands its candidates over through the workspace, with the
+//    chunk's threshold, and the last workgroup of the row to arrive (a
+//    release / acquire pair on the row's arrival counter) merges them;
+//  * the output is ordered by a bitonic sort in registers (cross-lane steps
+//    by ds_bpermute, cross-wave steps through LDS).
+//
+// NaN (narracomm.com, NaN paragraph): always checked over [0, end); a NaN sets
+// a status bit for the row instead of trapping.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ds_topk.h"
+#include "topk_internal.h"
+
+namespace dstk {
+namespace {
+
+typedef unsigned long long u64;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int NT = kChunkThreads;   // 256 lanes, 4 waves
+constexpr int NW = NT / 64;
+constexpr int V = kChunkLoads;      // 16-byte loads per lane per chunk
+constexpr uint32_t kBias = 0x80000000u;
+constexpr uint32_t kNegInfKey = 0x00800000u;   // key of -inf, the lowest non-NaN key
+constexpr uint32_t kQNaN32 = 0x7FC00000u;
+constexpr uint32_t kNegInf32 = 0xFF800000u;
+constexpr int kWinBins = 256;                  // the start histogram: one bin per lane
+constexpr int kCutBits = 11;
+constexpr int kCutBins = 1 << kCutBits;        // the cut's histogram
+constexpr int kCutBPT = kCutBins / NT;         // bins per lane
+constexpr uint32_t kRankMax = 64;              // boundary bins ranked directly
+constexpr uint32_t kNone = 0xFFFFFFFFu;
+constexpr u64 kTAll = static_cast<u64>(kNegInfKey) << 32;   // every non-NaN value passes
+
+static_assert(kWinBins == NT, "one start bin per lane");
+static_assert(kCutBins % NT == 0, "cut bins per lane");
+
+// ---------------------------------------------------------------- keys
+__device__ __forceinline__ uint32_t key_of_bits(uint32_t b) {
+  const uint32_t mag = b & 0x7FFFFFFFu;
+  return (b & 0x80000000u) ? kBias - mag : kBias + mag;
+}
+// Inverse for keys of non-NaN values; the key of both zeros gives +0.0.
+__device__ __forceinline__ uint32_t bits_of_key(uint32_t key) {
+  return key >= kBias ? key - kBias : ((kBias - key) | 0x80000000u);
+}
+__device__ __forceinline__ u64 comp_of(uint32_t key, uint32_t col) {
+  return (static_cast<u64>(key) << 32) | static_cast<uint32_t>(~col);
+}
+__device__ __forceinline__ uint32_t key_of(u64 c) { return static_cast<uint32_t>(c >> 32); }
+__device__ __forceinline__ uint32_t col_of(u64 c) { return ~static_cast<uint32_t>(c); }
+
+// "composite >= T" as float compares on the value:  x > f, or x == f and
+// column <= cmax.  For T = (K << 32) | ~C this is key > K or (key == K and
+// column <= C); keys order like values and both zeros share a key, so the
+// float compares agree with the key compares for every non-NaN x, and a NaN
+// passes nothing.
+struct Pass {
+  float f;
+  uint32_t cmax;
+};
+__device__ __forceinline__ Pass pass_of(u64 T) {
+  return {__uint_as_float(bits_of_key(key_of(T))), ~static_cast<uint32_t>(T)};
+}
+
+// ---------------------------------------------------------------- wave helpers
+__device__ __forceinline__ uint32_t uniform(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(v)));
+}
+__device__ __forceinline__ u64 uniform64(u64 v) {
+  return (static_cast<u64>(uniform(static_cast<uint32_t>(v >> 32))) << 32) |
+         uniform(static_cast<uint32_t>(v));
+}
+__device__ __forceinline__ u64 ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
+__device__ __forceinline__ uint32_t mbcnt64(u64 m) {
+  return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
+}
+__device__ __forceinline__ uint32_t lane_id() { return threadIdx.x & 63u; }
+
+template <int CTRL, int ROW_MASK, uint32_t IDENT>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+      static_cast<int>(IDENT), static_cast<int>(v), CTRL, ROW_MASK, 0xF, false));
+}
+// Inclusive scans over the 64 lanes (all lanes active): row_shr 1/2/4/8 in
+// each 16-lane row, then row_bcast 15 and 31 across rows.
+__device__ __forceinline__ uint32_t wave_incl_sum(uint32_t x) {
+  x += dpp<0x111, 0xF, 0u>(x);
+  x += dpp<0x112, 0xF, 0u>(x);
+  x += dpp<0x114, 0xF, 0u>(x);
+  x += dpp<0x118, 0xF, 0u>(x);
+  x += dpp<0x142, 0xA, 0u>(x);
+  x += dpp<0x143, 0xC, 0u>(x);
+  return x;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  x = max(x, dpp<0x111, 0xF, 0u>(x));
+  x = max(x, dpp<0x112, 0xF, 0u>(x));
+  x = max(x, dpp<0x114, 0xF, 0u>(x));
+  x = max(x, dpp<0x118, 0xF, 0u>(x));
+  x = max(x, dpp<0x142, 0xA, 0u>(x));
+  x = max(x, dpp<0x143, 0xC, 0u>(x));
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(x), 63));
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
+  x = min(x, dpp<0x111, 0xF, 0xFFFFFFFFu>(x));
+  x = min(x, dpp<0x112, 0xF, 0xFFFFFFFFu>(x));
+  x = min(x, dpp<0x114, 0xF, 0xFFFFFFFFu>(x));
+  x = min(x, dpp<0x118, 0xF, 0xFFFFFFFFu>(x));
+  x = min(x, dpp<0x142, 0xA, 0xFFFFFFFFu>(x));
+  x = min(x, dpp<0x143, 0xC, 0xFFFFFFFFu>(x));
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(x), 63));
+}
+__device__ __forceinline__ uint32_t bit_length64(u64 v) { return v ? 64u - __clzll(v) : 0u; }
+
+// Value of lane (lane ^ X), 64 bits, through the LDS crossbar.
+template <int X>
+__device__ __forceinline__ u64 xor_lane64(u64 v) {
+  const int addr = static_cast<int>((lane_id() ^ X) << 2);
+  const uint32_t lo = static_cast<uint32_t>(
+      __builtin_amdgcn_ds_bpermute(addr, static_cast<int>(static_cast<uint32_t>(v))));
+  const uint32_t hi = static_cast<uint32_t>(
+      __builtin_amdgcn_ds_bpermute(addr, static_cast<int>(static_cast<uint32_t>(v >> 32))));
+  return (static_cast<u64>(hi) << 32) | lo;
+}
+
+// Relaxed agent-scope accesses to the workspace: coherent across the XCDs'
+// L2 caches; the ordering comes from the release / acquire on the row's
+// arrival counter.
+template <typename W>
+__device__ __forceinline__ void st_agent(W* p, W v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename W>
+__device__ __forceinline__ W ld_agent(const W* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------- LDS
+template <int CAP>
+struct Smem {
+  u64 buf[CAP];                       // candidate composites (also the sort's exchange area)
+  alignas(16) uint32_t hist[kCutBins];  // zero whenever not in use
+  u64 side[kRankMax];                 // members of a small boundary bin
+  uint32_t wtot[2][NW];               // per-wave counts, alternating by use
+  uint32_t wmax[NW];
+  uint32_t wscan[2][NW];
+  u64 wred[NW];
+  u64 wred2[NW];
+  uint32_t res[4];
+  uint32_t side_n;
+  uint32_t err;
+  uint32_t is_last;
+  u64 res64;
+};
+
+// ---------------------------------------------------------------- block scans
+// Exclusive prefix over the lanes of the workgroup and the total.  `par`
+// alternates between consecutive calls so that a fast wave never overwrites
+// a total a slow wave has yet to read (a barrier separates any two calls with
+// the same parity).
+template <int CAP>
+__device__ __forceinline__ uint32_t block_excl(Smem<CAP>& sm, uint32_t v, int par,
+                                               uint32_t* total, uint32_t* wave_base = nullptr) {
+  const uint32_t incl = wave_incl_sum(v);
+  const int w = threadIdx.x >> 6;
+  if (lane_id() == 63) sm.wscan[par][w] = incl;
+  __syncthreads();
+  uint32_t before = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    const uint32_t s = sm.wscan[par][i];
+    before += i < w ? s : 0u;
+    tot += s;
+  }
+  *total = tot;
+  if (wave_base) *wave_base = uniform(before);
+  return before + incl - v;
+}
+
+// Bins in rank order (bin 0 ranks first), BPT of them per lane, lane t owning
+// bins [t*BPT, (t+1)*BPT).  Finds the bin b where the running count reaches
+// `need`: sum(bins < b) < need <= sum(bins <= b).  res = {b, sum below b,
+// count of b, total}; b = kNone when the total is below need.
+template <int BPT, int CAP>
+__device__ __forceinline__ void find_rank(Smem<CAP>& sm, const uint32_t (&h)[BPT], uint32_t need,
+                                          int par) {
+  uint32_t s = 0;
+#pragma unroll
+  for (int i = 0; i < BPT; ++i) s += h[i];
+  uint32_t total;
+  const uint32_t before = block_excl(sm, s, par, &total);
+  if (threadIdx.x == 0) {
+    sm.res[0] = kNone;
+    sm.res[3] = total;
+  }
+  __syncthreads();
+  if (before < need && need <= before + s) {
+    uint32_t acc = before;
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) {
+      if (acc < need && need <= acc + h[i]) {
+        sm.res[0] = threadIdx.x * BPT + i;
+        sm.res[1] = acc;
+        sm.res[2] = h[i];
+      }
+      acc += h[i];
+    }
+  }
+  __syncthreads();
+}
+
+
+// ---------------------------------------------------------------- chunks
+template <bool BF16>
+struct Geo {
+  static constexpr int EPV = BF16 ? 8 : 4;      // values per 16-byte vector
+  static constexpr int ESZ = BF16 ? 2 : 4;
+  static constexpr int EPL = V * EPV;           // values per lane per chunk
+  static constexpr uint32_t CE = NT * EPL;      // values per chunk
+};
+
+// Chunk c of a row: lane t's vector i covers columns c*CE + (i*NT + t)*EPV ...
+// A vector that starts at or past L is loaded from column 0 instead (a valid
+// address); its values are replaced before use (sanitize_ragged).
+template <bool BF16>
+__device__ __forceinline__ void load_chunk(u32x4 (&r)[V], const char* xrow, uint32_t c,
+                                           uint32_t L) {
+  using G = Geo<BF16>;
+  const uint32_t e0 = c * G::CE + threadIdx.x * G::EPV;
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    uint32_t e = e0 + static_cast<uint32_t>(i * NT * G::EPV);
+    e = e < L ? e : 0u;
+    r[i] = __builtin_nontemporal_load(
+        reinterpret_cast<const u32x4*>(xrow + static_cast<size_t>(e) * G::ESZ));
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ uint32_t col_at(uint32_t c, int i, int q) {
+  using G = Geo<BF16>;
+  return c * G::CE + (static_cast<uint32_t>(i * NT) + threadIdx.x) * G::EPV + q;
+}
+
+// Apply f(bits as fp32, value index q) to every value of vector r.
+template <bool BF16, typename F>
+__device__ __forceinline__ void for_values(const u32x4& r, F&& f) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t d = r[w];
+    if constexpr (BF16) {
+      f(d << 16, 2 * w);
+      f(d & 0xFFFF0000u, 2 * w + 1);
+    } else {
+      f(d, w);
+    }
+  }
+}
+
+// The chunk that holds column L-1: returns whether a NaN is among the valid
+// values, then replaces every value at or past L by a NaN, which no compare
+// admits, no histogram counts and fmaxf ignores.
+template <bool BF16>
+__device__ __forceinline__ bool sanitize_ragged(u32x4 (&r)[V], uint32_t c, uint32_t L) {
+  bool nan = false;
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t d = r[i][w];
+      if constexpr (BF16) {
+        const bool ok0 = col_at<true>(c, i, 2 * w) < L, ok1 = col_at<true>(c, i, 2 * w + 1) < L;
+        nan |= ok0 & ((d & 0x7FFFu) > 0x7F80u);
+        nan |= ok1 & (((d >> 16) & 0x7FFFu) > 0x7F80u);
+        r[i][w] = (ok0 ? (d & 0xFFFFu) : 0x7FFFu) | (ok1 ? (d & 0xFFFF0000u) : 0x7FFF0000u);
+      } else {
+        const bool ok = col_at<false>(c, i, w) < L;
+        nan |= ok & ((d & 0x7FFFFFFFu) > 0x7F800000u);
+        r[i][w] = ok ? d : 0x7FFFFFFFu;
+      }
+    }
+  }
+  return nan;
+}
+
+// Per lane: the largest key among the non-NaN values (0 if none) and, with
+// CHECK, whether any value is a NaN.
+template <bool BF16, bool CHECK>
+__device__ __forceinline__ void chunk_max_nan(const u32x4 (&r)[V], uint32_t* maxkey, bool* nan) {
+  float mx = __uint_as_float(kQNaN32);   // fmaxf(NaN, x) = x: stays NaN if every value is
+  uint32_t mag = 0;
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t d = r[i][w];
+      if constexpr (BF16) {
+        if (CHECK) {
+          mag = max(mag, d & 0x7FFFu);
+          mag = max(mag, (d >> 16) & 0x7FFFu);
+        }
+        mx = fmaxf(mx, __uint_as_float(d << 16));
+        mx = fmaxf(mx, __uint_as_float(d & 0xFFFF0000u));
+      } else {
+        if (CHECK) mag = max(mag, d & 0x7FFFFFFFu);
+        mx = fmaxf(mx, __uint_as_float(d));
+      }
+    }
+  }
+  *nan = CHECK && mag > (BF16 ? 0x7F80u : 0x7F800000u);
+  *maxkey = mx == mx ? key_of_bits(__float_as_uint(mx)) : 0u;
+}
+
+// Values of the lane >= f (NaN never).
+template <bool BF16>
+__device__ __forceinline__ uint32_t vec_count(const u32x4& r, float f) {
+  uint32_t n = 0;
+  for_values<BF16>(r, [&](uint32_t b, int) { n += __uint_as_float(b) >= f ? 1u : 0u; });
+  return n;
+}
+
+// Write the wave's values of vector i that are >= f to buf[pos ...] in
+// slot-major order; a slot that no lane keeps costs one compare.
+template <bool BF16, int CAP>
+__device__ __forceinline__ uint32_t vec_write(Smem<CAP>& sm, const u32x4& r, int i, uint32_t c,
+                                              float f, uint32_t pos) {
+  for_values<BF16>(r, [&](uint32_t b, int q) {
+    const bool ok = __uint_as_float(b) >= f;
+    const u64 m = ballot(ok);
+    if (m) {
+      if (ok) sm.buf[pos + mbcnt64(m)] = comp_of(key_of_bits(b), col_at<BF16>(c, i, q));
+      pos += static_cast<uint32_t>(__popcll(m));
+    }
+  });
+  return pos;
+}
+
+// ---------------------------------------------------------------- the start
+// The start threshold from a 256-bin histogram over the window of keys just
+// below `maxkey` (the chunk's largest key): bin j holds keys
+// maxkey - (j+1)*2^s < key <= maxkey - j*2^s, s = 16 first (one bin per bf16
+// value, 1/128 octave for fp32), then s = 24 (the window spans every key)
+// when the first window holds fewer than m.  With LANEMAX only each lane's
+// largest value is binned.  Returns T = (edge key << 32): at least m values
+// of the chunk are at or above it.  Leaves the histogram zeroed.
+template <bool BF16, bool LANEMAX, int CAP>
+__device__ __forceinline__ u64 start_threshold(Smem<CAP>& sm, const u32x4 (&r)[V],
+                                               uint32_t maxkey, uint32_t lane_max, uint32_t m) {
+  for (int pass = 0; pass < 2; ++pass) {
+    const uint32_t s = pass == 0 ? 16u : 24u;
+    const u64 span = static_cast<u64>(kWinBins) << s;   // keys the window covers
+    const uint32_t lo_key = static_cast<u64>(maxkey) - kNegInfKey >= span
+                                ? static_cast<uint32_t>(maxkey - span + 1u)
+                                : kNegInfKey;
+    if (LANEMAX) {
+      if (lane_max >= lo_key) atomicAdd(&sm.hist[(maxkey - lane_max) >> s], 1u);
+    } else {
+      const float flo = __uint_as_float(bits_of_key(lo_key));
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        for_values<BF16>(r[i], [&](uint32_t b, int) {
+          if (__uint_as_float(b) >= flo) atomicAdd(&sm.hist[(maxkey - key_of_bits(b)) >> s], 1u);
+        });
+      }
+    }
+    __syncthreads();
+    uint32_t h[1];
+    h[0] = sm.hist[threadIdx.x];
+    sm.hist[threadIdx.x] = 0u;   // own bin: no other lane touches it until the next barrier
+    find_rank<1>(sm, h, m, pass);
+    const uint32_t b = uniform(sm.res[0]);
+    if (b != kNone) {
+      const int64_t e = static_cast<int64_t>(maxkey) - (static_cast<int64_t>(b + 1) << s) + 1;
+      const uint32_t edge = e > static_cast<int64_t>(lo_key) ? static_cast<uint32_t>(e) : lo_key;
+      return static_cast<u64>(edge) << 32;
+    }
+    if (lo_key == kNegInfKey) return kTAll;
+  }
+  return kTAll;   // not reached: the second window spans every key
+}
+
+// ---------------------------------------------------------------- the cut
+// Keep exactly the `keep` largest of the n composites in buf (keep < n),
+// compacting them to buf[0, keep).  Returns the new threshold, the keep-th
+// largest composite.  An MSD radix select over the live composite range:
+// each level bins the range in 2048 bins (at most six levels for 64 bits),
+// and a boundary bin of at most 64 members is ranked directly.  If a level's
+// counts ever disagree with the previous level's (which a correct buffer
+// cannot produce) it sets sm.err and leaves the buffer as it is.  Enter and
+// leave with the histogram zeroed and after a barrier.
+template <int CAP>
+__device__ __noinline__ u64 cut_exact(Smem<CAP>& sm, uint32_t n, uint32_t keep) {
+  const int t = threadIdx.x;
+  // Live range of the composites.
+  u64 lo = ~0ull, hi = 0;
+  for (uint32_t j = t; j < n; j += NT) {
+    const u64 v = sm.buf[j];
+    lo = v < lo ? v : lo;
+    hi = v > hi ? v : hi;
+  }
+  {
+    const uint32_t a = wave_min_u32(static_cast<uint32_t>(lo >> 32));
+    const uint32_t b = wave_max_u32(static_cast<uint32_t>(hi >> 32));
+    // Exact 64-bit extremes: the low words among the lanes that hold the
+    // extreme high word.
+    const uint32_t al = wave_min_u32(static_cast<uint32_t>(lo >> 32) == a ? static_cast<uint32_t>(lo) : 0xFFFFFFFFu);
+    const uint32_t bl = wave_max_u32(static_cast<uint32_t>(hi >> 32) == b ? static_cast<uint32_t>(hi) : 0u);
+    if (lane_id() == 0) {
+      sm.wred[t >> 6] = (static_cast<u64>(a) << 32) | al;
+      sm.wred2[t >> 6] = (static_cast<u64>(b) << 32) | bl;
+    }
+    __syncthreads();
+    u64 l2 = ~0ull, h2 = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      l2 = sm.wred[w] < l2 ? sm.wred[w] : l2;
+      h2 = sm.wred2[w] > h2 ? sm.wred2[w] : h2;
+    }
+    lo = uniform64(l2);
+    hi = uniform64(h2);
+  }
+
+  uint32_t need = keep;
+  u64 T = 0;
+  bool done = false;
+  int par = 0;
+  for (int level = 0; level < 6 && !done; ++level) {
+    const u64 span = hi - lo;
+    const uint32_t bl = bit_length64(span);
+    const uint32_t shift = bl > kCutBits ? bl - kCutBits : 0u;
+    // Bin 0 holds the largest composites.
+    for (uint32_t j = t; j < n; j += NT) {
+      const u64 v = sm.buf[j];
+      if (v >= lo && v <= hi)
+        atomicAdd(&sm.hist[(kCutBins - 1) - static_cast<uint32_t>((v - lo) >> shift)], 1u);
+    }
+    __syncthreads();
+    uint32_t h[kCutBPT];
+#pragma unroll
+    for (int i = 0; i < kCutBPT; ++i) {
+      h[i] = sm.hist[t * kCutBPT + i];
+      sm.hist[t * kCutBPT + i] = 0u;
+    }
+    find_rank<kCutBPT>(sm, h, need, par);
+    par ^= 1;
+    const uint32_t b = uniform(sm.res[0]);
+    if (b == kNone) {   // fewer than `need` in range: inconsistent counts
+      if (t == 0) sm.err = 1u;
+      return 0;
+    }
+    const uint32_t below = uniform(sm.res[1]), hb = uniform(sm.res[2]);
+    need -= below;
+    // Composites of bin b: [blo, bhi].
+    const u64 blo = lo + (static_cast<u64>((kCutBins - 1) - b) << shift);
+    const u64 bhi_full = blo + ((1ull << shift) - 1ull);
+    const u64 bhi = bhi_full < hi ? bhi_full : hi;
+    if (hb == need) {   // the whole bin is kept
+      T = blo;
+      done = true;
+    } else if (hb <= kRankMax) {
+      // Rank the bin's members directly.
+      if (t == 0) sm.side_n = 0u;
+      __syncthreads();
+      for (uint32_t j0 = 0; j0 < n; j0 += NT) {
+        const uint32_t j = j0 + t;
+        const u64 v = j < n ? sm.buf[j] : 0ull;
+        const bool in = (j < n) & (v >= blo) & (v <= bhi);
+        const u64 mk = ballot(in);
+        if (mk) {
+          uint32_t base = 0;
+          if (lane_id() == 0) base = atomicAdd(&sm.side_n, static_cast<uint32_t>(__popcll(mk)));
+          base = uniform(base);
+          if (in && base + mbcnt64(mk) < kRankMax) sm.side[base + mbcnt64(mk)] = v;
+        }
+      }
+      __syncthreads();
+      const uint32_t ns = uniform(sm.side_n);
+      if (ns != hb) {
+        if (t == 0) sm.err = 1u;
+        return 0;
+      }
+      if (t < 64) {
+        const u64 mine = static_cast<uint32_t>(t) < ns ? sm.side[t] : 0ull;
+        uint32_t above = 0;
+        for (uint32_t j = 0; j < ns; ++j) above += sm.side[j] > mine ? 1u : 0u;
+        if (static_cast<uint32_t>(t) < ns && above + 1u == need) sm.res64 = mine;
+      }
+      __syncthreads();
+      T = uniform64(sm.res64);
+      done = true;
+    } else if (shift == 0) {   // cannot happen: a bin of width 1 holds one composite
+      if (t == 0) sm.err = 1u;
+      return 0;
+    } else {
+      lo = blo;
+      hi = bhi;
+    }
+  }
+  if (!done) {
+    if (t == 0) sm.err = 1u;
+    return 0;
+  }
+  // Compaction in groups: every lane reads its slots of a group before any
+  // write of that group, and a write position never exceeds the number of
+  // slots read so far, so no unread slot is overwritten.
+  uint32_t out = 0;
+  for (uint32_t g0 = 0; g0 < n; g0 += 8 * NT) {
+    u64 v[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const uint32_t j = g0 + q * NT + t;
+      v[q] = j < n ? sm.buf[j] : 0ull;
+    }
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) cnt += (v[q] >= T) ? 1u : 0u;   // empty slots read 0 < T
+    uint32_t total;
+    const uint32_t pre = block_excl(sm, cnt, par, &total);   // its barrier orders the reads
+    par ^= 1;
+    uint32_t pos = out + pre;
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (v[q] >= T) sm.buf[pos++] = v[q];
+    out += total;
+    __syncthreads();
+  }
+  return T;
+}
+
+// ---------------------------------------------------------------- appending a chunk
+// Shared state of one workgroup's candidate buffer (all fields uniform).
+struct Buf {
+  uint32_t count;   // candidates in buf
+  u64 T;            // every value of the row (or chunk) with composite >= T is in buf
+  int par;          // parity of the next block scan
+};
+
+// Append the values of vector i with key >= key(B.T), cutting first when they
+// might not fit.  Used when a whole chunk does not fit at once.
+template <bool BF16, int CAP>
+__device__ __forceinline__ void append_vec(Smem<CAP>& sm, Buf& B, const u32x4& r, int i,
+                                           uint32_t c, uint32_t k, uint32_t cap) {
+  using G = Geo<BF16>;
+  constexpr uint32_t PIECE = NT * G::EPV;
+  if (B.count + PIECE > cap && B.count > k) {
+    __syncthreads();
+    const u64 Tn = cut_exact(sm, B.count, k);
+    if (uniform(sm.err)) return;
+    B.T = Tn;
+    B.count = k;
+  }
+  const float f = __uint_as_float(bits_of_key(key_of(B.T)));
+  const uint32_t n = vec_count<BF16>(r, f);
+  uint32_t total, wb;
+  block_excl(sm, n, B.par, &total, &wb);
+  B.par ^= 1;
+  vec_write<BF16>(sm, r, i, c, f, B.count + wb);
+  B.count += total;
+}
+
+// Append every value of chunk c with key >= key(B.T).  Values at a key equal
+// to T's whose column lies past T's are admitted too: harmless, since every
+// later step keeps the buffer a superset of the values >= T.
+template <bool BF16, int CAP>
+__device__ __forceinline__ void append_chunk(Smem<CAP>& sm, Buf& B, const u32x4 (&r)[V], uint32_t c,
+                                             uint32_t k, uint32_t cap) {
+  const float f = __uint_as_float(bits_of_key(key_of(B.T)));
+  uint32_t n = 0;
+#pragma unroll
+  for (int i = 0; i < V; ++i) n += vec_count<BF16>(r[i], f);
+  uint32_t total, wb;
+  block_excl(sm, n, B.par, &total, &wb);
+  B.par ^= 1;
+  if (B.count + total <= cap) {
+    uint32_t pos = B.count + wb;
+#pragma unroll
+    for (int i = 0; i < V; ++i) pos = vec_write<BF16>(sm, r[i], i, c, f, pos);
+    B.count += total;
+    return;
+  }
+  // Piecewise: one vector per lane at a time (a cut leaves room for one).
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    append_vec<BF16>(sm, B, r[i], i, c, k, cap);
+    if (uniform(sm.err)) return;
+  }
+}
+
+// The first chunk of a workgroup: NaN check, start threshold, append.  With
+// `exact`, the chunk is a whole row and T is a valid start (at least
+// min(k, L) values pass); otherwise T is an estimate of the row's k-th value
+// for this chunk's share.  Returns whether a NaN was found.
+template <bool BF16, int CAP>
+__device__ __forceinline__ bool first_chunk(Smem<CAP>& sm, Buf& B, u32x4 (&r)[V], uint32_t c,
+                                            uint32_t L, uint32_t k, uint32_t cap, bool exact,
+                                            bool* spec) {
+  using G = Geo<BF16>;
+  const int t = threadIdx.x;
+  bool nan = false;
+  const bool rag = (c + 1) * G::CE > L;
+  if (rag) nan = sanitize_ragged<BF16>(r, c, L);
+  uint32_t mk;
+  bool nn;
+  if (rag) chunk_max_nan<BF16, false>(r, &mk, &nn);
+  else chunk_max_nan<BF16, true>(r, &mk, &nn);
+  nan |= nn;
+  const uint32_t wm = wave_max_u32(mk);
+  if (lane_id() == 0) sm.wmax[t >> 6] = wm;
+  __syncthreads();
+  uint32_t maxkey = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) maxkey = max(maxkey, sm.wmax[w]);
+  maxkey = uniform(maxkey);
+  const uint32_t nvalid = min(G::CE, L - c * G::CE);
+  uint32_t m;
+  if (exact) {
+    m = min(k, L);
+  } else {
+    // The chunk's expected share of the row's top k plus six standard
+    // deviations (its count is hypergeometric, variance below the mean).
+    const float E = static_cast<float>(k) * static_cast<float>(nvalid) / static_cast<float>(L);
+    const float mf = E + 6.0f * __builtin_sqrtf(E) + 8.0f;
+    m = mf >= static_cast<float>(k) ? k : static_cast<uint32_t>(mf) + 1u;
+  }
+  u64 T = kTAll;
+  if (maxkey != 0 && m < nvalid) {
+    if (m <= static_cast<uint32_t>(NT / 2)) T = start_threshold<BF16, true>(sm, r, maxkey, mk, m);
+    else T = start_threshold<BF16, false>(sm, r, maxkey, mk, m);
+  }
+  *spec = !exact && m < k && T != kTAll;
+  B.T = T;
+  append_chunk<BF16>(sm, B, r, c, k, cap);
+  return nan;
+}
+
+// A later chunk of a whole row.
+template <bool BF16, int CAP>
+__device__ __forceinline__ bool next_chunk(Smem<CAP>& sm, Buf& B, u32x4 (&r)[V], uint32_t c,
+                                           uint32_t L, uint32_t k, uint32_t cap) {
+  using G = Geo<BF16>;
+  bool nan = false;
+  uint32_t mk;
+  bool nn;
+  if ((c + 1) * G::CE > L) {
+    nan = sanitize_ragged<BF16>(r, c, L);
+  } else {
+    chunk_max_nan<BF16, true>(r, &mk, &nn);
+    nan = nn;
+  }
+  append_chunk<BF16>(sm, B, r, c, k, cap);
+  return nan;
+}
+
+// The row read again, in order, from T = every value (a start estimate that
+// turned out too high).  The NaN check was done on the first read.
+template <bool BF16, int CAP>
+__device__ __noinline__ Buf restream(Smem<CAP>& sm, int par, const char* xrow, uint32_t L,
+                                     uint32_t k, uint32_t cap) {
+  using G = Geo<BF16>;
+  const uint32_t nch = (L + G::CE - 1) / G::CE;
+  Buf B{0u, kTAll, par};
+  __syncthreads();
+  for (uint32_t j = 0; j < nch; ++j) {
+    u32x4 r[V];
+    load_chunk<BF16>(r, xrow, j, L);
+    if ((j + 1) * G::CE > L) sanitize_ragged<BF16>(r, j, L);
+    append_chunk<BF16>(sm, B, r, j, k, cap);
+    if (uniform(sm.err)) break;
+  }
+  return B;
+}
+
+// ---------------------------------------------------------------- the sort
+// Bitonic sort, descending, of PER*NT 64-bit keys; lane t holds elements
+// t*PER .. t*PER+PER-1.  Strides below PER are in registers, strides up to
+// 32*PER cross lanes by ds_bpermute, larger strides cross waves through
+// `xch` (PER*NT entries of LDS).
+template <int PER, int S>
+__device__ __forceinline__ void bitonic_in_lane(u64 (&v)[PER], uint32_t size) {
+  const uint32_t t = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int j = i ^ S;
+    if (j > i && j < PER) {
+      const bool desc = ((t * PER + i) & size) == 0;
+      const u64 a = v[i], b = v[j];
+      const bool sw = desc ? (a < b) : (a > b);
+      v[i] = sw ? b : a;
+      v[j] = sw ? a : b;
+    }
+  }
+}
+
+template <int PER>
+__device__ __forceinline__ void bitonic_sort_desc(u64 (&v)[PER], u64* xch) {
+  constexpr uint32_t N = PER * NT;
+  const uint32_t t = threadIdx.x;
+  for (uint32_t size = 2; size <= N; size <<= 1) {
+    for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
+      if (stride < PER) {
+        if (stride == 1) bitonic_in_lane<PER, 1>(v, size);
+        else if (stride == 2) bitonic_in_lane<PER, 2>(v, size);
+        else if (stride == 4) bitonic_in_lane<PER, 4>(v, size);
+        else bitonic_in_lane<PER, 8>(v, size);
+      } else if (stride < 64 * PER) {
+        const uint32_t lx = stride / PER;
+        const bool lower = (t & lx) == 0;
+        const int addr = static_cast<int>((lane_id() ^ lx) << 2);
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+          const uint32_t olo = static_cast<uint32_t>(
+              __builtin_amdgcn_ds_bpermute(addr, static_cast<int>(static_cast<uint32_t>(v[i]))));
+          const uint32_t ohi = static_cast<uint32_t>(
+              __builtin_amdgcn_ds_bpermute(addr, static_cast<int>(static_cast<uint32_t>(v[i] >> 32))));
+          const u64 o = (static_cast<u64>(ohi) << 32) | olo;
+          const bool desc = ((t * PER + i) & size) == 0;
+          const bool keep_max = lower == desc;
+          const u64 mx = v[i] > o ? v[i] : o;
+          const u64 mn = v[i] > o ? o : v[i];
+          v[i] = keep_max ? mx : mn;
+        }
+      } else {
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < PER; ++i) xch[t * PER + i] = v[i];
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+          const uint32_t e = t * PER + i;
+          const u64 o = xch[e ^ stride];
+          const bool lower = (e & stride) == 0;
+          const bool desc = (e & size) == 0;
+          const bool keep_max = lower == desc;
+          const u64 mx = v[i] > o ? v[i] : o;
+          const u64 mn = v[i] > o ? o : v[i];
+          v[i] = keep_max ? mx : mn;
+        }
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------- outputs
+__device__ __forceinline__ void store_one(const CArgs& a, bool bf16, const char* xrow, int64_t o,
+                                          u64 c, bool valid, uint32_t status) {
+  uint32_t ix, v;
+  if (valid) {
+    ix = col_of(c);
+    const uint32_t key = key_of(c);
+    if (key == kBias) {   // a zero: its sign is only in the input
+      v = bf16 ? static_cast<uint32_t>(reinterpret_cast<const uint16_t*>(xrow)[ix]) << 16
+               : reinterpret_cast<const uint32_t*>(xrow)[ix];
+    } else {
+      v = bits_of_key(key);
+    }
+  } else {
+    ix = 0xFFFFFFFFu;
+    v = status ? kQNaN32 : kNegInf32;
+  }
+  if (a.idx64)
+    static_cast<int64_t*>(a.indices)[o] = static_cast<int64_t>(static_cast<int32_t>(ix));
+  else
+    static_cast<int32_t*>(a.indices)[o] = static_cast<int32_t>(ix);
+  if (a.return_values) {
+    if (bf16)
+      static_cast<uint16_t*>(a.values)[o] = static_cast<uint16_t>(v >> 16);
+    else
+      static_cast<uint32_t*>(a.values)[o] = v;
+  }
+}
+
+// The epilogue of a row: the buffer holds `count` candidates, a superset of
+// the top m = min(k, L) (m = 0 for a flagged row).  Cut to exactly m, order,
+// write.
+template <int KMAX, int CAP>
+__device__ __forceinline__ void finish_row(Smem<CAP>& sm, const CArgs& a, bool bf16, int row,
+                                           uint32_t count, uint32_t L, uint32_t status) {
+  constexpr int PER = KMAX / NT;
+  const int t = threadIdx.x;
+  const uint32_t k = static_cast<uint32_t>(a.k);
+  uint32_t m = status ? 0u : min(k, L);
+  __syncthreads();
+  if (m > 0 && count > m) {
+    cut_exact(sm, count, m);
+    if (uniform(sm.err)) {
+      status |= DS_ROW_INTERNAL;
+      m = 0;
+    }
+  } else if (m > count) {   // cannot happen: every path leaves at least m candidates
+    status |= DS_ROW_INTERNAL;
+    m = 0;
+  }
+  __syncthreads();
+  const int64_t out0 = static_cast<int64_t>(row) * k;
+  const char* xrow = static_cast<const char*>(a.x) + static_cast<int64_t>(row) * a.row_stride * (bf16 ? 2 : 4);
+  if (a.sorted != 0 && m > 1) {
+    // Sort keys: the composite by value; (~column << 32) | key by column.
+    const bool by_col = a.sorted == 2;
+    u64 v[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const uint32_t e = t * PER + i;
+      u64 c = e < m ? sm.buf[e] : 0ull;
+      if (by_col && e < m) c = (static_cast<u64>(static_cast<uint32_t>(c)) << 32) | key_of(c);
+      v[i] = c;
+    }
+    bitonic_sort_desc<PER>(v, sm.buf);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const uint32_t e = t * PER + i;
+      if (e < k) {
+        u64 c = v[i];
+        if (by_col) c = (static_cast<u64>(static_cast<uint32_t>(c)) << 32) | static_cast<uint32_t>(c >> 32);
+        store_one(a, bf16, xrow, out0 + e, c, e < m, status);
+      }
+    }
+  } else {
+    for (uint32_t e = t; e < k; e += NT)
+      store_one(a, bf16, xrow, out0 + e, e < m ? sm.buf[e] : 0ull, e < m, status);
+  }
+  if (t == 0) a.row_status[row] = static_cast<int32_t>(status);
+}
+
+// OR of a per-lane flag over the workgroup (flag bits are small).
+template <int CAP>
+__device__ __forceinline__ uint32_t block_or(Smem<CAP>& sm, uint32_t f, int par) {
+  const u64 b1 = ballot(f & 1u), b2 = ballot(f & 2u), b4 = ballot(f & 4u);
+  if (lane_id() == 0) sm.wtot[par][threadIdx.x >> 6] = (b1 ? 1u : 0u) | (b2 ? 2u : 0u) | (b4 ? 4u : 0u);
+  __syncthreads();
+  uint32_t o = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) o |= sm.wtot[par][w];
+  return uniform(o);
+}
+
+// ---------------------------------------------------------------- the kernels
+// Row length and status of a row.
+__device__ __forceinline__ uint32_t row_len(const CArgs& a, int row, uint32_t* status) {
+  int64_t Ls = a.end ? static_cast<int64_t>(a.end[row]) : static_cast<int64_t>(a.n_cols);
+  if (Ls < 0 || Ls > a.n_cols) {
+    *status = DS_ROW_BAD_END;
+    return 0;
+  }
+  return static_cast<uint32_t>(Ls);
+}
+
+// A whole row per workgroup, chunk by chunk (the next chunk's loads in flight).
+template <bool BF16, int KC>
+__global__ __launch_bounds__(NT, 4) void chunk_row_kernel(CArgs a) {
+  using G = Geo<BF16>;
+  constexpr int KMAX = class_kmax(KC);
+  constexpr int CAP = chunk_cap(KC);
+  static_assert(CAP >= KMAX + NT * G::EPV, "a cut leaves room for one vector per lane");
+  __shared__ Smem<CAP> sm;
+  const int t = threadIdx.x;
+  const int row = a.reverse_rows ? a.batch - 1 - static_cast<int>(blockIdx.x) : static_cast<int>(blockIdx.x);
+  const uint32_t k = static_cast<uint32_t>(a.k);
+  const uint32_t cap = a.cap_eff;
+  const char* xrow = static_cast<const char*>(a.x) + static_cast<int64_t>(row) * a.row_stride * G::ESZ;
+  uint32_t status = 0;
+  const uint32_t L = row_len(a, row, &status);
+  const uint32_t nch = (L + G::CE - 1) / G::CE;
+
+  // Visiting order: an affine bijection j -> (p*j + q) mod nch, p coprime to
+  // nch (the pages visit blocks in a random order).
+  uint32_t pm = 1, pq = 0;
+  if (!a.in_order && nch > 2) {
+    uint32_t h = a.perm_seed * 0x9E3779B9u ^ (static_cast<uint32_t>(row) + 0x7F4A7C15u) * 0x85EBCA6Bu;
+    h ^= h >> 15;
+    h *= 0x2C1B3C6Du;
+    h ^= h >> 12;
+    pq = h % nch;
+    pm = 1u + (h >> 8) % (nch - 1u);
+    for (uint32_t guard = 0; guard < nch; ++guard) {   // the next value coprime to nch
+      uint32_t x = pm, y = nch;
+      while (y) {
+        const uint32_t r2 = x % y;
+        x = y;
+        y = r2;
+      }
+      if (x == 1u) break;
+      pm = pm + 1u < nch ? pm + 1u : 1u;
+    }
+  }
+  auto chunk_at = [&](uint32_t j) -> uint32_t {
+    return static_cast<uint32_t>((static_cast<u64>(pm) * j + pq) % nch);
+  };
+
+  for (int i = t; i < kCutBins / 4; i += NT) reinterpret_cast<u32x4*>(sm.hist)[i] = u32x4{0u, 0u, 0u, 0u};
+  if (t == 0) sm.err = 0u;
+
+  Buf B{0u, kTAll, 0};
+  bool spec = false, nan = false;
+  if (status == 0 && nch > 0) {
+    u32x4 ra[V], rb[V];
+    load_chunk<BF16>(ra, xrow, chunk_at(0), L);
+    if (nch > 1) load_chunk<BF16>(rb, xrow, chunk_at(1), L);
+    nan = first_chunk<BF16>(sm, B, ra, chunk_at(0), L, k, cap, nch == 1, &spec);
+    for (uint32_t j = 1; j < nch && !uniform(sm.err); ++j) {
+#pragma unroll
+      for (int i = 0; i < V; ++i) ra[i] = rb[i];
+      if (j + 1 < nch) load_chunk<BF16>(rb, xrow, chunk_at(j + 1), L);
+      nan |= next_chunk<BF16>(sm, B, ra, chunk_at(j), L, k, cap);
+    }
+  }
+  status |= block_or(sm, nan ? static_cast<uint32_t>(DS_ROW_NAN) : 0u, B.par);
+  B.par ^= 1;
+  if (uniform(sm.err)) status |= DS_ROW_INTERNAL;
+  // An estimated start is checked: with fewer than min(k, L) candidates at or
+  // above it, a value of the top k may lie below it.
+  if (status == 0 && spec && B.count < min(k, L)) {
+    B = restream<BF16>(sm, B.par, xrow, L, k, cap);
+    if (uniform(sm.err)) status |= DS_ROW_INTERNAL;
+  }
+  finish_row<KMAX>(sm, a, BF16, row, B.count, L, status);
+}
+
+// One chunk of a row per workgroup; the last workgroup of the row to finish
+// merges the others' candidates.
+template <bool BF16, int KC>
+__global__ __launch_bounds__(NT, 4) void chunk_split_kernel(CArgs a) {
+  using G = Geo<BF16>;
+  constexpr int KMAX = class_kmax(KC);
+  constexpr int CAP = chunk_cap(KC);
+  constexpr int G8 = 8;   // slots per lane per merge round
+  static_assert(CAP >= KMAX + NT * G::EPV, "a cut leaves room for one vector per lane");
+  static_assert(G8 * NT <= CAP - KMAX, "a merge round fits after a cut");
+  __shared__ Smem<CAP> sm;
+  const int t = threadIdx.x;
+  const int S = a.segments;
+  const int row = static_cast<int>(blockIdx.x) / S;
+  const int seg = static_cast<int>(blockIdx.x) - row * S;
+  const uint32_t k = static_cast<uint32_t>(a.k);
+  const uint32_t cap = a.cap_eff;
+  const char* xrow = static_cast<const char*>(a.x) + static_cast<int64_t>(row) * a.row_stride * G::ESZ;
+  uint32_t status = 0;
+  const uint32_t L = row_len(a, row, &status);
+  const uint32_t nch = (L + G::CE - 1) / G::CE;
+  const bool mine = static_cast<uint32_t>(seg) < nch;
+
+  for (int i = t; i < kCutBins / 4; i += NT) reinterpret_cast<u32x4*>(sm.hist)[i] = u32x4{0u, 0u, 0u, 0u};
+  if (t == 0) sm.err = 0u;
+
+  Buf B{0u, kTAll, 0};
+  bool nan = false, spec = false;
+  if (status == 0 && mine) {
+    u32x4 ra[V];
+    load_chunk<BF16>(ra, xrow, static_cast<uint32_t>(seg), L);
+    nan = first_chunk<BF16>(sm, B, ra, static_cast<uint32_t>(seg), L, k, cap, false, &spec);
+  }
+  status |= block_or(sm, nan ? static_cast<uint32_t>(DS_ROW_NAN) : 0u, B.par);
+  B.par ^= 1;
+  // At most k candidates are handed over: the chunk's own top k, exactly.
+  if (status == 0 && !uniform(sm.err) && B.count > k) {
+    __syncthreads();
+    const u64 Tn = cut_exact(sm, B.count, k);
+    if (!uniform(sm.err)) {
+      B.T = Tn;
+      B.count = k;
+    }
+  }
+  if (uniform(sm.err)) status |= DS_ROW_INTERNAL;
+
+  // ---- hand-over: the chunk's candidates, its threshold and its flags.
+  const int64_t rs = static_cast<int64_t>(row) * S + seg;
+  u64* slot = a.ws_slot + rs * static_cast<int64_t>(k);
+  const uint32_t hand = status ? 0u : B.count;
+  for (uint32_t j = t; j < hand; j += NT) st_agent(&slot[j], sm.buf[j]);
+  if (t == 0) {
+    st_agent(&a.ws_rec[2 * rs], mine ? B.T : kTAll);
+    st_agent(&a.ws_rec[2 * rs + 1], (static_cast<u64>(status) << 32) | hand);
+  }
+  // Every lane's stores happen before lane 0's release on the row's counter
+  // (the barrier), and the last workgroup's acquire of that counter happens
+  // before its loads: the hand-over is ordered by the memory model itself.
+  __syncthreads();
+  if (t == 0) {
+    const uint32_t prev = __hip_atomic_fetch_add(&a.ws_arrive[row], 1u, __ATOMIC_ACQ_REL,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+    sm.is_last = prev == static_cast<uint32_t>(S - 1) ? 1u : 0u;
+  }
+  __syncthreads();
+  if (!uniform(sm.is_last)) return;
+
+  // ---- merge: every chunk's candidates at or above the largest chunk threshold.
+  const u64* rec = a.ws_rec + static_cast<int64_t>(row) * S * 2;
+  u64 Tm = 0;
+  uint32_t fl = 0, cm = 0;
+  if (t < S) {
+    Tm = ld_agent(&rec[2 * t]);
+    const u64 info = ld_agent(&rec[2 * t + 1]);
+    fl = static_cast<uint32_t>(info >> 32);
+    cm = static_cast<uint32_t>(info);
+  }
+  {
+    const uint32_t hiw = wave_max_u32(static_cast<uint32_t>(Tm >> 32));
+    const uint32_t low = wave_max_u32(static_cast<uint32_t>(Tm >> 32) == hiw ? static_cast<uint32_t>(Tm) : 0u);
+    const uint32_t cmx = wave_max_u32(cm);
+    if (lane_id() == 0) {
+      sm.wred[t >> 6] = (static_cast<u64>(hiw) << 32) | low;
+      sm.wmax[t >> 6] = cmx;
+    }
+  }
+  status |= block_or(sm, fl, B.par);   // its barrier also publishes wred / wmax
+  B.par ^= 1;
+  u64 tm = 0;
+  uint32_t cmax = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    tm = sm.wred[w] > tm ? sm.wred[w] : tm;
+    cmax = max(cmax, sm.wmax[w]);
+  }
+  Tm = uniform64(tm);
+  cmax = uniform(cmax);
+
+  B.count = 0;
+  B.T = Tm;
+  // Chunk s's slots are read by lanes [s*PL, (s+1)*PL), PL = NT / S lanes per
+  // chunk, G8 slots per lane per round.
+  const uint32_t PL = static_cast<uint32_t>(NT / S);
+  const uint32_t my_s = static_cast<uint32_t>(t) / PL;
+  const uint32_t my_l = static_cast<uint32_t>(t) - my_s * PL;
+  const bool has_s = my_s < static_cast<uint32_t>(S);
+  const uint32_t my_c = has_s ? static_cast<uint32_t>(ld_agent(&rec[2 * my_s + 1])) : 0u;
+  u64* my_slot = a.ws_slot + (static_cast<int64_t>(row) * S + my_s) * static_cast<int64_t>(k);
+  const uint32_t per_round = PL * G8;
+  const uint32_t rounds = status ? 0u : (cmax + per_round - 1) / per_round;
+  __syncthreads();
+  for (uint32_t rd = 0; rd < rounds; ++rd) {
+    u64 v[G8];
+#pragma unroll
+    for (int q = 0; q < G8; ++q) {
+      const uint32_t j = rd * per_round + q * PL + my_l;
+      v[q] = (has_s && j < my_c) ? ld_agent(&my_slot[j]) : 0ull;
+    }
+    uint32_t n = 0;
+#pragma unroll
+    for (int q = 0; q < G8; ++q) n += v[q] >= B.T ? 1u : 0u;
+    uint32_t total;
+    uint32_t pre = block_excl(sm, n, B.par, &total);
+    B.par ^= 1;
+    if (B.count + total > cap) {
+      // Cut the buffer to k first; the round's values then fit.
+      const u64 Tn = cut_exact(sm, B.count, k);
+      if (uniform(sm.err)) break;
+      B.T = Tn;
+      B.count = k;
+      n = 0;
+#pragma unroll
+      for (int q = 0; q < G8; ++q) n += v[q] >= B.T ? 1u : 0u;
+      pre = block_excl(sm, n, B.par, &total);
+      B.par ^= 1;
+    }
+    uint32_t pos = B.count + pre;
+#pragma unroll
+    for (int q = 0; q < G8; ++q)
+      if (v[q] >= B.T) sm.buf[pos++] = v[q];
+    B.count += total;
+    __syncthreads();
+  }
+  // Leave the workspace as it was found: zero.
+  for (uint32_t rd = 0; rd * per_round < cmax; ++rd) {
+#pragma unroll
+    for (int q = 0; q < G8; ++q) {
+      const uint32_t j = rd * per_round + q * PL + my_l;
+      if (has_s && j < my_c) st_agent(&my_slot[j], 0ull);
+    }
+  }
+  if (t < S) {
+    u64* wrec = a.ws_rec + static_cast<int64_t>(row) * S * 2;
+    st_agent(&wrec[2 * t], 0ull);
+    st_agent(&wrec[2 * t + 1], 0ull);
+  }
+  if (t == 0) st_agent(&a.ws_arrive[row], 0u);
+  if (uniform(sm.err)) status |= DS_ROW_INTERNAL;
+  // The check: every chunk kept all of its values at or above its own
+  // threshold, so the buffer holds every value of the row at or above T*, the
+  // largest of those thresholds (or above a cut's threshold, which is valid).
+  // With at least min(k, L) of them, the top min(k, L) are all here.
+  if (status == 0 && B.count < min(k, L)) {
+    B = restream<BF16>(sm, B.par, xrow, L, k, cap);
+    if (uniform(sm.err)) status |= DS_ROW_INTERNAL;
+  }
+  finish_row<KMAX>(sm, a, BF16, row, B.count, L, status);
+}
+
+// ---------------------------------------------------------------- read ceiling
+// A measurement aid, not part of the selection: the chunk kernels' grid and
+// loads (a whole row chunk by chunk with the next chunk in flight, or one
+// chunk per workgroup), the data only folded into one word per lane, stored
+// only if it equals a constant.
+template <bool BF16>
+__global__ __launch_bounds__(NT) void chunk_read_kernel(CArgs a, uint32_t* sink) {
+  using G = Geo<BF16>;
+  const int S = a.segments;
+  int row = static_cast<int>(blockIdx.x) / S;
+  const int seg = static_cast<int>(blockIdx.x) - row * S;
+  if (S == 1 && a.reverse_rows) row = a.batch - 1 - row;
+  uint32_t status = 0;
+  const uint32_t L = row_len(a, row, &status);
+  const uint32_t nch = (L + G::CE - 1) / G::CE;
+  const char* xrow = static_cast<const char*>(a.x) + static_cast<int64_t>(row) * a.row_stride * G::ESZ;
+  const uint32_t c0 = S == 1 ? 0u : static_cast<uint32_t>(seg);
+  const uint32_t n = S == 1 ? nch : (c0 < nch ? 1u : 0u);
+  uint32_t acc = 0;
+  u32x4 ra[V], rb[V];
+  if (n > 0) load_chunk<BF16>(ra, xrow, c0, L);
+  for (uint32_t j = 0; j < n; ++j) {
+    if (j + 1 < n) load_chunk<BF16>(rb, xrow, c0 + j + 1, L);
+#pragma unroll
+    for (int i = 0; i < V; ++i) acc ^= ra[i].x ^ ra[i].y ^ ra[i].z ^ ra[i].w;
+#pragma unroll
+    for (int i = 0; i < V; ++i) ra[i] = rb[i];
+  }
+  if (acc == 0x9E3779B9u) sink[0] = acc;
+}
+
+template <bool BF16>
+const void* chunk_fn(int cls, bool split) {
+  if (split) {
+    return cls == 0 ? reinterpret_cast<const void*>(&chunk_split_kernel<BF16, 0>)
+         : cls == 1 ? reinterpret_cast<const void*>(&chunk_split_kernel<BF16, 1>)
+         : cls == 2 ? reinterpret_cast<const void*>(&chunk_split_kernel<BF16, 2>)
+                    : reinterpret_cast<const void*>(&chunk_split_kernel<BF16, 3>);
+  }
+  return cls == 0 ? reinterpret_cast<const void*>(&chunk_row_kernel<BF16, 0>)
+       : cls == 1 ? reinterpret_cast<const void*>(&chunk_row_kernel<BF16, 1>)
+       : cls == 2 ? reinterpret_cast<const void*>(&chunk_row_kernel<BF16, 2>)
+                  : reinterpret_cast<const void*>(&chunk_row_kernel<BF16, 3>);
+}
+
+}  // namespace
+
+ChunkWs chunk_ws_layout(int64_t batch, int segments, int k) {
+  auto up = [](size_t v) { return (v + 255) & ~static_cast<size_t>(255); };
+  ChunkWs l{};
+  const size_t b = static_cast<size_t>(batch);
+  const size_t s = static_cast<size_t>(segments);
+  l.arrive = 0;
+  l.rec = up(b * 4);
+  l.slot = up(l.rec + b * s * 16);
+  l.total = up(l.slot + b * s * static_cast<size_t>(k) * 8);
+  return l;
+}
+
+// The launch's own error code (hipLaunchKernel returns it; an earlier,
+// unrelated error left in the runtime is neither returned nor cleared).
+int launch_chunk(const CArgs& a, int dtype, int cls, hipStream_t stream) {
+  const unsigned grid = static_cast<unsigned>(static_cast<int64_t>(a.batch) * a.segments);
+  CArgs arg = a;
+  void* args[] = {&arg};
+  const void* fn = dtype == 0 ? chunk_fn<false>(cls, a.segments > 1) : chunk_fn<true>(cls, a.segments > 1);
+  return static_cast<int>(hipLaunchKernel(fn, dim3(grid), dim3(NT), args, 0, stream));
+}
+
+int launch_chunk_read(const CArgs& a, int dtype, uint32_t* sink, hipStream_t stream) {
+  const unsigned grid = static_cast<unsigned>(static_cast<int64_t>(a.batch) * a.segments);
+  CArgs arg = a;
+  void* args[] = {&arg, &sink};
+  const void* fn = dtype == 0 ? reinterpret_cast<const void*>(&chunk_read_kernel<false>)
+                              : reinterpret_cast<const void*>(&chunk_read_kernel<true>);
+  return static_cast<int>(hipLaunchKernel(fn, dim3(grid), dim3(NT), args, 0, stream));
+}
+
+}  // namespace dstk

@@ -21,6 +21,7 @@ namespace {
 using namespace dstk;
 
 struct Plan {
+  int kernel;     // DS_KERNEL_STREAM or DS_KERNEL_CHUNK
   int cls;
   int segments;
   uint32_t seed;
@@ -57,32 +58,71 @@ int auto_segments(int64_t batch, int64_t n_cols, int cls, int dtype) {
   return static_cast<int>(s);
 }
 
+// Chunks of a row of n_cols values.
+int64_t chunks_of(int64_t n_cols, int dtype) {
+  const int64_t ce = chunk_elems(dtype);
+  return (n_cols + ce - 1) / ce;
+}
+
+// Workgroups per row for the chunk kernels: one per chunk when the batch is
+// too small to fill the chip with whole rows, else one per row.
+int chunk_segments(int64_t batch, int64_t n_cols, int dtype) {
+  const int64_t nch = chunks_of(n_cols, dtype);
+  return (batch < kChunkSplitBatch && nch > 1 && nch <= kMaxSegments) ? static_cast<int>(nch) : 1;
+}
+
 // Fills `out`; returns DS_ERR_PLAN for an out-of-range override.
 ds_status_t resolve_plan(int64_t batch, int64_t n_cols, int32_t k, ds_dtype_t dtype,
                          const ds_topk_plan_t* p, Plan* out) {
+  const int dt = dtype == DS_BF16 ? 1 : 0;
   Plan pl{};
   pl.cls = class_of_k(k);
-  pl.segments = auto_segments(batch, n_cols, pl.cls, dtype == DS_BF16 ? 1 : 0);
+  const int64_t nch = chunks_of(n_cols, dt);
+  pl.kernel = nch <= kChunkMaxPerRow ? DS_KERNEL_CHUNK : DS_KERNEL_STREAM;
   pl.seed = 0x5EEDu;
   pl.in_order = 0;
-  pl.trigger = class_trigger(pl.cls);
+  if (p) {
+    if (p->kernel < DS_KERNEL_AUTO || p->kernel > DS_KERNEL_CHUNK) return DS_ERR_PLAN;
+    if (p->kernel != DS_KERNEL_AUTO) pl.kernel = p->kernel;
+  }
+  if (pl.kernel == DS_KERNEL_CHUNK) {
+    pl.segments = chunk_segments(batch, n_cols, dt);
+    pl.trigger = chunk_cap(pl.cls);
+  } else {
+    pl.segments = auto_segments(batch, n_cols, pl.cls, dt);
+    pl.trigger = class_trigger(pl.cls);
+  }
   if (p) {
     if (p->segments < 0 || p->segments > kMaxSegments) return DS_ERR_PLAN;
     if (p->in_order != 0 && p->in_order != 1) return DS_ERR_PLAN;
     if (p->flush_at != 0 && (p->flush_at <= k || p->flush_at > class_trigger(pl.cls)))
       return DS_ERR_PLAN;
-    if (p->segments > 0) pl.segments = p->segments;
+    if (pl.kernel == DS_KERNEL_CHUNK) {
+      if (p->segments == 1) pl.segments = 1;
+      else if (p->segments > 1) {
+        if (nch > kMaxSegments) return DS_ERR_PLAN;
+        pl.segments = nch > 1 ? static_cast<int>(nch) : 1;
+      }
+      if (p->flush_at) {
+        const int lo = k + 2048;
+        pl.trigger = p->flush_at < lo ? lo : p->flush_at;
+        if (pl.trigger > chunk_cap(pl.cls)) pl.trigger = chunk_cap(pl.cls);
+      }
+    } else {
+      if (p->segments > 0) pl.segments = p->segments;
+      if (p->flush_at) pl.trigger = p->flush_at;
+    }
     pl.seed = p->perm_seed;
     pl.in_order = p->in_order;
-    if (p->flush_at) pl.trigger = p->flush_at;
   }
   *out = pl;
   return DS_OK;
 }
 
-size_t workspace_bytes_for(int64_t batch, int segments, int32_t k) {
-  if (segments <= 1 || batch <= 0) return 0;
-  return ws_layout(batch, segments, k).total;
+size_t workspace_bytes_for(const Plan& pl, int64_t batch, int32_t k) {
+  if (pl.segments <= 1 || batch <= 0) return 0;
+  if (pl.kernel == DS_KERNEL_CHUNK) return chunk_ws_layout(batch, pl.segments, k).total;
+  return ws_layout(batch, pl.segments, k).total;
 }
 
 ds_status_t check_scalars(ds_dtype_t dtype, int64_t batch, int64_t n_cols, int64_t row_stride,
@@ -115,7 +155,7 @@ ds_status_t validate(const void* x, ds_dtype_t dtype, int64_t batch, int64_t n_c
   if (return_values && misaligned(values, static_cast<uintptr_t>(es))) return DS_ERR_ALIGN;
   if (misaligned(row_status, 4) || (end && misaligned(end, 4))) return DS_ERR_ALIGN;
   if (batch * static_cast<int64_t>(pl->segments) > INT32_MAX) return DS_ERR_SHAPE;
-  const size_t need = workspace_bytes_for(batch, pl->segments, k);
+  const size_t need = workspace_bytes_for(*pl, batch, k);
   if (need > 0 && (!workspace || workspace_bytes < need || misaligned(workspace, 16)))
     return DS_ERR_WORKSPACE;
   return DS_OK;
@@ -147,6 +187,38 @@ ds_status_t ds_topk_ex(const void* x, ds_dtype_t dtype, int64_t batch, int64_t n
                             index_dtype, values, indices, row_status, workspace,
                             workspace_bytes, plan, &pl);
   if (st != DS_OK || batch == 0) return st;
+
+  if (pl.kernel == DS_KERNEL_CHUNK) {
+    CArgs c{};
+    c.x = x;
+    c.row_stride = row_stride;
+    c.n_cols = static_cast<int32_t>(n_cols);
+    c.batch = static_cast<int32_t>(batch);
+    c.end = end;
+    c.k = k;
+    c.sorted = sorted;
+    c.return_values = return_values ? 1 : 0;
+    c.idx64 = index_dtype == DS_INT64 ? 1 : 0;
+    c.values = return_values ? values : nullptr;
+    c.indices = indices;
+    c.row_status = row_status;
+    c.segments = pl.segments;
+    c.perm_seed = pl.seed;
+    c.in_order = pl.in_order;
+    // Rows of a causal prefill grow with the row index: whole rows go
+    // longest-first when their lengths vary.
+    c.reverse_rows = (pl.segments == 1 && end != nullptr) ? 1 : 0;
+    c.cap_eff = static_cast<uint32_t>(pl.trigger);
+    if (pl.segments > 1) {
+      const ChunkWs l = chunk_ws_layout(batch, pl.segments, k);
+      char* w = static_cast<char*>(workspace);
+      c.ws_arrive = reinterpret_cast<uint32_t*>(w + l.arrive);
+      c.ws_rec = reinterpret_cast<unsigned long long*>(w + l.rec);
+      c.ws_slot = reinterpret_cast<unsigned long long*>(w + l.slot);
+    }
+    const int err = launch_chunk(c, dtype == DS_BF16 ? 1 : 0, pl.cls, stream);
+    return err == 0 ? DS_OK : DS_ERR_HIP;
+  }
 
   KArgs a{};
   a.x = x;
@@ -195,7 +267,7 @@ size_t ds_topk_workspace_size_ex(ds_dtype_t dtype, int64_t batch, int64_t n_cols
   if (check_scalars(dtype, batch, n_cols, n_cols, k, 1, DS_INT32) != DS_OK) return 0;
   Plan pl;
   if (resolve_plan(batch, n_cols, k, dtype, plan, &pl) != DS_OK) return 0;
-  return workspace_bytes_for(batch, pl.segments, k);
+  return workspace_bytes_for(pl, batch, k);
 }
 
 size_t ds_topk_workspace_size(ds_dtype_t dtype, int64_t batch, int64_t n_cols, int32_t k) {
@@ -214,6 +286,21 @@ ds_status_t ds_read_ceiling(const void* x, ds_dtype_t dtype, int64_t batch, int6
   if ((x && misaligned(x, 16)) || (row_stride * elem_size(dtype)) % 16 != 0) return DS_ERR_ALIGN;
   if (misaligned(sink, 4) || (end && misaligned(end, 4))) return DS_ERR_ALIGN;
   if (batch * static_cast<int64_t>(pl.segments) > INT32_MAX) return DS_ERR_SHAPE;
+  if (pl.kernel == DS_KERNEL_CHUNK) {
+    CArgs c{};
+    c.x = x;
+    c.row_stride = row_stride;
+    c.n_cols = static_cast<int32_t>(n_cols);
+    c.batch = static_cast<int32_t>(batch);
+    c.end = end;
+    c.k = k;
+    c.segments = pl.segments;
+    c.perm_seed = pl.seed;
+    c.in_order = pl.in_order;
+    c.reverse_rows = (pl.segments == 1 && end != nullptr) ? 1 : 0;
+    const int err = launch_chunk_read(c, dtype == DS_BF16 ? 1 : 0, sink, stream);
+    return err == 0 ? DS_OK : DS_ERR_HIP;
+  }
   KArgs a{};
   a.x = x;
   a.row_stride = row_stride;

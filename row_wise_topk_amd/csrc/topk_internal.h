@@ -46,6 +46,55 @@ constexpr int wgs_per_cu(int c, int nt) {
 }
 inline int class_of_k(int k) { return k <= 256 ? 0 : k <= 1024 ? 1 : k <= 2048 ? 2 : 3; }
 
+// ---- chunk kernels (chunk_kernels.hip)
+// A chunk: kChunkLoads 16-byte loads per lane of a kChunkThreads-lane
+// workgroup, all in flight at once.
+constexpr int kChunkThreads = 256;
+constexpr int kChunkLoads = 8;
+constexpr int64_t chunk_elems(int dtype) { return int64_t{kChunkThreads} * kChunkLoads * (dtype == 0 ? 4 : 8); }
+// Candidate buffer: k plus room for the larger of k and 2048 more (one
+// vector per lane of bf16 is 2048 values; a merge round is 2048 slots).
+constexpr int chunk_cap(int c) { return class_kmax(c) + (class_kmax(c) > 2048 ? class_kmax(c) : 2048); }
+// Rows of at most this many chunks go to the chunk kernels by default.
+constexpr int64_t kChunkMaxPerRow = 64;
+// Below this many rows, a row is split into one workgroup per chunk.
+constexpr int64_t kChunkSplitBatch = 512;
+
+struct CArgs {
+  const void* x;
+  int64_t row_stride;     // elements
+  int32_t n_cols;
+  int32_t batch;
+  const int32_t* end;     // nullable
+  int32_t k;
+  int32_t sorted;
+  int32_t return_values;
+  int32_t idx64;
+  void* values;
+  void* indices;
+  int32_t* row_status;
+  int32_t segments;       // 1 (a whole row per workgroup) or the row's chunk count
+  uint32_t perm_seed;     // chunk visiting order of a whole row
+  int32_t in_order;
+  int32_t reverse_rows;   // segments == 1: workgroup g takes row batch-1-g
+  uint32_t cap_eff;       // candidate count that triggers a cut (<= chunk_cap)
+  // workspace (segments > 1)
+  uint32_t* ws_arrive;            // [batch] arrivals per row, zero at rest
+  unsigned long long* ws_rec;     // [batch * segments * 2] threshold, (status << 32) | count
+  unsigned long long* ws_slot;    // [batch * segments * k] candidate composites
+};
+
+struct ChunkWs {
+  size_t arrive, rec, slot, total;
+};
+ChunkWs chunk_ws_layout(int64_t batch, int segments, int k);
+
+// Queue the chunk kernel for k class `cls` and dtype (0 fp32, 1 bf16).
+// Returns the hipError_t of the launch.
+int launch_chunk(const CArgs& a, int dtype, int cls, hipStream_t stream);
+// Queue the read-ceiling kernel of the chunk kernels' access pattern.
+int launch_chunk_read(const CArgs& a, int dtype, uint32_t* sink, hipStream_t stream);
+
 struct KArgs {
   const void* x;
   int64_t row_stride;     // elements

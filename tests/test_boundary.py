@@ -93,6 +93,10 @@ ERR = {n: i for i, n in enumerate(rt.STATUS_NAMES)}
     ({"plan": {"flush_at": 100000}}, "DS_ERR_PLAN"),   # beyond the buffer's trigger
     ({"plan": {"flush_at": 11}}, "DS_OK"),
     ({"plan": {"segments": 1}}, "DS_OK"),
+    ({"plan": {"kernel": 3}}, "DS_ERR_PLAN"),
+    ({"plan": {"kernel": -1}}, "DS_ERR_PLAN"),
+    ({"plan": {"kernel": 1}}, "DS_OK"),
+    ({"plan": {"kernel": 2, "segments": 9}}, "DS_OK"),
 ])
 def test_validate_codes(kw, code):
     assert _v(**kw) == ERR[code]
@@ -109,12 +113,21 @@ def test_workspace_rules():
     assert _v(**base, workspace=A16w, workspace_bytes=need) == ERR["DS_OK"]
     # Many rows: one workgroup per row, no workspace.
     assert rt.ds_topk_workspace_size(rt.DS_BF16, 4096, 65536, 2048) == 0
-    # Explicit single-segment plan needs none; more segments need more.
-    one = {"segments": 1}
-    assert rt.ds_topk_workspace_size_ex(rt.DS_FP32, 64, 129280, 1024, one) == 0
-    s4 = rt.ds_topk_workspace_size_ex(rt.DS_FP32, 64, 129280, 1024, {"segments": 4})
-    s16 = rt.ds_topk_workspace_size_ex(rt.DS_FP32, 64, 129280, 1024, {"segments": 16})
+    # Explicit single-segment plan needs none; more segments need more (the
+    # stream kernel takes any count; the chunk kernels one per chunk).
+    for kern in (1, 2):
+        one = {"segments": 1, "kernel": kern}
+        assert rt.ds_topk_workspace_size_ex(rt.DS_FP32, 64, 129280, 1024, one) == 0
+    s4 = rt.ds_topk_workspace_size_ex(rt.DS_FP32, 64, 129280, 1024, {"segments": 4, "kernel": 1})
+    s16 = rt.ds_topk_workspace_size_ex(rt.DS_FP32, 64, 129280, 1024, {"segments": 16, "kernel": 1})
     assert 0 < s4 < s16
+    # The chunk kernels split a row into its 16 chunks: a fixed header of
+    # arrival counters, a record and k slots per chunk.
+    c = rt.ds_topk_workspace_size_ex(rt.DS_FP32, 64, 129280, 1024, {"kernel": 2, "segments": 2})
+    assert c == rt.ds_topk_workspace_size(rt.DS_FP32, 64, 129280, 1024)
+    assert c >= 64 * 16 * 1024 * 8
+    # A plan's kernel field is checked.
+    assert rt.ds_topk_workspace_size_ex(rt.DS_FP32, 64, 129280, 1024, {"kernel": 3}) == 0
     # Invalid arguments give 0.
     assert rt.ds_topk_workspace_size(rt.DS_FP32, 64, 129280, 0) == 0
     assert rt.ds_topk_workspace_size(9, 64, 129280, 10) == 0

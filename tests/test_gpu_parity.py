@@ -164,12 +164,14 @@ def test_ascending_and_descending_rows():
 
 
 # ---------------------------------------------------------------- plans: same answer
+@pytest.mark.parametrize("kernel", [1, 2])
 @pytest.mark.parametrize("plan", [
     {"segments": 1}, {"segments": 2}, {"segments": 3}, {"segments": 7}, {"segments": 16},
     {"segments": 64}, {"perm_seed": 1}, {"perm_seed": 0xDEADBEEF}, {"in_order": 1},
     {"in_order": 1, "segments": 5}, {"flush_at": 1100}, {"flush_at": 1030, "segments": 3},
 ])
-def test_plan_independence(plan):
+def test_plan_independence(plan, kernel):
+    plan = dict(plan, kernel=kernel)
     w = workloads.workload(2, batch=6)
     x, _ = workloads.make_input(w)
     check_case(x, w.dtype, w.n_cols, w.k, 1, True, "int64", plan=plan, name=f"plan {plan}")
@@ -188,7 +190,9 @@ def test_adversarial_plans_many_cuts():
     f = np.stack([asc + np.float32(1e-3) * rng.random(n, dtype=np.float32) for _ in range(2)])
     for plan in ({"in_order": 1}, {"in_order": 1, "flush_at": 4100}, {"segments": 32},
                  {"segments": 1, "flush_at": 4097}):
-        check_case(f, FP32, n, 4096, 1, plan=plan, name=f"ascending {plan}")
+        for kernel in (1, 2):
+            p = dict(plan, kernel=kernel)
+            check_case(f, FP32, n, 4096, 1, plan=p, name=f"ascending {p}")
 
 
 def test_repeat_determinism():
@@ -197,10 +201,10 @@ def test_repeat_determinism():
     w = workloads.workload(3, batch=16)
     x, _ = workloads.make_input(w)
     xt = to_device(x, w.dtype)
-    say("repeat determinism x50 (sorted=1 and sorted=0)")
+    say("repeat determinism x100 (sorted=1 and sorted=0)")
     first = gpu_topk(x, w.dtype, w.n_cols, w.k, 1, True, xt=xt)
     first0 = gpu_topk(x, w.dtype, w.n_cols, w.k, 0, False, xt=xt)
-    for _ in range(50):
+    for _ in range(100):
         again = gpu_topk(x, w.dtype, w.n_cols, w.k, 1, True, xt=xt)
         assert all(np.array_equal(a, b) for a, b in zip(first, again))
         again0 = gpu_topk(x, w.dtype, w.n_cols, w.k, 0, False, xt=xt)
@@ -216,8 +220,10 @@ def test_workspace_all_zero_after_every_call():
     from tests.gpu_util import to_device
     rng = np.random.Generator(np.random.PCG64(12))
     shapes = [(8, 129280, 1024, {}), (5, 50001, 1024, {}), (8, 131072, 512, {}),
-              (3, 9000, 7, {}), (2, 262144, 1, {}), (6, 129280, 1024, {"segments": 64}),
-              (1, 1 << 20, 4096, {}), (64, 20000, 300, {"segments": 3})]
+              (3, 9000, 7, {}), (2, 262144, 1, {}), (6, 129280, 1024, {"segments": 64, "kernel": 1}),
+              (1, 1 << 20, 4096, {}), (64, 20000, 300, {"segments": 3, "kernel": 1}),
+              (8, 129280, 1024, {"kernel": 1}), (6, 131072, 512, {"kernel": 2}),
+              (3, 200000, 2048, {"kernel": 2, "segments": 2}), (40, 70000, 64, {"kernel": 1})]
     for i, (batch, n, k, plan) in enumerate(shapes):
         dtype = BF16 if i % 2 else FP32
         step = 8 if dtype == BF16 else 4

@@ -44,10 +44,10 @@ def _blocky_rows(nblocks: int, big_every: int, seed: int, batch: int = 3) -> np.
 
 
 @pytest.mark.parametrize("plan", [
-    {"segments": 1, "in_order": 1},   # ring 0,1,2: big, small, small -> estimate rejected
-    {"segments": 2, "in_order": 1},   # one workgroup rejects, the other confirms
-    {"segments": 3, "in_order": 1},
-    {"segments": 1},                  # random order: either outcome
+    {"segments": 1, "in_order": 1, "kernel": 1},   # ring 0,1,2: big, small, small -> estimate rejected
+    {"segments": 2, "in_order": 1, "kernel": 1},   # one workgroup rejects, the other confirms
+    {"segments": 3, "in_order": 1, "kernel": 1},
+    {"segments": 1, "kernel": 1},                  # random order: either outcome
 ])
 @pytest.mark.parametrize("k", [1024, 2048])
 def test_start_estimate_rejected_or_confirmed_fp32(plan, k):
@@ -56,7 +56,7 @@ def test_start_estimate_rejected_or_confirmed_fp32(plan, k):
                name=f"blocky fp32 k={k} {plan}")
 
 
-@pytest.mark.parametrize("plan", [{"segments": 1, "in_order": 1}, {"segments": 2, "in_order": 1}])
+@pytest.mark.parametrize("plan", [{"segments": 1, "in_order": 1, "kernel": 1}, {"segments": 2, "in_order": 1, "kernel": 1}])
 def test_start_estimate_rejected_bf16(plan):
     x = workloads.to_bf16_bits(_blocky_rows(12, 3, seed=41))
     check_case(x, BF16, x.shape[1], 512, 0, False, "int32", plan=plan,
@@ -82,7 +82,7 @@ def _hot_blocks(nblocks: int, hot, seed: int, batch: int = 3) -> np.ndarray:
 @pytest.mark.parametrize("k", [512, 1024])
 def test_start_estimate_fails_merge_check_fp32(segments, k):
     x = _hot_blocks(32, (0, segments, 2 * segments), seed=53 + segments + k)
-    plan = {"segments": segments, "in_order": 1}
+    plan = {"segments": segments, "in_order": 1, "kernel": 1}
     check_case(x, FP32, x.shape[1], k, 1, True, "int64", plan=plan,
                name=f"hot ring fp32 k={k} S={segments}")
     check_case(x, FP32, x.shape[1], k, 0, False, "int32", plan=plan,
@@ -95,7 +95,7 @@ def test_start_estimate_fails_merge_check_ragged_and_end():
     """The row read again ends in a partial block (n_cols and end)."""
     x = _hot_blocks(32, (0, 8, 16), seed=59)
     n = x.shape[1] - 1000
-    plan = {"segments": 8, "in_order": 1}
+    plan = {"segments": 8, "in_order": 1, "kernel": 1}
     check_case(x[:, :n].copy(), FP32, n, 1024, 1, True, "int32", plan=plan,
                name="hot ring fp32 ragged")
     end = np.array([n, x.shape[1], x.shape[1] - 4096 - 7], dtype=np.int32)
@@ -111,7 +111,7 @@ def test_start_estimate_fails_merge_check_bf16():
     for b in (0, 4, 8):
         x[:, b * B:(b + 1) * B] = np.float32(1.0) + rng.random((3, B), dtype=np.float32)
     x = workloads.to_bf16_bits(x)
-    plan = {"segments": 4, "in_order": 1}
+    plan = {"segments": 4, "in_order": 1, "kernel": 1}
     check_case(x, BF16, x.shape[1], 512, 0, False, "int32", plan=plan,
                name="hot ring bf16 k=512")
     check_case(x, BF16, x.shape[1], 512, 1, True, "int32", plan=plan,
@@ -125,7 +125,7 @@ def test_start_estimate_fails_merge_check_bf16():
 @pytest.mark.parametrize("k", [1024, 2048])
 def test_start_estimate_fails_final_count_one_workgroup(k):
     x = _hot_blocks(16, (0, 1, 2), seed=71 + k)
-    plan = {"segments": 1, "in_order": 1}
+    plan = {"segments": 1, "in_order": 1, "kernel": 1}
     check_case(x, FP32, x.shape[1], k, 1, True, "int32", plan=plan,
                name=f"hot ring one wg fp32 k={k}")
     check_case(x, FP32, x.shape[1], k, 0, False, "int64", plan=plan,
@@ -141,7 +141,7 @@ def test_start_estimate_fails_final_count_one_workgroup_bf16():
     for b in (0, 1, 2):
         x[:, b * B:(b + 1) * B] = np.float32(1.0) + rng.random((3, B), dtype=np.float32)
     x = workloads.to_bf16_bits(x)
-    plan = {"segments": 1, "in_order": 1}
+    plan = {"segments": 1, "in_order": 1, "kernel": 1}
     check_case(x, BF16, x.shape[1], 2048, 1, True, "int32", plan=plan,
                name="hot ring one wg bf16 k=2048")
     check_case(x, BF16, x.shape[1], 1024, 2, False, "int32", plan=plan,
@@ -156,7 +156,7 @@ def test_start_estimate_refused_by_ring(dtype):
     x = _hot_blocks(32, (0,), seed=67)
     if dtype == BF16:
         x = workloads.to_bf16_bits(x)
-    plan = {"segments": 8, "in_order": 1}
+    plan = {"segments": 8, "in_order": 1, "kernel": 1}
     check_case(x, dtype, x.shape[1], 1024, 1, True, "int32", plan=plan,
                name=f"hot block 0 {'bf16' if dtype else 'fp32'}")
 
@@ -171,12 +171,12 @@ def test_three_block_start_large_k(k, dtype, segments):
     rng = np.random.Generator(np.random.PCG64(k + segments))
     f = rng.standard_normal((3, 16 * B)).astype(np.float32)
     x = workloads.to_bf16_bits(f) if dtype == BF16 else f
-    plan = {"segments": segments}
+    plan = {"segments": segments, "kernel": 1}
     check_case(x, dtype, 16 * B, k, 1, True, "int32", plan=plan,
                name=f"three-block start k={k} S={segments}")
     h = _hot_blocks(16, (0, segments, 2 * segments), seed=k)
     h = workloads.to_bf16_bits(h) if dtype == BF16 else h
-    check_case(h, dtype, 16 * B, k, 0, False, "int32", plan={"segments": segments, "in_order": 1},
+    check_case(h, dtype, 16 * B, k, 0, False, "int32", plan={"segments": segments, "in_order": 1, "kernel": 1},
                name=f"three-block start, large ring k={k} S={segments}")
 
 
@@ -196,9 +196,9 @@ def _levels_bf16(batch: int, n: int, levels: int, seed: int) -> np.ndarray:
 @pytest.mark.parametrize("segments", [1, 4])
 def test_sort_with_tie_groups(levels, k, segments):
     x = _levels_bf16(4, 65536, levels, seed=levels + k)
-    check_case(x, BF16, 65536, k, 1, True, "int32", plan={"segments": segments},
+    check_case(x, BF16, 65536, k, 1, True, "int32", plan={"segments": segments, "kernel": 1},
                name=f"ties levels={levels} k={k} S={segments}")
-    check_case(x, BF16, 65536, k, 2, False, "int32", plan={"segments": segments},
+    check_case(x, BF16, 65536, k, 2, False, "int32", plan={"segments": segments, "kernel": 1},
                name=f"ties by column levels={levels} k={k} S={segments}")
 
 
@@ -213,7 +213,7 @@ def test_sort_with_tie_groups(levels, k, segments):
 def test_merge_small_cut(segments, k):
     rng = np.random.Generator(np.random.PCG64(101 + k + segments))
     f = rng.standard_normal((4, 16 * B)).astype(np.float32)
-    plan = {"segments": segments}
+    plan = {"segments": segments, "kernel": 1}
     check_case(f, FP32, 16 * B, k, 0, True, "int32", plan=plan,
                name=f"small cut fp32 k={k} S={segments}")
     check_case(workloads.to_bf16_bits(f), BF16, 16 * B, k, 0, True, "int32", plan=plan,
@@ -242,7 +242,7 @@ def test_local_bin_edge_threshold(sorted_mode, dtype):
     for b in (5, 9, 13):
         f[:, b * B:(b + 1) * B] += np.float32(0.5)
     x = workloads.to_bf16_bits(f) if dtype == BF16 else f
-    plan = {"segments": 4, "in_order": 1}
+    plan = {"segments": 4, "in_order": 1, "kernel": 1}
     check_case(x, dtype, 16 * B, 512, sorted_mode, True, "int32", plan=plan,
                name=f"local bin edge {'bf16' if dtype else 'fp32'} sorted={sorted_mode}")
     levels = _levels_bf16(4, 16 * B, 256, seed=7 + sorted_mode)
@@ -266,5 +266,5 @@ def test_start_on_signed_zeros(segments, sorted_mode, dtype):
     f[rng.random((3, n)) < 0.01] = -np.inf
     x = workloads.to_bf16_bits(f) if dtype == BF16 else f
     for k in (256, 1024, 2048):
-        check_case(x, dtype, n, k, sorted_mode, True, "int32", plan={"segments": segments},
+        check_case(x, dtype, n, k, sorted_mode, True, "int32", plan={"segments": segments, "kernel": 1},
                    name=f"signed zeros k={k} S={segments} sorted={sorted_mode}")
