@@ -61,6 +61,8 @@ def _parse():
     p.add_argument("--no-torch", action="store_true", help="skip the torch.topk context timing")
     p.add_argument("--segments", type=int, default=0,
                    help="workgroups per row (0 = the library's automatic plan)")
+    p.add_argument("--kernel", type=int, default=0,
+                   help="0 automatic, 1 the streaming kernel, 2 the chunk kernels")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="run a plain elementwise copy of known size before the TopK calls")
     p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -186,7 +188,8 @@ def main():
     status = torch.empty((w.batch,), dtype=torch.int32, device=dev)
     out = (values, indices, status)
 
-    plan = rt.Plan(segments=args.segments) if args.segments else None
+    plan = (rt.Plan(segments=args.segments, perm_seed=0x5EED, kernel=args.kernel)
+            if (args.segments or args.kernel) else None)
 
     def call(i):
         rt.topk(views[i % n_copies], w.k, end=end_t, sorted=w.sorted,

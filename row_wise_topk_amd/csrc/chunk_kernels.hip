@@ -156,17 +156,6 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
 }
 __device__ __forceinline__ uint32_t bit_length64(u64 v) { return v ? 64u - __clzll(v) : 0u; }
 
-// Value of lane (lane ^ X), 64 bits, through the LDS crossbar.
-template <int X>
-__device__ __forceinline__ u64 xor_lane64(u64 v) {
-  const int addr = static_cast<int>((lane_id() ^ X) << 2);
-  const uint32_t lo = static_cast<uint32_t>(
-      __builtin_amdgcn_ds_bpermute(addr, static_cast<int>(static_cast<uint32_t>(v))));
-  const uint32_t hi = static_cast<uint32_t>(
-      __builtin_amdgcn_ds_bpermute(addr, static_cast<int>(static_cast<uint32_t>(v >> 32))));
-  return (static_cast<u64>(hi) << 32) | lo;
-}
-
 // Relaxed agent-scope accesses to the workspace: coherent across the XCDs'
 // L2 caches; the ordering comes from the release / acquire on the row's
 // arrival counter.
@@ -177,6 +166,13 @@ __device__ __forceinline__ void st_agent(W* p, W v) {
 template <typename W>
 __device__ __forceinline__ W ld_agent(const W* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wait until every memory access this wave has issued is complete.
+__device__ __forceinline__ void wait_all_memory() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
 // ---------------------------------------------------------------- LDS
@@ -192,6 +188,7 @@ struct Smem {
   u64 wred2[NW];
   uint32_t res[4];
   uint32_t side_n;
+  uint32_t cnt_out;
   uint32_t err;
   uint32_t is_last;
   u64 res64;
@@ -424,6 +421,23 @@ __device__ __forceinline__ u64 start_threshold(Smem<CAP>& sm, const u32x4 (&r)[V
 }
 
 // ---------------------------------------------------------------- the cut
+// f(value, valid) over buf[0, n): each lane reads its G slots of a group
+// (slot q of lane t is j0 + q*NT + t) back to back before using any.
+template <int G, int CAP, typename F>
+__device__ __forceinline__ void for_buf(const Smem<CAP>& sm, uint32_t n, F&& f) {
+  const uint32_t t = threadIdx.x;
+  for (uint32_t j0 = 0; j0 < n; j0 += G * NT) {
+    u64 v[G];
+#pragma unroll
+    for (int q = 0; q < G; ++q) {
+      const uint32_t j = j0 + q * NT + t;
+      v[q] = sm.buf[j < n ? j : 0u];
+    }
+#pragma unroll
+    for (int q = 0; q < G; ++q) f(v[q], j0 + q * NT + t < n);
+  }
+}
+
 // Keep exactly the `keep` largest of the n composites in buf (keep < n),
 // compacting them to buf[0, keep).  Returns the new threshold, the keep-th
 // largest composite.  An MSD radix select over the live composite range:
@@ -437,11 +451,12 @@ __device__ __noinline__ u64 cut_exact(Smem<CAP>& sm, uint32_t n, uint32_t keep) 
   const int t = threadIdx.x;
   // Live range of the composites.
   u64 lo = ~0ull, hi = 0;
-  for (uint32_t j = t; j < n; j += NT) {
-    const u64 v = sm.buf[j];
-    lo = v < lo ? v : lo;
-    hi = v > hi ? v : hi;
-  }
+  for_buf<8>(sm, n, [&](u64 v, bool ok) {
+    if (ok) {
+      lo = v < lo ? v : lo;
+      hi = v > hi ? v : hi;
+    }
+  });
   {
     const uint32_t a = wave_min_u32(static_cast<uint32_t>(lo >> 32));
     const uint32_t b = wave_max_u32(static_cast<uint32_t>(hi >> 32));
@@ -473,11 +488,10 @@ __device__ __noinline__ u64 cut_exact(Smem<CAP>& sm, uint32_t n, uint32_t keep) 
     const uint32_t bl = bit_length64(span);
     const uint32_t shift = bl > kCutBits ? bl - kCutBits : 0u;
     // Bin 0 holds the largest composites.
-    for (uint32_t j = t; j < n; j += NT) {
-      const u64 v = sm.buf[j];
-      if (v >= lo && v <= hi)
+    for_buf<8>(sm, n, [&](u64 v, bool ok) {
+      if (ok && v >= lo && v <= hi)
         atomicAdd(&sm.hist[(kCutBins - 1) - static_cast<uint32_t>((v - lo) >> shift)], 1u);
-    }
+    });
     __syncthreads();
     uint32_t h[kCutBPT];
 #pragma unroll
@@ -523,10 +537,15 @@ __device__ __noinline__ u64 cut_exact(Smem<CAP>& sm, uint32_t n, uint32_t keep) 
         if (t == 0) sm.err = 1u;
         return 0;
       }
-      if (t < 64) {
+      if (t < 64) {   // wave 0: one member per lane, the others read by readlane
         const u64 mine = static_cast<uint32_t>(t) < ns ? sm.side[t] : 0ull;
+        const uint32_t mlo = static_cast<uint32_t>(mine), mhi = static_cast<uint32_t>(mine >> 32);
         uint32_t above = 0;
-        for (uint32_t j = 0; j < ns; ++j) above += sm.side[j] > mine ? 1u : 0u;
+        for (uint32_t j = 0; j < ns; ++j) {
+          const uint32_t olo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(mlo), static_cast<int>(j)));
+          const uint32_t ohi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(mhi), static_cast<int>(j)));
+          above += ((static_cast<u64>(ohi) << 32) | olo) > mine ? 1u : 0u;
+        }
         if (static_cast<uint32_t>(t) < ns && above + 1u == need) sm.res64 = mine;
       }
       __syncthreads();
@@ -630,14 +649,13 @@ __device__ __forceinline__ void append_chunk(Smem<CAP>& sm, Buf& B, const u32x4 
   }
 }
 
-// The first chunk of a workgroup: NaN check, start threshold, append.  With
-// `exact`, the chunk is a whole row and T is a valid start (at least
+// The first chunk of a workgroup: NaN check and start threshold (into B.T).
+// With `exact`, the chunk is a whole row and T is a valid start (at least
 // min(k, L) values pass); otherwise T is an estimate of the row's k-th value
 // for this chunk's share.  Returns whether a NaN was found.
 template <bool BF16, int CAP>
-__device__ __forceinline__ bool first_chunk(Smem<CAP>& sm, Buf& B, u32x4 (&r)[V], uint32_t c,
-                                            uint32_t L, uint32_t k, uint32_t cap, bool exact,
-                                            bool* spec) {
+__device__ __forceinline__ bool start_chunk(Smem<CAP>& sm, Buf& B, u32x4 (&r)[V], uint32_t c,
+                                            uint32_t L, uint32_t k, bool exact, bool* spec) {
   using G = Geo<BF16>;
   const int t = threadIdx.x;
   bool nan = false;
@@ -673,8 +691,32 @@ __device__ __forceinline__ bool first_chunk(Smem<CAP>& sm, Buf& B, u32x4 (&r)[V]
   }
   *spec = !exact && m < k && T != kTAll;
   B.T = T;
-  append_chunk<BF16>(sm, B, r, c, k, cap);
   return nan;
+}
+
+// Write the wave's values >= f of a chunk to its own region of buf (R slots
+// from w*R) as raw pairs (bits << 32) | column, in slot-major order, with no
+// count first: a slot no lane keeps costs one compare.  Returns the wave's
+// count (uniform), which exceeds R when the region overflowed (then it holds
+// only the first R).
+template <bool BF16, int CAP>
+__device__ __forceinline__ uint32_t region_write(Smem<CAP>& sm, const u32x4 (&r)[V], uint32_t c,
+                                                 float f, uint32_t R) {
+  u64* reg = sm.buf + (threadIdx.x >> 6) * R;
+  uint32_t pos = 0;
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    for_values<BF16>(r[i], [&](uint32_t b, int q) {
+      const bool ok = __uint_as_float(b) >= f;
+      const u64 m = ballot(ok);
+      if (m) {
+        const uint32_t p = pos + mbcnt64(m);
+        if (ok && p < R) reg[p] = (static_cast<u64>(b) << 32) | col_at<BF16>(c, i, q);
+        pos += static_cast<uint32_t>(__popcll(m));
+      }
+    });
+  }
+  return pos;
 }
 
 // A later chunk of a whole row.
@@ -714,74 +756,150 @@ __device__ __noinline__ Buf restream(Smem<CAP>& sm, int par, const char* xrow, u
   return B;
 }
 
+// Chunk c appended again, contiguously, from its bytes in memory, starting
+// from B (its threshold kept): the rare path of a split row's chunk whose
+// candidates overflowed their per-wave regions.  Out of line, so that no
+// register of the first pass has to live across it.
+template <bool BF16, int CAP>
+__device__ __noinline__ Buf reappend_chunk(Smem<CAP>& sm, Buf B, const char* xrow, uint32_t c,
+                                           uint32_t L, uint32_t k, uint32_t cap) {
+  using G = Geo<BF16>;
+  u32x4 r[V];
+  load_chunk<BF16>(r, xrow, c, L);
+  if ((c + 1) * G::CE > L) sanitize_ragged<BF16>(r, c, L);
+  __syncthreads();
+  B.count = 0;
+  append_chunk<BF16>(sm, B, r, c, k, cap);
+  return B;
+}
+
 // ---------------------------------------------------------------- the sort
-// Bitonic sort, descending, of PER*NT 64-bit keys; lane t holds elements
-// t*PER .. t*PER+PER-1.  Strides below PER are in registers, strides up to
-// 32*PER cross lanes by ds_bpermute, larger strides cross waves through
-// `xch` (PER*NT entries of LDS).
-template <int PER, int S>
-__device__ __forceinline__ void bitonic_in_lane(u64 (&v)[PER], uint32_t size) {
+// Value of lane (lane ^ X), on the VALU: DPP quad permutes for 1 and 2, row
+// shifts for 4 and 8 (each half of a 8- or 16-lane group reads the other
+// half), and the gfx950 permlane swaps for 16 and 32 (which pair up rows and
+// halves of the wave).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_mov(uint32_t v) {
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, false));
+}
+template <int X>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
+  const uint32_t lane = lane_id();
+  if constexpr (X == 1) {
+    return dpp_mov<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+  } else if constexpr (X == 2) {
+    return dpp_mov<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+  } else if constexpr (X == 4) {
+    const uint32_t up = dpp_mov<0x104>(v), down = dpp_mov<0x114>(v);   // row_shl:4, row_shr:4
+    return (lane & 4u) ? down : up;
+  } else if constexpr (X == 8) {
+    const uint32_t up = dpp_mov<0x108>(v), down = dpp_mov<0x118>(v);   // row_shl:8, row_shr:8
+    return (lane & 8u) ? down : up;
+  } else if constexpr (X == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return (lane & 16u) ? r[0] : r[1];
+  } else {
+    static_assert(X == 32, "lane distance");
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (lane & 32u) ? r[0] : r[1];
+  }
+}
+template <int X>
+__device__ __forceinline__ u64 xor_lane(u64 v) {
+  return (static_cast<u64>(xor_lane<X>(static_cast<uint32_t>(v >> 32))) << 32) |
+         xor_lane<X>(static_cast<uint32_t>(v));
+}
+
+// Bitonic sort, descending, of PER*NT keys (32- or 64-bit); lane t holds
+// elements t*PER .. t*PER+PER-1.  Before the merge of blocks of `size`, the
+// keys of every block that must come out ascending are complemented, so each
+// compare-exchange of the merge puts the larger key at the lower position;
+// the next merge's complement pattern replaces this one, and the last merge
+// (one block) complements nothing.  Strides below PER stay in registers,
+// strides up to 32*PER cross lanes on the VALU, larger strides cross waves
+// through `xch` (PER*NT keys of LDS).
+// The larger (keep_max) or the smaller of v and o.  For 64-bit keys one
+// compare serves both choices.
+__device__ __forceinline__ uint32_t pick(uint32_t v, uint32_t o, bool keep_max) {
+  return keep_max ? max(v, o) : min(v, o);
+}
+__device__ __forceinline__ u64 pick(u64 v, u64 o, bool keep_max) {
+  return ((v > o) == keep_max) ? v : o;
+}
+
+template <int PER, int S, typename K>
+__device__ __forceinline__ void bitonic_in_lane(K (&v)[PER]) {
+  K a[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) a[i] = v[i];
+#pragma unroll
+  for (int i = 0; i < PER; ++i)
+    if ((i | S) < PER) v[i] = pick(a[i], a[i ^ S], (i & S) == 0);
+}
+// The stage's exchanges first, then its compares: the PER independent chains
+// interleave instead of waiting on one another.
+template <int PER, int X, typename K>
+__device__ __forceinline__ void bitonic_cross_lane(K (&v)[PER]) {
+  const bool lower = (lane_id() & X) == 0;
+  K o[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) o[i] = xor_lane<X>(v[i]);
+#pragma unroll
+  for (int i = 0; i < PER; ++i) v[i] = pick(v[i], o[i], lower);
+}
+// One stage of the merge of blocks of SIZE: compare-exchange at distance
+// STRIDE, then the next stage down to distance 1 (all resolved at compile
+// time, so every stage is straight-line code).
+template <typename K, int PER, int SIZE, int STRIDE>
+__device__ __forceinline__ void bitonic_stage(K (&v)[PER], K* xch) {
+  if constexpr (STRIDE < PER) {
+    bitonic_in_lane<PER, STRIDE>(v);
+  } else if constexpr (STRIDE < 64 * PER) {
+    bitonic_cross_lane<PER, STRIDE / PER>(v);
+  } else {
+    const uint32_t t = threadIdx.x;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < PER; ++i) xch[t * PER + i] = v[i];
+    __syncthreads();
+    K o[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) o[i] = xch[(t * PER + i) ^ STRIDE];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) v[i] = pick(v[i], o[i], ((t * PER + i) & STRIDE) == 0);
+  }
+  if constexpr (STRIDE > 1) bitonic_stage<K, PER, SIZE, STRIDE / 2>(v, xch);
+}
+
+// The merges of blocks of SIZE, 2*SIZE, ... N.  Before the merge of blocks of
+// SIZE, the keys of every block that must come out ascending (element e with
+// e & SIZE set) are complemented, so each compare-exchange of the merge puts
+// the larger key at the lower position; the pattern of the previous merge
+// (e & SIZE/2) is undone in the same step.  The last merge (one block)
+// complements nothing.
+template <typename K, int PER, int SIZE>
+__device__ __forceinline__ void bitonic_merges(K (&v)[PER], K* xch) {
+  constexpr int N = PER * NT;
   const uint32_t t = threadIdx.x;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    const int j = i ^ S;
-    if (j > i && j < PER) {
-      const bool desc = ((t * PER + i) & size) == 0;
-      const u64 a = v[i], b = v[j];
-      const bool sw = desc ? (a < b) : (a > b);
-      v[i] = sw ? b : a;
-      v[j] = sw ? a : b;
-    }
+    const uint32_t e = t * PER + i;
+    const bool was = SIZE > 2 && (e & (SIZE / 2)) != 0;
+    const bool now = SIZE < N && (e & SIZE) != 0;
+    if (was != now) v[i] = ~v[i];
   }
+  bitonic_stage<K, PER, SIZE, SIZE / 2>(v, xch);
+  if constexpr (SIZE < N) bitonic_merges<K, PER, SIZE * 2>(v, xch);
 }
 
-template <int PER>
-__device__ __forceinline__ void bitonic_sort_desc(u64 (&v)[PER], u64* xch) {
-  constexpr uint32_t N = PER * NT;
-  const uint32_t t = threadIdx.x;
-  for (uint32_t size = 2; size <= N; size <<= 1) {
-    for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
-      if (stride < PER) {
-        if (stride == 1) bitonic_in_lane<PER, 1>(v, size);
-        else if (stride == 2) bitonic_in_lane<PER, 2>(v, size);
-        else if (stride == 4) bitonic_in_lane<PER, 4>(v, size);
-        else bitonic_in_lane<PER, 8>(v, size);
-      } else if (stride < 64 * PER) {
-        const uint32_t lx = stride / PER;
-        const bool lower = (t & lx) == 0;
-        const int addr = static_cast<int>((lane_id() ^ lx) << 2);
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-          const uint32_t olo = static_cast<uint32_t>(
-              __builtin_amdgcn_ds_bpermute(addr, static_cast<int>(static_cast<uint32_t>(v[i]))));
-          const uint32_t ohi = static_cast<uint32_t>(
-              __builtin_amdgcn_ds_bpermute(addr, static_cast<int>(static_cast<uint32_t>(v[i] >> 32))));
-          const u64 o = (static_cast<u64>(ohi) << 32) | olo;
-          const bool desc = ((t * PER + i) & size) == 0;
-          const bool keep_max = lower == desc;
-          const u64 mx = v[i] > o ? v[i] : o;
-          const u64 mn = v[i] > o ? o : v[i];
-          v[i] = keep_max ? mx : mn;
-        }
-      } else {
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < PER; ++i) xch[t * PER + i] = v[i];
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-          const uint32_t e = t * PER + i;
-          const u64 o = xch[e ^ stride];
-          const bool lower = (e & stride) == 0;
-          const bool desc = (e & size) == 0;
-          const bool keep_max = lower == desc;
-          const u64 mx = v[i] > o ? v[i] : o;
-          const u64 mn = v[i] > o ? o : v[i];
-          v[i] = keep_max ? mx : mn;
-        }
-      }
-    }
-  }
+// Bitonic sort, descending, of PER*NT keys (32- or 64-bit); lane t holds
+// elements t*PER .. t*PER+PER-1.  Strides below PER stay in registers,
+// strides up to 32*PER cross lanes on the VALU, larger strides cross waves
+// through `xch` (PER*NT keys of LDS).
+template <typename K, int PER>
+__device__ __forceinline__ void sort_desc(K (&v)[PER], K* xch) {
+  bitonic_merges<K, PER, 2>(v, xch);
   __syncthreads();
 }
 
@@ -814,6 +932,288 @@ __device__ __forceinline__ void store_one(const CArgs& a, bool bf16, const char*
   }
 }
 
+// Sort keys of a composite: by value the composite itself, by column
+// (~column << 32) | key; with 32-bit keys (bf16 values, columns below 2^16)
+// the top 16 bits of the key and the low 16 of ~column.
+template <typename K>
+__device__ __forceinline__ K sort_key(u64 c, bool by_col) {
+  if constexpr (sizeof(K) == 8) {
+    return by_col ? ((static_cast<u64>(static_cast<uint32_t>(c)) << 32) | key_of(c)) : c;
+  } else {
+    const uint32_t hi = key_of(c) >> 16, lo = static_cast<uint32_t>(c) & 0xFFFFu;
+    return by_col ? ((lo << 16) | hi) : ((hi << 16) | lo);
+  }
+}
+template <typename K>
+__device__ __forceinline__ u64 comp_of_sort_key(K s, bool by_col) {
+  if constexpr (sizeof(K) == 8) {
+    return by_col ? ((static_cast<u64>(static_cast<uint32_t>(s)) << 32) | static_cast<uint32_t>(s >> 32)) : s;
+  } else {
+    const uint32_t hi = by_col ? (s & 0xFFFFu) : (s >> 16);
+    const uint32_t lo = by_col ? (s >> 16) : (s & 0xFFFFu);
+    return (static_cast<u64>(hi << 16) << 32) | (0xFFFF0000u | lo);
+  }
+}
+
+template <typename K, int PER, int CAP>
+__device__ __forceinline__ void sort_and_store(Smem<CAP>& sm, const CArgs& a, bool bf16,
+                                               const char* xrow, int64_t out0, uint32_t m,
+                                               uint32_t status) {
+  const uint32_t t = threadIdx.x;
+  const uint32_t k = static_cast<uint32_t>(a.k);
+  const bool by_col = a.sorted == 2;
+  K v[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const uint32_t e = t * PER + i;
+    v[i] = e < m ? sort_key<K>(sm.buf[e], by_col) : K(0);
+  }
+  sort_desc<K, PER>(v, reinterpret_cast<K*>(sm.buf));
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const uint32_t e = t * PER + i;
+    if (e < k) store_one(a, bf16, xrow, out0 + e, comp_of_sort_key<K>(v[i], by_col), e < m, status);
+  }
+}
+
+// Rank selection: the exact output position of every candidate, without a
+// cut or a sort.  One 2048-bin histogram over the candidates' composite range
+// [lo, hi] (bin 0 the largest) gives each bin its first position; the
+// candidates are scattered into their bins, and each one's rank is its bin's
+// first position plus the number of its bin-mates above it.  A candidate of
+// rank below m is stored at output position `rank` (value order), the rest are
+// dropped.  Returns false, having stored nothing, when a bin holds more than
+// kBinRankMax candidates (long runs of equal values); the caller then cuts and
+// sorts.  Needs n <= RPT * NT.
+constexpr uint32_t kBinRankMax = 128;
+constexpr int kRankPerLane = 16;
+
+template <int CAP>
+__device__ __forceinline__ bool rank_store(Smem<CAP>& sm, const CArgs& a, bool bf16,
+                                           const char* xrow, int64_t out0, uint32_t n, uint32_t m,
+                                           uint32_t status) {
+  constexpr int RPT = kRankPerLane;
+  const uint32_t t = threadIdx.x;
+  u64 v[RPT];
+  u64 lo = ~0ull, hi = 0;
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const uint32_t j = i * NT + t;
+    v[i] = sm.buf[j < n ? j : 0u];
+    if (j < n) {
+      lo = v[i] < lo ? v[i] : lo;
+      hi = v[i] > hi ? v[i] : hi;
+    }
+  }
+  {
+    const uint32_t a0 = wave_min_u32(static_cast<uint32_t>(lo >> 32));
+    const uint32_t b0 = wave_max_u32(static_cast<uint32_t>(hi >> 32));
+    const uint32_t al = wave_min_u32(static_cast<uint32_t>(lo >> 32) == a0 ? static_cast<uint32_t>(lo) : 0xFFFFFFFFu);
+    const uint32_t bl = wave_max_u32(static_cast<uint32_t>(hi >> 32) == b0 ? static_cast<uint32_t>(hi) : 0u);
+    if (lane_id() == 0) {
+      sm.wred[t >> 6] = (static_cast<u64>(a0) << 32) | al;
+      sm.wred2[t >> 6] = (static_cast<u64>(b0) << 32) | bl;
+    }
+    __syncthreads();
+    u64 l2 = ~0ull, h2 = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      l2 = sm.wred[w] < l2 ? sm.wred[w] : l2;
+      h2 = sm.wred2[w] > h2 ? sm.wred2[w] : h2;
+    }
+    lo = uniform64(l2);
+    hi = uniform64(h2);
+  }
+  const uint32_t bl = bit_length64(hi - lo);
+  const uint32_t shift = bl > kCutBits ? bl - kCutBits : 0u;
+  auto bin_of = [&](u64 x) { return (kCutBins - 1) - static_cast<uint32_t>((x - lo) >> shift); };
+#pragma unroll
+  for (int i = 0; i < RPT; ++i)
+    if (i * NT + t < n) atomicAdd(&sm.hist[bin_of(v[i])], 1u);
+  __syncthreads();
+  // Own bins: the largest, then each bin's first position.
+  uint32_t h[kCutBPT], sum = 0, big = 0;
+#pragma unroll
+  for (int i = 0; i < kCutBPT; ++i) {
+    h[i] = sm.hist[t * kCutBPT + i];
+    sum += h[i];
+    big = max(big, h[i]);
+  }
+  big = wave_max_u32(big);
+  if (lane_id() == 0) sm.wmax[t >> 6] = big;
+  uint32_t total;
+  uint32_t run = block_excl(sm, sum, 0, &total);   // its barrier also publishes wmax
+#pragma unroll
+  for (int w = 0; w < NW; ++w) big = max(big, sm.wmax[w]);
+  if (uniform(big) > kBinRankMax) {
+#pragma unroll
+    for (int i = 0; i < kCutBPT; ++i) sm.hist[t * kCutBPT + i] = 0u;
+    __syncthreads();
+    return false;
+  }
+#pragma unroll
+  for (int i = 0; i < kCutBPT; ++i) {
+    sm.hist[t * kCutBPT + i] = run;
+    run += h[i];
+  }
+  __syncthreads();
+  // Scatter: afterwards hist[b] is the end of bin b, and bin b starts where
+  // bin b-1 ends (bin 0 at 0).
+#pragma unroll
+  for (int i = 0; i < RPT; ++i)
+    if (i * NT + t < n) sm.buf[atomicAdd(&sm.hist[bin_of(v[i])], 1u)] = v[i];
+  __syncthreads();
+  // Rank within the bin, by position (the lanes of a wave mostly share a
+  // bin, so its members are read as broadcasts).  Every position's value and
+  // bin bounds are read in one batch; a bin of one member needs no loop.
+  {
+    u64 x[RPT];
+    uint32_t st[RPT], en[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const uint32_t p = i * NT + t;
+      x[i] = sm.buf[p < n ? p : 0u];
+    }
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const uint32_t b = bin_of(x[i]);
+      st[i] = b ? sm.hist[b - 1] : 0u;
+      en[i] = sm.hist[b];
+    }
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const uint32_t p = i * NT + t;
+      if (p >= n) continue;
+      uint32_t r = st[i];
+      if (en[i] - st[i] > 1u) {
+        for (uint32_t q0 = st[i]; q0 < en[i]; q0 += 8) {   // eight reads in flight
+          u64 y[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) y[j] = sm.buf[q0 + j < en[i] ? q0 + j : st[i]];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) r += (q0 + j < en[i] && y[j] > x[i]) ? 1u : 0u;
+        }
+      }
+      if (r < m) store_one(a, bf16, xrow, out0 + r, x[i], true, status);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kCutBPT; ++i) sm.hist[t * kCutBPT + i] = 0u;
+  return true;
+}
+
+// Selection without order (unsorted output): the m largest of buf[0, n)
+// stored in any order.  The candidates stay in registers; one 2048-bin
+// histogram over their composite range finds the boundary bin, whose members
+// (at most kRankMax, else false is returned with nothing stored) are ranked
+// by one wave; every candidate at or above the m-th is stored at a position
+// taken from a per-wave counter.  Needs n <= kRankPerLane * NT.
+template <int CAP>
+__device__ __forceinline__ bool select_store(Smem<CAP>& sm, const CArgs& a, bool bf16,
+                                             const char* xrow, int64_t out0, uint32_t n, uint32_t m,
+                                             uint32_t status) {
+  constexpr int RPT = kRankPerLane;
+  const uint32_t t = threadIdx.x;
+  u64 v[RPT];
+  u64 lo = ~0ull, hi = 0;
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const uint32_t j = i * NT + t;
+    v[i] = j < n ? sm.buf[j] : 0ull;   // 0: below every candidate
+    if (j < n) {
+      lo = v[i] < lo ? v[i] : lo;
+      hi = v[i] > hi ? v[i] : hi;
+    }
+  }
+  {
+    const uint32_t a0 = wave_min_u32(static_cast<uint32_t>(lo >> 32));
+    const uint32_t b0 = wave_max_u32(static_cast<uint32_t>(hi >> 32));
+    const uint32_t al = wave_min_u32(static_cast<uint32_t>(lo >> 32) == a0 ? static_cast<uint32_t>(lo) : 0xFFFFFFFFu);
+    const uint32_t bl = wave_max_u32(static_cast<uint32_t>(hi >> 32) == b0 ? static_cast<uint32_t>(hi) : 0u);
+    if (lane_id() == 0) {
+      sm.wred[t >> 6] = (static_cast<u64>(a0) << 32) | al;
+      sm.wred2[t >> 6] = (static_cast<u64>(b0) << 32) | bl;
+    }
+    if (t == 0) {
+      sm.side_n = 0u;
+      sm.cnt_out = 0u;
+    }
+    __syncthreads();
+    u64 l2 = ~0ull, h2 = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      l2 = sm.wred[w] < l2 ? sm.wred[w] : l2;
+      h2 = sm.wred2[w] > h2 ? sm.wred2[w] : h2;
+    }
+    lo = uniform64(l2);
+    hi = uniform64(h2);
+  }
+  const uint32_t bl = bit_length64(hi - lo);
+  const uint32_t shift = bl > kCutBits ? bl - kCutBits : 0u;
+#pragma unroll
+  for (int i = 0; i < RPT; ++i)
+    if (i * NT + t < n)
+      atomicAdd(&sm.hist[(kCutBins - 1) - static_cast<uint32_t>((v[i] - lo) >> shift)], 1u);
+  __syncthreads();
+  uint32_t h[kCutBPT];
+#pragma unroll
+  for (int i = 0; i < kCutBPT; ++i) {
+    h[i] = sm.hist[t * kCutBPT + i];
+    sm.hist[t * kCutBPT + i] = 0u;
+  }
+  find_rank<kCutBPT>(sm, h, m, 0);
+  const uint32_t b = uniform(sm.res[0]);
+  if (b == kNone) return false;   // cannot happen: n >= m
+  const uint32_t need = m - uniform(sm.res[1]), hb = uniform(sm.res[2]);
+  const u64 blo = lo + (static_cast<u64>((kCutBins - 1) - b) << shift);
+  const u64 bhi_full = blo + ((1ull << shift) - 1ull);
+  const u64 bhi = bhi_full < hi ? bhi_full : hi;
+  u64 T = blo;
+  if (hb != need) {
+    if (hb > kRankMax) return false;
+    // The boundary bin's members, ranked by one wave.
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const bool in = (i * NT + t < n) & (v[i] >= blo) & (v[i] <= bhi);
+      const u64 mk = ballot(in);
+      if (mk) {
+        uint32_t base = 0;
+        if (lane_id() == 0) base = atomicAdd(&sm.side_n, static_cast<uint32_t>(__popcll(mk)));
+        base = uniform(base);
+        if (in) sm.side[base + mbcnt64(mk)] = v[i];
+      }
+    }
+    __syncthreads();
+    if (t < 64) {
+      const uint32_t ns = uniform(sm.side_n);
+      const u64 mine = static_cast<uint32_t>(t) < ns ? sm.side[t] : 0ull;
+      const uint32_t mlo = static_cast<uint32_t>(mine), mhi = static_cast<uint32_t>(mine >> 32);
+      uint32_t above = 0;
+      for (uint32_t j = 0; j < ns; ++j) {
+        const uint32_t olo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(mlo), static_cast<int>(j)));
+        const uint32_t ohi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(mhi), static_cast<int>(j)));
+        above += ((static_cast<u64>(ohi) << 32) | olo) > mine ? 1u : 0u;
+      }
+      if (static_cast<uint32_t>(t) < ns && above + 1u == need) sm.res64 = mine;
+    }
+    __syncthreads();
+    T = uniform64(sm.res64);
+  }
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const bool keep = (i * NT + t < n) & (v[i] >= T);
+    const u64 mk = ballot(keep);
+    if (mk) {
+      uint32_t base = 0;
+      if (lane_id() == 0) base = atomicAdd(&sm.cnt_out, static_cast<uint32_t>(__popcll(mk)));
+      base = uniform(base);
+      if (keep) store_one(a, bf16, xrow, out0 + base + mbcnt64(mk), v[i], true, status);
+    }
+  }
+  return true;
+}
+
 // The epilogue of a row: the buffer holds `count` candidates, a superset of
 // the top m = min(k, L) (m = 0 for a flagged row).  Cut to exactly m, order,
 // write.
@@ -825,6 +1225,17 @@ __device__ __forceinline__ void finish_row(Smem<CAP>& sm, const CArgs& a, bool b
   const uint32_t k = static_cast<uint32_t>(a.k);
   uint32_t m = status ? 0u : min(k, L);
   __syncthreads();
+  const int64_t out0 = static_cast<int64_t>(row) * k;
+  const char* xrow = static_cast<const char*>(a.x) + static_cast<int64_t>(row) * a.row_stride * (bf16 ? 2 : 4);
+  // Any order: the boundary found, every candidate above it stored.  Value
+  // order: every candidate's rank, stored directly.
+  if (m > 0 && count >= m && count <= static_cast<uint32_t>(kRankPerLane * NT) &&
+      ((a.sorted == 0 && select_store(sm, a, bf16, xrow, out0, count, m, status)) ||
+       (a.sorted == 1 && rank_store(sm, a, bf16, xrow, out0, count, m, status)))) {
+    for (uint32_t e = m + t; e < k; e += NT) store_one(a, bf16, xrow, out0 + e, 0ull, false, status);
+    if (t == 0) a.row_status[row] = static_cast<int32_t>(status);
+    return;
+  }
   if (m > 0 && count > m) {
     cut_exact(sm, count, m);
     if (uniform(sm.err)) {
@@ -836,29 +1247,9 @@ __device__ __forceinline__ void finish_row(Smem<CAP>& sm, const CArgs& a, bool b
     m = 0;
   }
   __syncthreads();
-  const int64_t out0 = static_cast<int64_t>(row) * k;
-  const char* xrow = static_cast<const char*>(a.x) + static_cast<int64_t>(row) * a.row_stride * (bf16 ? 2 : 4);
   if (a.sorted != 0 && m > 1) {
-    // Sort keys: the composite by value; (~column << 32) | key by column.
-    const bool by_col = a.sorted == 2;
-    u64 v[PER];
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const uint32_t e = t * PER + i;
-      u64 c = e < m ? sm.buf[e] : 0ull;
-      if (by_col && e < m) c = (static_cast<u64>(static_cast<uint32_t>(c)) << 32) | key_of(c);
-      v[i] = c;
-    }
-    bitonic_sort_desc<PER>(v, sm.buf);
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const uint32_t e = t * PER + i;
-      if (e < k) {
-        u64 c = v[i];
-        if (by_col) c = (static_cast<u64>(static_cast<uint32_t>(c)) << 32) | static_cast<uint32_t>(c >> 32);
-        store_one(a, bf16, xrow, out0 + e, c, e < m, status);
-      }
-    }
+    if (bf16 && a.n_cols <= 65536) sort_and_store<uint32_t, PER>(sm, a, bf16, xrow, out0, m, status);
+    else sort_and_store<u64, PER>(sm, a, bf16, xrow, out0, m, status);
   } else {
     for (uint32_t e = t; e < k; e += NT)
       store_one(a, bf16, xrow, out0 + e, e < m ? sm.buf[e] : 0ull, e < m, status);
@@ -940,7 +1331,8 @@ __global__ __launch_bounds__(NT, 4) void chunk_row_kernel(CArgs a) {
     u32x4 ra[V], rb[V];
     load_chunk<BF16>(ra, xrow, chunk_at(0), L);
     if (nch > 1) load_chunk<BF16>(rb, xrow, chunk_at(1), L);
-    nan = first_chunk<BF16>(sm, B, ra, chunk_at(0), L, k, cap, nch == 1, &spec);
+    nan = start_chunk<BF16>(sm, B, ra, chunk_at(0), L, k, nch == 1, &spec);
+    append_chunk<BF16>(sm, B, ra, chunk_at(0), k, cap);
     for (uint32_t j = 1; j < nch && !uniform(sm.err); ++j) {
 #pragma unroll
       for (int i = 0; i < V; ++i) ra[i] = rb[i];
@@ -988,15 +1380,59 @@ __global__ __launch_bounds__(NT, 4) void chunk_split_kernel(CArgs a) {
 
   Buf B{0u, kTAll, 0};
   bool nan = false, spec = false;
+  // The chunk's candidates go to one region of buf per wave, as raw pairs,
+  // in one pass over the registers (regions == true); should a region
+  // overflow, the chunk is appended again contiguously, cutting as needed.
+  const uint32_t R = cap / NW;
+  bool regions = false;
+  uint32_t cnt[NW] = {};
   if (status == 0 && mine) {
     u32x4 ra[V];
     load_chunk<BF16>(ra, xrow, static_cast<uint32_t>(seg), L);
-    nan = first_chunk<BF16>(sm, B, ra, static_cast<uint32_t>(seg), L, k, cap, false, &spec);
+    nan = start_chunk<BF16>(sm, B, ra, static_cast<uint32_t>(seg), L, k, false, &spec);
+    const float f = __uint_as_float(bits_of_key(key_of(B.T)));
+    const uint32_t wc = region_write<BF16>(sm, ra, static_cast<uint32_t>(seg), f, R);
+    if (lane_id() == 0) sm.wtot[B.par][t >> 6] = wc;
+    __syncthreads();
+    uint32_t total = 0;
+    bool over = false;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      cnt[w] = uniform(sm.wtot[B.par][w]);
+      total += cnt[w];
+      over |= cnt[w] > R;
+    }
+    B.par ^= 1;
+    if (over) {
+      B = reappend_chunk<BF16>(sm, B, xrow, static_cast<uint32_t>(seg), L, k, cap);
+    } else {
+      regions = true;
+      B.count = total;
+    }
   }
   status |= block_or(sm, nan ? static_cast<uint32_t>(DS_ROW_NAN) : 0u, B.par);
   B.par ^= 1;
   // At most k candidates are handed over: the chunk's own top k, exactly.
-  if (status == 0 && !uniform(sm.err) && B.count > k) {
+  if (status == 0 && regions && B.count > k) {
+    // Make the regions one run of composites: each wave converts its own,
+    // then waves 1..3 in turn move theirs down (a move never overwrites a
+    // slot it has still to read).
+    const uint32_t w = t >> 6;
+    u64* reg = sm.buf + w * R;
+    for (uint32_t j = lane_id(); j < cnt[w]; j += 64) {
+      const u64 pr = reg[j];
+      reg[j] = comp_of(key_of_bits(static_cast<uint32_t>(pr >> 32)), static_cast<uint32_t>(pr));
+    }
+    uint32_t dst = cnt[0];
+    for (uint32_t ww = 1; ww < static_cast<uint32_t>(NW); ++ww) {
+      __syncthreads();
+      if (w == ww)
+        for (uint32_t j = lane_id(); j < cnt[ww]; j += 64) sm.buf[dst + j] = reg[j];
+      dst += cnt[ww];
+    }
+    regions = false;
+  }
+  if (status == 0 && !uniform(sm.err) && !regions && B.count > k) {
     __syncthreads();
     const u64 Tn = cut_exact(sm, B.count, k);
     if (!uniform(sm.err)) {
@@ -1010,17 +1446,38 @@ __global__ __launch_bounds__(NT, 4) void chunk_split_kernel(CArgs a) {
   const int64_t rs = static_cast<int64_t>(row) * S + seg;
   u64* slot = a.ws_slot + rs * static_cast<int64_t>(k);
   const uint32_t hand = status ? 0u : B.count;
-  for (uint32_t j = t; j < hand; j += NT) st_agent(&slot[j], sm.buf[j]);
+  if (regions) {
+    const uint32_t w = t >> 6;
+    uint32_t base = 0;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) base += static_cast<uint32_t>(ww) < w ? cnt[ww] : 0u;
+    const u64* reg = sm.buf + w * R;
+    const uint32_t mc = status ? 0u : cnt[w];
+    for (uint32_t j = lane_id(); j < mc; j += 64) {
+      const u64 pr = reg[j];
+      st_agent(&slot[base + j], comp_of(key_of_bits(static_cast<uint32_t>(pr >> 32)), static_cast<uint32_t>(pr)));
+    }
+  } else {
+    for (uint32_t j = t; j < hand; j += NT) st_agent(&slot[j], sm.buf[j]);
+  }
   if (t == 0) {
     st_agent(&a.ws_rec[2 * rs], mine ? B.T : kTAll);
     st_agent(&a.ws_rec[2 * rs + 1], (static_cast<u64>(status) << 32) | hand);
   }
-  // Every lane's stores happen before lane 0's release on the row's counter
-  // (the barrier), and the last workgroup's acquire of that counter happens
-  // before its loads: the hand-over is ordered by the memory model itself.
+  // Ordering of the hand-over.  Every store above is an agent-scope atomic
+  // store: on gfx950 it is written through to the device-coherent level
+  // (sc1), past the per-XCD L2 caches.  Each wave waits until all of its
+  // stores are complete (vmcnt 0) before the barrier, so they are visible
+  // device-wide before lane 0 moves the row's counter.  The last workgroup
+  // reads the counter's old value, then (after a barrier on that value)
+  // loads with agent-scope atomic loads, which also read the coherent level,
+  // so it sees every hand-over.  A release / acquire pair on the counter
+  // would order the same accesses but costs an L2 write-back and invalidate
+  // in every workgroup (about 14 us per call on a 128-row split).
+  wait_all_memory();
   __syncthreads();
   if (t == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(&a.ws_arrive[row], 1u, __ATOMIC_ACQ_REL,
+    const uint32_t prev = __hip_atomic_fetch_add(&a.ws_arrive[row], 1u, __ATOMIC_RELAXED,
                                                  __HIP_MEMORY_SCOPE_AGENT);
     sm.is_last = prev == static_cast<uint32_t>(S - 1) ? 1u : 0u;
   }
@@ -1028,7 +1485,24 @@ __global__ __launch_bounds__(NT, 4) void chunk_split_kernel(CArgs a) {
   if (!uniform(sm.is_last)) return;
 
   // ---- merge: every chunk's candidates at or above the largest chunk threshold.
+  // Chunk s's slots are read by lanes [s*PL, (s+1)*PL), PL = NT / S lanes per
+  // chunk, G8 slots per lane per round.  The first round goes out together
+  // with the records, before the counts are known: slots past a chunk's count
+  // read as zero (the workspace is zero at rest), below every threshold.
   const u64* rec = a.ws_rec + static_cast<int64_t>(row) * S * 2;
+  const uint32_t PL = static_cast<uint32_t>(NT / S);
+  const uint32_t my_s = static_cast<uint32_t>(t) / PL;
+  const uint32_t my_l = static_cast<uint32_t>(t) - my_s * PL;
+  const bool has_s = my_s < static_cast<uint32_t>(S);
+  u64* my_slot = a.ws_slot + (static_cast<int64_t>(row) * S + my_s) * static_cast<int64_t>(k);
+  const uint32_t per_round = PL * G8;
+  u64 v0[G8];
+#pragma unroll
+  for (int q = 0; q < G8; ++q) {
+    const uint32_t j = q * PL + my_l;
+    v0[q] = (has_s && j < k) ? ld_agent(&my_slot[j]) : 0ull;
+  }
+  const uint32_t my_c = has_s ? static_cast<uint32_t>(ld_agent(&rec[2 * my_s + 1])) : 0u;
   u64 Tm = 0;
   uint32_t fl = 0, cm = 0;
   if (t < S) {
@@ -1060,15 +1534,6 @@ __global__ __launch_bounds__(NT, 4) void chunk_split_kernel(CArgs a) {
 
   B.count = 0;
   B.T = Tm;
-  // Chunk s's slots are read by lanes [s*PL, (s+1)*PL), PL = NT / S lanes per
-  // chunk, G8 slots per lane per round.
-  const uint32_t PL = static_cast<uint32_t>(NT / S);
-  const uint32_t my_s = static_cast<uint32_t>(t) / PL;
-  const uint32_t my_l = static_cast<uint32_t>(t) - my_s * PL;
-  const bool has_s = my_s < static_cast<uint32_t>(S);
-  const uint32_t my_c = has_s ? static_cast<uint32_t>(ld_agent(&rec[2 * my_s + 1])) : 0u;
-  u64* my_slot = a.ws_slot + (static_cast<int64_t>(row) * S + my_s) * static_cast<int64_t>(k);
-  const uint32_t per_round = PL * G8;
   const uint32_t rounds = status ? 0u : (cmax + per_round - 1) / per_round;
   __syncthreads();
   for (uint32_t rd = 0; rd < rounds; ++rd) {
@@ -1076,7 +1541,7 @@ __global__ __launch_bounds__(NT, 4) void chunk_split_kernel(CArgs a) {
 #pragma unroll
     for (int q = 0; q < G8; ++q) {
       const uint32_t j = rd * per_round + q * PL + my_l;
-      v[q] = (has_s && j < my_c) ? ld_agent(&my_slot[j]) : 0ull;
+      v[q] = rd == 0 ? v0[q] : ((has_s && j < my_c) ? ld_agent(&my_slot[j]) : 0ull);
     }
     uint32_t n = 0;
 #pragma unroll

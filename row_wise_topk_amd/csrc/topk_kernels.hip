@@ -54,6 +54,7 @@
 #include <type_traits>
 
 #include "ds_topk.h"
+#include "level_search.h"
 #include "topk_internal.h"
 
 namespace dstk {
@@ -61,6 +62,7 @@ namespace {
 
 constexpr int kRadixBits = 11;
 constexpr int kBins = 1 << kRadixBits;
+static_assert(kRadixBits == RangeLevel::kBits, "the cuts and their level arithmetic use one bin width");
 constexpr uint32_t kBias = 0x80000000u;
 constexpr uint32_t kQNaN32 = 0x7FC00000u;
 constexpr uint32_t kNegInf32 = 0xFF800000u;
@@ -446,14 +448,17 @@ __device__ __forceinline__ void read_group(const Smem<CAP, NT>& sm, uint32_t e0,
 }
 
 // Among the candidates with key E_key and composite > T, the column of the
-// need-th smallest column (need >= 1 and at least need such candidates).
+// need-th smallest column (need >= 1 and at least need such candidates).  At
+// most three levels (31-bit columns); if a level's counts disagree with the
+// cut's (no buffer can make them), the row is flagged DS_ROW_INTERNAL and
+// the top of the current range is returned, so the loop always ends.
 template <int NT, int CAP>
 __device__ __noinline__ uint32_t index_cut(Smem<CAP, NT>& sm, uint32_t c, uint32_t E_key,
                                            uint32_t need, u64 T, uint32_t n_cols) {
-  uint32_t ibase = 0;
-  uint32_t itop = n_cols > 0 ? n_cols - 1u : 0u;
-  for (;;) {
-    const uint32_t shift = shift_for_span(itop - ibase);
+  RangeLevel lv{0u, n_cols > 0 ? n_cols - 1u : 0u, need, 0};
+  for (int it = 0; it < RangeLevel::kMaxLevels; ++it) {
+    const uint32_t shift = lv.shift();
+    const uint32_t ibase = lv.base, span = lv.top - lv.base;
     for_groups<NT>(c, [&](auto gs, uint32_t e0) {
       constexpr int G = decltype(gs)::value;
       u64 v[G];
@@ -461,21 +466,23 @@ __device__ __noinline__ uint32_t index_cut(Smem<CAP, NT>& sm, uint32_t c, uint32
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         const uint32_t ci = col_of(v[g]) - ibase;
-        if ((key_of(v[g]) == E_key) & (ci <= itop - ibase) & (v[g] > T))
+        if ((key_of(v[g]) == E_key) & (ci <= span) & (v[g] > T))
           atomicAdd(&sm.hist[(kBins - 1) - (ci >> shift)], 1u);
       }
     });
     __syncthreads();
-    hist_find_top(sm, need);
-    const uint32_t b = (kBins - 1) - uniform(sm.res[0]);   // bin in ascending column order
+    hist_find_top(sm, lv.need);
+    // Bin in ascending column order (wraps past the bins when none was found,
+    // which narrow() refuses).
+    const uint32_t b = (kBins - 1) - uniform(sm.res[0]);
     const uint32_t below = uniform(sm.res[1]), bc = uniform(sm.res[2]);
-    need -= below;
-    ibase += b << shift;
-    const uint32_t bin_top = ibase + ((1u << shift) - 1u);
-    if (bc == need) return bin_top < itop ? bin_top : itop;
-    if (shift == 0) return ibase;
-    itop = bin_top < itop ? bin_top : itop;
+    if (!lv.narrow(b, below, bc)) break;
+    if (bc == lv.need) return lv.top;   // the whole bin is taken
+    if (lv.single()) return lv.base;
   }
+  if (threadIdx.x == 0) atomicOr(&sm.flags, static_cast<uint32_t>(DS_ROW_INTERNAL));
+  __syncthreads();
+  return lv.top;
 }
 
 // Compaction into counter `nxt`, one group of slots at a time: all threads
@@ -531,12 +538,10 @@ __device__ __forceinline__ void compact_buffer(Smem<CAP, NT>& sm, uint32_t c, in
 }
 
 constexpr uint32_t kSmallBin = 64;   // largest boundary bin ranked directly
-#ifndef SMALL_CUT_G
-#define SMALL_CUT_G 4
-#endif
+constexpr int kSmallCutG = 4;   // candidates per thread of the small cut
 // small_cut: candidates per thread, within the buffer's room
 constexpr int small_cut_g(int cap, int nt) {
-  return SMALL_CUT_G * nt + static_cast<int>(kSmallBin) <= cap ? SMALL_CUT_G
+  return kSmallCutG * nt + static_cast<int>(kSmallBin) <= cap ? kSmallCutG
                                                                : (cap - static_cast<int>(kSmallBin)) / nt;
 }
 
@@ -619,12 +624,20 @@ __device__ __noinline__ int cut_buffer(Smem<CAP, NT>& sm, int cur, uint32_t k,
   bool keep_all = false;   // every candidate is above T and kept: no compaction
   u64 sb_lo = 0;
   uint32_t sb_need = 0;
+  bool err = false;   // a level's counts disagreed with the previous level's
   if (hi >= klo && c > 0) {
-    uint32_t need = k, above = 0, base = klo, top = hi;
+    RangeLevel lv{klo, hi, k, 0};
+    uint32_t above = 0;
     bool first = true;
-    for (;;) {
-      const uint32_t shift = shift_for_span(top - base);
+    for (int it = 0; it <= RangeLevel::kMaxLevels; ++it) {
+      if (it == RangeLevel::kMaxLevels) {   // no 32-bit range needs another level
+        err = true;
+        break;
+      }
+      const uint32_t shift = lv.shift();
+      const uint32_t base = lv.base, top = lv.top;
       const uint32_t span = top - base;
+      const uint32_t need = lv.need;
       for_groups<NT>(c, [&](auto gs, uint32_t e0) {
         constexpr int G = decltype(gs)::value;
         u64 v[G];
@@ -659,10 +672,12 @@ __device__ __noinline__ int cut_buffer(Smem<CAP, NT>& sm, int cur, uint32_t k,
         }
       }
       const uint32_t b = uniform(sm.res[0]), ab = uniform(sm.res[1]), bc = uniform(sm.res[2]);
+      if (!lv.narrow(b, ab, bc)) {
+        err = true;
+        break;
+      }
       above += ab;
-      need -= ab;
-      base += b << shift;
-      const u64 lo_edge = (static_cast<u64>(base) << 32) - 1u;
+      const u64 lo_edge = (static_cast<u64>(lv.base) << 32) - 1u;
       if (above + bc <= keep_max) {
         newT = lo_edge > T ? lo_edge : T;
         kept = above + bc;
@@ -673,24 +688,38 @@ __device__ __noinline__ int cut_buffer(Smem<CAP, NT>& sm, int cur, uint32_t k,
         // of the range this level divides (keys above it were counted in
         // higher bins before).  ub + 1 fits in 32 bits for any non-NaN key.
         // Everything above the bin is kept outright.
-        const uint32_t bin_hi = base + ((1u << shift) - 1u);
-        const uint32_t ub = bin_hi < top ? bin_hi : top;
+        const uint32_t ub = lv.top;
         small = true;
         sb_lo = lo_edge > T ? lo_edge : T;
-        sb_need = need;
-        kept = above + need;
+        sb_need = lv.need;
+        kept = above + lv.need;
         newT = (static_cast<u64>(ub + 1u) << 32) - 1u;
         break;
       }
-      if (shift == 0) {
-        const uint32_t I = index_cut<NT, CAP>(sm, c, base, need, T, n_cols);
-        const u64 cand = comp_of(base, I) - 1u;
+      if (lv.single()) {
+        const uint32_t I = index_cut<NT, CAP>(sm, c, lv.base, lv.need, T, n_cols);
+        if (uniform(sm.flags) & static_cast<uint32_t>(DS_ROW_INTERNAL)) {
+          err = true;
+          break;
+        }
+        const u64 cand = comp_of(lv.base, I) - 1u;
         newT = cand > T ? cand : T;
-        kept = above + need;
+        kept = above + lv.need;
         break;
       }
-      top = base + ((1u << shift) - 1u);
     }
+  }
+  if (err) {
+    // The row is flagged and its buffer emptied (the threshold stays), so no
+    // later append can overflow it; the row's outputs become -1 / qNaN.
+    if (t == 0) {
+      atomicOr(&sm.flags, static_cast<uint32_t>(DS_ROW_INTERNAL));
+      sm.thr = T;
+      sm.xv = 0;
+      sm.kept = 0;
+    }
+    __syncthreads();
+    return cur ^ 1;   // sm.cnt[cur ^ 1] was set to zero above
   }
 
   int nxt = cur ^ 1;
