@@ -167,6 +167,21 @@ _DT = {torch.float32: DS_FP32, torch.bfloat16: DS_BF16}
 _IT = {torch.int32: DS_INT32, torch.int64: DS_INT64}
 
 
+def _check_out(values, indices, status, batch, k, dtype, index_dtype, return_values, dev):
+    """Caller-supplied outputs must be exactly what the kernel writes: dense
+    [batch, k] of the right dtypes (values only with return_values) and an
+    int32 [batch] status, all contiguous on x's device."""
+    want = [("indices", indices, index_dtype, (batch, k)), ("row_status", status, torch.int32, (batch,))]
+    if return_values:
+        want.append(("values", values, dtype, (batch, k)))
+    for name, t, dt, shape in want:
+        if not isinstance(t, torch.Tensor):
+            raise ValueError(f"out: {name} must be a tensor")
+        if t.dtype != dt or tuple(t.shape) != shape or t.device != dev or not t.is_contiguous():
+            raise ValueError(f"out: {name} must be a contiguous {dt} tensor of shape {shape} "
+                             f"on {dev} (got {t.dtype} {tuple(t.shape)} on {t.device})")
+
+
 def topk(x: torch.Tensor, k: int, *, end: torch.Tensor | None = None, sorted: int = 1,
          return_values: bool = True, index_dtype: torch.dtype = torch.int32,
          n_cols: int | None = None, plan=None, out=None):
@@ -203,6 +218,7 @@ def topk(x: torch.Tensor, k: int, *, end: torch.Tensor | None = None, sorted: in
         status = torch.empty((batch,), dtype=torch.int32, device=dev)
     else:
         values, indices, status = out
+        _check_out(values, indices, status, batch, k, x.dtype, index_dtype, return_values, dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
     dt = _DT[x.dtype]
     ws_bytes = ds_topk_workspace_size_ex(dt, batch, n_cols, k, plan)

@@ -1641,18 +1641,6 @@ const void* chunk_fn(int cls, bool split) {
 
 }  // namespace
 
-ChunkWs chunk_ws_layout(int64_t batch, int segments, int k) {
-  auto up = [](size_t v) { return (v + 255) & ~static_cast<size_t>(255); };
-  ChunkWs l{};
-  const size_t b = static_cast<size_t>(batch);
-  const size_t s = static_cast<size_t>(segments);
-  l.arrive = 0;
-  l.rec = up(b * 4);
-  l.slot = up(l.rec + b * s * 16);
-  l.total = up(l.slot + b * s * static_cast<size_t>(k) * 8);
-  return l;
-}
-
 // The launch's own error code (hipLaunchKernel returns it; an earlier,
 // unrelated error left in the runtime is neither returned nor cleared).
 int launch_chunk(const CArgs& a, int dtype, int cls, hipStream_t stream) {

@@ -163,6 +163,38 @@ ds_status_t validate(const void* x, ds_dtype_t dtype, int64_t batch, int64_t n_c
 
 }  // namespace
 
+namespace dstk {
+
+WsLayout ws_layout(int64_t batch, int segments, int k) {
+  auto up = [](size_t v) { return (v + 15) & ~static_cast<size_t>(15); };
+  WsLayout l{};
+  const size_t b = static_cast<size_t>(batch);
+  const size_t s = static_cast<size_t>(segments);
+  l.thr = 0;
+  l.done = up(l.thr + b * 8);
+  l.flags = up(l.done + b * 4);
+  l.fill = up(l.flags + b * 4);
+  l.x = up(l.fill + b * 4);
+  l.spec = up(l.x + b * s * 8);
+  l.comp = up(l.spec + b * 8);
+  l.total = up(l.comp + b * s * (static_cast<size_t>(k) + kStreamSlotSlack) * 8);
+  return l;
+}
+
+ChunkWs chunk_ws_layout(int64_t batch, int segments, int k) {
+  auto up = [](size_t v) { return (v + 255) & ~static_cast<size_t>(255); };
+  ChunkWs l{};
+  const size_t b = static_cast<size_t>(batch);
+  const size_t s = static_cast<size_t>(segments);
+  l.arrive = 0;
+  l.rec = up(b * 4);
+  l.slot = up(l.rec + b * s * 16);
+  l.total = up(l.slot + b * s * static_cast<size_t>(k) * 8);
+  return l;
+}
+
+}  // namespace dstk
+
 extern "C" {
 
 ds_status_t ds_topk_validate(const void* x, ds_dtype_t dtype, int64_t batch, int64_t n_cols,

@@ -95,6 +95,9 @@ int launch_chunk(const CArgs& a, int dtype, int cls, hipStream_t stream);
 // Queue the read-ceiling kernel of the chunk kernels' access pattern.
 int launch_chunk_read(const CArgs& a, int dtype, uint32_t* sink, hipStream_t stream);
 
+// Survivor slots a shared row's workgroup may hand over beyond k.
+constexpr int kStreamSlotSlack = 64;
+
 struct KArgs {
   const void* x;
   int64_t row_stride;     // elements

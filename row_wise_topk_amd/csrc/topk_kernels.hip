@@ -538,6 +538,7 @@ __device__ __forceinline__ void compact_buffer(Smem<CAP, NT>& sm, uint32_t c, in
 }
 
 constexpr uint32_t kSmallBin = 64;   // largest boundary bin ranked directly
+static_assert(kSmallBin == static_cast<uint32_t>(kStreamSlotSlack), "survivor slots per workgroup: k + kSmallBin");
 constexpr int kSmallCutG = 4;   // candidates per thread of the small cut
 // small_cut: candidates per thread, within the buffer's room
 constexpr int small_cut_g(int cap, int nt) {
@@ -2243,45 +2244,35 @@ __global__ __launch_bounds__(NT, 2) void read_kernel(KArgs a, uint32_t* sink) {
 
 }  // namespace
 
-WsLayout ws_layout(int64_t batch, int segments, int k) {
-  auto up = [](size_t v) { return (v + 15) & ~static_cast<size_t>(15); };
-  WsLayout l{};
-  const size_t b = static_cast<size_t>(batch);
-  const size_t s = static_cast<size_t>(segments);
-  l.thr = 0;
-  l.done = up(l.thr + b * 8);
-  l.flags = up(l.done + b * 4);
-  l.fill = up(l.flags + b * 4);
-  l.x = up(l.fill + b * 4);
-  l.spec = up(l.x + b * s * 8);
-  l.comp = up(l.spec + b * 8);
-  l.total = up(l.comp + b * s * (static_cast<size_t>(k) + kSmallBin) * 8);
-  return l;
+// The launch's own error code: hipLaunchKernel returns it, and an earlier,
+// unrelated error left in the runtime is neither returned nor cleared.
+static int launch_fn(const void* fn, unsigned grid, unsigned block, void** args, hipStream_t stream) {
+  return static_cast<int>(hipLaunchKernel(fn, dim3(grid), dim3(block), args, 0, stream));
 }
 
 template <bool BF16, int CLS>
 static int launch_one(const KArgs& a, hipStream_t stream) {
-  const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.batch) * a.segments));
+  const unsigned grid = static_cast<unsigned>(static_cast<int64_t>(a.batch) * a.segments);
+  KArgs arg = a;
+  void* args[] = {&arg};
   if (a.segments > 1)
-    hipLaunchKernelGGL((topk_kernel<BF16, CLS, true>), grid, dim3(kernel_threads(CLS, BF16 ? 1 : 0, true)),
-                       0, stream, a);
-  else
-    hipLaunchKernelGGL((topk_kernel<BF16, CLS, false>), grid,
-                       dim3(kernel_threads(CLS, BF16 ? 1 : 0, false)), 0, stream, a);
-  return static_cast<int>(hipGetLastError());
+    return launch_fn(reinterpret_cast<const void*>(&topk_kernel<BF16, CLS, true>), grid,
+                     kernel_threads(CLS, BF16 ? 1 : 0, true), args, stream);
+  return launch_fn(reinterpret_cast<const void*>(&topk_kernel<BF16, CLS, false>), grid,
+                   kernel_threads(CLS, BF16 ? 1 : 0, false), args, stream);
 }
 
 int launch_read(const KArgs& a, int dtype, int cls, uint32_t* sink, hipStream_t stream) {
-  const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.batch) * a.segments));
+  const unsigned grid = static_cast<unsigned>(static_cast<int64_t>(a.batch) * a.segments);
   const int nt = kernel_threads(cls, dtype, a.segments > 1);
-  if (dtype == 0) {
-    if (nt == 512) hipLaunchKernelGGL((read_kernel<false, 512>), grid, dim3(512), 0, stream, a, sink);
-    else hipLaunchKernelGGL((read_kernel<false, 256>), grid, dim3(256), 0, stream, a, sink);
-  } else {
-    if (nt == 512) hipLaunchKernelGGL((read_kernel<true, 512>), grid, dim3(512), 0, stream, a, sink);
-    else hipLaunchKernelGGL((read_kernel<true, 256>), grid, dim3(256), 0, stream, a, sink);
-  }
-  return static_cast<int>(hipGetLastError());
+  KArgs arg = a;
+  void* args[] = {&arg, &sink};
+  const void* fn;
+  if (dtype == 0) fn = nt == 512 ? reinterpret_cast<const void*>(&read_kernel<false, 512>)
+                                 : reinterpret_cast<const void*>(&read_kernel<false, 256>);
+  else fn = nt == 512 ? reinterpret_cast<const void*>(&read_kernel<true, 512>)
+                      : reinterpret_cast<const void*>(&read_kernel<true, 256>);
+  return launch_fn(fn, grid, static_cast<unsigned>(nt), args, stream);
 }
 
 int launch_topk(const KArgs& a, int dtype, int cls, hipStream_t stream) {

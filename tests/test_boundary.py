@@ -171,3 +171,26 @@ def test_product_path_has_no_oracle_or_fallback():
     src = inspect.getsource(rt)
     assert "oracle" not in src.replace("no fallback", "")
     assert "import numpy" not in src
+
+
+def test_out_tensors_are_checked():
+    """topk(out=...) refuses buffers the kernel would write past or misread
+    (checked before anything is launched, so no GPU is needed)."""
+    import pytest
+    import torch
+
+    x = torch.empty((4, 1000), dtype=torch.float32)
+    ok = (torch.empty((4, 8), dtype=torch.float32), torch.empty((4, 8), dtype=torch.int32),
+          torch.empty((4,), dtype=torch.int32))
+    bad = [
+        (ok[0], torch.empty((4, 8), dtype=torch.int64), ok[2]),      # index dtype
+        (ok[0], torch.empty((4, 7), dtype=torch.int32), ok[2]),      # k
+        (torch.empty((4, 8), dtype=torch.bfloat16), ok[1], ok[2]),   # value dtype
+        (ok[0], ok[1], torch.empty((3,), dtype=torch.int32)),        # status shape
+        (ok[0], torch.empty((8, 4), dtype=torch.int32).t(), ok[2]),  # not contiguous
+    ]
+    for out in bad:
+        with pytest.raises(ValueError):
+            rt._check_out(*out, 4, 8, torch.float32, torch.int32, True, x.device)
+    rt._check_out(*ok, 4, 8, torch.float32, torch.int32, True, x.device)
+    rt._check_out(None, ok[1], ok[2], 4, 8, torch.float32, torch.int32, False, x.device)
