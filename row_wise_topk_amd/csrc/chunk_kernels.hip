@@ -178,7 +178,8 @@ __device__ __forceinline__ void wait_all_memory() {
 // ---------------------------------------------------------------- LDS
 template <int CAP>
 struct Smem {
-  u64 buf[CAP];                       // candidate composites (also the sort's exchange area)
+  u64 buf[CAP + 8];                   // candidate composites (also the sort's exchange area);
+                                      // the last 8 are zero padding for the rank epilogue
   alignas(16) uint32_t hist[kCutBins];  // zero whenever not in use
   u64 side[kRankMax];                 // members of a small boundary bin
   uint32_t wtot[2][NW];               // per-wave counts, alternating by use
@@ -702,19 +703,32 @@ __device__ __forceinline__ bool start_chunk(Smem<CAP>& sm, Buf& B, u32x4 (&r)[V]
 template <bool BF16, int CAP>
 __device__ __forceinline__ uint32_t region_write(Smem<CAP>& sm, const u32x4 (&r)[V], uint32_t c,
                                                  float f, uint32_t R) {
+  using G = Geo<BF16>;
   u64* reg = sm.buf + (threadIdx.x >> 6) * R;
   uint32_t pos = 0;
 #pragma unroll
   for (int i = 0; i < V; ++i) {
-    for_values<BF16>(r[i], [&](uint32_t b, int q) {
-      const bool ok = __uint_as_float(b) >= f;
-      const u64 m = ballot(ok);
-      if (m) {
-        const uint32_t p = pos + mbcnt64(m);
-        if (ok && p < R) reg[p] = (static_cast<u64>(b) << 32) | col_at<BF16>(c, i, q);
-        pos += static_cast<uint32_t>(__popcll(m));
-      }
-    });
+    if (pos + 64u * G::EPV <= R) {
+      // The whole vector fits whatever passes: no bound per value.
+      for_values<BF16>(r[i], [&](uint32_t b, int q) {
+        const bool ok = __uint_as_float(b) >= f;
+        const u64 m = ballot(ok);
+        if (m) {
+          if (ok) reg[pos + mbcnt64(m)] = (static_cast<u64>(b) << 32) | col_at<BF16>(c, i, q);
+          pos += static_cast<uint32_t>(__popcll(m));
+        }
+      });
+    } else {
+      for_values<BF16>(r[i], [&](uint32_t b, int q) {
+        const bool ok = __uint_as_float(b) >= f;
+        const u64 m = ballot(ok);
+        if (m) {
+          const uint32_t p = pos + mbcnt64(m);
+          if (ok && p < R) reg[p] = (static_cast<u64>(b) << 32) | col_at<BF16>(c, i, q);
+          pos += static_cast<uint32_t>(__popcll(m));
+        }
+      });
+    }
   }
   return pos;
 }
@@ -1062,10 +1076,13 @@ __device__ __forceinline__ bool rank_store(Smem<CAP>& sm, const CArgs& a, bool b
 #pragma unroll
   for (int i = 0; i < RPT; ++i)
     if (i * NT + t < n) sm.buf[atomicAdd(&sm.hist[bin_of(v[i])], 1u)] = v[i];
+  if (t < 8) sm.buf[n + t] = 0ull;
   __syncthreads();
-  // Rank within the bin, by position (the lanes of a wave mostly share a
-  // bin, so its members are read as broadcasts).  Every position's value and
-  // bin bounds are read in one batch; a bin of one member needs no loop.
+  // Rank within the bin: the number of members above, read eight positions
+  // at a time from the bin's start.  Positions past the bin's end hold lower
+  // bins, whose members are all smaller, and past n the zero padding, so the
+  // reads need no bound.  Every position's value and bin bounds are read in
+  // one batch.
   {
     u64 x[RPT];
     uint32_t st[RPT], en[RPT];
@@ -1089,9 +1106,9 @@ __device__ __forceinline__ bool rank_store(Smem<CAP>& sm, const CArgs& a, bool b
         for (uint32_t q0 = st[i]; q0 < en[i]; q0 += 8) {   // eight reads in flight
           u64 y[8];
 #pragma unroll
-          for (int j = 0; j < 8; ++j) y[j] = sm.buf[q0 + j < en[i] ? q0 + j : st[i]];
+          for (int j = 0; j < 8; ++j) y[j] = sm.buf[q0 + j];
 #pragma unroll
-          for (int j = 0; j < 8; ++j) r += (q0 + j < en[i] && y[j] > x[i]) ? 1u : 0u;
+          for (int j = 0; j < 8; ++j) r += y[j] > x[i] ? 1u : 0u;
         }
       }
       if (r < m) store_one(a, bf16, xrow, out0 + r, x[i], true, status);
@@ -1172,16 +1189,25 @@ __device__ __forceinline__ bool select_store(Smem<CAP>& sm, const CArgs& a, bool
   u64 T = blo;
   if (hb != need) {
     if (hb > kRankMax) return false;
-    // The boundary bin's members, ranked by one wave.
+    // The boundary bin's members, ranked by one wave.  Each wave takes its
+    // span of the side buffer with one atomic.
+    {
+      u64 mk[RPT];
+      uint32_t wn = 0;
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      const bool in = (i * NT + t < n) & (v[i] >= blo) & (v[i] <= bhi);
-      const u64 mk = ballot(in);
-      if (mk) {
+      for (int i = 0; i < RPT; ++i) {
+        mk[i] = ballot((i * NT + t < n) & (v[i] >= blo) & (v[i] <= bhi));
+        wn += static_cast<uint32_t>(__popcll(mk[i]));
+      }
+      if (wn) {
         uint32_t base = 0;
-        if (lane_id() == 0) base = atomicAdd(&sm.side_n, static_cast<uint32_t>(__popcll(mk)));
+        if (lane_id() == 0) base = atomicAdd(&sm.side_n, wn);
         base = uniform(base);
-        if (in) sm.side[base + mbcnt64(mk)] = v[i];
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+          if ((mk[i] >> lane_id()) & 1ull) sm.side[base + mbcnt64(mk[i])] = v[i];
+          base += static_cast<uint32_t>(__popcll(mk[i]));
+        }
       }
     }
     __syncthreads();
@@ -1200,16 +1226,22 @@ __device__ __forceinline__ bool select_store(Smem<CAP>& sm, const CArgs& a, bool
     __syncthreads();
     T = uniform64(sm.res64);
   }
+  // Each wave takes its span of the output with one atomic, then stores its
+  // kept candidates in lane order.
+  u64 mk[RPT];
+  uint32_t wn = 0;
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
-    const bool keep = (i * NT + t < n) & (v[i] >= T);
-    const u64 mk = ballot(keep);
-    if (mk) {
-      uint32_t base = 0;
-      if (lane_id() == 0) base = atomicAdd(&sm.cnt_out, static_cast<uint32_t>(__popcll(mk)));
-      base = uniform(base);
-      if (keep) store_one(a, bf16, xrow, out0 + base + mbcnt64(mk), v[i], true, status);
-    }
+    mk[i] = ballot((i * NT + t < n) & (v[i] >= T));
+    wn += static_cast<uint32_t>(__popcll(mk[i]));
+  }
+  uint32_t base = 0;
+  if (lane_id() == 0 && wn) base = atomicAdd(&sm.cnt_out, wn);
+  base = uniform(base);
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    if ((mk[i] >> lane_id()) & 1ull) store_one(a, bf16, xrow, out0 + base + mbcnt64(mk[i]), v[i], true, status);
+    base += static_cast<uint32_t>(__popcll(mk[i]));
   }
   return true;
 }
