@@ -29,7 +29,8 @@
  * Conventions for every entry point:
  *   - All array pointers passed to ds_topk / ds_topk_ex are DEVICE pointers
  *     owned by the caller.  The library allocates no memory and keeps no
- *     state between calls.
+ *     state between calls (ds_topk_noalloc's static scratch array, one per
+ *     device, is the one exception).
  *   - Calls are asynchronous on `stream`; the library never synchronises and
  *     never prints.  Argument errors are returned before anything is launched.
  *   - Data errors never abort (unlike the trap of [NC]/[IT]): they set bits in
@@ -70,7 +71,9 @@ typedef enum {
   DS_ERR_SORTED_MODE = 7,   /* sorted not in {0, 1, 2}                             */
   DS_ERR_WORKSPACE = 8,     /* workspace NULL, too small or not 16-B aligned       */
   DS_ERR_HIP = 9,           /* the HIP runtime reported an error at launch         */
-  DS_ERR_PLAN = 10          /* a ds_topk_plan_t field is out of range              */
+  DS_ERR_PLAN = 10,         /* a ds_topk_plan_t field is out of range              */
+  DS_ERR_SCRATCH_LIMIT = 11 /* ds_topk_noalloc: the problem needs more workspace than
+                               DS_TOPK_NOALLOC_SCRATCH_BYTES                        */
 } ds_status_t;
 
 #define DS_TOPK_MAX_K 4096            /* [NC coverage]: topk must be 4096 or less   */
@@ -179,6 +182,33 @@ size_t ds_topk_workspace_size(ds_dtype_t dtype, int64_t batch, int64_t n_cols, i
  * only: the automatic plan depends on the problem shape alone. */
 size_t ds_topk_workspace_size_ex(ds_dtype_t dtype, int64_t batch, int64_t n_cols, int32_t k,
                                  const ds_topk_plan_t* plan);
+
+/*
+ * ds_topk_noalloc -- ds_topk_ex for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments, meaning, ownership and errors as
+ * ds_topk_ex, without workspace / workspace_bytes: the workspace is a static
+ * device array of DS_TOPK_NOALLOC_SCRATCH_BYTES inside the library, one per
+ * GPU, held until the process ends.  The caller still passes x, end and the
+ * outputs.  The call allocates nothing and calls no allocating routine; its
+ * first call on a device that needs scratch takes the array's address on
+ * that device (the device must be current) and clears it with one kernel on
+ * `stream`, ahead of the selection.
+ *   Returns DS_ERR_SCRATCH_LIMIT, before any HIP call, when
+ *   ds_topk_workspace_size_ex(dtype, batch, n_cols, k, plan) exceeds
+ *   DS_TOPK_NOALLOC_SCRATCH_BYTES (16 MiB: rows split over several
+ *   workgroups, batch * segments * k * 8 bytes and a little more); DS_ERR_HIP
+ *   if the address cannot be taken or the clearing kernel cannot be queued.
+ *   Every call on one GPU shares that GPU's array: calls that may overlap on
+ *   one GPU (streams with no ordering between them) race on it.  Calls
+ *   ordered on one stream are safe; each leaves the array zero.
+ */
+#define DS_TOPK_NOALLOC_SCRATCH_BYTES (16u << 20)
+ds_status_t ds_topk_noalloc(const void* x, ds_dtype_t dtype, int64_t batch, int64_t n_cols,
+                            int64_t row_stride, const int32_t* end, int32_t k, int32_t sorted,
+                            int32_t return_values, ds_index_dtype_t index_dtype, void* values,
+                            void* indices, int32_t* row_status, hipStream_t stream,
+                            const ds_topk_plan_t* plan);
 
 /* Row strides must be a multiple of this many elements (16 B / sizeof(dtype));
  * the counterpart of the pages' get_stride_requirement [NC install/API].

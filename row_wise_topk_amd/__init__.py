@@ -7,8 +7,8 @@ and the current stream.
 
 Raw entry points carry the C names and arguments (``ds_topk``, ``ds_topk_ex``,
 ``ds_topk_validate``, ``ds_topk_workspace_size``, ``ds_topk_workspace_size_ex``,
-``ds_topk_stride_requirement``, ``ds_topk_status_string``, and the measurement
-aid ``ds_read_ceiling``).  :func:`topk` is the
+``ds_topk_stride_requirement``, ``ds_topk_status_string``, the allocation-free
+``ds_topk_noalloc`` and the measurement aid ``ds_read_ceiling``).  :func:`topk` is the
 tensor-level call, the counterpart of ``deep_select.topk(x, topk, sorted_index,
 indices_type, return_value)`` described on xhh.club, "DeepSeek开源DeepSelect：
 比torch.topk快二十倍！" (Q&A), with a per-row ``end`` as described on
@@ -40,7 +40,9 @@ DS_KERNEL_AUTO, DS_KERNEL_STREAM, DS_KERNEL_CHUNK = 0, 1, 2
 DS_TOPK_MAX_K = 4096
 STATUS_NAMES = ["DS_OK", "DS_ERR_NULL", "DS_ERR_DTYPE", "DS_ERR_INDEX_DTYPE", "DS_ERR_K_RANGE",
                 "DS_ERR_SHAPE", "DS_ERR_ALIGN", "DS_ERR_SORTED_MODE", "DS_ERR_WORKSPACE",
-                "DS_ERR_HIP", "DS_ERR_PLAN"]
+                "DS_ERR_HIP", "DS_ERR_PLAN", "DS_ERR_SCRATCH_LIMIT"]
+DS_ERR_SCRATCH_LIMIT = 11
+DS_TOPK_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
 class Plan(ctypes.Structure):
@@ -75,6 +77,9 @@ _lib.ds_topk_status_string.restype = ctypes.c_char_p
 _lib.ds_read_ceiling.argtypes = [_vp, ctypes.c_int, _i64, _i64, _i64, _vp, _i32,
                                 ctypes.POINTER(Plan), _vp, _vp]
 _lib.ds_read_ceiling.restype = ctypes.c_int
+_lib.ds_topk_noalloc.argtypes = [_vp, ctypes.c_int, _i64, _i64, _i64, _vp, _i32, _i32, _i32,
+                                 ctypes.c_int, _vp, _vp, _vp, _vp, ctypes.POINTER(Plan)]
+_lib.ds_topk_noalloc.restype = ctypes.c_int
 
 
 def exported_names() -> list[str]:
@@ -107,6 +112,12 @@ def ds_topk_ex(x, dtype, batch, n_cols, row_stride, end, k, sorted, return_value
     return _lib.ds_topk_ex(x, dtype, batch, n_cols, row_stride, end, k, sorted, return_values,
                            index_dtype, values, indices, row_status, workspace, workspace_bytes,
                            stream, _plan_ptr(plan))
+
+
+def ds_topk_noalloc(x, dtype, batch, n_cols, row_stride, end, k, sorted, return_values,
+                    index_dtype, values, indices, row_status, stream, plan=None) -> int:
+    return _lib.ds_topk_noalloc(x, dtype, batch, n_cols, row_stride, end, k, sorted, return_values,
+                                index_dtype, values, indices, row_status, stream, _plan_ptr(plan))
 
 
 def ds_topk_validate(x, dtype, batch, n_cols, row_stride, end, k, sorted, return_values,

@@ -30,14 +30,18 @@ def build(verbose: bool = False, extra: list[str] | None = None) -> str:
     k_obj = os.path.join(bdir, "topk_kernels.o")
     c_obj = os.path.join(bdir, "chunk_kernels.o")
     a_obj = os.path.join(bdir, "topk_api.o")
+    n_obj = os.path.join(bdir, "noalloc.o")
     _run([HIPCC, *COMMON, *DEVICE, *extra, "-c", os.path.join(CSRC, "topk_kernels.hip"),
           "-o", k_obj], verbose)
     _run([HIPCC, *COMMON, *DEVICE, *extra, "-c", os.path.join(CSRC, "chunk_kernels.hip"),
           "-o", c_obj], verbose)
     _run([HIPCC, *COMMON, *DEVICE, *extra, "-x", "hip", "-c", os.path.join(CSRC, "topk_api.cpp"),
           "-o", a_obj], verbose)
+    _run([HIPCC, *COMMON, *DEVICE, *extra, "-c", os.path.join(CSRC, "noalloc.hip"), "-o", n_obj],
+         verbose)
     tmp = LIB + ".tmp"
-    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", k_obj, c_obj, a_obj, "-o", tmp], verbose)
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", k_obj, c_obj, a_obj, n_obj, "-o", tmp],
+         verbose)
     os.replace(tmp, LIB)
     return LIB
 

@@ -194,3 +194,19 @@ def test_out_tensors_are_checked():
             rt._check_out(*out, 4, 8, torch.float32, torch.int32, True, x.device)
     rt._check_out(*ok, 4, 8, torch.float32, torch.int32, True, x.device)
     rt._check_out(None, ok[1], ok[2], 4, 8, torch.float32, torch.int32, False, x.device)
+
+
+def test_noalloc_refusals_need_no_gpu():
+    """The allocation-free entry point refuses, before any HIP call, a problem
+    whose workspace exceeds its static scratch, and bad arguments."""
+    plan = rt.Plan(segments=16, perm_seed=1, kernel=rt.DS_KERNEL_CHUNK)
+    assert rt.ds_topk_workspace_size_ex(rt.DS_FP32, 256, 129280, 4096, plan) > rt.DS_TOPK_NOALLOC_SCRATCH_BYTES
+    rc = rt.ds_topk_noalloc(None, rt.DS_FP32, 256, 129280, 129280, None, 4096, 1, 0, rt.DS_INT32,
+                            None, None, None, None, plan)
+    assert rc == rt.DS_ERR_SCRATCH_LIMIT
+    rc = rt.ds_topk_noalloc(None, rt.DS_BF16, 4, 1000, 1000, None, 10, 1, 0, rt.DS_INT32, None,
+                            None, None, None, None)
+    assert rt.STATUS_NAMES[rc] == "DS_ERR_NULL"
+    rc = rt.ds_topk_noalloc(None, rt.DS_BF16, 4, 1000, 1000, None, 0, 1, 0, rt.DS_INT32, None,
+                            None, None, None, None)
+    assert rt.STATUS_NAMES[rc] == "DS_ERR_K_RANGE"
