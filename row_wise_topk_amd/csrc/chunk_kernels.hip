@@ -58,6 +58,7 @@ namespace {
 
 typedef unsigned long long u64;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int NT = kChunkThreads;   // 256 lanes, 4 waves
 constexpr int NW = NT / 64;
@@ -285,13 +286,22 @@ __device__ __forceinline__ uint32_t col_at(uint32_t c, int i, int q) {
 }
 
 // Apply f(bits as fp32, value index q) to every value of vector r.
+// The low bf16 of a word as an fp32 bit pattern.  Computed where it is used
+// (an opaque shift the compiler cannot hoist), so a chunk's 32 shifted words
+// are never held in registers across passes.
+__device__ __forceinline__ uint32_t lo_half(uint32_t d) {
+  uint32_t r;
+  asm volatile("v_lshlrev_b32 %0, 16, %1" : "=v"(r) : "v"(d));
+  return r;
+}
+
 template <bool BF16, typename F>
 __device__ __forceinline__ void for_values(const u32x4& r, F&& f) {
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
     const uint32_t d = r[w];
     if constexpr (BF16) {
-      f(d << 16, 2 * w);
+      f(lo_half(d), 2 * w);
       f(d & 0xFFFF0000u, 2 * w + 1);
     } else {
       f(d, w);
@@ -331,17 +341,15 @@ template <bool BF16, bool CHECK>
 __device__ __forceinline__ void chunk_max_nan(const u32x4 (&r)[V], uint32_t* maxkey, bool* nan) {
   float mx = __uint_as_float(kQNaN32);   // fmaxf(NaN, x) = x: stays NaN if every value is
   uint32_t mag = 0;
+  u16x2 mag2 = {0, 0};   // bf16: both halves' magnitudes at once
 #pragma unroll
   for (int i = 0; i < V; ++i) {
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const uint32_t d = r[i][w];
       if constexpr (BF16) {
-        if (CHECK) {
-          mag = max(mag, d & 0x7FFFu);
-          mag = max(mag, (d >> 16) & 0x7FFFu);
-        }
-        mx = fmaxf(mx, __uint_as_float(d << 16));
+        if (CHECK) mag2 = __builtin_elementwise_max(mag2, __builtin_bit_cast(u16x2, d & 0x7FFF7FFFu));
+        mx = fmaxf(mx, __uint_as_float(lo_half(d)));
         mx = fmaxf(mx, __uint_as_float(d & 0xFFFF0000u));
       } else {
         if (CHECK) mag = max(mag, d & 0x7FFFFFFFu);
@@ -349,6 +357,7 @@ __device__ __forceinline__ void chunk_max_nan(const u32x4 (&r)[V], uint32_t* max
       }
     }
   }
+  if constexpr (BF16) mag = max(static_cast<uint32_t>(mag2.x), static_cast<uint32_t>(mag2.y));
   *nan = CHECK && mag > (BF16 ? 0x7F80u : 0x7F800000u);
   *maxkey = mx == mx ? key_of_bits(__float_as_uint(mx)) : 0u;
 }
@@ -1008,10 +1017,12 @@ __device__ __forceinline__ bool rank_store(Smem<CAP>& sm, const CArgs& a, bool b
                                            uint32_t status) {
   constexpr int RPT = kRankPerLane;
   const uint32_t t = threadIdx.x;
+  // Iterations past the last candidate are skipped as a whole (n is uniform).
+  const uint32_t nit = uniform((n + NT - 1) / NT);
   u64 v[RPT];
   u64 lo = ~0ull, hi = 0;
 #pragma unroll
-  for (int i = 0; i < RPT; ++i) {
+  for (int i = 0; i < RPT; ++i) if (i < nit) {
     const uint32_t j = i * NT + t;
     v[i] = sm.buf[j < n ? j : 0u];
     if (j < n) {
@@ -1038,11 +1049,20 @@ __device__ __forceinline__ bool rank_store(Smem<CAP>& sm, const CArgs& a, bool b
     lo = uniform64(l2);
     hi = uniform64(h2);
   }
-  const uint32_t bl = bit_length64(hi - lo);
+  // Bins over the composites' range.  bf16 values of rows of at most 2^16
+  // columns repeat often; their composites are binned in a 32-bit form
+  // (the value's 16 key bits, then the low 16 bits of ~column), which orders
+  // them the same way but spreads a run of equal values over the column bits.
+  const bool narrow = bf16 && a.n_cols <= 65536;
+  auto red = [&](u64 x) -> u64 {
+    return narrow ? ((static_cast<u64>(key_of(x) >> 16) << 16) | (static_cast<uint32_t>(x) & 0xFFFFu)) : x;
+  };
+  const u64 rlo = red(lo);
+  const uint32_t bl = bit_length64(red(hi) - rlo);
   const uint32_t shift = bl > kCutBits ? bl - kCutBits : 0u;
-  auto bin_of = [&](u64 x) { return (kCutBins - 1) - static_cast<uint32_t>((x - lo) >> shift); };
+  auto bin_of = [&](u64 x) { return (kCutBins - 1) - static_cast<uint32_t>((red(x) - rlo) >> shift); };
 #pragma unroll
-  for (int i = 0; i < RPT; ++i)
+  for (int i = 0; i < RPT; ++i) if (i < nit)
     if (i * NT + t < n) atomicAdd(&sm.hist[bin_of(v[i])], 1u);
   __syncthreads();
   // Own bins: the largest, then each bin's first position.
@@ -1074,7 +1094,7 @@ __device__ __forceinline__ bool rank_store(Smem<CAP>& sm, const CArgs& a, bool b
   // Scatter: afterwards hist[b] is the end of bin b, and bin b starts where
   // bin b-1 ends (bin 0 at 0).
 #pragma unroll
-  for (int i = 0; i < RPT; ++i)
+  for (int i = 0; i < RPT; ++i) if (i < nit)
     if (i * NT + t < n) sm.buf[atomicAdd(&sm.hist[bin_of(v[i])], 1u)] = v[i];
   if (t < 8) sm.buf[n + t] = 0ull;
   __syncthreads();
@@ -1087,18 +1107,18 @@ __device__ __forceinline__ bool rank_store(Smem<CAP>& sm, const CArgs& a, bool b
     u64 x[RPT];
     uint32_t st[RPT], en[RPT];
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
+    for (int i = 0; i < RPT; ++i) if (i < nit) {
       const uint32_t p = i * NT + t;
       x[i] = sm.buf[p < n ? p : 0u];
     }
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
+    for (int i = 0; i < RPT; ++i) if (i < nit) {
       const uint32_t b = bin_of(x[i]);
       st[i] = b ? sm.hist[b - 1] : 0u;
       en[i] = sm.hist[b];
     }
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
+    for (int i = 0; i < RPT; ++i) if (i < nit) {
       const uint32_t p = i * NT + t;
       if (p >= n) continue;
       uint32_t r = st[i];
@@ -1132,10 +1152,12 @@ __device__ __forceinline__ bool select_store(Smem<CAP>& sm, const CArgs& a, bool
                                              uint32_t status) {
   constexpr int RPT = kRankPerLane;
   const uint32_t t = threadIdx.x;
+  // Iterations past the last candidate are skipped as a whole (n is uniform).
+  const uint32_t nit = uniform((n + NT - 1) / NT);
   u64 v[RPT];
   u64 lo = ~0ull, hi = 0;
 #pragma unroll
-  for (int i = 0; i < RPT; ++i) {
+  for (int i = 0; i < RPT; ++i) if (i < nit) {
     const uint32_t j = i * NT + t;
     v[i] = j < n ? sm.buf[j] : 0ull;   // 0: below every candidate
     if (j < n) {
@@ -1169,7 +1191,7 @@ __device__ __forceinline__ bool select_store(Smem<CAP>& sm, const CArgs& a, bool
   const uint32_t bl = bit_length64(hi - lo);
   const uint32_t shift = bl > kCutBits ? bl - kCutBits : 0u;
 #pragma unroll
-  for (int i = 0; i < RPT; ++i)
+  for (int i = 0; i < RPT; ++i) if (i < nit)
     if (i * NT + t < n)
       atomicAdd(&sm.hist[(kCutBins - 1) - static_cast<uint32_t>((v[i] - lo) >> shift)], 1u);
   __syncthreads();
@@ -1195,7 +1217,7 @@ __device__ __forceinline__ bool select_store(Smem<CAP>& sm, const CArgs& a, bool
       u64 mk[RPT];
       uint32_t wn = 0;
 #pragma unroll
-      for (int i = 0; i < RPT; ++i) {
+      for (int i = 0; i < RPT; ++i) if (i < nit) {
         mk[i] = ballot((i * NT + t < n) & (v[i] >= blo) & (v[i] <= bhi));
         wn += static_cast<uint32_t>(__popcll(mk[i]));
       }
@@ -1204,7 +1226,7 @@ __device__ __forceinline__ bool select_store(Smem<CAP>& sm, const CArgs& a, bool
         if (lane_id() == 0) base = atomicAdd(&sm.side_n, wn);
         base = uniform(base);
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) {
+        for (int i = 0; i < RPT; ++i) if (i < nit) {
           if ((mk[i] >> lane_id()) & 1ull) sm.side[base + mbcnt64(mk[i])] = v[i];
           base += static_cast<uint32_t>(__popcll(mk[i]));
         }
@@ -1231,7 +1253,7 @@ __device__ __forceinline__ bool select_store(Smem<CAP>& sm, const CArgs& a, bool
   u64 mk[RPT];
   uint32_t wn = 0;
 #pragma unroll
-  for (int i = 0; i < RPT; ++i) {
+  for (int i = 0; i < RPT; ++i) if (i < nit) {
     mk[i] = ballot((i * NT + t < n) & (v[i] >= T));
     wn += static_cast<uint32_t>(__popcll(mk[i]));
   }
@@ -1239,7 +1261,7 @@ __device__ __forceinline__ bool select_store(Smem<CAP>& sm, const CArgs& a, bool
   if (lane_id() == 0 && wn) base = atomicAdd(&sm.cnt_out, wn);
   base = uniform(base);
 #pragma unroll
-  for (int i = 0; i < RPT; ++i) {
+  for (int i = 0; i < RPT; ++i) if (i < nit) {
     if ((mk[i] >> lane_id()) & 1ull) store_one(a, bf16, xrow, out0 + base + mbcnt64(mk[i]), v[i], true, status);
     base += static_cast<uint32_t>(__popcll(mk[i]));
   }
@@ -1312,9 +1334,9 @@ __device__ __forceinline__ uint32_t row_len(const CArgs& a, int row, uint32_t* s
   return static_cast<uint32_t>(Ls);
 }
 
-// A whole row per workgroup, chunk by chunk (the next chunk's loads in flight).
+// A whole row per workgroup, chunk by chunk.
 template <bool BF16, int KC>
-__global__ __launch_bounds__(NT, 4) void chunk_row_kernel(CArgs a) {
+__global__ __launch_bounds__(NT, KC >= 2 ? 3 : 4) void chunk_row_kernel(CArgs a) {
   using G = Geo<BF16>;
   constexpr int KMAX = class_kmax(KC);
   constexpr int CAP = chunk_cap(KC);
@@ -1360,15 +1382,14 @@ __global__ __launch_bounds__(NT, 4) void chunk_row_kernel(CArgs a) {
   Buf B{0u, kTAll, 0};
   bool spec = false, nan = false;
   if (status == 0 && nch > 0) {
-    u32x4 ra[V], rb[V];
+    // One chunk in registers at a time: the workgroups sharing a CU (many
+    // rows) keep the loads in flight while this one filters.
+    u32x4 ra[V];
     load_chunk<BF16>(ra, xrow, chunk_at(0), L);
-    if (nch > 1) load_chunk<BF16>(rb, xrow, chunk_at(1), L);
     nan = start_chunk<BF16>(sm, B, ra, chunk_at(0), L, k, nch == 1, &spec);
     append_chunk<BF16>(sm, B, ra, chunk_at(0), k, cap);
     for (uint32_t j = 1; j < nch && !uniform(sm.err); ++j) {
-#pragma unroll
-      for (int i = 0; i < V; ++i) ra[i] = rb[i];
-      if (j + 1 < nch) load_chunk<BF16>(rb, xrow, chunk_at(j + 1), L);
+      load_chunk<BF16>(ra, xrow, chunk_at(j), L);
       nan |= next_chunk<BF16>(sm, B, ra, chunk_at(j), L, k, cap);
     }
   }
@@ -1528,11 +1549,23 @@ __global__ __launch_bounds__(NT, 4) void chunk_split_kernel(CArgs a) {
   const bool has_s = my_s < static_cast<uint32_t>(S);
   u64* my_slot = a.ws_slot + (static_cast<int64_t>(row) * S + my_s) * static_cast<int64_t>(k);
   const uint32_t per_round = PL * G8;
-  u64 v0[G8];
+  // A second round goes out with the first when a chunk's expected
+  // hand-over (its share estimate, plus the spread of a lane-maximum start)
+  // exceeds one round.
+  const float Es = static_cast<float>(k) * static_cast<float>(G::CE) / static_cast<float>(L > 0 ? L : 1u);
+  const bool two = per_round < k && 1.5f * (Es + 6.0f * __builtin_sqrtf(Es) + 8.0f) > static_cast<float>(per_round);
+  u64 v0[G8], v1[G8];
 #pragma unroll
   for (int q = 0; q < G8; ++q) {
     const uint32_t j = q * PL + my_l;
     v0[q] = (has_s && j < k) ? ld_agent(&my_slot[j]) : 0ull;
+  }
+  if (two) {
+#pragma unroll
+    for (int q = 0; q < G8; ++q) {
+      const uint32_t j = per_round + q * PL + my_l;
+      v1[q] = (has_s && j < k) ? ld_agent(&my_slot[j]) : 0ull;
+    }
   }
   const uint32_t my_c = has_s ? static_cast<uint32_t>(ld_agent(&rec[2 * my_s + 1])) : 0u;
   u64 Tm = 0;
@@ -1573,7 +1606,9 @@ __global__ __launch_bounds__(NT, 4) void chunk_split_kernel(CArgs a) {
 #pragma unroll
     for (int q = 0; q < G8; ++q) {
       const uint32_t j = rd * per_round + q * PL + my_l;
-      v[q] = rd == 0 ? v0[q] : ((has_s && j < my_c) ? ld_agent(&my_slot[j]) : 0ull);
+      v[q] = rd == 0 ? v0[q]
+           : (rd == 1 && two) ? v1[q]
+           : ((has_s && j < my_c) ? ld_agent(&my_slot[j]) : 0ull);
     }
     uint32_t n = 0;
 #pragma unroll
