@@ -77,6 +77,10 @@ typedef enum {
 } ds_status_t;
 
 #define DS_TOPK_MAX_K 4096            /* [NC coverage]: topk must be 4096 or less   */
+#define DS_TOPK_WS_HEADER_BYTES (256u << 10) /* the workspace's counter header: 32 B for
+                                               each of at most 8192 rows shared by
+                                               several workgroups (DS_TOPK_MAX_SPLIT_ROWS) */
+#define DS_TOPK_MAX_SPLIT_ROWS 8192   /* batch limit of a plan with segments > 1  */
 #define DS_ROW_NAN 1                  /* row_status bit: a NaN in x[i, 0:L)          */
 #define DS_ROW_BAD_END 2              /* row_status bit: end[i] < 0 or end[i] > n_cols */
 #define DS_ROW_INTERNAL 4             /* row_status bit: a consistency check inside the
@@ -112,9 +116,13 @@ typedef enum {
  *   row_status   device int32 [batch]: 0, or DS_ROW_NAN / DS_ROW_BAD_END, in
  *                which case the row's indices are -1 and values qNaN.
  *   workspace    device scratch of at least ds_topk_workspace_size(...)
- *                bytes, 16-B aligned, ZEROED before its first use; every call
- *                leaves it zeroed again.  May be NULL when that size is 0.
- *                Calls that may overlap in time need distinct workspaces.
+ *                bytes, 16-B aligned, ZEROED before its first use.  Its first
+ *                DS_TOPK_WS_HEADER_BYTES hold the per-row counters of rows
+ *                shared by several workgroups; every call leaves them zero
+ *                again.  The rest is scratch that every call writes before
+ *                it reads, so any content is fine there.  May be NULL when
+ *                that size is 0.  Calls that may overlap in time need
+ *                distinct workspaces.
  *   stream       HIP stream the single kernel launch is queued on.
  * Returns DS_OK or the first argument error found (nothing launched), or
  * DS_ERR_HIP if the launch failed.
@@ -130,7 +138,8 @@ ds_status_t ds_topk(const void* x, ds_dtype_t dtype, int64_t batch, int64_t n_co
  * DS_UNSORTED: the same set); the plan only changes speed.  ds_topk uses the
  * automatic plan.  [NC method]: blocks are visited in a random order and B,
  * B2 are tuning parameters.
- *   segments     workgroups that share one row (0 = automatic, else 1..256).
+ *   segments     workgroups that share one row (0 = automatic, else 1..256;
+ *                above 1 needs batch <= DS_TOPK_MAX_SPLIT_ROWS).
  *                With the chunk kernels any value above 1 means one
  *                workgroup per chunk of the row (at most 256 chunks).
  *   perm_seed    seed of the per-row block permutation (any value).

@@ -43,6 +43,8 @@ STATUS_NAMES = ["DS_OK", "DS_ERR_NULL", "DS_ERR_DTYPE", "DS_ERR_INDEX_DTYPE", "D
                 "DS_ERR_HIP", "DS_ERR_PLAN", "DS_ERR_SCRATCH_LIMIT"]
 DS_ERR_SCRATCH_LIMIT = 11
 DS_TOPK_NOALLOC_SCRATCH_BYTES = 16 << 20
+DS_TOPK_WS_HEADER_BYTES = 256 << 10
+DS_TOPK_MAX_SPLIT_ROWS = 8192
 
 
 class Plan(ctypes.Structure):
@@ -161,10 +163,12 @@ _workspaces: dict = {}
 
 
 def workspace_for(device: torch.device, stream_ptr: int, nbytes: int) -> torch.Tensor:
-    """A zeroed device buffer of at least ``nbytes`` for calls on one stream.
+    """A device buffer of at least ``nbytes`` for calls on one stream, zeroed
+    when allocated.
 
-    Every call leaves the workspace zeroed, so one buffer serves all calls that
-    are ordered on the same stream.
+    Every call leaves the workspace's counter header zero again (the rest is
+    scratch), so one buffer serves all calls that are ordered on the same
+    stream.
     """
     key = (device.index, stream_ptr)
     buf = _workspaces.get(key)

@@ -1540,8 +1540,9 @@ __global__ __launch_bounds__(NT, 4) void chunk_split_kernel(CArgs a) {
   // ---- merge: every chunk's candidates at or above the largest chunk threshold.
   // Chunk s's slots are read by lanes [s*PL, (s+1)*PL), PL = NT / S lanes per
   // chunk, G8 slots per lane per round.  The first round goes out together
-  // with the records, before the counts are known: slots past a chunk's count
-  // read as zero (the workspace is zero at rest), below every threshold.
+  // with the records, before the counts are known; what it read past a
+  // chunk's count (whatever an earlier call left there) is then replaced by
+  // zero, which is below every threshold.
   const u64* rec = a.ws_rec + static_cast<int64_t>(row) * S * 2;
   const uint32_t PL = static_cast<uint32_t>(NT / S);
   const uint32_t my_s = static_cast<uint32_t>(t) / PL;
@@ -1568,6 +1569,11 @@ __global__ __launch_bounds__(NT, 4) void chunk_split_kernel(CArgs a) {
     }
   }
   const uint32_t my_c = has_s ? static_cast<uint32_t>(ld_agent(&rec[2 * my_s + 1])) : 0u;
+#pragma unroll
+  for (int q = 0; q < G8; ++q) {
+    if (q * PL + my_l >= my_c) v0[q] = 0ull;
+    if (two && per_round + q * PL + my_l >= my_c) v1[q] = 0ull;
+  }
   u64 Tm = 0;
   uint32_t fl = 0, cm = 0;
   if (t < S) {
@@ -1635,19 +1641,8 @@ __global__ __launch_bounds__(NT, 4) void chunk_split_kernel(CArgs a) {
     B.count += total;
     __syncthreads();
   }
-  // Leave the workspace as it was found: zero.
-  for (uint32_t rd = 0; rd * per_round < cmax; ++rd) {
-#pragma unroll
-    for (int q = 0; q < G8; ++q) {
-      const uint32_t j = rd * per_round + q * PL + my_l;
-      if (has_s && j < my_c) st_agent(&my_slot[j], 0ull);
-    }
-  }
-  if (t < S) {
-    u64* wrec = a.ws_rec + static_cast<int64_t>(row) * S * 2;
-    st_agent(&wrec[2 * t], 0ull);
-    st_agent(&wrec[2 * t + 1], 0ull);
-  }
+  // The row's counter goes back to zero; slots and records need no clearing
+  // (every call writes them before reading).
   if (t == 0) st_agent(&a.ws_arrive[row], 0u);
   if (uniform(sm.err)) status |= DS_ROW_INTERNAL;
   // The check: every chunk kept all of its values at or above its own

@@ -115,6 +115,12 @@ ds_status_t resolve_plan(int64_t batch, int64_t n_cols, int32_t k, ds_dtype_t dt
     pl.seed = p->perm_seed;
     pl.in_order = p->in_order;
   }
+  // Rows shared by several workgroups keep their counters in the
+  // workspace's fixed header, which has room for kMaxSplitRows of them.
+  if (pl.segments > 1 && batch > kMaxSplitRows) {
+    if (p && p->segments > 1) return DS_ERR_PLAN;
+    pl.segments = 1;
+  }
   *out = pl;
   return DS_OK;
 }
@@ -165,18 +171,34 @@ ds_status_t validate(const void* x, ds_dtype_t dtype, int64_t batch, int64_t n_c
 
 namespace dstk {
 
+// The workspace starts with a header of per-row counters at fixed offsets,
+// the same for every (batch, segments, k) and both kernels: the only words
+// that must be zero when a call starts, and every call leaves them zero.
+// Everything after it is written before it is read within a call, so calls
+// with different layouts can share one workspace without clearing it.
+//   [0, 8R)    u64 shared threshold per row (stream kernel)
+//   [8R, 16R)  u64 largest estimated start per row (stream kernel)
+//   [16R, 20R) u32 arrival count per row (both kernels)
+//   [20R, 24R) u32 status OR per row (stream kernel)
+//   [24R, 28R) u32 fill cursor per row (stream kernel)
+// with R = kMaxSplitRows.
+namespace {
+constexpr size_t kR = static_cast<size_t>(kMaxSplitRows);
+static_assert(28 * kR <= kWsHeaderBytes, "the header holds every counter");
+}  // namespace
+
 WsLayout ws_layout(int64_t batch, int segments, int k) {
-  auto up = [](size_t v) { return (v + 15) & ~static_cast<size_t>(15); };
+  auto up = [](size_t v) { return (v + 255) & ~static_cast<size_t>(255); };
   WsLayout l{};
   const size_t b = static_cast<size_t>(batch);
   const size_t s = static_cast<size_t>(segments);
   l.thr = 0;
-  l.done = up(l.thr + b * 8);
-  l.flags = up(l.done + b * 4);
-  l.fill = up(l.flags + b * 4);
-  l.x = up(l.fill + b * 4);
-  l.spec = up(l.x + b * s * 8);
-  l.comp = up(l.spec + b * 8);
+  l.spec = 8 * kR;
+  l.done = 16 * kR;
+  l.flags = 20 * kR;
+  l.fill = 24 * kR;
+  l.x = kWsHeaderBytes;
+  l.comp = up(l.x + b * s * 8);
   l.total = up(l.comp + b * s * (static_cast<size_t>(k) + kStreamSlotSlack) * 8);
   return l;
 }
@@ -186,8 +208,8 @@ ChunkWs chunk_ws_layout(int64_t batch, int segments, int k) {
   ChunkWs l{};
   const size_t b = static_cast<size_t>(batch);
   const size_t s = static_cast<size_t>(segments);
-  l.arrive = 0;
-  l.rec = up(b * 4);
+  l.arrive = 16 * kR;
+  l.rec = kWsHeaderBytes;
   l.slot = up(l.rec + b * s * 16);
   l.total = up(l.slot + b * s * static_cast<size_t>(k) * 8);
   return l;

@@ -7,12 +7,18 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include "ds_topk.h"
+
 namespace dstk {
 
 // Fixed geometry shared by host planning and the kernels.
 constexpr int kBlockElems = 4096;   // B: contiguous elements per block (both dtypes)
 constexpr int kNumCU = 256;         // MI355X compute units (planning constant)
 constexpr int kMaxSegments = 256;
+// Rows a plan may share between workgroups, and the workspace header that
+// holds their counters (DS_TOPK_MAX_SPLIT_ROWS, DS_TOPK_WS_HEADER_BYTES).
+constexpr int64_t kMaxSplitRows = DS_TOPK_MAX_SPLIT_ROWS;
+constexpr size_t kWsHeaderBytes = DS_TOPK_WS_HEADER_BYTES;
 
 // k classes: each has its own buffer capacity, threads per workgroup and trigger.
 constexpr int kNumClasses = 4;

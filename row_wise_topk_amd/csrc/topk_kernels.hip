@@ -1942,16 +1942,14 @@ __global__ __launch_bounds__(kernel_threads(CLS, BF16 ? 1 : 0, MULTI), kWavesPer
   }
 
   if (MULTI) {
-    // Hand the survivors to the row's last workgroup.  When the row's whole
-    // survivor array (k + kSmallBin slots per workgroup) fits the merge's
-    // first two chunks, each workgroup fills its own slots from the start:
-    // the array is all zero between calls and zero is never above a
-    // threshold, so the merge reads every slot and no count is needed.
-    // Otherwise each workgroup reserves a range of the row's contiguous
-    // array with one atomic and fills it, and the merge reads up to the
-    // row's fill.  Every shared word is written and read with agent-scope
-    // atomic accesses, and the stores are complete before the arrival
-    // counter moves, so no L2 write-back or invalidate is needed.
+    // Hand the survivors to the row's last workgroup.  Each workgroup
+    // reserves a range of the row's contiguous array with one atomic on the
+    // row's fill cursor and fills all of it, and the merge reads up to the
+    // row's fill, so the array needs no clearing between calls (slots past
+    // the fill hold whatever an earlier call left).  Every shared word is
+    // written and read with agent-scope atomic accesses, and the stores are
+    // complete before the arrival counter moves, so no L2 write-back or
+    // invalidate is needed.
     constexpr int PER_FIT = (8 * (KMAX + static_cast<int>(kSmallBin)) + 2 * NT - 1) / (2 * NT);
     constexpr int PER_ROOM = (CAP - (3 * KMAX + class_trigger(CLS)) / 4) / NT;
     constexpr int PER_A = PER_FIT > 9 ? 9 : PER_FIT;
@@ -1960,7 +1958,7 @@ __global__ __launch_bounds__(kernel_threads(CLS, BF16 ? 1 : 0, MULTI), kWavesPer
     static_assert(PER * NT + (3 * KMAX + class_trigger(CLS)) / 4 <= CAP, "merge chunk room");
     constexpr uint32_t CHUNK = PER * NT;
     const uint32_t area = static_cast<uint32_t>(S) * (k + kSmallBin);
-    const bool fixed_slots = area <= 2u * CHUNK;
+    constexpr bool fixed_slots = false;
     const uint32_t c = uniform(sm.cnt[cur]);
     const u64 Tk = (x_only && !cut) ? t_keep : uniform64(sm.thr);
     u64* wsc = reinterpret_cast<u64*>(a.ws_comp) + static_cast<int64_t>(row) * S * (k + kSmallBin);
@@ -2007,6 +2005,11 @@ __global__ __launch_bounds__(kernel_threads(CLS, BF16 ? 1 : 0, MULTI), kWavesPer
         }
       }
     });
+    // Every reserved slot is written: should fewer than `mine` candidates
+    // pass (never expected), the rest of the range gets zero, which no
+    // threshold admits.
+    __syncthreads();
+    for (uint32_t j = uniform(sm.cnt[cur ^ 1]) + t; j < mine; j += NT) st_agent(&wsc[own0 + j], 0ull);
     wait_all_memory();
     __syncthreads();
     if (t == 0) {
@@ -2023,8 +2026,9 @@ __global__ __launch_bounds__(kernel_threads(CLS, BF16 ? 1 : 0, MULTI), kWavesPer
     // than ceil(k / S) survivors).
     // Every load goes out at once: the row's counters and bounds first (so
     // that using them waits for nothing else), then the first two chunks of
-    // survivor slots.  The slots need no count: unused ones are zero, and
-    // zero is never above a threshold.  A chunk is at most 9 slots per
+    // survivor slots, before the row's fill is known: positions at or past
+    // the fill (whatever an earlier call left there) are dropped once it
+    // is.  A chunk is at most 9 slots per
     // thread: two chunks hold the slots of up to 4 workgroups at k near the
     // class's largest (all of them, for the sampler and indexer shapes) in
     // one round trip, and the registers stay clear of the spills whose
@@ -2032,8 +2036,7 @@ __global__ __launch_bounds__(kernel_threads(CLS, BF16 ? 1 : 0, MULTI), kWavesPer
     // also fit in the buffer after a cut (at most k + slack candidates
     // remain).
     // Loads of one chunk; positions past the array read position 0 (a valid
-    // address) and are dropped.  Every used position read is cleared, so the
-    // workspace is all zero again when the call ends.
+    // address) and are dropped.
     auto load_chunk = [&](uint32_t c0, u64 (&mv)[PER]) {
 #pragma unroll
       for (int q = 0; q < PER; ++q) {
@@ -2055,7 +2058,6 @@ __global__ __launch_bounds__(kernel_threads(CLS, BF16 ? 1 : 0, MULTI), kWavesPer
     u64 va[PER], vb[PER];
     load_chunk(0, va);
     load_chunk(CHUNK, vb);
-    if (t < S) st_agent(xp, 0ull);
     xs = wave_extreme64<false>(xs);
     if (lane == 0 && t < S) atomicMin(&sm.rng[0], xs);   // rng[0] was set before the arrival count
     if (t == 0) {
@@ -2077,13 +2079,6 @@ __global__ __launch_bounds__(kernel_threads(CLS, BF16 ? 1 : 0, MULTI), kWavesPer
       sm.thr = T0;
       if (xmin > sm.tvalid) sm.tvalid = xmin;
     }
-    auto clear_chunk = [&](uint32_t c0, const u64 (&mv)[PER]) {   // every used position
-#pragma unroll
-      for (int q = 0; q < PER; ++q) {
-        const uint32_t p = c0 + t + q * NT;
-        if ((p < total) & (!fixed_slots | (mv[q] != 0ull))) st_agent(&wsc[p], 0ull);
-      }
-    };
     u64 Tm = T0;
     // Appended candidates above the row's largest estimated start (checked
     // after the merge).  A cut inside the merge can only drop candidates at
@@ -2144,12 +2139,8 @@ __global__ __launch_bounds__(kernel_threads(CLS, BF16 ? 1 : 0, MULTI), kWavesPer
     };
     for (uint32_t c0 = 0; c0 < total; c0 += 2 * CHUNK) {
       merge_chunk(c0, va);
-      clear_chunk(c0, va);
       if (c0 + 2 * CHUNK < total) load_chunk(c0 + 2 * CHUNK, va);
-      if (c0 + CHUNK < total) {
-        merge_chunk(c0 + CHUNK, vb);
-        clear_chunk(c0 + CHUNK, vb);
-      }
+      if (c0 + CHUNK < total) merge_chunk(c0 + CHUNK, vb);
       if (c0 + 3 * CHUNK < total) load_chunk(c0 + 3 * CHUNK, vb);
     }
     n_above = static_cast<uint32_t>(

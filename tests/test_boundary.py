@@ -126,6 +126,14 @@ def test_workspace_rules():
     c = rt.ds_topk_workspace_size_ex(rt.DS_FP32, 64, 129280, 1024, {"kernel": 2, "segments": 2})
     assert c == rt.ds_topk_workspace_size(rt.DS_FP32, 64, 129280, 1024)
     assert c >= 64 * 16 * 1024 * 8
+    # Every split layout starts after the fixed counter header.
+    assert c > rt.DS_TOPK_WS_HEADER_BYTES and s4 > rt.DS_TOPK_WS_HEADER_BYTES
+    # Rows shared by workgroups are limited to the header's capacity: an
+    # explicit split beyond it is refused, the automatic plan does not split.
+    big = rt.DS_TOPK_MAX_SPLIT_ROWS + 1
+    assert rt.ds_topk_workspace_size_ex(rt.DS_FP32, big, 129280, 64, {"segments": 4, "kernel": 1}) == 0
+    assert _v(batch=big, n_cols=8192, row_stride=8192, k=64, plan={"segments": 4, "kernel": 1}) == ERR["DS_ERR_PLAN"]
+    assert rt.ds_topk_workspace_size(rt.DS_FP32, big, 8192, 64) == 0
     # A plan's kernel field is checked.
     assert rt.ds_topk_workspace_size_ex(rt.DS_FP32, 64, 129280, 1024, {"kernel": 3}) == 0
     # Invalid arguments give 0.
