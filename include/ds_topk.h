@@ -152,6 +152,9 @@ ds_status_t ds_topk(const void* x, ds_dtype_t dtype, int64_t batch, int64_t n_co
  *                DS_KERNEL_CHUNK (2): a workgroup holds 32 KiB of a row in
  *                registers at a time (rows of up to 64 chunks: 524,288 fp32 or
  *                1,048,576 bf16 values).
+ *   stats        NULL, or a device uint32 array [batch * 4], 4-B aligned, to
+ *                which the call ADDS per-row counts at [4 i + DS_STAT_*] (the
+ *                caller zeroes it); results are unchanged.  A debug aid.
  */
 typedef struct {
   int32_t segments;
@@ -159,7 +162,17 @@ typedef struct {
   int32_t in_order;
   int32_t flush_at;
   int32_t kernel;
+  uint32_t* stats;
 } ds_topk_plan_t;
+
+/* Per-row statistics (plan.stats): the debug counters of the method's
+ * data-dependent paths.  A re-read is the only extra input traffic the
+ * method makes: a start estimated from part of a row that turns out too high
+ * makes the row (or one chunk of a split row) be read again. */
+#define DS_STAT_ROW_REREADS 0        /* whole-row re-reads                               */
+#define DS_STAT_CHUNK_REREADS 1      /* chunks of a split row appended again from memory */
+#define DS_STAT_CUTS 2               /* radix cuts back to k (streaming, merge, final)   */
+#define DS_STAT_FINAL_CANDIDATES 3   /* candidates entering the row's final selection    */
 
 #define DS_KERNEL_AUTO 0
 #define DS_KERNEL_STREAM 1

@@ -44,14 +44,16 @@ STATUS_NAMES = ["DS_OK", "DS_ERR_NULL", "DS_ERR_DTYPE", "DS_ERR_INDEX_DTYPE", "D
 DS_ERR_SCRATCH_LIMIT = 11
 DS_TOPK_NOALLOC_SCRATCH_BYTES = 16 << 20
 DS_TOPK_WS_HEADER_BYTES = 256 << 10
+DS_STAT_ROW_REREADS, DS_STAT_CHUNK_REREADS, DS_STAT_CUTS, DS_STAT_FINAL_CANDIDATES = 0, 1, 2, 3
 DS_TOPK_MAX_SPLIT_ROWS = 8192
 
 
 class Plan(ctypes.Structure):
-    """ds_topk_plan_t: segments, perm_seed, in_order, flush_at, kernel (0 = automatic)."""
+    """ds_topk_plan_t: segments, perm_seed, in_order, flush_at, kernel (0 =
+    automatic), stats (device pointer to uint32 [batch * 4] or None)."""
     _fields_ = [("segments", ctypes.c_int32), ("perm_seed", ctypes.c_uint32),
                 ("in_order", ctypes.c_int32), ("flush_at", ctypes.c_int32),
-                ("kernel", ctypes.c_int32)]
+                ("kernel", ctypes.c_int32), ("stats", ctypes.c_void_p)]
 
 
 if not os.path.exists(LIB_PATH):
@@ -97,7 +99,7 @@ def _plan_ptr(plan):
         return ctypes.pointer(plan)
     p = Plan(int(plan.get("segments", 0)), int(plan.get("perm_seed", 0x5EED)) & 0xFFFFFFFF,
              int(plan.get("in_order", 0)), int(plan.get("flush_at", 0)),
-             int(plan.get("kernel", 0)))
+             int(plan.get("kernel", 0)), plan.get("stats"))
     return ctypes.pointer(p)
 
 

@@ -192,6 +192,7 @@ struct Smem {
   uint32_t side_n;
   uint32_t cnt_out;
   uint32_t err;
+  uint32_t n_cut;                     // cuts back to k made by this workgroup (statistics)
   uint32_t is_last;
   u64 res64;
 };
@@ -459,6 +460,7 @@ __device__ __forceinline__ void for_buf(const Smem<CAP>& sm, uint32_t n, F&& f) 
 template <int CAP>
 __device__ __noinline__ u64 cut_exact(Smem<CAP>& sm, uint32_t n, uint32_t keep) {
   const int t = threadIdx.x;
+  if (t == 0) sm.n_cut += 1u;
   // Live range of the composites.
   u64 lo = ~0ull, hi = 0;
   for_buf<8>(sm, n, [&](u64 v, bool ok) {
@@ -1268,6 +1270,12 @@ __device__ __forceinline__ bool select_store(Smem<CAP>& sm, const CArgs& a, bool
   return true;
 }
 
+// Per-row statistics, when the caller asked for them (a.stats non-null):
+// counts added with device-scope atomics by lane 0 of the workgroup.
+__device__ __forceinline__ void stat_add(const CArgs& a, int row, int field, uint32_t v) {
+  if (a.stats && threadIdx.x == 0 && v) atomicAdd(&a.stats[4 * static_cast<int64_t>(row) + field], v);
+}
+
 // The epilogue of a row: the buffer holds `count` candidates, a superset of
 // the top m = min(k, L) (m = 0 for a flagged row).  Cut to exactly m, order,
 // write.
@@ -1278,6 +1286,7 @@ __device__ __forceinline__ void finish_row(Smem<CAP>& sm, const CArgs& a, bool b
   const int t = threadIdx.x;
   const uint32_t k = static_cast<uint32_t>(a.k);
   uint32_t m = status ? 0u : min(k, L);
+  stat_add(a, row, DS_STAT_FINAL_CANDIDATES, count);
   __syncthreads();
   const int64_t out0 = static_cast<int64_t>(row) * k;
   const char* xrow = static_cast<const char*>(a.x) + static_cast<int64_t>(row) * a.row_stride * (bf16 ? 2 : 4);
@@ -1288,6 +1297,7 @@ __device__ __forceinline__ void finish_row(Smem<CAP>& sm, const CArgs& a, bool b
        (a.sorted == 1 && rank_store(sm, a, bf16, xrow, out0, count, m, status)))) {
     for (uint32_t e = m + t; e < k; e += NT) store_one(a, bf16, xrow, out0 + e, 0ull, false, status);
     if (t == 0) a.row_status[row] = static_cast<int32_t>(status);
+    stat_add(a, row, DS_STAT_CUTS, sm.n_cut);
     return;
   }
   if (m > 0 && count > m) {
@@ -1309,6 +1319,7 @@ __device__ __forceinline__ void finish_row(Smem<CAP>& sm, const CArgs& a, bool b
       store_one(a, bf16, xrow, out0 + e, e < m ? sm.buf[e] : 0ull, e < m, status);
   }
   if (t == 0) a.row_status[row] = static_cast<int32_t>(status);
+  stat_add(a, row, DS_STAT_CUTS, sm.n_cut);
 }
 
 // OR of a per-lane flag over the workgroup (flag bits are small).
@@ -1377,7 +1388,10 @@ __global__ __launch_bounds__(NT, KC >= 2 ? 3 : 4) void chunk_row_kernel(CArgs a)
   };
 
   for (int i = t; i < kCutBins / 4; i += NT) reinterpret_cast<u32x4*>(sm.hist)[i] = u32x4{0u, 0u, 0u, 0u};
-  if (t == 0) sm.err = 0u;
+  if (t == 0) {
+    sm.err = 0u;
+    sm.n_cut = 0u;
+  }
 
   Buf B{0u, kTAll, 0};
   bool spec = false, nan = false;
@@ -1400,6 +1414,7 @@ __global__ __launch_bounds__(NT, KC >= 2 ? 3 : 4) void chunk_row_kernel(CArgs a)
   // above it, a value of the top k may lie below it.
   if (status == 0 && spec && B.count < min(k, L)) {
     B = restream<BF16>(sm, B.par, xrow, L, k, cap);
+    stat_add(a, row, DS_STAT_ROW_REREADS, 1u);
     if (uniform(sm.err)) status |= DS_ROW_INTERNAL;
   }
   finish_row<KMAX>(sm, a, BF16, row, B.count, L, status);
@@ -1429,7 +1444,10 @@ __global__ __launch_bounds__(NT, 4) void chunk_split_kernel(CArgs a) {
   const bool mine = static_cast<uint32_t>(seg) < nch;
 
   for (int i = t; i < kCutBins / 4; i += NT) reinterpret_cast<u32x4*>(sm.hist)[i] = u32x4{0u, 0u, 0u, 0u};
-  if (t == 0) sm.err = 0u;
+  if (t == 0) {
+    sm.err = 0u;
+    sm.n_cut = 0u;
+  }
 
   Buf B{0u, kTAll, 0};
   bool nan = false, spec = false;
@@ -1458,6 +1476,7 @@ __global__ __launch_bounds__(NT, 4) void chunk_split_kernel(CArgs a) {
     B.par ^= 1;
     if (over) {
       B = reappend_chunk<BF16>(sm, B, xrow, static_cast<uint32_t>(seg), L, k, cap);
+      stat_add(a, row, DS_STAT_CHUNK_REREADS, 1u);
     } else {
       regions = true;
       B.count = total;
@@ -1535,7 +1554,10 @@ __global__ __launch_bounds__(NT, 4) void chunk_split_kernel(CArgs a) {
     sm.is_last = prev == static_cast<uint32_t>(S - 1) ? 1u : 0u;
   }
   __syncthreads();
-  if (!uniform(sm.is_last)) return;
+  if (!uniform(sm.is_last)) {
+    stat_add(a, row, DS_STAT_CUTS, sm.n_cut);
+    return;
+  }
 
   // ---- merge: every chunk's candidates at or above the largest chunk threshold.
   // Chunk s's slots are read by lanes [s*PL, (s+1)*PL), PL = NT / S lanes per
@@ -1651,6 +1673,7 @@ __global__ __launch_bounds__(NT, 4) void chunk_split_kernel(CArgs a) {
   // With at least min(k, L) of them, the top min(k, L) are all here.
   if (status == 0 && B.count < min(k, L)) {
     B = restream<BF16>(sm, B.par, xrow, L, k, cap);
+    stat_add(a, row, DS_STAT_ROW_REREADS, 1u);
     if (uniform(sm.err)) status |= DS_ROW_INTERNAL;
   }
   finish_row<KMAX>(sm, a, BF16, row, B.count, L, status);

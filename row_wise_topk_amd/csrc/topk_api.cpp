@@ -160,6 +160,7 @@ ds_status_t validate(const void* x, ds_dtype_t dtype, int64_t batch, int64_t n_c
   if (misaligned(indices, index_dtype == DS_INT64 ? 8 : 4)) return DS_ERR_ALIGN;
   if (return_values && misaligned(values, static_cast<uintptr_t>(es))) return DS_ERR_ALIGN;
   if (misaligned(row_status, 4) || (end && misaligned(end, 4))) return DS_ERR_ALIGN;
+  if (plan && plan->stats && misaligned(plan->stats, 4)) return DS_ERR_ALIGN;
   if (batch * static_cast<int64_t>(pl->segments) > INT32_MAX) return DS_ERR_SHAPE;
   const size_t need = workspace_bytes_for(*pl, batch, k);
   if (need > 0 && (!workspace || workspace_bytes < need || misaligned(workspace, 16)))
@@ -263,6 +264,7 @@ ds_status_t ds_topk_ex(const void* x, ds_dtype_t dtype, int64_t batch, int64_t n
     // longest-first when their lengths vary.
     c.reverse_rows = (pl.segments == 1 && end != nullptr) ? 1 : 0;
     c.cap_eff = static_cast<uint32_t>(pl.trigger);
+    c.stats = plan ? plan->stats : nullptr;
     if (pl.segments > 1) {
       const ChunkWs l = chunk_ws_layout(batch, pl.segments, k);
       char* w = static_cast<char*>(workspace);
@@ -291,6 +293,7 @@ ds_status_t ds_topk_ex(const void* x, ds_dtype_t dtype, int64_t batch, int64_t n
   a.perm_seed = pl.seed;
   a.in_order = pl.in_order;
   a.trigger = pl.trigger;
+  a.stats = plan ? plan->stats : nullptr;
   if (pl.segments > 1) {
     const WsLayout l = ws_layout(batch, pl.segments, k);
     char* w = static_cast<char*>(workspace);

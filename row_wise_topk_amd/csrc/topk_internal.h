@@ -88,6 +88,7 @@ struct CArgs {
   uint32_t* ws_arrive;            // [batch] arrivals per row, zero at rest
   unsigned long long* ws_rec;     // [batch * segments * 2] threshold, (status << 32) | count
   unsigned long long* ws_slot;    // [batch * segments * k] candidate composites
+  uint32_t* stats;                // nullable: [batch * 4] counts added per row (DS_STAT_*)
 };
 
 struct ChunkWs {
@@ -129,6 +130,7 @@ struct KArgs {
   unsigned long long* ws_x;     // [batch * segments]  per-workgroup merge bound
   unsigned long long* ws_spec;  // [batch]  largest estimated start used on the row (0: none)
   unsigned long long* ws_comp;  // [batch * segments * (k + 64)]  candidate composites, contiguous per row
+  uint32_t* stats;              // nullable: [batch * 4] counts added per row (DS_STAT_*)
 };
 
 // Workspace layout for `segments` workgroups per row (bytes, 16-B aligned parts).

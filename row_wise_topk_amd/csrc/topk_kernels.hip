@@ -274,6 +274,8 @@ struct Smem {
   uint32_t bt[5];             // first-block start: min key, max key, t0 key, t2 key, ring count
   u64 specmax;                // merge: the largest estimated start used on the row (0: none)
   u64 tvalid;                 // merge: the largest bound known to leave k of the row above it
+  uint32_t n_cut;             // statistics: cuts made by this workgroup
+  uint32_t n_reread;          // statistics: whole-row re-reads by this workgroup
 };
 
 // A thread's own run of BPT consecutive bins, read and written 16 bytes at a
@@ -606,7 +608,10 @@ __device__ __noinline__ int cut_buffer(Smem<CAP, NT>& sm, int cur, uint32_t k,
   const int t = threadIdx.x, lane = t & 63;
   const uint32_t hk = wave_max(hi_key);
   if (lane == 0) atomicMax(&sm.hikey, hk);
-  if (t == 0) sm.cnt[cur ^ 1] = 0u;
+  if (t == 0) {
+    sm.cnt[cur ^ 1] = 0u;
+    sm.n_cut += 1u;
+  }
   __syncthreads();
   const uint32_t c = min(uniform(sm.cnt[cur]), static_cast<uint32_t>(CAP));
   const u64 T = uniform64(sm.thr);
@@ -756,6 +761,7 @@ __device__ __forceinline__ int small_cut(Smem<CAP, NT>& sm, int cur, uint32_t k,
   static_assert(G * NT + static_cast<int>(kSmallBin) <= CAP, "small cut room");
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int nxt = cur ^ 1;
+  if (t == 0) sm.n_cut += 1u;
   const uint32_t c = min(uniform(sm.cnt[cur]), static_cast<uint32_t>(CAP));
   const u64 T = uniform64(sm.thr);
   const uint32_t hi = uniform(sm.hikey);
@@ -1530,6 +1536,8 @@ __global__ __launch_bounds__(kernel_threads(CLS, BF16 ? 1 : 0, MULTI), kWavesPer
     sm.cnt[1] = 0u;
     sm.hikey = 0u;
     sm.flags = 0u;
+    sm.n_cut = 0u;
+    sm.n_reread = 0u;
     sm.thr = kThrInit;
     sm.bt[0] = 0xFFFFFFFFu;   // the start's reductions, used once, start here
     sm.bt[1] = 0u;
@@ -1785,6 +1793,7 @@ __global__ __launch_bounds__(kernel_threads(CLS, BF16 ? 1 : 0, MULTI), kWavesPer
     if (t == 0) {
       sm.cnt[cur] = 0u;
       sm.thr = sm.tvalid;
+      sm.n_reread += 1u;
     }
     __syncthreads();
     thr = uniform64(sm.thr);
@@ -2019,7 +2028,10 @@ __global__ __launch_bounds__(kernel_threads(CLS, BF16 ? 1 : 0, MULTI), kWavesPer
       sm.is_last = prev == static_cast<uint32_t>(S - 1) ? 1u : 0u;
     }
     __syncthreads();
-    if (!uniform(sm.is_last)) return;
+    if (!uniform(sm.is_last)) {
+      if (a.stats && t == 0 && sm.n_cut) atomicAdd(&a.stats[4 * static_cast<int64_t>(row) + DS_STAT_CUTS], sm.n_cut);
+      return;
+    }
 
     // Last arrival: merge every workgroup's survivors.  Start from the largest
     // of the shared threshold and min_seg x_seg (0 if any workgroup had fewer
@@ -2179,7 +2191,13 @@ __global__ __launch_bounds__(kernel_threads(CLS, BF16 ? 1 : 0, MULTI), kWavesPer
   }
 
   status |= sm.flags;
+  if (a.stats && t == 0) {
+    uint32_t* st = a.stats + 4 * static_cast<int64_t>(row);
+    if (sm.n_reread) atomicAdd(&st[DS_STAT_ROW_REREADS], sm.n_reread);
+    atomicAdd(&st[DS_STAT_FINAL_CANDIDATES], uniform(sm.cnt[cur]));
+  }
   write_outputs<NT, CAP, SORT_CAP>(sm, a, BF16, row, cur, status, L);
+  if (a.stats && t == 0 && sm.n_cut) atomicAdd(&a.stats[4 * static_cast<int64_t>(row) + DS_STAT_CUTS], sm.n_cut);
 }
 
 // ---------------------------------------------------------------- read ceiling

@@ -1,0 +1,70 @@
+"""Debug counters of the data-dependent paths (plan.stats), on the six
+workloads at full size.
+
+Per row the library adds: whole-row re-reads, chunk re-reads (a split row's
+chunk appended again from memory), radix cuts back to k, and the candidates
+entering the final selection.  A re-read is the only extra input traffic the
+method makes (a start estimated from part of a row that turns out too high),
+so none may happen on these workloads.  A row built to defeat the estimate
+shows that the counter does count.  The counts are printed for the record.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import workloads
+from tests.gpu_util import FP32, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_with_stats(x_np, w, end_np, plan=None):
+    import torch
+    import row_wise_topk_amd as rt
+    xt = to_device(x_np, w.dtype)[:, : w.n_cols]
+    stats = torch.zeros(w.batch * 4, dtype=torch.int32, device="cuda")
+    p = dict(plan or {}, stats=stats.data_ptr())
+    endt = None if end_np is None else torch.from_numpy(end_np).cuda()
+    it = torch.int64 if w.index_dtype == "int64" else torch.int32
+    _, _, st = rt.topk(xt, w.k, end=endt, sorted=w.sorted, return_values=w.return_values,
+                       index_dtype=it, plan=p)
+    torch.cuda.synchronize()
+    assert int(st.abs().sum().item()) == 0
+    return stats.view(w.batch, 4).cpu().numpy()
+
+
+@pytest.mark.parametrize("num", [1, 2, 3, 4, 5, 6])
+def test_no_rereads_on_the_workloads(num):
+    import row_wise_topk_amd as rt
+    w = workloads.workload(num)
+    print(f"[stats] {w.name}: generating", flush=True)
+    x, end = workloads.make_input(w)
+    s = _run_with_stats(x, w, end)
+    del x
+    L = np.full(w.batch, w.n_cols, dtype=np.int64) if end is None else np.minimum(end, w.n_cols)
+    fin = s[:, rt.DS_STAT_FINAL_CANDIDATES]
+    print(f"[stats] {w.name}: row re-reads {int(s[:, rt.DS_STAT_ROW_REREADS].sum())}, "
+          f"chunk re-reads {int(s[:, rt.DS_STAT_CHUNK_REREADS].sum())}, "
+          f"cuts per row mean {s[:, rt.DS_STAT_CUTS].mean():.2f} max {int(s[:, rt.DS_STAT_CUTS].max())}, "
+          f"final candidates per row mean {fin.mean():.1f} max {int(fin.max())} "
+          f"(k = {w.k})", flush=True)
+    assert int(s[:, rt.DS_STAT_ROW_REREADS].sum()) == 0
+    assert int(s[:, rt.DS_STAT_CHUNK_REREADS].sum()) == 0
+    # Every row's final selection sees at least its min(k, L) results.
+    assert (fin >= np.minimum(w.k, L)).all()
+
+
+def test_reread_counter_counts():
+    """One chunk holds every large value: the split row's share estimate is
+    too high, the merge check fails and the row is read again."""
+    import row_wise_topk_amd as rt
+    ce = 8192
+    n = 6 * ce
+    rng = np.random.Generator(np.random.PCG64(501))
+    f = rng.standard_normal((2, n)).astype(np.float32)
+    f[:, 2 * ce:3 * ce] += np.float32(50.0)
+    w = workloads.workload(1, batch=2, n_cols=n, k=1024)
+    s = _run_with_stats(f, w, None, plan={"kernel": rt.DS_KERNEL_CHUNK, "segments": 2})
+    print(f"[stats] hot chunk: {s.tolist()}", flush=True)
+    assert (s[:, rt.DS_STAT_ROW_REREADS] == 1).all()
