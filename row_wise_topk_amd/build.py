@@ -13,7 +13,9 @@ LIB = os.path.join(PKG, "libdstopk.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}"]
-# Device code: gfx950 only; packed fp32 instructions disabled.
+# Device code: gfx950 only; packed fp32 instructions disabled.  No fast-math
+# and no denormal-flush option: the kernels compare values as floats, and
+# subnormals must order exactly (the default keeps them).
 DEVICE = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
