@@ -1014,20 +1014,15 @@ constexpr uint32_t kBinRankMax = 128;
 constexpr int kRankPerLane = 16;
 
 template <int CAP>
-__device__ __forceinline__ bool rank_store(Smem<CAP>& sm, const CArgs& a, bool bf16,
-                                           const char* xrow, int64_t out0, uint32_t n, uint32_t m,
-                                           uint32_t status) {
+__device__ __forceinline__ bool rank_core(Smem<CAP>& sm, const CArgs& a, bool bf16,
+                                          const char* xrow, int64_t out0, u64 (&v)[kRankPerLane],
+                                          uint32_t nit, uint32_t n, uint32_t m, uint32_t status) {
   constexpr int RPT = kRankPerLane;
   const uint32_t t = threadIdx.x;
-  // Iterations past the last candidate are skipped as a whole (n is uniform).
-  const uint32_t nit = uniform((n + NT - 1) / NT);
-  u64 v[RPT];
   u64 lo = ~0ull, hi = 0;
 #pragma unroll
   for (int i = 0; i < RPT; ++i) if (i < nit) {
-    const uint32_t j = i * NT + t;
-    v[i] = sm.buf[j < n ? j : 0u];
-    if (j < n) {
+    if (v[i] != 0ull) {
       lo = v[i] < lo ? v[i] : lo;
       hi = v[i] > hi ? v[i] : hi;
     }
@@ -1065,7 +1060,7 @@ __device__ __forceinline__ bool rank_store(Smem<CAP>& sm, const CArgs& a, bool b
   auto bin_of = [&](u64 x) { return (kCutBins - 1) - static_cast<uint32_t>((red(x) - rlo) >> shift); };
 #pragma unroll
   for (int i = 0; i < RPT; ++i) if (i < nit)
-    if (i * NT + t < n) atomicAdd(&sm.hist[bin_of(v[i])], 1u);
+    if (v[i] != 0ull) atomicAdd(&sm.hist[bin_of(v[i])], 1u);
   __syncthreads();
   // Own bins: the largest, then each bin's first position.
   uint32_t h[kCutBPT], sum = 0, big = 0;
@@ -1097,31 +1092,34 @@ __device__ __forceinline__ bool rank_store(Smem<CAP>& sm, const CArgs& a, bool b
   // bin b-1 ends (bin 0 at 0).
 #pragma unroll
   for (int i = 0; i < RPT; ++i) if (i < nit)
-    if (i * NT + t < n) sm.buf[atomicAdd(&sm.hist[bin_of(v[i])], 1u)] = v[i];
+    if (v[i] != 0ull) sm.buf[atomicAdd(&sm.hist[bin_of(v[i])], 1u)] = v[i];
   if (t < 8) sm.buf[n + t] = 0ull;
   __syncthreads();
   // Rank within the bin: the number of members above, read eight positions
   // at a time from the bin's start.  Positions past the bin's end hold lower
   // bins, whose members are all smaller, and past n the zero padding, so the
-  // reads need no bound.  Every position's value and bin bounds are read in
-  // one batch.
-  {
-    u64 x[RPT];
-    uint32_t st[RPT], en[RPT];
+  // reads need no bound.  Positions are taken eight per lane at a time, each
+  // batch's values and bin bounds read together.
+  const uint32_t npos = uniform((n + NT - 1) / NT);
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) if (i < nit) {
-      const uint32_t p = i * NT + t;
+  for (int g = 0; g < RPT; g += 8) if (static_cast<uint32_t>(g) < npos) {
+    constexpr int RB = 8;
+    u64 x[RB];
+    uint32_t st[RB], en[RB];
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+      const uint32_t p = (g + i) * NT + t;
       x[i] = sm.buf[p < n ? p : 0u];
     }
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) if (i < nit) {
+    for (int i = 0; i < RB; ++i) {
       const uint32_t b = bin_of(x[i]);
       st[i] = b ? sm.hist[b - 1] : 0u;
       en[i] = sm.hist[b];
     }
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) if (i < nit) {
-      const uint32_t p = i * NT + t;
+    for (int i = 0; i < RB; ++i) {
+      const uint32_t p = (g + i) * NT + t;
       if (p >= n) continue;
       uint32_t r = st[i];
       if (en[i] - st[i] > 1u) {
@@ -1142,6 +1140,23 @@ __device__ __forceinline__ bool rank_store(Smem<CAP>& sm, const CArgs& a, bool b
   return true;
 }
 
+// rank_core over buf[0, n).
+template <int CAP>
+__device__ __forceinline__ bool rank_store(Smem<CAP>& sm, const CArgs& a, bool bf16,
+                                           const char* xrow, int64_t out0, uint32_t n, uint32_t m,
+                                           uint32_t status) {
+  const uint32_t t = threadIdx.x;
+  // Iterations past the last candidate are skipped as a whole (n is uniform).
+  const uint32_t nit = uniform((n + NT - 1) / NT);
+  u64 v[kRankPerLane];
+#pragma unroll
+  for (int i = 0; i < kRankPerLane; ++i) if (i < nit) {
+    const uint32_t j = i * NT + t;
+    v[i] = j < n ? sm.buf[j] : 0ull;
+  }
+  return rank_core(sm, a, bf16, xrow, out0, v, nit, n, m, status);
+}
+
 // Selection without order (unsorted output): the m largest of buf[0, n)
 // stored in any order.  The candidates stay in registers; one 2048-bin
 // histogram over their composite range finds the boundary bin, whose members
@@ -1149,20 +1164,15 @@ __device__ __forceinline__ bool rank_store(Smem<CAP>& sm, const CArgs& a, bool b
 // by one wave; every candidate at or above the m-th is stored at a position
 // taken from a per-wave counter.  Needs n <= kRankPerLane * NT.
 template <int CAP>
-__device__ __forceinline__ bool select_store(Smem<CAP>& sm, const CArgs& a, bool bf16,
-                                             const char* xrow, int64_t out0, uint32_t n, uint32_t m,
-                                             uint32_t status) {
+__device__ __forceinline__ bool select_core(Smem<CAP>& sm, const CArgs& a, bool bf16,
+                                            const char* xrow, int64_t out0, u64 (&v)[kRankPerLane],
+                                            uint32_t nit, uint32_t m, uint32_t status) {
   constexpr int RPT = kRankPerLane;
   const uint32_t t = threadIdx.x;
-  // Iterations past the last candidate are skipped as a whole (n is uniform).
-  const uint32_t nit = uniform((n + NT - 1) / NT);
-  u64 v[RPT];
   u64 lo = ~0ull, hi = 0;
 #pragma unroll
   for (int i = 0; i < RPT; ++i) if (i < nit) {
-    const uint32_t j = i * NT + t;
-    v[i] = j < n ? sm.buf[j] : 0ull;   // 0: below every candidate
-    if (j < n) {
+    if (v[i] != 0ull) {
       lo = v[i] < lo ? v[i] : lo;
       hi = v[i] > hi ? v[i] : hi;
     }
@@ -1194,7 +1204,7 @@ __device__ __forceinline__ bool select_store(Smem<CAP>& sm, const CArgs& a, bool
   const uint32_t shift = bl > kCutBits ? bl - kCutBits : 0u;
 #pragma unroll
   for (int i = 0; i < RPT; ++i) if (i < nit)
-    if (i * NT + t < n)
+    if (v[i] != 0ull)
       atomicAdd(&sm.hist[(kCutBins - 1) - static_cast<uint32_t>((v[i] - lo) >> shift)], 1u);
   __syncthreads();
   uint32_t h[kCutBPT];
@@ -1220,7 +1230,7 @@ __device__ __forceinline__ bool select_store(Smem<CAP>& sm, const CArgs& a, bool
       uint32_t wn = 0;
 #pragma unroll
       for (int i = 0; i < RPT; ++i) if (i < nit) {
-        mk[i] = ballot((i * NT + t < n) & (v[i] >= blo) & (v[i] <= bhi));
+        mk[i] = ballot((v[i] != 0ull) & (v[i] >= blo) & (v[i] <= bhi));
         wn += static_cast<uint32_t>(__popcll(mk[i]));
       }
       if (wn) {
@@ -1256,7 +1266,7 @@ __device__ __forceinline__ bool select_store(Smem<CAP>& sm, const CArgs& a, bool
   uint32_t wn = 0;
 #pragma unroll
   for (int i = 0; i < RPT; ++i) if (i < nit) {
-    mk[i] = ballot((i * NT + t < n) & (v[i] >= T));
+    mk[i] = ballot((v[i] != 0ull) & (v[i] >= T));
     wn += static_cast<uint32_t>(__popcll(mk[i]));
   }
   uint32_t base = 0;
@@ -1270,6 +1280,22 @@ __device__ __forceinline__ bool select_store(Smem<CAP>& sm, const CArgs& a, bool
   return true;
 }
 
+// select_core over buf[0, n).
+template <int CAP>
+__device__ __forceinline__ bool select_store(Smem<CAP>& sm, const CArgs& a, bool bf16,
+                                             const char* xrow, int64_t out0, uint32_t n, uint32_t m,
+                                             uint32_t status) {
+  const uint32_t t = threadIdx.x;
+  const uint32_t nit = uniform((n + NT - 1) / NT);
+  u64 v[kRankPerLane];
+#pragma unroll
+  for (int i = 0; i < kRankPerLane; ++i) if (i < nit) {
+    const uint32_t j = i * NT + t;
+    v[i] = j < n ? sm.buf[j] : 0ull;   // 0: no candidate (every composite is above 0)
+  }
+  return select_core(sm, a, bf16, xrow, out0, v, nit, m, status);
+}
+
 // Per-row statistics, when the caller asked for them (a.stats non-null):
 // counts added with device-scope atomics by lane 0 of the workgroup.
 __device__ __forceinline__ void stat_add(const CArgs& a, int row, int field, uint32_t v) {
@@ -1281,18 +1307,19 @@ __device__ __forceinline__ void stat_add(const CArgs& a, int row, int field, uin
 // write.
 template <int KMAX, int CAP>
 __device__ __forceinline__ void finish_row(Smem<CAP>& sm, const CArgs& a, bool bf16, int row,
-                                           uint32_t count, uint32_t L, uint32_t status) {
+                                           uint32_t count, uint32_t L, uint32_t status,
+                                           bool direct = true) {
   constexpr int PER = KMAX / NT;
   const int t = threadIdx.x;
   const uint32_t k = static_cast<uint32_t>(a.k);
   uint32_t m = status ? 0u : min(k, L);
-  stat_add(a, row, DS_STAT_FINAL_CANDIDATES, count);
+  if (direct) stat_add(a, row, DS_STAT_FINAL_CANDIDATES, count);
   __syncthreads();
   const int64_t out0 = static_cast<int64_t>(row) * k;
   const char* xrow = static_cast<const char*>(a.x) + static_cast<int64_t>(row) * a.row_stride * (bf16 ? 2 : 4);
   // Any order: the boundary found, every candidate above it stored.  Value
   // order: every candidate's rank, stored directly.
-  if (m > 0 && count >= m && count <= static_cast<uint32_t>(kRankPerLane * NT) &&
+  if (direct && m > 0 && count >= m && count <= static_cast<uint32_t>(kRankPerLane * NT) &&
       ((a.sorted == 0 && select_store(sm, a, bf16, xrow, out0, count, m, status)) ||
        (a.sorted == 1 && rank_store(sm, a, bf16, xrow, out0, count, m, status)))) {
     for (uint32_t e = m + t; e < k; e += NT) store_one(a, bf16, xrow, out0 + e, 0ull, false, status);
@@ -1320,6 +1347,40 @@ __device__ __forceinline__ void finish_row(Smem<CAP>& sm, const CArgs& a, bool b
   }
   if (t == 0) a.row_status[row] = static_cast<int32_t>(status);
   stat_add(a, row, DS_STAT_CUTS, sm.n_cut);
+}
+
+// finish_row for candidates held in registers: v[i] for i < nit, 0 where
+// there is none, n of them in the workgroup.  The direct selections work on
+// the registers; their fallback (long runs of equal values, sorted by
+// column) first packs the candidates into buf.
+template <int KMAX, int CAP>
+__device__ __forceinline__ void finish_row_regs(Smem<CAP>& sm, const CArgs& a, bool bf16, int row,
+                                                u64 (&v)[kRankPerLane], uint32_t nit, uint32_t n,
+                                                uint32_t L, uint32_t status, int par) {
+  const int t = threadIdx.x;
+  const uint32_t k = static_cast<uint32_t>(a.k);
+  const uint32_t m = status ? 0u : min(k, L);
+  stat_add(a, row, DS_STAT_FINAL_CANDIDATES, n);
+  const int64_t out0 = static_cast<int64_t>(row) * k;
+  const char* xrow = static_cast<const char*>(a.x) + static_cast<int64_t>(row) * a.row_stride * (bf16 ? 2 : 4);
+  if (m > 0 && n >= m &&
+      ((a.sorted == 0 && select_core(sm, a, bf16, xrow, out0, v, nit, m, status)) ||
+       (a.sorted == 1 && rank_core(sm, a, bf16, xrow, out0, v, nit, n, m, status)))) {
+    for (uint32_t e = m + t; e < k; e += NT) store_one(a, bf16, xrow, out0 + e, 0ull, false, status);
+    if (t == 0) a.row_status[row] = static_cast<int32_t>(status);
+    stat_add(a, row, DS_STAT_CUTS, sm.n_cut);
+    return;
+  }
+  uint32_t c = 0;
+#pragma unroll
+  for (int i = 0; i < kRankPerLane; ++i) if (i < nit) c += v[i] != 0ull ? 1u : 0u;
+  uint32_t total;
+  uint32_t pos = block_excl(sm, c, par, &total);
+#pragma unroll
+  for (int i = 0; i < kRankPerLane; ++i) if (i < nit) {
+    if (v[i] != 0ull) sm.buf[pos++] = v[i];
+  }
+  finish_row<KMAX>(sm, a, bf16, row, total, L, status, false);
 }
 
 // OR of a per-lane flag over the workgroup (flag bits are small).
@@ -1577,24 +1638,29 @@ __global__ __launch_bounds__(NT, 4) void chunk_split_kernel(CArgs a) {
   // exceeds one round.
   const float Es = static_cast<float>(k) * static_cast<float>(G::CE) / static_cast<float>(L > 0 ? L : 1u);
   const bool two = per_round < k && 1.5f * (Es + 6.0f * __builtin_sqrtf(Es) + 8.0f) > static_cast<float>(per_round);
-  u64 v0[G8], v1[G8];
+  // The first two rounds' slots: [0, G8) the first, [G8, 2 G8) the second.
+  static_assert(2 * G8 == kRankPerLane, "two merge rounds fill the epilogue's registers");
+  u64 vr[kRankPerLane];
 #pragma unroll
   for (int q = 0; q < G8; ++q) {
     const uint32_t j = q * PL + my_l;
-    v0[q] = (has_s && j < k) ? ld_agent(&my_slot[j]) : 0ull;
+    vr[q] = (has_s && j < k) ? ld_agent(&my_slot[j]) : 0ull;
   }
   if (two) {
 #pragma unroll
     for (int q = 0; q < G8; ++q) {
       const uint32_t j = per_round + q * PL + my_l;
-      v1[q] = (has_s && j < k) ? ld_agent(&my_slot[j]) : 0ull;
+      vr[G8 + q] = (has_s && j < k) ? ld_agent(&my_slot[j]) : 0ull;
     }
+  } else {
+#pragma unroll
+    for (int q = 0; q < G8; ++q) vr[G8 + q] = 0ull;
   }
   const uint32_t my_c = has_s ? static_cast<uint32_t>(ld_agent(&rec[2 * my_s + 1])) : 0u;
 #pragma unroll
   for (int q = 0; q < G8; ++q) {
-    if (q * PL + my_l >= my_c) v0[q] = 0ull;
-    if (two && per_round + q * PL + my_l >= my_c) v1[q] = 0ull;
+    if (q * PL + my_l >= my_c) vr[q] = 0ull;
+    if (per_round + q * PL + my_l >= my_c) vr[G8 + q] = 0ull;
   }
   u64 Tm = 0;
   uint32_t fl = 0, cm = 0;
@@ -1625,6 +1691,29 @@ __global__ __launch_bounds__(NT, 4) void chunk_split_kernel(CArgs a) {
   Tm = uniform64(tm);
   cmax = uniform(cmax);
 
+  // Every chunk's slots already in registers: the candidates at or above Tm
+  // go to the epilogue from there, with no append.
+  // (Values below Tm are dropped in place: the append below drops them too.)
+  if (status == 0 && cmax <= (two ? 2u : 1u) * per_round) {
+    uint32_t c = 0;
+#pragma unroll
+    for (int q = 0; q < kRankPerLane; ++q) {
+      vr[q] = vr[q] >= Tm ? vr[q] : 0ull;
+      c += vr[q] != 0ull ? 1u : 0u;
+    }
+    uint32_t n;
+    block_excl(sm, c, B.par, &n);
+    B.par ^= 1;
+    n = uniform(n);
+    if (n >= min(k, L)) {
+      if (t == 0) st_agent(&a.ws_arrive[row], 0u);
+      finish_row_regs<KMAX>(sm, a, BF16, row, vr, two ? 2u * G8 : static_cast<uint32_t>(G8), n, L,
+                            status, B.par);
+      return;
+    }
+    __syncthreads();
+  }
+
   B.count = 0;
   B.T = Tm;
   const uint32_t rounds = status ? 0u : (cmax + per_round - 1) / per_round;
@@ -1634,8 +1723,8 @@ __global__ __launch_bounds__(NT, 4) void chunk_split_kernel(CArgs a) {
 #pragma unroll
     for (int q = 0; q < G8; ++q) {
       const uint32_t j = rd * per_round + q * PL + my_l;
-      v[q] = rd == 0 ? v0[q]
-           : (rd == 1 && two) ? v1[q]
+      v[q] = rd == 0 ? vr[q]
+           : (rd == 1 && two) ? vr[G8 + q]
            : ((has_s && j < my_c) ? ld_agent(&my_slot[j]) : 0ull);
     }
     uint32_t n = 0;
