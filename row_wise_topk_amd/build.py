@@ -30,19 +30,23 @@ def build(verbose: bool = False, extra: list[str] | None = None) -> str:
     bdir = os.path.join(PKG, "_build")
     os.makedirs(bdir, exist_ok=True)
     k_obj = os.path.join(bdir, "topk_kernels.o")
-    c_obj = os.path.join(bdir, "chunk_kernels.o")
+    c_obj = os.path.join(bdir, "chunk_kernels_row.o")
+    c2_obj = os.path.join(bdir, "chunk_kernels_split.o")
     a_obj = os.path.join(bdir, "topk_api.o")
     n_obj = os.path.join(bdir, "noalloc.o")
     _run([HIPCC, *COMMON, *DEVICE, *extra, "-c", os.path.join(CSRC, "topk_kernels.hip"),
           "-o", k_obj], verbose)
-    _run([HIPCC, *COMMON, *DEVICE, *extra, "-c", os.path.join(CSRC, "chunk_kernels.hip"),
-          "-o", c_obj], verbose)
+    # The chunk kernels twice: whole rows (256 lanes) and split rows (1024).
+    _run([HIPCC, *COMMON, *DEVICE, *extra, "-DCHUNK_NT=256", "-c",
+          os.path.join(CSRC, "chunk_kernels.hip"), "-o", c_obj], verbose)
+    _run([HIPCC, *COMMON, *DEVICE, *extra, "-DCHUNK_NT=1024", "-c",
+          os.path.join(CSRC, "chunk_kernels.hip"), "-o", c2_obj], verbose)
     _run([HIPCC, *COMMON, *DEVICE, *extra, "-x", "hip", "-c", os.path.join(CSRC, "topk_api.cpp"),
           "-o", a_obj], verbose)
     _run([HIPCC, *COMMON, *DEVICE, *extra, "-c", os.path.join(CSRC, "noalloc.hip"), "-o", n_obj],
          verbose)
     tmp = LIB + ".tmp"
-    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", k_obj, c_obj, a_obj, n_obj, "-o", tmp],
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", k_obj, c_obj, c2_obj, a_obj, n_obj, "-o", tmp],
          verbose)
     os.replace(tmp, LIB)
     return LIB

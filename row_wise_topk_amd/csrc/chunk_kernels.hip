@@ -60,8 +60,16 @@ typedef unsigned long long u64;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int NT = kChunkThreads;   // 256 lanes, 4 waves
+#ifndef CHUNK_NT
+#error "built with CHUNK_NT = kChunkThreadsRow (whole rows) or kChunkThreadsSplit (split rows)"
+#endif
+constexpr int NT = CHUNK_NT;         // lanes per workgroup
+constexpr bool kSplit = NT == kChunkThreadsSplit;
+static_assert(kSplit || NT == kChunkThreadsRow, "one of the two chunk kernel builds");
 constexpr int NW = NT / 64;
+// Workgroups per CU the kernels are built for: `waves256` groups of four
+// waves, at least one workgroup.
+constexpr int blocks_per_cu(int waves256) { return waves256 * 256 / NT > 0 ? waves256 * 256 / NT : 1; }
 constexpr int V = kChunkLoads;      // 16-byte loads per lane per chunk
 constexpr uint32_t kBias = 0x80000000u;
 constexpr uint32_t kNegInfKey = 0x00800000u;   // key of -inf, the lowest non-NaN key
@@ -75,7 +83,9 @@ constexpr uint32_t kRankMax = 64;              // boundary bins ranked directly
 constexpr uint32_t kNone = 0xFFFFFFFFu;
 constexpr u64 kTAll = static_cast<u64>(kNegInfKey) << 32;   // every non-NaN value passes
 
-static_assert(kWinBins == NT, "one start bin per lane");
+// The start histogram is scanned one bin per lane; lanes past its bins read
+// bins that are zero at rest.
+static_assert(kWinBins <= NT && NT <= kCutBins, "one start bin per lane");
 static_assert(kCutBins % NT == 0, "cut bins per lane");
 
 // ---------------------------------------------------------------- keys
@@ -283,7 +293,14 @@ __device__ __forceinline__ void load_chunk(u32x4 (&r)[V], const char* xrow, uint
 template <bool BF16>
 __device__ __forceinline__ uint32_t col_at(uint32_t c, int i, int q) {
   using G = Geo<BF16>;
-  return c * G::CE + (static_cast<uint32_t>(i * NT) + threadIdx.x) * G::EPV + q;
+  // The lane's first column plus a constant, added where it is used (an
+  // opaque add the compiler cannot hoist), so the 32-64 column numbers of a
+  // chunk are never held in registers at once.
+  const uint32_t base = c * G::CE + threadIdx.x * G::EPV;
+  const uint32_t off = static_cast<uint32_t>(i * NT * G::EPV + q);
+  uint32_t r;
+  asm volatile("v_add_u32 %0, %1, %2" : "=v"(r) : "s"(off), "v"(base));
+  return r;
 }
 
 // Apply f(bits as fp32, value index q) to every value of vector r.
@@ -1011,7 +1028,7 @@ __device__ __forceinline__ void sort_and_store(Smem<CAP>& sm, const CArgs& a, bo
 // kBinRankMax candidates (long runs of equal values); the caller then cuts and
 // sorts.  Needs n <= RPT * NT.
 constexpr uint32_t kBinRankMax = 128;
-constexpr int kRankPerLane = 16;
+constexpr int kRankPerLane = 4096 / NT;
 
 template <int CAP>
 __device__ __forceinline__ bool rank_core(Smem<CAP>& sm, const CArgs& a, bool bf16,
@@ -1309,7 +1326,7 @@ template <int KMAX, int CAP>
 __device__ __forceinline__ void finish_row(Smem<CAP>& sm, const CArgs& a, bool bf16, int row,
                                            uint32_t count, uint32_t L, uint32_t status,
                                            bool direct = true) {
-  constexpr int PER = KMAX / NT;
+  constexpr int PER = KMAX > NT ? KMAX / NT : 1;
   const int t = threadIdx.x;
   const uint32_t k = static_cast<uint32_t>(a.k);
   uint32_t m = status ? 0u : min(k, L);
@@ -1408,10 +1425,10 @@ __device__ __forceinline__ uint32_t row_len(const CArgs& a, int row, uint32_t* s
 
 // A whole row per workgroup, chunk by chunk.
 template <bool BF16, int KC>
-__global__ __launch_bounds__(NT, KC >= 2 ? 3 : 4) void chunk_row_kernel(CArgs a) {
+__global__ __launch_bounds__(NT, blocks_per_cu(KC >= 2 ? 3 : 4)) void chunk_row_kernel(CArgs a) {
   using G = Geo<BF16>;
   constexpr int KMAX = class_kmax(KC);
-  constexpr int CAP = chunk_cap(KC);
+  constexpr int CAP = chunk_cap(KC, NT);
   static_assert(CAP >= KMAX + NT * G::EPV, "a cut leaves room for one vector per lane");
   __shared__ Smem<CAP> sm;
   const int t = threadIdx.x;
@@ -1484,11 +1501,11 @@ __global__ __launch_bounds__(NT, KC >= 2 ? 3 : 4) void chunk_row_kernel(CArgs a)
 // One chunk of a row per workgroup; the last workgroup of the row to finish
 // merges the others' candidates.
 template <bool BF16, int KC>
-__global__ __launch_bounds__(NT, 4) void chunk_split_kernel(CArgs a) {
+__global__ __launch_bounds__(NT, blocks_per_cu(4)) void chunk_split_kernel(CArgs a) {
   using G = Geo<BF16>;
   constexpr int KMAX = class_kmax(KC);
-  constexpr int CAP = chunk_cap(KC);
-  constexpr int G8 = 8;   // slots per lane per merge round
+  constexpr int CAP = chunk_cap(KC, NT);
+  constexpr int G8 = kRankPerLane / 2;   // slots per lane per merge round
   static_assert(CAP >= KMAX + NT * G::EPV, "a cut leaves room for one vector per lane");
   static_assert(G8 * NT <= CAP - KMAX, "a merge round fits after a cut");
   __shared__ Smem<CAP> sm;
@@ -1799,33 +1816,43 @@ __global__ __launch_bounds__(NT) void chunk_read_kernel(CArgs a, uint32_t* sink)
   if (acc == 0x9E3779B9u) sink[0] = acc;
 }
 
+// This build's kernel: split rows or whole rows.
 template <bool BF16>
-const void* chunk_fn(int cls, bool split) {
-  if (split) {
+const void* chunk_fn(int cls) {
+  if constexpr (kSplit) {
     return cls == 0 ? reinterpret_cast<const void*>(&chunk_split_kernel<BF16, 0>)
          : cls == 1 ? reinterpret_cast<const void*>(&chunk_split_kernel<BF16, 1>)
          : cls == 2 ? reinterpret_cast<const void*>(&chunk_split_kernel<BF16, 2>)
                     : reinterpret_cast<const void*>(&chunk_split_kernel<BF16, 3>);
+  } else {
+    return cls == 0 ? reinterpret_cast<const void*>(&chunk_row_kernel<BF16, 0>)
+         : cls == 1 ? reinterpret_cast<const void*>(&chunk_row_kernel<BF16, 1>)
+         : cls == 2 ? reinterpret_cast<const void*>(&chunk_row_kernel<BF16, 2>)
+                    : reinterpret_cast<const void*>(&chunk_row_kernel<BF16, 3>);
   }
-  return cls == 0 ? reinterpret_cast<const void*>(&chunk_row_kernel<BF16, 0>)
-       : cls == 1 ? reinterpret_cast<const void*>(&chunk_row_kernel<BF16, 1>)
-       : cls == 2 ? reinterpret_cast<const void*>(&chunk_row_kernel<BF16, 2>)
-                  : reinterpret_cast<const void*>(&chunk_row_kernel<BF16, 3>);
 }
 
 }  // namespace
 
+#if CHUNK_NT == 1024
+#define DSTK_LAUNCH_CHUNK launch_chunk_split
+#define DSTK_LAUNCH_CHUNK_READ launch_chunk_read_split
+#else
+#define DSTK_LAUNCH_CHUNK launch_chunk_row
+#define DSTK_LAUNCH_CHUNK_READ launch_chunk_read_row
+#endif
+
 // The launch's own error code (hipLaunchKernel returns it; an earlier,
 // unrelated error left in the runtime is neither returned nor cleared).
-int launch_chunk(const CArgs& a, int dtype, int cls, hipStream_t stream) {
+int DSTK_LAUNCH_CHUNK(const CArgs& a, int dtype, int cls, hipStream_t stream) {
   const unsigned grid = static_cast<unsigned>(static_cast<int64_t>(a.batch) * a.segments);
   CArgs arg = a;
   void* args[] = {&arg};
-  const void* fn = dtype == 0 ? chunk_fn<false>(cls, a.segments > 1) : chunk_fn<true>(cls, a.segments > 1);
+  const void* fn = dtype == 0 ? chunk_fn<false>(cls) : chunk_fn<true>(cls);
   return static_cast<int>(hipLaunchKernel(fn, dim3(grid), dim3(NT), args, 0, stream));
 }
 
-int launch_chunk_read(const CArgs& a, int dtype, uint32_t* sink, hipStream_t stream) {
+int DSTK_LAUNCH_CHUNK_READ(const CArgs& a, int dtype, uint32_t* sink, hipStream_t stream) {
   const unsigned grid = static_cast<unsigned>(static_cast<int64_t>(a.batch) * a.segments);
   CArgs arg = a;
   void* args[] = {&arg, &sink};

@@ -58,16 +58,17 @@ int auto_segments(int64_t batch, int64_t n_cols, int cls, int dtype) {
   return static_cast<int>(s);
 }
 
-// Chunks of a row of n_cols values.
-int64_t chunks_of(int64_t n_cols, int dtype) {
-  const int64_t ce = chunk_elems(dtype);
+// Chunks of a row of n_cols values, for workgroups of nt lanes.
+int64_t chunks_of(int64_t n_cols, int dtype, int nt) {
+  const int64_t ce = chunk_elems(dtype, nt);
   return (n_cols + ce - 1) / ce;
 }
 
-// Workgroups per row for the chunk kernels: one per chunk when the batch is
-// too small to fill the chip with whole rows, else one per row.
+// Workgroups per row for the chunk kernels: one (1024-lane) workgroup per
+// split chunk when the batch is too small to fill the chip with whole rows,
+// else one (256-lane) workgroup per row.
 int chunk_segments(int64_t batch, int64_t n_cols, int dtype) {
-  const int64_t nch = chunks_of(n_cols, dtype);
+  const int64_t nch = chunks_of(n_cols, dtype, kChunkThreadsSplit);
   return (batch < kChunkSplitBatch && nch > 1 && nch <= kMaxSegments) ? static_cast<int>(nch) : 1;
 }
 
@@ -77,8 +78,9 @@ ds_status_t resolve_plan(int64_t batch, int64_t n_cols, int32_t k, ds_dtype_t dt
   const int dt = dtype == DS_BF16 ? 1 : 0;
   Plan pl{};
   pl.cls = class_of_k(k);
-  const int64_t nch = chunks_of(n_cols, dt);
-  pl.kernel = nch <= kChunkMaxPerRow ? DS_KERNEL_CHUNK : DS_KERNEL_STREAM;
+  pl.kernel = chunks_of(n_cols, dt, kChunkThreadsRow) <= kChunkMaxPerRow ? DS_KERNEL_CHUNK
+                                                                         : DS_KERNEL_STREAM;
+  const int64_t nch = chunks_of(n_cols, dt, kChunkThreadsSplit);   // split chunks
   pl.seed = 0x5EEDu;
   pl.in_order = 0;
   if (p) {
@@ -87,7 +89,6 @@ ds_status_t resolve_plan(int64_t batch, int64_t n_cols, int32_t k, ds_dtype_t dt
   }
   if (pl.kernel == DS_KERNEL_CHUNK) {
     pl.segments = chunk_segments(batch, n_cols, dt);
-    pl.trigger = chunk_cap(pl.cls);
   } else {
     pl.segments = auto_segments(batch, n_cols, pl.cls, dt);
     pl.trigger = class_trigger(pl.cls);
@@ -103,11 +104,6 @@ ds_status_t resolve_plan(int64_t batch, int64_t n_cols, int32_t k, ds_dtype_t dt
         if (nch > kMaxSegments) return DS_ERR_PLAN;
         pl.segments = nch > 1 ? static_cast<int>(nch) : 1;
       }
-      if (p->flush_at) {
-        const int lo = k + 2048;
-        pl.trigger = p->flush_at < lo ? lo : p->flush_at;
-        if (pl.trigger > chunk_cap(pl.cls)) pl.trigger = chunk_cap(pl.cls);
-      }
     } else {
       if (p->segments > 0) pl.segments = p->segments;
       if (p->flush_at) pl.trigger = p->flush_at;
@@ -120,6 +116,17 @@ ds_status_t resolve_plan(int64_t batch, int64_t n_cols, int32_t k, ds_dtype_t dt
   if (pl.segments > 1 && batch > kMaxSplitRows) {
     if (p && p->segments > 1) return DS_ERR_PLAN;
     pl.segments = 1;
+  }
+  if (pl.kernel == DS_KERNEL_CHUNK) {
+    // The buffer's trigger: its capacity, or a requested flush point raised
+    // to at least k plus one vector per lane.
+    const int nt = pl.segments > 1 ? kChunkThreadsSplit : kChunkThreadsRow;
+    pl.trigger = chunk_cap(pl.cls, nt);
+    if (p && p->flush_at) {
+      const int lo = k + chunk_room(nt);
+      const int f = p->flush_at < lo ? lo : p->flush_at;
+      pl.trigger = f < pl.trigger ? f : pl.trigger;
+    }
   }
   *out = pl;
   return DS_OK;
@@ -272,7 +279,9 @@ ds_status_t ds_topk_ex(const void* x, ds_dtype_t dtype, int64_t batch, int64_t n
       c.ws_rec = reinterpret_cast<unsigned long long*>(w + l.rec);
       c.ws_slot = reinterpret_cast<unsigned long long*>(w + l.slot);
     }
-    const int err = launch_chunk(c, dtype == DS_BF16 ? 1 : 0, pl.cls, stream);
+    const int dt = dtype == DS_BF16 ? 1 : 0;
+    const int err = pl.segments > 1 ? launch_chunk_split(c, dt, pl.cls, stream)
+                                    : launch_chunk_row(c, dt, pl.cls, stream);
     return err == 0 ? DS_OK : DS_ERR_HIP;
   }
 
@@ -355,7 +364,9 @@ ds_status_t ds_read_ceiling(const void* x, ds_dtype_t dtype, int64_t batch, int6
     c.perm_seed = pl.seed;
     c.in_order = pl.in_order;
     c.reverse_rows = (pl.segments == 1 && end != nullptr) ? 1 : 0;
-    const int err = launch_chunk_read(c, dtype == DS_BF16 ? 1 : 0, sink, stream);
+    const int dt = dtype == DS_BF16 ? 1 : 0;
+    const int err = pl.segments > 1 ? launch_chunk_read_split(c, dt, sink, stream)
+                                    : launch_chunk_read_row(c, dt, sink, stream);
     return err == 0 ? DS_OK : DS_ERR_HIP;
   }
   KArgs a{};

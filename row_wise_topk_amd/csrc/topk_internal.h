@@ -53,15 +53,22 @@ constexpr int wgs_per_cu(int c, int nt) {
 inline int class_of_k(int k) { return k <= 256 ? 0 : k <= 1024 ? 1 : k <= 2048 ? 2 : 3; }
 
 // ---- chunk kernels (chunk_kernels.hip)
-// A chunk: kChunkLoads 16-byte loads per lane of a kChunkThreads-lane
-// workgroup, all in flight at once.
-constexpr int kChunkThreads = 256;
+// A chunk: kChunkLoads 16-byte loads per lane of the workgroup, all in
+// flight at once.  chunk_kernels.hip is built twice: whole rows with
+// 256-lane workgroups (several rows per CU), split rows with 1024-lane
+// workgroups (one per CU), so that a split row's merge and exact selection
+// run on 16 waves.
+constexpr int kChunkThreadsRow = 256;
+constexpr int kChunkThreadsSplit = 1024;
 constexpr int kChunkLoads = 8;
-constexpr int64_t chunk_elems(int dtype) { return int64_t{kChunkThreads} * kChunkLoads * (dtype == 0 ? 4 : 8); }
-// Candidate buffer: k plus room for the larger of k and 2048 more (one
-// vector per lane of bf16 is 2048 values; a merge round is 2048 slots).
-constexpr int chunk_cap(int c) { return class_kmax(c) + (class_kmax(c) > 2048 ? class_kmax(c) : 2048); }
-// Rows of at most this many chunks go to the chunk kernels by default.
+constexpr int64_t chunk_elems(int dtype, int nt) { return int64_t{nt} * kChunkLoads * (dtype == 0 ? 4 : 8); }
+// Candidate buffer: k plus room for the larger of k and one bf16 vector per
+// lane (8 values per lane).
+constexpr int chunk_room(int nt) { return nt * 8; }
+constexpr int chunk_cap(int c, int nt) {
+  return class_kmax(c) + (class_kmax(c) > chunk_room(nt) ? class_kmax(c) : chunk_room(nt));
+}
+// Rows of at most this many whole-row chunks go to the chunk kernels by default.
 constexpr int64_t kChunkMaxPerRow = 64;
 // Below this many rows, a row is split into one workgroup per chunk.
 constexpr int64_t kChunkSplitBatch = 512;
@@ -98,9 +105,11 @@ ChunkWs chunk_ws_layout(int64_t batch, int segments, int k);
 
 // Queue the chunk kernel for k class `cls` and dtype (0 fp32, 1 bf16).
 // Returns the hipError_t of the launch.
-int launch_chunk(const CArgs& a, int dtype, int cls, hipStream_t stream);
+int launch_chunk_row(const CArgs& a, int dtype, int cls, hipStream_t stream);
+int launch_chunk_split(const CArgs& a, int dtype, int cls, hipStream_t stream);
 // Queue the read-ceiling kernel of the chunk kernels' access pattern.
-int launch_chunk_read(const CArgs& a, int dtype, uint32_t* sink, hipStream_t stream);
+int launch_chunk_read_row(const CArgs& a, int dtype, uint32_t* sink, hipStream_t stream);
+int launch_chunk_read_split(const CArgs& a, int dtype, uint32_t* sink, hipStream_t stream);
 
 // Survivor slots a shared row's workgroup may hand over beyond k.
 constexpr int kStreamSlotSlack = 64;

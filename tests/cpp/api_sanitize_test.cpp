@@ -44,13 +44,15 @@ int launch_read(const KArgs& a, int, int, uint32_t* sink, hipStream_t) {
   CHECK(a.segments >= 1);
   return 0;
 }
-int launch_chunk(const CArgs& a, int dtype, int cls, hipStream_t) {
+static void check_chunk(const CArgs& a, int dtype, int cls, int nt) {
   ++launches;
   CHECK(dtype == 0 || dtype == 1);
   CHECK(cls >= 0 && cls < kNumClasses);
   CHECK(a.segments >= 1 && a.segments <= kMaxSegments);
-  CHECK(a.cap_eff >= static_cast<uint32_t>(a.k) + 2048u || a.cap_eff == static_cast<uint32_t>(chunk_cap(cls)));
-  CHECK(a.cap_eff <= static_cast<uint32_t>(chunk_cap(cls)));
+  CHECK((a.segments > 1) == (nt == kChunkThreadsSplit));
+  CHECK(a.cap_eff >= static_cast<uint32_t>(a.k + chunk_room(nt)) ||
+        a.cap_eff == static_cast<uint32_t>(chunk_cap(cls, nt)));
+  CHECK(a.cap_eff <= static_cast<uint32_t>(chunk_cap(cls, nt)));
   if (a.segments > 1) {
     const ChunkWs l = chunk_ws_layout(a.batch, a.segments, a.k);
     CHECK(in_ws(a.ws_arrive, static_cast<size_t>(a.batch) * 4));
@@ -58,12 +60,26 @@ int launch_chunk(const CArgs& a, int dtype, int cls, hipStream_t) {
     CHECK(in_ws(a.ws_slot, static_cast<size_t>(a.batch) * a.segments * a.k * 8));
     CHECK(l.total <= g_ws_bytes);
   }
+}
+int launch_chunk_row(const CArgs& a, int dtype, int cls, hipStream_t) {
+  check_chunk(a, dtype, cls, kChunkThreadsRow);
   return 0;
 }
-int launch_chunk_read(const CArgs& a, int, uint32_t* sink, hipStream_t) {
+int launch_chunk_split(const CArgs& a, int dtype, int cls, hipStream_t) {
+  check_chunk(a, dtype, cls, kChunkThreadsSplit);
+  return 0;
+}
+static void check_read(const CArgs& a, uint32_t* sink) {
   ++launches;
   CHECK(sink != nullptr);
   CHECK(a.segments >= 1);
+}
+int launch_chunk_read_row(const CArgs& a, int, uint32_t* sink, hipStream_t) {
+  check_read(a, sink);
+  return 0;
+}
+int launch_chunk_read_split(const CArgs& a, int, uint32_t* sink, hipStream_t) {
+  check_read(a, sink);
   return 0;
 }
 }  // namespace dstk

@@ -8,6 +8,10 @@ import oracle
 from tests.build_util import ensure_built
 
 FP32, BF16 = 0, 1
+# Values per chunk of the chunk kernels: eight 16-byte loads per lane of a
+# 1024-lane workgroup for split rows, of a 256-lane workgroup for whole rows.
+CHUNK_ELEMS = {FP32: 32768, BF16: 65536}
+CHUNK_ELEMS_ROW = {FP32: 8192, BF16: 16384}
 
 
 def say(msg: str):

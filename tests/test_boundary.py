@@ -121,11 +121,12 @@ def test_workspace_rules():
     s4 = rt.ds_topk_workspace_size_ex(rt.DS_FP32, 64, 129280, 1024, {"segments": 4, "kernel": 1})
     s16 = rt.ds_topk_workspace_size_ex(rt.DS_FP32, 64, 129280, 1024, {"segments": 16, "kernel": 1})
     assert 0 < s4 < s16
-    # The chunk kernels split a row into its 16 chunks: a fixed header of
-    # arrival counters, a record and k slots per chunk.
+    # The chunk kernels split a row into its chunks (32768 fp32 values each:
+    # four for 129,280 columns): a fixed header of counters, a record and k
+    # slots per chunk.
     c = rt.ds_topk_workspace_size_ex(rt.DS_FP32, 64, 129280, 1024, {"kernel": 2, "segments": 2})
     assert c == rt.ds_topk_workspace_size(rt.DS_FP32, 64, 129280, 1024)
-    assert c >= 64 * 16 * 1024 * 8
+    assert c >= rt.DS_TOPK_WS_HEADER_BYTES + 64 * 4 * 1024 * 8
     # Every split layout starts after the fixed counter header.
     assert c > rt.DS_TOPK_WS_HEADER_BYTES and s4 > rt.DS_TOPK_WS_HEADER_BYTES
     # Rows shared by workgroups are limited to the header's capacity: an

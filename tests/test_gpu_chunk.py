@@ -1,9 +1,10 @@
 """GPU parity for the data-dependent paths of the chunk kernels.
 
-A workgroup of the chunk kernels holds 32 KiB of a row in registers: 8192
-fp32 or 16384 bf16 values.  A row is either split into one workgroup per
-chunk (the last to finish merges the others' candidates) or taken whole by
-one workgroup, chunk by chunk.  The first chunk of a workgroup sets the start
+A workgroup of the chunk kernels holds a chunk of a row in registers: a row
+is either split into one 1024-lane workgroup per chunk of 32768 fp32 or
+65536 bf16 values (the last to finish merges the others' candidates) or
+taken whole by one 256-lane workgroup, chunk by chunk (8192 fp32 or 16384
+bf16 values each).  The first chunk of a workgroup sets the start
 threshold: exact when the chunk is the whole row, otherwise an estimate of
 the row's k-th value for the chunk's share, checked once the row is
 complete (the row is read again from -inf when fewer than min(k, L)
@@ -19,13 +20,17 @@ import numpy as np
 import pytest
 
 import workloads
-from tests.gpu_util import BF16, FP32, check_case
+from tests.gpu_util import BF16, CHUNK_ELEMS, CHUNK_ELEMS_ROW, FP32, check_case
 
 pytestmark = pytest.mark.gpu
 
-CE = {FP32: 8192, BF16: 16384}   # values per chunk
 SPLIT = {"kernel": 2, "segments": 2}
 WHOLE = {"kernel": 2, "segments": 1}
+
+
+def ce_of(dtype, plan):
+    """Values per chunk for the plan (whole rows: segments 1)."""
+    return (CHUNK_ELEMS_ROW if plan.get("segments") == 1 else CHUNK_ELEMS)[dtype]
 
 
 def _bits(f, dtype):
@@ -47,11 +52,12 @@ def _bits(f, dtype):
 @pytest.mark.parametrize("k", [64, 1024])
 def test_estimate_rejected_hot_chunk(plan, dtype, k):
     rng = np.random.Generator(np.random.PCG64(500 + k + dtype))
-    n = 6 * CE[dtype]
+    ce = ce_of(dtype, plan)
+    n = 6 * ce
     f = rng.standard_normal((3, n)).astype(np.float32)
     for r in range(3):
         c = r % 6
-        f[r, c * CE[dtype]:(c + 1) * CE[dtype]] += np.float32(50.0)
+        f[r, c * ce:(c + 1) * ce] += np.float32(50.0)
     x = _bits(f, dtype)
     check_case(x, dtype, n, k, 1, True, "int32", plan=plan, name=f"hot chunk k={k} {plan}")
     check_case(x, dtype, n, k, 0, False, "int64", plan=plan, name=f"hot chunk unsorted k={k} {plan}")
@@ -60,10 +66,10 @@ def test_estimate_rejected_hot_chunk(plan, dtype, k):
 # Descending rows: the first chunk in address order holds the whole top k.
 @pytest.mark.parametrize("dtype", [FP32, BF16])
 def test_descending_rows_whole(dtype):
-    n = 5 * CE[dtype] + 777
-    f = (np.arange(n, dtype=np.float64)[::-1] / n).astype(np.float32)[None, :].repeat(2, axis=0)
-    x = _bits(f, dtype)
     for plan in (dict(WHOLE, in_order=1), WHOLE, SPLIT):
+        n = 5 * ce_of(dtype, plan) + 777
+        f = (np.arange(n, dtype=np.float64)[::-1] / n).astype(np.float32)[None, :].repeat(2, axis=0)
+        x = _bits(f, dtype)
         for k in (100, 2048):
             check_case(x, dtype, n, k, 1, True, "int32", plan=plan, name=f"descending k={k} {plan}")
 
@@ -73,14 +79,15 @@ def test_descending_rows_whole(dtype):
 @pytest.mark.parametrize("dtype", [FP32, BF16])
 @pytest.mark.parametrize("flush_at", [0, 1])
 def test_piecewise_appends(dtype, flush_at):
-    n = 7 * CE[dtype] + 5
     rng = np.random.Generator(np.random.PCG64(77 + dtype))
-    f = (np.arange(n, dtype=np.float64) / n).astype(np.float32)[None, :] \
-        + np.float32(1e-4) * rng.random((2, n), dtype=np.float32)
-    x = _bits(f, dtype)
     for plan in (dict(WHOLE, in_order=1), SPLIT):
+        n = 7 * ce_of(dtype, plan) + 5
+        f = (np.arange(n, dtype=np.float64) / n).astype(np.float32)[None, :] \
+            + np.float32(1e-4) * rng.random((2, n), dtype=np.float32)
+        x = _bits(f, dtype)
         for k, sm, idx in ((4096, 1, "int32"), (1000, 2, "int64")):
-            # flush_at = k + 1: the chunk kernels raise it to their least, k + 2048
+            # flush_at = k + 1: the chunk kernels raise it to their least,
+            # k plus one vector per lane
             p = dict(plan, flush_at=k + 1) if flush_at else plan
             check_case(x, dtype, n, k, sm, True, idx, plan=p, name=f"ascending k={k} {p}")
 
@@ -90,7 +97,7 @@ def test_piecewise_appends(dtype, flush_at):
 @pytest.mark.parametrize("dtype", [FP32, BF16])
 @pytest.mark.parametrize("plan", [SPLIT, WHOLE])
 def test_one_value_rows(dtype, plan):
-    n = 3 * CE[dtype] - 11
+    n = 3 * ce_of(dtype, plan) - 11
     f = np.full((2, n), -2.5, dtype=np.float32)
     x = _bits(f, dtype)
     for k in (1, 700, 4096):
@@ -105,7 +112,7 @@ def test_one_value_rows(dtype, plan):
 def test_tie_groups_and_signed_zeros(dtype, plan):
     rng = np.random.Generator(np.random.PCG64(91 + dtype))
     alpha = np.array([-0.0, 0.0, 0.5, -0.5, 1.0, -np.inf, 2.0], dtype=np.float32)
-    n = 4 * CE[dtype] + 3
+    n = 4 * ce_of(dtype, plan) + 3
     f = alpha[rng.integers(0, len(alpha), size=(3, n))]
     x = _bits(f, dtype)
     for k in (5, 512, 3000):
@@ -120,7 +127,7 @@ def test_tie_groups_and_signed_zeros(dtype, plan):
 @pytest.mark.parametrize("plan", [SPLIT, WHOLE, {"kernel": 1}, {"kernel": 1, "segments": 3}])
 def test_subnormals_around_kth(dtype, plan):
     rng = np.random.Generator(np.random.PCG64(13 + dtype))
-    n = 3 * CE[dtype]
+    n = 3 * ce_of(dtype, plan)
     if dtype == FP32:
         tiny = np.array([1, 2, 3, 0x7FFFFF], dtype=np.uint32)
         sub = np.concatenate([tiny, tiny | 0x80000000]).view(np.float32)
@@ -143,7 +150,7 @@ def test_subnormals_around_kth(dtype, plan):
 @pytest.mark.parametrize("plan", [SPLIT, WHOLE])
 def test_ragged_ends_and_nan(dtype, plan):
     rng = np.random.Generator(np.random.PCG64(19 + dtype))
-    ce = CE[dtype]
+    ce = ce_of(dtype, plan)
     n = 3 * ce
     batch = 10
     f = rng.standard_normal((batch, n)).astype(np.float32)
@@ -164,7 +171,7 @@ def test_ragged_ends_and_nan(dtype, plan):
 @pytest.mark.parametrize("dtype", [FP32, BF16])
 def test_split_hand_over_capped_at_k(dtype):
     rng = np.random.Generator(np.random.PCG64(23 + dtype))
-    n = 2 * CE[dtype] + 100
+    n = 2 * CHUNK_ELEMS[dtype] + 100
     f = rng.standard_normal((4, n)).astype(np.float32)
     x = _bits(f, dtype)
     for k in (2048, 4096):

@@ -14,7 +14,7 @@ import numpy as np
 import pytest
 
 import workloads
-from tests.gpu_util import FP32, to_device
+from tests.gpu_util import CHUNK_ELEMS, FP32, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -59,7 +59,7 @@ def test_reread_counter_counts():
     """One chunk holds every large value: the split row's share estimate is
     too high, the merge check fails and the row is read again."""
     import row_wise_topk_amd as rt
-    ce = 8192
+    ce = CHUNK_ELEMS[FP32]
     n = 6 * ce
     rng = np.random.Generator(np.random.PCG64(501))
     f = rng.standard_normal((2, n)).astype(np.float32)

@@ -62,9 +62,9 @@ def test_noalloc_matches_ex_twice_then_smaller():
     import torch
     import row_wise_topk_amd as rt
     cases = [
-        # (workload, batch, n_cols, plan): the sampler shape split 16 ways, then a smaller bf16 problem
+        # (workload, batch, n_cols, plan): the sampler shape split by chunks, then a smaller bf16 problem
         (2, 64, 129280, None),
-        (3, 16, 40000, rt.Plan(segments=3, perm_seed=7, kernel=rt.DS_KERNEL_CHUNK)),
+        (3, 16, 140000, rt.Plan(segments=3, perm_seed=7, kernel=rt.DS_KERNEL_CHUNK)),
     ]
     for num, batch, n, plan in cases:
         w = workloads.workload(num, batch=batch, n_cols=n)
