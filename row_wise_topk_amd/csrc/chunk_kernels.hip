@@ -684,7 +684,8 @@ __device__ __forceinline__ void append_chunk(Smem<CAP>& sm, Buf& B, const u32x4 
 // for this chunk's share.  Returns whether a NaN was found.
 template <bool BF16, int CAP>
 __device__ __forceinline__ bool start_chunk(Smem<CAP>& sm, Buf& B, u32x4 (&r)[V], uint32_t c,
-                                            uint32_t L, uint32_t k, bool exact, bool* spec) {
+                                            uint32_t L, uint32_t k, bool exact, bool* spec,
+                                            uint32_t* top = nullptr) {
   using G = Geo<BF16>;
   const int t = threadIdx.x;
   bool nan = false;
@@ -702,6 +703,7 @@ __device__ __forceinline__ bool start_chunk(Smem<CAP>& sm, Buf& B, u32x4 (&r)[V]
 #pragma unroll
   for (int w = 0; w < NW; ++w) maxkey = max(maxkey, sm.wmax[w]);
   maxkey = uniform(maxkey);
+  if (top) *top = maxkey;
   const uint32_t nvalid = min(G::CE, L - c * G::CE);
   uint32_t m;
   if (exact) {
@@ -1033,10 +1035,12 @@ constexpr int kRankPerLane = 4096 / NT;
 template <int CAP>
 __device__ __forceinline__ bool rank_core(Smem<CAP>& sm, const CArgs& a, bool bf16,
                                           const char* xrow, int64_t out0, u64 (&v)[kRankPerLane],
-                                          uint32_t nit, uint32_t n, uint32_t m, uint32_t status) {
+                                          uint32_t nit, uint32_t n, uint32_t m, uint32_t status,
+                                          u64 lo_in = 0, u64 hi_in = 0) {
   constexpr int RPT = kRankPerLane;
   const uint32_t t = threadIdx.x;
-  u64 lo = ~0ull, hi = 0;
+  u64 lo = hi_in != 0 ? lo_in : ~0ull, hi = hi_in;
+  if (hi_in == 0) {   // else a known range holding every candidate
 #pragma unroll
   for (int i = 0; i < RPT; ++i) if (i < nit) {
     if (v[i] != 0ull) {
@@ -1062,6 +1066,7 @@ __device__ __forceinline__ bool rank_core(Smem<CAP>& sm, const CArgs& a, bool bf
     }
     lo = uniform64(l2);
     hi = uniform64(h2);
+  }
   }
   // Bins over the composites' range.  bf16 values of rows of at most 2^16
   // columns repeat often; their composites are binned in a 32-bit form
@@ -1183,10 +1188,17 @@ __device__ __forceinline__ bool rank_store(Smem<CAP>& sm, const CArgs& a, bool b
 template <int CAP>
 __device__ __forceinline__ bool select_core(Smem<CAP>& sm, const CArgs& a, bool bf16,
                                             const char* xrow, int64_t out0, u64 (&v)[kRankPerLane],
-                                            uint32_t nit, uint32_t m, uint32_t status) {
+                                            uint32_t nit, uint32_t m, uint32_t status,
+                                            u64 lo_in = 0, u64 hi_in = 0) {
   constexpr int RPT = kRankPerLane;
   const uint32_t t = threadIdx.x;
-  u64 lo = ~0ull, hi = 0;
+  u64 lo = hi_in != 0 ? lo_in : ~0ull, hi = hi_in;
+  if (hi_in != 0) {   // a known range holding every candidate
+    if (t == 0) {
+      sm.side_n = 0u;
+      sm.cnt_out = 0u;
+    }
+  } else {
 #pragma unroll
   for (int i = 0; i < RPT; ++i) if (i < nit) {
     if (v[i] != 0ull) {
@@ -1194,7 +1206,6 @@ __device__ __forceinline__ bool select_core(Smem<CAP>& sm, const CArgs& a, bool 
       hi = v[i] > hi ? v[i] : hi;
     }
   }
-  {
     const uint32_t a0 = wave_min_u32(static_cast<uint32_t>(lo >> 32));
     const uint32_t b0 = wave_max_u32(static_cast<uint32_t>(hi >> 32));
     const uint32_t al = wave_min_u32(static_cast<uint32_t>(lo >> 32) == a0 ? static_cast<uint32_t>(lo) : 0xFFFFFFFFu);
@@ -1373,7 +1384,7 @@ __device__ __forceinline__ void finish_row(Smem<CAP>& sm, const CArgs& a, bool b
 template <int KMAX, int CAP>
 __device__ __forceinline__ void finish_row_regs(Smem<CAP>& sm, const CArgs& a, bool bf16, int row,
                                                 u64 (&v)[kRankPerLane], uint32_t nit, uint32_t n,
-                                                uint32_t L, uint32_t status, int par) {
+                                                uint32_t L, uint32_t status, int par, u64 lo, u64 hi) {
   const int t = threadIdx.x;
   const uint32_t k = static_cast<uint32_t>(a.k);
   const uint32_t m = status ? 0u : min(k, L);
@@ -1381,8 +1392,8 @@ __device__ __forceinline__ void finish_row_regs(Smem<CAP>& sm, const CArgs& a, b
   const int64_t out0 = static_cast<int64_t>(row) * k;
   const char* xrow = static_cast<const char*>(a.x) + static_cast<int64_t>(row) * a.row_stride * (bf16 ? 2 : 4);
   if (m > 0 && n >= m &&
-      ((a.sorted == 0 && select_core(sm, a, bf16, xrow, out0, v, nit, m, status)) ||
-       (a.sorted == 1 && rank_core(sm, a, bf16, xrow, out0, v, nit, n, m, status)))) {
+      ((a.sorted == 0 && select_core(sm, a, bf16, xrow, out0, v, nit, m, status, lo, hi)) ||
+       (a.sorted == 1 && rank_core(sm, a, bf16, xrow, out0, v, nit, n, m, status, lo, hi)))) {
     for (uint32_t e = m + t; e < k; e += NT) store_one(a, bf16, xrow, out0 + e, 0ull, false, status);
     if (t == 0) a.row_status[row] = static_cast<int32_t>(status);
     stat_add(a, row, DS_STAT_CUTS, sm.n_cut);
@@ -1529,6 +1540,7 @@ __global__ __launch_bounds__(NT, blocks_per_cu(4)) void chunk_split_kernel(CArgs
 
   Buf B{0u, kTAll, 0};
   bool nan = false, spec = false;
+  uint32_t top_key = 0;   // the chunk's largest key (0: no values)
   // The chunk's candidates go to one region of buf per wave, as raw pairs,
   // in one pass over the registers (regions == true); should a region
   // overflow, the chunk is appended again contiguously, cutting as needed.
@@ -1538,7 +1550,7 @@ __global__ __launch_bounds__(NT, blocks_per_cu(4)) void chunk_split_kernel(CArgs
   if (status == 0 && mine) {
     u32x4 ra[V];
     load_chunk<BF16>(ra, xrow, static_cast<uint32_t>(seg), L);
-    nan = start_chunk<BF16>(sm, B, ra, static_cast<uint32_t>(seg), L, k, false, &spec);
+    nan = start_chunk<BF16>(sm, B, ra, static_cast<uint32_t>(seg), L, k, false, &spec, &top_key);
     const float f = __uint_as_float(bits_of_key(key_of(B.T)));
     const uint32_t wc = region_write<BF16>(sm, ra, static_cast<uint32_t>(seg), f, R);
     if (lane_id() == 0) sm.wtot[B.par][t >> 6] = wc;
@@ -1612,7 +1624,8 @@ __global__ __launch_bounds__(NT, blocks_per_cu(4)) void chunk_split_kernel(CArgs
   }
   if (t == 0) {
     st_agent(&a.ws_rec[2 * rs], mine ? B.T : kTAll);
-    st_agent(&a.ws_rec[2 * rs + 1], (static_cast<u64>(status) << 32) | hand);
+    st_agent(&a.ws_rec[2 * rs + 1],
+             (static_cast<u64>(status) << 56) | (static_cast<u64>(top_key) << 24) | hand);
   }
   // Ordering of the hand-over.  Every store above is an agent-scope atomic
   // store: on gfx950 it is written through to the device-coherent level
@@ -1673,40 +1686,46 @@ __global__ __launch_bounds__(NT, blocks_per_cu(4)) void chunk_split_kernel(CArgs
 #pragma unroll
     for (int q = 0; q < G8; ++q) vr[G8 + q] = 0ull;
   }
-  const uint32_t my_c = has_s ? static_cast<uint32_t>(ld_agent(&rec[2 * my_s + 1])) : 0u;
+  const uint32_t my_c = has_s ? static_cast<uint32_t>(ld_agent(&rec[2 * my_s + 1]) & 0xFFFFFFu) : 0u;
 #pragma unroll
   for (int q = 0; q < G8; ++q) {
     if (q * PL + my_l >= my_c) vr[q] = 0ull;
     if (per_round + q * PL + my_l >= my_c) vr[G8 + q] = 0ull;
   }
   u64 Tm = 0;
-  uint32_t fl = 0, cm = 0;
+  uint32_t fl = 0, cm = 0, tk = 0;
   if (t < S) {
     Tm = ld_agent(&rec[2 * t]);
     const u64 info = ld_agent(&rec[2 * t + 1]);
-    fl = static_cast<uint32_t>(info >> 32);
-    cm = static_cast<uint32_t>(info);
+    fl = static_cast<uint32_t>(info >> 56);
+    cm = static_cast<uint32_t>(info & 0xFFFFFFu);
+    tk = static_cast<uint32_t>(info >> 24);
   }
   {
     const uint32_t hiw = wave_max_u32(static_cast<uint32_t>(Tm >> 32));
     const uint32_t low = wave_max_u32(static_cast<uint32_t>(Tm >> 32) == hiw ? static_cast<uint32_t>(Tm) : 0u);
     const uint32_t cmx = wave_max_u32(cm);
+    const uint32_t tkx = wave_max_u32(tk);
     if (lane_id() == 0) {
       sm.wred[t >> 6] = (static_cast<u64>(hiw) << 32) | low;
+      sm.wred2[t >> 6] = tkx;
       sm.wmax[t >> 6] = cmx;
     }
   }
   status |= block_or(sm, fl, B.par);   // its barrier also publishes wred / wmax
   B.par ^= 1;
-  u64 tm = 0;
+  u64 tm = 0, tkm = 0;
   uint32_t cmax = 0;
 #pragma unroll
   for (int w = 0; w < NW; ++w) {
     tm = sm.wred[w] > tm ? sm.wred[w] : tm;
+    tkm = sm.wred2[w] > tkm ? sm.wred2[w] : tkm;
     cmax = max(cmax, sm.wmax[w]);
   }
   Tm = uniform64(tm);
   cmax = uniform(cmax);
+  // Every candidate lies in [Tm, the largest chunk key's last composite].
+  const u64 range_hi = (uniform64(tkm) << 32) | 0xFFFFFFFFull;
 
   // Every chunk's slots already in registers: the candidates at or above Tm
   // go to the epilogue from there, with no append.
@@ -1725,7 +1744,7 @@ __global__ __launch_bounds__(NT, blocks_per_cu(4)) void chunk_split_kernel(CArgs
     if (n >= min(k, L)) {
       if (t == 0) st_agent(&a.ws_arrive[row], 0u);
       finish_row_regs<KMAX>(sm, a, BF16, row, vr, two ? 2u * G8 : static_cast<uint32_t>(G8), n, L,
-                            status, B.par);
+                            status, B.par, Tm, range_hi);
       return;
     }
     __syncthreads();
