@@ -37,7 +37,7 @@ def build(verbose: bool = False, extra: list[str] | None = None) -> str:
     _run([HIPCC, *COMMON, *DEVICE, *extra, "-c", os.path.join(CSRC, "topk_kernels.hip"),
           "-o", k_obj], verbose)
     # The chunk kernels twice: whole rows (256 lanes) and split rows (1024).
-    _run([HIPCC, *COMMON, *DEVICE, *extra, "-DCHUNK_NT=256", "-c",
+    _run([HIPCC, *COMMON, *DEVICE, *extra, "-DCHUNK_NT=512", "-c",
           os.path.join(CSRC, "chunk_kernels.hip"), "-o", c_obj], verbose)
     _run([HIPCC, *COMMON, *DEVICE, *extra, "-DCHUNK_NT=1024", "-c",
           os.path.join(CSRC, "chunk_kernels.hip"), "-o", c2_obj], verbose)

@@ -67,9 +67,8 @@ constexpr int NT = CHUNK_NT;         // lanes per workgroup
 constexpr bool kSplit = NT == kChunkThreadsSplit;
 static_assert(kSplit || NT == kChunkThreadsRow, "one of the two chunk kernel builds");
 constexpr int NW = NT / 64;
-// Workgroups per CU the kernels are built for: `waves256` groups of four
-// waves, at least one workgroup.
-constexpr int blocks_per_cu(int waves256) { return waves256 * 256 / NT > 0 ? waves256 * 256 / NT : 1; }
+// Waves per SIMD for `blocks` workgroups per CU (the second launch bound).
+constexpr int waves_per_simd(int blocks) { return blocks * NT / 256 > 0 ? blocks * NT / 256 : 1; }
 constexpr int V = kChunkLoads;      // 16-byte loads per lane per chunk
 constexpr uint32_t kBias = 0x80000000u;
 constexpr uint32_t kNegInfKey = 0x00800000u;   // key of -inf, the lowest non-NaN key
@@ -1436,7 +1435,7 @@ __device__ __forceinline__ uint32_t row_len(const CArgs& a, int row, uint32_t* s
 
 // A whole row per workgroup, chunk by chunk.
 template <bool BF16, int KC>
-__global__ __launch_bounds__(NT, blocks_per_cu(KC >= 2 ? 3 : 4)) void chunk_row_kernel(CArgs a) {
+__global__ __launch_bounds__(NT, waves_per_simd(NT == 256 ? (KC >= 2 ? 3 : 4) : 2)) void chunk_row_kernel(CArgs a) {
   using G = Geo<BF16>;
   constexpr int KMAX = class_kmax(KC);
   constexpr int CAP = chunk_cap(KC, NT);
@@ -1512,7 +1511,7 @@ __global__ __launch_bounds__(NT, blocks_per_cu(KC >= 2 ? 3 : 4)) void chunk_row_
 // One chunk of a row per workgroup; the last workgroup of the row to finish
 // merges the others' candidates.
 template <bool BF16, int KC>
-__global__ __launch_bounds__(NT, blocks_per_cu(4)) void chunk_split_kernel(CArgs a) {
+__global__ __launch_bounds__(NT, waves_per_simd(1)) void chunk_split_kernel(CArgs a) {
   using G = Geo<BF16>;
   constexpr int KMAX = class_kmax(KC);
   constexpr int CAP = chunk_cap(KC, NT);

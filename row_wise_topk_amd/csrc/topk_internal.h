@@ -58,7 +58,7 @@ inline int class_of_k(int k) { return k <= 256 ? 0 : k <= 1024 ? 1 : k <= 2048 ?
 // 256-lane workgroups (several rows per CU), split rows with 1024-lane
 // workgroups (one per CU), so that a split row's merge and exact selection
 // run on 16 waves.
-constexpr int kChunkThreadsRow = 256;
+constexpr int kChunkThreadsRow = 512;
 constexpr int kChunkThreadsSplit = 1024;
 constexpr int kChunkLoads = 8;
 constexpr int64_t chunk_elems(int dtype, int nt) { return int64_t{nt} * kChunkLoads * (dtype == 0 ? 4 : 8); }

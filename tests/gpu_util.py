@@ -11,7 +11,7 @@ FP32, BF16 = 0, 1
 # Values per chunk of the chunk kernels: eight 16-byte loads per lane of a
 # 1024-lane workgroup for split rows, of a 256-lane workgroup for whole rows.
 CHUNK_ELEMS = {FP32: 32768, BF16: 65536}
-CHUNK_ELEMS_ROW = {FP32: 8192, BF16: 16384}
+CHUNK_ELEMS_ROW = {FP32: 16384, BF16: 32768}
 
 
 def say(msg: str):
