@@ -147,13 +147,12 @@ ds_status_t ds_topk(const void* x, ds_dtype_t dtype, int64_t batch, int64_t n_co
  *   flush_at     candidate count that triggers a cut back to k (0 = automatic;
  *                else k+1 .. the buffer's fixed trigger for this k class; the
  *                chunk kernels raise it to at least k plus one vector per
- *                lane: k + 2048 for whole rows, k + 8192 for split rows).
+ *                lane: k + 4096).
  *   kernel       DS_KERNEL_AUTO (0), DS_KERNEL_STREAM (1): one or more
  *                workgroups stream a row block by block (long rows), or
- *                DS_KERNEL_CHUNK (2): a workgroup holds a chunk of a row in
- *                registers (32 KiB per 256-lane workgroup for whole rows,
- *                128 KiB per 1024-lane workgroup for split rows); rows of up
- *                to 524,288 fp32 or 1,048,576 bf16 values.
+ *                DS_KERNEL_CHUNK (2): a 512-lane workgroup holds 64 KiB of a
+ *                row in registers at a time; rows of up to 64 such chunks
+ *                (1,048,576 fp32 or 2,097,152 bf16 values).
  *   stats        NULL, or a device uint32 array [batch * 4], 4-B aligned, to
  *                which the call ADDS per-row counts at [4 i + DS_STAT_*] (the
  *                caller zeroes it); results are unchanged.  A debug aid.

@@ -36,10 +36,10 @@ def build(verbose: bool = False, extra: list[str] | None = None) -> str:
     n_obj = os.path.join(bdir, "noalloc.o")
     _run([HIPCC, *COMMON, *DEVICE, *extra, "-c", os.path.join(CSRC, "topk_kernels.hip"),
           "-o", k_obj], verbose)
-    # The chunk kernels twice: whole rows (256 lanes) and split rows (1024).
-    _run([HIPCC, *COMMON, *DEVICE, *extra, "-DCHUNK_NT=512", "-c",
+    # The chunk kernels twice: whole rows and split rows.
+    _run([HIPCC, *COMMON, *DEVICE, *extra, "-DCHUNK_SPLIT=0", "-c",
           os.path.join(CSRC, "chunk_kernels.hip"), "-o", c_obj], verbose)
-    _run([HIPCC, *COMMON, *DEVICE, *extra, "-DCHUNK_NT=1024", "-c",
+    _run([HIPCC, *COMMON, *DEVICE, *extra, "-DCHUNK_SPLIT=1", "-c",
           os.path.join(CSRC, "chunk_kernels.hip"), "-o", c2_obj], verbose)
     _run([HIPCC, *COMMON, *DEVICE, *extra, "-x", "hip", "-c", os.path.join(CSRC, "topk_api.cpp"),
           "-o", a_obj], verbose)

@@ -60,12 +60,11 @@ typedef unsigned long long u64;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
-#ifndef CHUNK_NT
-#error "built with CHUNK_NT = kChunkThreadsRow (whole rows) or kChunkThreadsSplit (split rows)"
+#ifndef CHUNK_SPLIT
+#error "built with CHUNK_SPLIT = 1 (split rows) or 0 (whole rows)"
 #endif
-constexpr int NT = CHUNK_NT;         // lanes per workgroup
-constexpr bool kSplit = NT == kChunkThreadsSplit;
-static_assert(kSplit || NT == kChunkThreadsRow, "one of the two chunk kernel builds");
+constexpr bool kSplit = CHUNK_SPLIT != 0;
+constexpr int NT = kSplit ? kChunkThreadsSplit : kChunkThreadsRow;   // lanes per workgroup
 constexpr int NW = NT / 64;
 // Waves per SIMD for `blocks` workgroups per CU (the second launch bound).
 constexpr int waves_per_simd(int blocks) { return blocks * NT / 256 > 0 ? blocks * NT / 256 : 1; }
@@ -1511,7 +1510,7 @@ __global__ __launch_bounds__(NT, waves_per_simd(NT == 256 ? (KC >= 2 ? 3 : 4) : 
 // One chunk of a row per workgroup; the last workgroup of the row to finish
 // merges the others' candidates.
 template <bool BF16, int KC>
-__global__ __launch_bounds__(NT, waves_per_simd(1)) void chunk_split_kernel(CArgs a) {
+__global__ __launch_bounds__(NT, waves_per_simd(1024 / NT)) void chunk_split_kernel(CArgs a) {
   using G = Geo<BF16>;
   constexpr int KMAX = class_kmax(KC);
   constexpr int CAP = chunk_cap(KC, NT);
@@ -1852,7 +1851,7 @@ const void* chunk_fn(int cls) {
 
 }  // namespace
 
-#if CHUNK_NT == 1024
+#if CHUNK_SPLIT
 #define DSTK_LAUNCH_CHUNK launch_chunk_split
 #define DSTK_LAUNCH_CHUNK_READ launch_chunk_read_split
 #else

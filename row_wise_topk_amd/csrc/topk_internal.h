@@ -54,12 +54,11 @@ inline int class_of_k(int k) { return k <= 256 ? 0 : k <= 1024 ? 1 : k <= 2048 ?
 
 // ---- chunk kernels (chunk_kernels.hip)
 // A chunk: kChunkLoads 16-byte loads per lane of the workgroup, all in
-// flight at once.  chunk_kernels.hip is built twice: whole rows with
-// 256-lane workgroups (several rows per CU), split rows with 1024-lane
-// workgroups (one per CU), so that a split row's merge and exact selection
-// run on 16 waves.
+// flight at once.  chunk_kernels.hip is built twice, for whole rows and for
+// split rows; both use 512-lane workgroups, two per CU, so that a row's
+// merge and exact selection run on 8 waves.
 constexpr int kChunkThreadsRow = 512;
-constexpr int kChunkThreadsSplit = 1024;
+constexpr int kChunkThreadsSplit = 512;
 constexpr int kChunkLoads = 8;
 constexpr int64_t chunk_elems(int dtype, int nt) { return int64_t{nt} * kChunkLoads * (dtype == 0 ? 4 : 8); }
 // Candidate buffer: k plus room for the larger of k and one bf16 vector per

@@ -44,12 +44,12 @@ int launch_read(const KArgs& a, int, int, uint32_t* sink, hipStream_t) {
   CHECK(a.segments >= 1);
   return 0;
 }
-static void check_chunk(const CArgs& a, int dtype, int cls, int nt) {
+static void check_chunk(const CArgs& a, int dtype, int cls, int nt, bool split) {
   ++launches;
   CHECK(dtype == 0 || dtype == 1);
   CHECK(cls >= 0 && cls < kNumClasses);
   CHECK(a.segments >= 1 && a.segments <= kMaxSegments);
-  CHECK((a.segments > 1) == (nt == kChunkThreadsSplit));
+  CHECK((a.segments > 1) == split);
   CHECK(a.cap_eff >= static_cast<uint32_t>(a.k + chunk_room(nt)) ||
         a.cap_eff == static_cast<uint32_t>(chunk_cap(cls, nt)));
   CHECK(a.cap_eff <= static_cast<uint32_t>(chunk_cap(cls, nt)));
@@ -62,11 +62,11 @@ static void check_chunk(const CArgs& a, int dtype, int cls, int nt) {
   }
 }
 int launch_chunk_row(const CArgs& a, int dtype, int cls, hipStream_t) {
-  check_chunk(a, dtype, cls, kChunkThreadsRow);
+  check_chunk(a, dtype, cls, kChunkThreadsRow, false);
   return 0;
 }
 int launch_chunk_split(const CArgs& a, int dtype, int cls, hipStream_t) {
-  check_chunk(a, dtype, cls, kChunkThreadsSplit);
+  check_chunk(a, dtype, cls, kChunkThreadsSplit, true);
   return 0;
 }
 static void check_read(const CArgs& a, uint32_t* sink) {

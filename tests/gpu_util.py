@@ -9,8 +9,8 @@ from tests.build_util import ensure_built
 
 FP32, BF16 = 0, 1
 # Values per chunk of the chunk kernels: eight 16-byte loads per lane of a
-# 1024-lane workgroup for split rows, of a 256-lane workgroup for whole rows.
-CHUNK_ELEMS = {FP32: 32768, BF16: 65536}
+# 512-lane workgroup (split rows and whole rows alike).
+CHUNK_ELEMS = {FP32: 16384, BF16: 32768}
 CHUNK_ELEMS_ROW = {FP32: 16384, BF16: 32768}
 
 

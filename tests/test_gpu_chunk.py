@@ -1,10 +1,9 @@
 """GPU parity for the data-dependent paths of the chunk kernels.
 
-A workgroup of the chunk kernels holds a chunk of a row in registers: a row
-is either split into one 1024-lane workgroup per chunk of 32768 fp32 or
-65536 bf16 values (the last to finish merges the others' candidates) or
-taken whole by one 256-lane workgroup, chunk by chunk (8192 fp32 or 16384
-bf16 values each).  The first chunk of a workgroup sets the start
+A 512-lane workgroup of the chunk kernels holds a chunk of a row in
+registers, 16384 fp32 or 32768 bf16 values: a row is either split into one
+workgroup per chunk (the last to finish merges the others' candidates) or
+taken whole by one workgroup, chunk by chunk.  The first chunk of a workgroup sets the start
 threshold: exact when the chunk is the whole row, otherwise an estimate of
 the row's k-th value for the chunk's share, checked once the row is
 complete (the row is read again from -inf when fewer than min(k, L)
