@@ -59,6 +59,7 @@ namespace {
 typedef unsigned long long u64;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x2 __attribute__((ext_vector_type(2)));
 
 #ifndef CHUNK_SPLIT
 #error "built with CHUNK_SPLIT = 1 (split rows) or 0 (whole rows)"
@@ -326,8 +327,9 @@ __device__ __forceinline__ void for_values(const u32x4& r, F&& f) {
 }
 
 // The chunk that holds column L-1: returns whether a NaN is among the valid
-// values, then replaces every value at or past L by a NaN, which no compare
-// admits, no histogram counts and fmaxf ignores.
+// values, then replaces every value at or past L by a negative NaN (all bits
+// set), which no float compare admits, no histogram counts, and which sits
+// below every positive pattern as a signed integer.
 template <bool BF16>
 __device__ __forceinline__ bool sanitize_ragged(u32x4 (&r)[V], uint32_t c, uint32_t L) {
   bool nan = false;
@@ -340,42 +342,91 @@ __device__ __forceinline__ bool sanitize_ragged(u32x4 (&r)[V], uint32_t c, uint3
         const bool ok0 = col_at<true>(c, i, 2 * w) < L, ok1 = col_at<true>(c, i, 2 * w + 1) < L;
         nan |= ok0 & ((d & 0x7FFFu) > 0x7F80u);
         nan |= ok1 & (((d >> 16) & 0x7FFFu) > 0x7F80u);
-        r[i][w] = (ok0 ? (d & 0xFFFFu) : 0x7FFFu) | (ok1 ? (d & 0xFFFF0000u) : 0x7FFF0000u);
+        r[i][w] = (ok0 ? (d & 0xFFFFu) : 0xFFFFu) | (ok1 ? (d & 0xFFFF0000u) : 0xFFFF0000u);
       } else {
         const bool ok = col_at<false>(c, i, w) < L;
         nan |= ok & ((d & 0x7FFFFFFFu) > 0x7F800000u);
-        r[i][w] = ok ? d : 0x7FFFFFFFu;
+        r[i][w] = ok ? d : 0xFFFFFFFFu;
       }
     }
   }
   return nan;
 }
 
-// Per lane: the largest key among the non-NaN values (0 if none) and, with
-// CHECK, whether any value is a NaN.
+// Per lane: the key of its largest value (0 if that is a NaN or the lane
+// has none) and, with CHECK, whether any value is a NaN.  Integer maxima of
+// the raw patterns, two bf16 per instruction: as signed integers the
+// non-negative values order like their floats, above every negative one,
+// with positive NaNs above +inf; as unsigned integers negative NaNs lie
+// above -inf.  A lane whose values are all negative takes its largest as
+// the smallest unsigned pattern, on a branch that typical data never takes.
 template <bool BF16, bool CHECK>
 __device__ __forceinline__ void chunk_max_nan(const u32x4 (&r)[V], uint32_t* maxkey, bool* nan) {
-  float mx = __uint_as_float(kQNaN32);   // fmaxf(NaN, x) = x: stays NaN if every value is
-  uint32_t mag = 0;
-  u16x2 mag2 = {0, 0};   // bf16: both halves' magnitudes at once
-#pragma unroll
-  for (int i = 0; i < V; ++i) {
+  uint32_t top;   // the lane's largest value as an fp32 pattern
+  bool bad;
+  if constexpr (BF16) {
+    // One accumulator per word of a vector: four independent chains.
+    i16x2 smax[4];
+    u16x2 umax[4];
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const uint32_t d = r[i][w];
-      if constexpr (BF16) {
-        if (CHECK) mag2 = __builtin_elementwise_max(mag2, __builtin_bit_cast(u16x2, d & 0x7FFF7FFFu));
-        mx = fmaxf(mx, __uint_as_float(lo_half(d)));
-        mx = fmaxf(mx, __uint_as_float(d & 0xFFFF0000u));
-      } else {
-        if (CHECK) mag = max(mag, d & 0x7FFFFFFFu);
-        mx = fmaxf(mx, __uint_as_float(d));
+      smax[w] = i16x2{-32768, -32768};
+      umax[w] = u16x2{0, 0};
+    }
+#pragma unroll
+    for (int i = 0; i < V; ++i)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        // (a copy first: a bit cast of a vector element in place reads the
+        // vector's first element with this compiler)
+        const uint32_t d = r[i][w];
+        smax[w] = __builtin_elementwise_max(smax[w], __builtin_bit_cast(i16x2, d));
+        if (CHECK) umax[w] = __builtin_elementwise_max(umax[w], __builtin_bit_cast(u16x2, d));
+      }
+    const i16x2 s2 = __builtin_elementwise_max(__builtin_elementwise_max(smax[0], smax[1]),
+                                               __builtin_elementwise_max(smax[2], smax[3]));
+    const u16x2 u2 = __builtin_elementwise_max(__builtin_elementwise_max(umax[0], umax[1]),
+                                               __builtin_elementwise_max(umax[2], umax[3]));
+    const int sm = max(static_cast<int>(s2.x), static_cast<int>(s2.y));
+    bad = sm > 0x7F80 || max(static_cast<uint32_t>(u2.x), static_cast<uint32_t>(u2.y)) > 0xFF80u;
+    top = static_cast<uint32_t>(sm) << 16;
+    if (sm < 0) {
+      u16x2 umin = {0xFFFF, 0xFFFF};
+#pragma unroll
+      for (int i = 0; i < V; ++i)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t d = r[i][w];
+          umin = __builtin_elementwise_min(umin, __builtin_bit_cast(u16x2, d));
+        }
+      top = min(static_cast<uint32_t>(umin.x), static_cast<uint32_t>(umin.y)) << 16;
+    }
+  } else {
+    int32_t sa = INT32_MIN, sb = INT32_MIN;
+    uint32_t ua = 0, ub = 0;
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      sa = max(sa, max(static_cast<int32_t>(r[i][0]), static_cast<int32_t>(r[i][1])));
+      sb = max(sb, max(static_cast<int32_t>(r[i][2]), static_cast<int32_t>(r[i][3])));
+      if (CHECK) {
+        ua = max(ua, max(r[i][0], r[i][1]));
+        ub = max(ub, max(r[i][2], r[i][3]));
       }
     }
+    const int32_t smax = max(sa, sb);
+    bad = smax > 0x7F800000 || max(ua, ub) > 0xFF800000u;
+    top = static_cast<uint32_t>(smax);
+    if (smax < 0) {
+      uint32_t umin = 0xFFFFFFFFu;
+#pragma unroll
+      for (int i = 0; i < V; ++i)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) umin = min(umin, r[i][w]);
+      top = umin;
+    }
   }
-  if constexpr (BF16) mag = max(static_cast<uint32_t>(mag2.x), static_cast<uint32_t>(mag2.y));
-  *nan = CHECK && mag > (BF16 ? 0x7F80u : 0x7F800000u);
-  *maxkey = mx == mx ? key_of_bits(__float_as_uint(mx)) : 0u;
+  *nan = CHECK && bad;
+  *maxkey = (top & 0x7FFFFFFFu) > 0x7F800000u ? 0u : key_of_bits(top);
 }
 
 // Values of the lane >= f (NaN never).
@@ -723,42 +774,156 @@ __device__ __forceinline__ bool start_chunk(Smem<CAP>& sm, Buf& B, u32x4 (&r)[V]
   return nan;
 }
 
-// Write the wave's values >= f of a chunk to its own region of buf (R slots
-// from w*R) as raw pairs (bits << 32) | column, in slot-major order, with no
-// count first: a slot no lane keeps costs one compare.  Returns the wave's
-// count (uniform), which exceeds R when the region overflowed (then it holds
-// only the first R).
-template <bool BF16, int CAP>
-__device__ __forceinline__ uint32_t region_write(Smem<CAP>& sm, const u32x4 (&r)[V], uint32_t c,
-                                                 float f, uint32_t R) {
+// Write the wave's values that pass `ok` (a test on the raw word d and the
+// half h of it) to the region reg of R slots as raw pairs (d << 32) | column;
+// `hit` tells whether a 16-byte vector holds a value that passes.  For bf16
+// the column's parity tells which half of d is the value.  Returns the
+// wave's count (uniform), which exceeds R when the region overflowed (then
+// it holds only the first R).
+//
+// Few vectors hold a candidate (about one lane in sixteen per vector on a
+// split row), so the vectors that do are first copied, with their first
+// column, to the top of the region, one lane each; the wave then compacts
+// their values slot by slot: EPV ballots over the copies instead of EPV
+// ballots per vector of every lane.  With more than SM such vectors in the
+// wave, or a region too small, the compaction runs over the registers.
+template <bool BF16, typename OK, typename HIT>
+__device__ __forceinline__ uint32_t region_pass(u64* buf, uint32_t rb, const u32x4 (&r)[V],
+                                                uint32_t c, uint32_t R, OK&& ok, HIT&& hit) {
   using G = Geo<BF16>;
-  u64* reg = sm.buf + (threadIdx.x >> 6) * R;
-  uint32_t pos = 0;
+  constexpr uint32_t SM = 64;   // copies per wave
+  u64* reg = buf + rb;
+  bool hl[V];
+  u64 hv[V];
+  uint32_t nh = 0;
 #pragma unroll
   for (int i = 0; i < V; ++i) {
-    if (pos + 64u * G::EPV <= R) {
-      // The whole vector fits whatever passes: no bound per value.
-      for_values<BF16>(r[i], [&](uint32_t b, int q) {
-        const bool ok = __uint_as_float(b) >= f;
-        const u64 m = ballot(ok);
+    hl[i] = hit(r[i]);
+    hv[i] = ballot(hl[i]);
+    nh += static_cast<uint32_t>(__popcll(hv[i]));
+  }
+  uint32_t pos = 0;
+  if (nh <= SM && nh * G::EPV <= R && R >= 3 * SM) {
+    // Copies at the top of the region: SM vectors (16-byte aligned), below
+    // them SM first columns.  Every copy is read back by one instruction
+    // before any candidate is written, so the candidates, written from the
+    // region's start, may overwrite them.
+    u32x4* st = reinterpret_cast<u32x4*>(buf + ((rb + R - 2 * SM) & ~1u));
+    uint32_t* stc = reinterpret_cast<uint32_t*>(st) - SM;
+    const uint32_t col0 = c * G::CE + threadIdx.x * G::EPV;
+    uint32_t sp = 0;
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      if (hv[i]) {
+        if (hl[i]) {
+          const uint32_t j = sp + mbcnt64(hv[i]);
+          st[j] = r[i];
+          stc[j] = col0 + static_cast<uint32_t>(i * NT * G::EPV);
+        }
+        sp += static_cast<uint32_t>(__popcll(hv[i]));
+      }
+    }
+    // Lanes past the copies hold negative NaNs, which pass no test.
+    u32x4 v = {~0u, ~0u, ~0u, ~0u};
+    uint32_t cb = 0;
+    if (lane_id() < sp) {
+      v = st[lane_id()];
+      cb = stc[lane_id()];
+    }
+#pragma unroll
+    for (int q = 0; q < G::EPV; ++q) {
+      const uint32_t d = v[BF16 ? q >> 1 : q];
+      const bool p = ok(d, q & 1);
+      const u64 m = ballot(p);
+      if (m) {
+        if (p) reg[pos + mbcnt64(m)] = (static_cast<u64>(d) << 32) | (cb + static_cast<uint32_t>(q));
+        pos += static_cast<uint32_t>(__popcll(m));
+      }
+    }
+    return pos;
+  }
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    if (!hv[i]) continue;
+    if (pos + 64u * G::EPV <= R) {   // the whole vector fits whatever passes
+#pragma unroll
+      for (int q = 0; q < G::EPV; ++q) {
+        const uint32_t d = r[i][BF16 ? q >> 1 : q];
+        const bool p = ok(d, q & 1);
+        const u64 m = ballot(p);
         if (m) {
-          if (ok) reg[pos + mbcnt64(m)] = (static_cast<u64>(b) << 32) | col_at<BF16>(c, i, q);
+          if (p) reg[pos + mbcnt64(m)] = (static_cast<u64>(d) << 32) | col_at<BF16>(c, i, q);
           pos += static_cast<uint32_t>(__popcll(m));
         }
-      });
+      }
     } else {
-      for_values<BF16>(r[i], [&](uint32_t b, int q) {
-        const bool ok = __uint_as_float(b) >= f;
-        const u64 m = ballot(ok);
+#pragma unroll
+      for (int q = 0; q < G::EPV; ++q) {
+        const uint32_t d = r[i][BF16 ? q >> 1 : q];
+        const bool p = ok(d, q & 1);
+        const u64 m = ballot(p);
         if (m) {
-          const uint32_t p = pos + mbcnt64(m);
-          if (ok && p < R) reg[p] = (static_cast<u64>(b) << 32) | col_at<BF16>(c, i, q);
+          const uint32_t at = pos + mbcnt64(m);
+          if (p && at < R) reg[at] = (static_cast<u64>(d) << 32) | col_at<BF16>(c, i, q);
           pos += static_cast<uint32_t>(__popcll(m));
         }
-      });
+      }
     }
   }
   return pos;
+}
+
+// A raw pair of region_pass as a composite.
+template <bool BF16>
+__device__ __forceinline__ u64 comp_of_raw(u64 pr) {
+  const uint32_t d = static_cast<uint32_t>(pr >> 32), col = static_cast<uint32_t>(pr);
+  uint32_t b = d;
+  if constexpr (BF16) b = (col & 1u) ? (d & 0xFFFF0000u) : (d << 16);
+  return comp_of(key_of_bits(b), col);
+}
+
+// Write the wave's values >= f of a chunk to its own region of buf (R slots
+// from w*R) as raw pairs.  Returns the wave's count (uniform), which exceeds
+// R when the region overflowed (then it holds only the first R).  For bf16
+// and f > 0 the test is an integer compare of each half's pattern with the
+// smallest bf16 pattern >= f (positive floats order like their patterns,
+// every negative one and the ragged padding lie below); else a float compare.
+template <bool BF16, int CAP>
+__device__ __forceinline__ uint32_t region_write(Smem<CAP>& sm, const u32x4 (&r)[V], uint32_t c,
+                                                 float f, uint32_t R) {
+  const uint32_t rb = uniform(threadIdx.x >> 6) * R;   // the wave's region: buf[rb, rb + R)
+  const uint32_t fb = __float_as_uint(f);
+  if constexpr (BF16) {
+    if (static_cast<int32_t>(fb) > 0) {
+      const uint32_t tb = (fb + 0xFFFFu) >> 16;
+      const int16_t tlo = static_cast<int16_t>(tb);
+      const int32_t thi = static_cast<int32_t>(tb << 16);
+      return region_pass<true>(
+          sm.buf, rb, r, c, R,
+          [&](uint32_t d, int h) { return h ? static_cast<int32_t>(d) >= thi : static_cast<int16_t>(d) >= tlo; },
+          [&](const u32x4& v) {
+            const uint32_t w0 = v[0], w1 = v[1], w2 = v[2], w3 = v[3];
+            const i16x2 a = __builtin_elementwise_max(__builtin_bit_cast(i16x2, w0), __builtin_bit_cast(i16x2, w1));
+            const i16x2 b = __builtin_elementwise_max(__builtin_bit_cast(i16x2, w2), __builtin_bit_cast(i16x2, w3));
+            const i16x2 m = __builtin_elementwise_max(a, b);
+            return max(m.x, m.y) >= tlo;
+          });
+    }
+    const auto ok = [&](uint32_t d, int h) { return __uint_as_float(h ? (d & 0xFFFF0000u) : lo_half(d)) >= f; };
+    return region_pass<true>(sm.buf, rb, r, c, R, ok, [&](const u32x4& v) {
+      bool any = false;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) any |= ok(v[q >> 1], q & 1);
+      return any;
+    });
+  } else {
+    return region_pass<false>(
+        sm.buf, rb, r, c, R, [&](uint32_t d, int) { return __uint_as_float(d) >= f; },
+        [&](const u32x4& v) {
+          return fmaxf(fmaxf(__uint_as_float(v[0]), __uint_as_float(v[1])),
+                       fmaxf(__uint_as_float(v[2]), __uint_as_float(v[3]))) >= f;
+        });
+  }
 }
 
 // A later chunk of a whole row.
@@ -1580,8 +1745,7 @@ __global__ __launch_bounds__(NT, waves_per_simd(1024 / NT)) void chunk_split_ker
     const uint32_t w = t >> 6;
     u64* reg = sm.buf + w * R;
     for (uint32_t j = lane_id(); j < cnt[w]; j += 64) {
-      const u64 pr = reg[j];
-      reg[j] = comp_of(key_of_bits(static_cast<uint32_t>(pr >> 32)), static_cast<uint32_t>(pr));
+      reg[j] = comp_of_raw<BF16>(reg[j]);
     }
     uint32_t dst = cnt[0];
     for (uint32_t ww = 1; ww < static_cast<uint32_t>(NW); ++ww) {
@@ -1614,8 +1778,7 @@ __global__ __launch_bounds__(NT, waves_per_simd(1024 / NT)) void chunk_split_ker
     const u64* reg = sm.buf + w * R;
     const uint32_t mc = status ? 0u : cnt[w];
     for (uint32_t j = lane_id(); j < mc; j += 64) {
-      const u64 pr = reg[j];
-      st_agent(&slot[base + j], comp_of(key_of_bits(static_cast<uint32_t>(pr >> 32)), static_cast<uint32_t>(pr)));
+      st_agent(&slot[base + j], comp_of_raw<BF16>(reg[j]));
     }
   } else {
     for (uint32_t j = t; j < hand; j += NT) st_agent(&slot[j], sm.buf[j]);
