@@ -203,6 +203,7 @@ struct Smem {
   uint32_t err;
   uint32_t n_cut;                     // cuts back to k made by this workgroup (statistics)
   uint32_t is_last;
+  uint32_t zeros;                     // a zero was stored as an output value
   u64 res64;
 };
 
@@ -231,22 +232,21 @@ __device__ __forceinline__ uint32_t block_excl(Smem<CAP>& sm, uint32_t v, int pa
 }
 
 // Bins in rank order (bin 0 ranks first), BPT of them per lane, lane t owning
-// bins [t*BPT, (t+1)*BPT).  Finds the bin b where the running count reaches
-// `need`: sum(bins < b) < need <= sum(bins <= b).  res = {b, sum below b,
-// count of b, total}; b = kNone when the total is below need.
+// bins [t*BPT, (t+1)*BPT).  Returns the bin b where the running count reaches
+// `need`: sum(bins < b) < need <= sum(bins <= b), or kNone when the total is
+// below need; then res = {b, sum below b, count of b}.  The total goes to
+// *total_out when given.
 template <int BPT, int CAP>
-__device__ __forceinline__ void find_rank(Smem<CAP>& sm, const uint32_t (&h)[BPT], uint32_t need,
-                                          int par) {
+__device__ __forceinline__ uint32_t find_rank(Smem<CAP>& sm, const uint32_t (&h)[BPT], uint32_t need,
+                                              int par, uint32_t* total_out = nullptr) {
   uint32_t s = 0;
 #pragma unroll
   for (int i = 0; i < BPT; ++i) s += h[i];
   uint32_t total;
   const uint32_t before = block_excl(sm, s, par, &total);
-  if (threadIdx.x == 0) {
-    sm.res[0] = kNone;
-    sm.res[3] = total;
-  }
-  __syncthreads();
+  if (total_out) *total_out = total;
+  // Exactly one lane holds the crossing when total >= need; every reader of
+  // an earlier result has passed block_excl's barrier.
   if (before < need && need <= before + s) {
     uint32_t acc = before;
 #pragma unroll
@@ -260,6 +260,7 @@ __device__ __forceinline__ void find_rank(Smem<CAP>& sm, const uint32_t (&h)[BPT
     }
   }
   __syncthreads();
+  return total < need ? kNone : uniform(sm.res[0]);
 }
 
 
@@ -485,8 +486,7 @@ __device__ __forceinline__ u64 start_threshold(Smem<CAP>& sm, const u32x4 (&r)[V
     uint32_t h[1];
     h[0] = sm.hist[threadIdx.x];
     sm.hist[threadIdx.x] = 0u;   // own bin: no other lane touches it until the next barrier
-    find_rank<1>(sm, h, m, pass);
-    const uint32_t b = uniform(sm.res[0]);
+    const uint32_t b = find_rank<1>(sm, h, m, pass);
     if (b != kNone) {
       const int64_t e = static_cast<int64_t>(maxkey) - (static_cast<int64_t>(b + 1) << s) + 1;
       const uint32_t edge = e > static_cast<int64_t>(lo_key) ? static_cast<uint32_t>(e) : lo_key;
@@ -577,9 +577,8 @@ __device__ __noinline__ u64 cut_exact(Smem<CAP>& sm, uint32_t n, uint32_t keep) 
       h[i] = sm.hist[t * kCutBPT + i];
       sm.hist[t * kCutBPT + i] = 0u;
     }
-    find_rank<kCutBPT>(sm, h, need, par);
+    const uint32_t b = find_rank<kCutBPT>(sm, h, need, par);
     par ^= 1;
-    const uint32_t b = uniform(sm.res[0]);
     if (b == kNone) {   // fewer than `need` in range: inconsistent counts
       if (t == 0) sm.err = 1u;
       return 0;
@@ -1111,18 +1110,18 @@ __device__ __forceinline__ void sort_desc(K (&v)[PER], K* xch) {
 }
 
 // ---------------------------------------------------------------- outputs
-__device__ __forceinline__ void store_one(const CArgs& a, bool bf16, const char* xrow, int64_t o,
+__device__ __forceinline__ bool store_one(const CArgs& a, bool bf16, const char* xrow, int64_t o,
                                           u64 c, bool valid, uint32_t status) {
+  (void)xrow;
   uint32_t ix, v;
+  bool zero = false;
   if (valid) {
     ix = col_of(c);
     const uint32_t key = key_of(c);
-    if (key == kBias) {   // a zero: its sign is only in the input
-      v = bf16 ? static_cast<uint32_t>(reinterpret_cast<const uint16_t*>(xrow)[ix]) << 16
-               : reinterpret_cast<const uint32_t*>(xrow)[ix];
-    } else {
-      v = bits_of_key(key);
-    }
+    // Both zeros share a key; +0 is stored and fix_zero_signs restores a -0
+    // from the input afterwards (no load here, so the stores never wait).
+    zero = key == kBias;
+    v = zero ? 0u : bits_of_key(key);
   } else {
     ix = 0xFFFFFFFFu;
     v = status ? kQNaN32 : kNegInf32;
@@ -1136,6 +1135,28 @@ __device__ __forceinline__ void store_one(const CArgs& a, bool bf16, const char*
       static_cast<uint16_t*>(a.values)[o] = static_cast<uint16_t>(v >> 16);
     else
       static_cast<uint32_t*>(a.values)[o] = v;
+  }
+  return zero && a.return_values;
+}
+
+// After a barrier that follows a row's stores: every output value stored as
+// +0 takes the zero's sign from the input (its index was stored beside it).
+__device__ __forceinline__ void fix_zero_signs(const CArgs& a, bool bf16, const char* xrow,
+                                            int64_t out0, uint32_t m) {
+  for (uint32_t e = threadIdx.x; e < m; e += NT) {
+    const int64_t o = out0 + e;
+    const uint32_t vb = bf16 ? static_cast<uint32_t>(static_cast<const uint16_t*>(a.values)[o])
+                             : static_cast<const uint32_t*>(a.values)[o];
+    if (vb != 0u) continue;
+    const uint32_t ix = a.idx64 ? static_cast<uint32_t>(static_cast<const int64_t*>(a.indices)[o])
+                                : static_cast<uint32_t>(static_cast<const int32_t*>(a.indices)[o]);
+    if (bf16) {
+      const uint16_t xb = reinterpret_cast<const uint16_t*>(xrow)[ix];
+      if (xb != 0u) static_cast<uint16_t*>(a.values)[o] = xb;
+    } else {
+      const uint32_t xb = reinterpret_cast<const uint32_t*>(xrow)[ix];
+      if (xb != 0u) static_cast<uint32_t*>(a.values)[o] = xb;
+    }
   }
 }
 
@@ -1176,11 +1197,13 @@ __device__ __forceinline__ void sort_and_store(Smem<CAP>& sm, const CArgs& a, bo
     v[i] = e < m ? sort_key<K>(sm.buf[e], by_col) : K(0);
   }
   sort_desc<K, PER>(v, reinterpret_cast<K*>(sm.buf));
+  bool z = false;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const uint32_t e = t * PER + i;
-    if (e < k) store_one(a, bf16, xrow, out0 + e, comp_of_sort_key<K>(v[i], by_col), e < m, status);
+    if (e < k) z |= store_one(a, bf16, xrow, out0 + e, comp_of_sort_key<K>(v[i], by_col), e < m, status);
   }
+  if (z) sm.zeros = 1u;
 }
 
 // Rank selection: the exact output position of every candidate, without a
@@ -1189,17 +1212,18 @@ __device__ __forceinline__ void sort_and_store(Smem<CAP>& sm, const CArgs& a, bo
 // candidates are scattered into their bins, and each one's rank is its bin's
 // first position plus the number of its bin-mates above it.  A candidate of
 // rank below m is stored at output position `rank` (value order), the rest are
-// dropped.  Returns false, having stored nothing, when a bin holds more than
-// kBinRankMax candidates (long runs of equal values); the caller then cuts and
-// sorts.  Needs n <= RPT * NT.
+// dropped.  Returns false, having stored nothing, when there are fewer than m
+// candidates or a bin holds more than kBinRankMax of them (long runs of equal
+// values; the caller then cuts and sorts).  The count goes to *n_out when
+// given.  Needs a count <= RPT * NT.
 constexpr uint32_t kBinRankMax = 128;
 constexpr int kRankPerLane = 4096 / NT;
 
 template <int CAP>
 __device__ __forceinline__ bool rank_core(Smem<CAP>& sm, const CArgs& a, bool bf16,
                                           const char* xrow, int64_t out0, u64 (&v)[kRankPerLane],
-                                          uint32_t nit, uint32_t n, uint32_t m, uint32_t status,
-                                          u64 lo_in = 0, u64 hi_in = 0) {
+                                          uint32_t nit, uint32_t m, uint32_t status,
+                                          u64 lo_in = 0, u64 hi_in = 0, uint32_t* n_out = nullptr) {
   constexpr int RPT = kRankPerLane;
   const uint32_t t = threadIdx.x;
   u64 lo = hi_in != 0 ? lo_in : ~0ull, hi = hi_in;
@@ -1259,9 +1283,11 @@ __device__ __forceinline__ bool rank_core(Smem<CAP>& sm, const CArgs& a, bool bf
   if (lane_id() == 0) sm.wmax[t >> 6] = big;
   uint32_t total;
   uint32_t run = block_excl(sm, sum, 0, &total);   // its barrier also publishes wmax
+  const uint32_t n = total;
+  if (n_out) *n_out = n;
 #pragma unroll
   for (int w = 0; w < NW; ++w) big = max(big, sm.wmax[w]);
-  if (uniform(big) > kBinRankMax) {
+  if (n < m || uniform(big) > kBinRankMax) {
 #pragma unroll
     for (int i = 0; i < kCutBPT; ++i) sm.hist[t * kCutBPT + i] = 0u;
     __syncthreads();
@@ -1286,6 +1312,7 @@ __device__ __forceinline__ bool rank_core(Smem<CAP>& sm, const CArgs& a, bool bf
   // reads need no bound.  Positions are taken eight per lane at a time, each
   // batch's values and bin bounds read together.
   const uint32_t npos = uniform((n + NT - 1) / NT);
+  bool z = false;
 #pragma unroll
   for (int g = 0; g < RPT; g += 8) if (static_cast<uint32_t>(g) < npos) {
     constexpr int RB = 8;
@@ -1316,9 +1343,10 @@ __device__ __forceinline__ bool rank_core(Smem<CAP>& sm, const CArgs& a, bool bf
           for (int j = 0; j < 8; ++j) r += y[j] > x[i] ? 1u : 0u;
         }
       }
-      if (r < m) store_one(a, bf16, xrow, out0 + r, x[i], true, status);
+      if (r < m) z |= store_one(a, bf16, xrow, out0 + r, x[i], true, status);
     }
   }
+  if (z) sm.zeros = 1u;
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < kCutBPT; ++i) sm.hist[t * kCutBPT + i] = 0u;
@@ -1339,7 +1367,7 @@ __device__ __forceinline__ bool rank_store(Smem<CAP>& sm, const CArgs& a, bool b
     const uint32_t j = i * NT + t;
     v[i] = j < n ? sm.buf[j] : 0ull;
   }
-  return rank_core(sm, a, bf16, xrow, out0, v, nit, n, m, status);
+  return rank_core(sm, a, bf16, xrow, out0, v, nit, m, status);
 }
 
 // Selection without order (unsorted output): the m largest of buf[0, n)
@@ -1352,7 +1380,7 @@ template <int CAP>
 __device__ __forceinline__ bool select_core(Smem<CAP>& sm, const CArgs& a, bool bf16,
                                             const char* xrow, int64_t out0, u64 (&v)[kRankPerLane],
                                             uint32_t nit, uint32_t m, uint32_t status,
-                                            u64 lo_in = 0, u64 hi_in = 0) {
+                                            u64 lo_in = 0, u64 hi_in = 0, uint32_t* n_out = nullptr) {
   constexpr int RPT = kRankPerLane;
   const uint32_t t = threadIdx.x;
   u64 lo = hi_in != 0 ? lo_in : ~0ull, hi = hi_in;
@@ -1404,9 +1432,8 @@ __device__ __forceinline__ bool select_core(Smem<CAP>& sm, const CArgs& a, bool 
     h[i] = sm.hist[t * kCutBPT + i];
     sm.hist[t * kCutBPT + i] = 0u;
   }
-  find_rank<kCutBPT>(sm, h, m, 0);
-  const uint32_t b = uniform(sm.res[0]);
-  if (b == kNone) return false;   // cannot happen: n >= m
+  const uint32_t b = find_rank<kCutBPT>(sm, h, m, 0, n_out);
+  if (b == kNone) return false;   // fewer than m candidates
   const uint32_t need = m - uniform(sm.res[1]), hb = uniform(sm.res[2]);
   const u64 blo = lo + (static_cast<u64>((kCutBins - 1) - b) << shift);
   const u64 bhi_full = blo + ((1ull << shift) - 1ull);
@@ -1463,11 +1490,13 @@ __device__ __forceinline__ bool select_core(Smem<CAP>& sm, const CArgs& a, bool 
   uint32_t base = 0;
   if (lane_id() == 0 && wn) base = atomicAdd(&sm.cnt_out, wn);
   base = uniform(base);
+  bool z = false;
 #pragma unroll
   for (int i = 0; i < RPT; ++i) if (i < nit) {
-    if ((mk[i] >> lane_id()) & 1ull) store_one(a, bf16, xrow, out0 + base + mbcnt64(mk[i]), v[i], true, status);
+    if ((mk[i] >> lane_id()) & 1ull) z |= store_one(a, bf16, xrow, out0 + base + mbcnt64(mk[i]), v[i], true, status);
     base += static_cast<uint32_t>(__popcll(mk[i]));
   }
+  if (z) sm.zeros = 1u;
   return true;
 }
 
@@ -1505,6 +1534,7 @@ __device__ __forceinline__ void finish_row(Smem<CAP>& sm, const CArgs& a, bool b
   const uint32_t k = static_cast<uint32_t>(a.k);
   uint32_t m = status ? 0u : min(k, L);
   if (direct) stat_add(a, row, DS_STAT_FINAL_CANDIDATES, count);
+  if (t == 0) sm.zeros = 0u;
   __syncthreads();
   const int64_t out0 = static_cast<int64_t>(row) * k;
   const char* xrow = static_cast<const char*>(a.x) + static_cast<int64_t>(row) * a.row_stride * (bf16 ? 2 : 4);
@@ -1516,6 +1546,8 @@ __device__ __forceinline__ void finish_row(Smem<CAP>& sm, const CArgs& a, bool b
     for (uint32_t e = m + t; e < k; e += NT) store_one(a, bf16, xrow, out0 + e, 0ull, false, status);
     if (t == 0) a.row_status[row] = static_cast<int32_t>(status);
     stat_add(a, row, DS_STAT_CUTS, sm.n_cut);
+    __syncthreads();
+    if (uniform(sm.zeros)) fix_zero_signs(a, bf16, xrow, out0, m);
     return;
   }
   if (m > 0 && count > m) {
@@ -1533,45 +1565,59 @@ __device__ __forceinline__ void finish_row(Smem<CAP>& sm, const CArgs& a, bool b
     if (bf16 && a.n_cols <= 65536) sort_and_store<uint32_t, PER>(sm, a, bf16, xrow, out0, m, status);
     else sort_and_store<u64, PER>(sm, a, bf16, xrow, out0, m, status);
   } else {
+    bool z = false;
     for (uint32_t e = t; e < k; e += NT)
-      store_one(a, bf16, xrow, out0 + e, e < m ? sm.buf[e] : 0ull, e < m, status);
+      z |= store_one(a, bf16, xrow, out0 + e, e < m ? sm.buf[e] : 0ull, e < m, status);
+    if (z) sm.zeros = 1u;
   }
   if (t == 0) a.row_status[row] = static_cast<int32_t>(status);
   stat_add(a, row, DS_STAT_CUTS, sm.n_cut);
+  __syncthreads();
+  if (uniform(sm.zeros)) fix_zero_signs(a, bf16, xrow, out0, m);
 }
 
 // finish_row for candidates held in registers: v[i] for i < nit, 0 where
-// there is none, n of them in the workgroup.  The direct selections work on
-// the registers; their fallback (long runs of equal values, sorted by
-// column) first packs the candidates into buf.
+// there is none.  The direct selections work on the registers and count the
+// candidates on the way; their fallback (long runs of equal values, sorted by
+// column) first packs the candidates into buf.  Returns false, having stored
+// nothing, when there are fewer than min(k, L) candidates.
 template <int KMAX, int CAP>
-__device__ __forceinline__ void finish_row_regs(Smem<CAP>& sm, const CArgs& a, bool bf16, int row,
-                                                u64 (&v)[kRankPerLane], uint32_t nit, uint32_t n,
-                                                uint32_t L, uint32_t status, int par, u64 lo, u64 hi) {
+__device__ __forceinline__ bool finish_row_regs(Smem<CAP>& sm, const CArgs& a, bool bf16, int row,
+                                                u64 (&v)[kRankPerLane], uint32_t nit, uint32_t L,
+                                                uint32_t status, int par, u64 lo, u64 hi) {
   const int t = threadIdx.x;
   const uint32_t k = static_cast<uint32_t>(a.k);
   const uint32_t m = status ? 0u : min(k, L);
-  stat_add(a, row, DS_STAT_FINAL_CANDIDATES, n);
+  if (t == 0) sm.zeros = 0u;   // ordered before any store by the selections' first barrier
   const int64_t out0 = static_cast<int64_t>(row) * k;
   const char* xrow = static_cast<const char*>(a.x) + static_cast<int64_t>(row) * a.row_stride * (bf16 ? 2 : 4);
-  if (m > 0 && n >= m &&
-      ((a.sorted == 0 && select_core(sm, a, bf16, xrow, out0, v, nit, m, status, lo, hi)) ||
-       (a.sorted == 1 && rank_core(sm, a, bf16, xrow, out0, v, nit, n, m, status, lo, hi)))) {
-    for (uint32_t e = m + t; e < k; e += NT) store_one(a, bf16, xrow, out0 + e, 0ull, false, status);
-    if (t == 0) a.row_status[row] = static_cast<int32_t>(status);
-    stat_add(a, row, DS_STAT_CUTS, sm.n_cut);
-    return;
+  if (m > 0 && a.sorted != 2) {
+    uint32_t n = 0;
+    if ((a.sorted == 0 && select_core(sm, a, bf16, xrow, out0, v, nit, m, status, lo, hi, &n)) ||
+        (a.sorted == 1 && rank_core(sm, a, bf16, xrow, out0, v, nit, m, status, lo, hi, &n))) {
+      stat_add(a, row, DS_STAT_FINAL_CANDIDATES, n);
+      for (uint32_t e = m + t; e < k; e += NT) store_one(a, bf16, xrow, out0 + e, 0ull, false, status);
+      if (t == 0) a.row_status[row] = static_cast<int32_t>(status);
+      stat_add(a, row, DS_STAT_CUTS, sm.n_cut);
+      __syncthreads();
+      if (uniform(sm.zeros)) fix_zero_signs(a, bf16, xrow, out0, m);
+      return true;
+    }
+    if (n < m) return false;
   }
   uint32_t c = 0;
 #pragma unroll
   for (int i = 0; i < kRankPerLane; ++i) if (i < nit) c += v[i] != 0ull ? 1u : 0u;
   uint32_t total;
   uint32_t pos = block_excl(sm, c, par, &total);
+  if (total < m) return false;
+  stat_add(a, row, DS_STAT_FINAL_CANDIDATES, total);
 #pragma unroll
   for (int i = 0; i < kRankPerLane; ++i) if (i < nit) {
     if (v[i] != 0ull) sm.buf[pos++] = v[i];
   }
   finish_row<KMAX>(sm, a, bf16, row, total, L, status, false);
+  return true;
 }
 
 // OR of a per-lane flag over the workgroup (flag bits are small).
@@ -1892,22 +1938,14 @@ __global__ __launch_bounds__(NT, waves_per_simd(1024 / NT)) void chunk_split_ker
   // go to the epilogue from there, with no append.
   // (Values below Tm are dropped in place: the append below drops them too.)
   if (status == 0 && cmax <= (two ? 2u : 1u) * per_round) {
-    uint32_t c = 0;
 #pragma unroll
-    for (int q = 0; q < kRankPerLane; ++q) {
-      vr[q] = vr[q] >= Tm ? vr[q] : 0ull;
-      c += vr[q] != 0ull ? 1u : 0u;
-    }
-    uint32_t n;
-    block_excl(sm, c, B.par, &n);
-    B.par ^= 1;
-    n = uniform(n);
-    if (n >= min(k, L)) {
-      if (t == 0) st_agent(&a.ws_arrive[row], 0u);
-      finish_row_regs<KMAX>(sm, a, BF16, row, vr, two ? 2u * G8 : static_cast<uint32_t>(G8), n, L,
-                            status, B.par, Tm, range_hi);
+    for (int q = 0; q < kRankPerLane; ++q) vr[q] = vr[q] >= Tm ? vr[q] : 0ull;
+    if (t == 0) st_agent(&a.ws_arrive[row], 0u);
+    if (finish_row_regs<KMAX>(sm, a, BF16, row, vr, two ? 2u * G8 : static_cast<uint32_t>(G8), L,
+                              status, B.par, Tm, range_hi)) {
       return;
     }
+    // Fewer than min(k, L) at or above Tm: appended below, then read again.
     __syncthreads();
   }
 
