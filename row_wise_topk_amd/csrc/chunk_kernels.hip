@@ -188,7 +188,7 @@ __device__ __forceinline__ void wait_all_memory() {
 // ---------------------------------------------------------------- LDS
 template <int CAP>
 struct Smem {
-  u64 buf[CAP + 8];                   // candidate composites (also the sort's exchange area);
+  alignas(16) u64 buf[CAP + 8];       // candidate composites (also the sort's exchange area);
                                       // the last 8 are zero padding for the rank epilogue
   alignas(16) uint32_t hist[kCutBins];  // zero whenever not in use
   u64 side[kRankMax];                 // members of a small boundary bin
@@ -204,6 +204,8 @@ struct Smem {
   uint32_t n_cut;                     // cuts back to k made by this workgroup (statistics)
   uint32_t is_last;
   uint32_t zeros;                     // a zero was stored as an output value
+  uint32_t acnt;                      // append_fast: candidates reserved so far
+  uint32_t aovf;                      // append_fast: a reservation ran past its limit
   u64 res64;
 };
 
@@ -273,20 +275,37 @@ struct Geo {
   static constexpr uint32_t CE = NT * EPL;      // values per chunk
 };
 
+// Vectors per lane of chunk c that hold a column below L (uniform): vector
+// i of every lane lies at or past L for i >= chunk_nv.
+template <bool BF16>
+__device__ __forceinline__ uint32_t chunk_nv(uint32_t c, uint32_t L) {
+  using G = Geo<BF16>;
+  constexpr uint32_t VW = NT * G::EPV;   // columns of vector i over the workgroup
+  const uint32_t c0 = c * G::CE;
+  return L > c0 ? min(static_cast<uint32_t>(V), (L - c0 + VW - 1) / VW) : 0u;
+}
+
 // Chunk c of a row: lane t's vector i covers columns c*CE + (i*NT + t)*EPV ...
-// A vector that starts at or past L is loaded from column 0 instead (a valid
-// address); its values are replaced before use (sanitize_ragged).
+// Vectors past chunk_nv are not loaded: they hold negative NaNs (the ragged
+// padding, see sanitize_ragged).  A vector below it that starts at or past L
+// is loaded from column 0 instead (a valid address); its values are replaced
+// before use (sanitize_ragged).
 template <bool BF16>
 __device__ __forceinline__ void load_chunk(u32x4 (&r)[V], const char* xrow, uint32_t c,
                                            uint32_t L) {
   using G = Geo<BF16>;
   const uint32_t e0 = c * G::CE + threadIdx.x * G::EPV;
+  const uint32_t nv = chunk_nv<BF16>(c, L);
 #pragma unroll
   for (int i = 0; i < V; ++i) {
-    uint32_t e = e0 + static_cast<uint32_t>(i * NT * G::EPV);
-    e = e < L ? e : 0u;
-    r[i] = __builtin_nontemporal_load(
-        reinterpret_cast<const u32x4*>(xrow + static_cast<size_t>(e) * G::ESZ));
+    if (static_cast<uint32_t>(i) < nv) {
+      uint32_t e = e0 + static_cast<uint32_t>(i * NT * G::EPV);
+      e = e < L ? e : 0u;
+      r[i] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(xrow + static_cast<size_t>(e) * G::ESZ));
+    } else {
+      r[i] = u32x4{~0u, ~0u, ~0u, ~0u};
+    }
   }
 }
 
@@ -334,8 +353,10 @@ __device__ __forceinline__ void for_values(const u32x4& r, F&& f) {
 template <bool BF16>
 __device__ __forceinline__ bool sanitize_ragged(u32x4 (&r)[V], uint32_t c, uint32_t L) {
   bool nan = false;
+  const uint32_t nv = chunk_nv<BF16>(c, L);
 #pragma unroll
   for (int i = 0; i < V; ++i) {
+    if (static_cast<uint32_t>(i) >= nv) continue;   // padding already
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const uint32_t d = r[i][w];
@@ -362,7 +383,8 @@ __device__ __forceinline__ bool sanitize_ragged(u32x4 (&r)[V], uint32_t c, uint3
 // above -inf.  A lane whose values are all negative takes its largest as
 // the smallest unsigned pattern, on a branch that typical data never takes.
 template <bool BF16, bool CHECK>
-__device__ __forceinline__ void chunk_max_nan(const u32x4 (&r)[V], uint32_t* maxkey, bool* nan) {
+__device__ __forceinline__ void chunk_max_nan(const u32x4 (&r)[V], uint32_t* maxkey, bool* nan,
+                                              uint32_t nv = V) {
   uint32_t top;   // the lane's largest value as an fp32 pattern
   bool bad;
   if constexpr (BF16) {
@@ -378,6 +400,7 @@ __device__ __forceinline__ void chunk_max_nan(const u32x4 (&r)[V], uint32_t* max
     for (int i = 0; i < V; ++i)
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
+        if (static_cast<uint32_t>(i) >= nv) continue;   // padding: below every value
         // (a copy first: a bit cast of a vector element in place reads the
         // vector's first element with this compiler)
         const uint32_t d = r[i][w];
@@ -397,6 +420,7 @@ __device__ __forceinline__ void chunk_max_nan(const u32x4 (&r)[V], uint32_t* max
       for (int i = 0; i < V; ++i)
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
+          if (static_cast<uint32_t>(i) >= nv) continue;
           const uint32_t d = r[i][w];
           umin = __builtin_elementwise_min(umin, __builtin_bit_cast(u16x2, d));
         }
@@ -407,6 +431,7 @@ __device__ __forceinline__ void chunk_max_nan(const u32x4 (&r)[V], uint32_t* max
     uint32_t ua = 0, ub = 0;
 #pragma unroll
     for (int i = 0; i < V; ++i) {
+      if (static_cast<uint32_t>(i) >= nv) continue;
       sa = max(sa, max(static_cast<int32_t>(r[i][0]), static_cast<int32_t>(r[i][1])));
       sb = max(sb, max(static_cast<int32_t>(r[i][2]), static_cast<int32_t>(r[i][3])));
       if (CHECK) {
@@ -422,7 +447,7 @@ __device__ __forceinline__ void chunk_max_nan(const u32x4 (&r)[V], uint32_t* max
 #pragma unroll
       for (int i = 0; i < V; ++i)
 #pragma unroll
-        for (int w = 0; w < 4; ++w) umin = min(umin, r[i][w]);
+        for (int w = 0; w < 4; ++w) if (static_cast<uint32_t>(i) < nv) umin = min(umin, r[i][w]);
       top = umin;
     }
   }
@@ -455,29 +480,82 @@ __device__ __forceinline__ uint32_t vec_write(Smem<CAP>& sm, const u32x4& r, int
 }
 
 // ---------------------------------------------------------------- the start
+// Per-group representatives of a vector: for GS > 0, one value of each run
+// of GS consecutive values, the group's largest as a signed integer pattern
+// (its largest value when it holds a non-negative one, else some member:
+// always a member, which is all the start needs).  f(bits as fp32) is called
+// once per representative.
+template <bool BF16, int GS, typename F>
+__device__ __forceinline__ void for_reps(const u32x4& v, F&& f) {
+  if constexpr (BF16) {
+    const uint32_t w0 = v[0], w1 = v[1], w2 = v[2], w3 = v[3];
+    const i16x2 a0 = __builtin_bit_cast(i16x2, w0), a1 = __builtin_bit_cast(i16x2, w1);
+    const i16x2 a2 = __builtin_bit_cast(i16x2, w2), a3 = __builtin_bit_cast(i16x2, w3);
+    auto bits = [](int x) { return static_cast<uint32_t>(static_cast<uint16_t>(x)) << 16; };
+    if constexpr (GS == 8) {
+      const i16x2 m = __builtin_elementwise_max(__builtin_elementwise_max(a0, a1),
+                                                __builtin_elementwise_max(a2, a3));
+      f(bits(max(static_cast<int>(m.x), static_cast<int>(m.y))));
+    } else if constexpr (GS == 4) {
+      const i16x2 m0 = __builtin_elementwise_max(a0, a1), m1 = __builtin_elementwise_max(a2, a3);
+      f(bits(max(static_cast<int>(m0.x), static_cast<int>(m0.y))));
+      f(bits(max(static_cast<int>(m1.x), static_cast<int>(m1.y))));
+    } else if constexpr (GS == 2) {
+      f(bits(max(static_cast<int>(a0.x), static_cast<int>(a0.y))));
+      f(bits(max(static_cast<int>(a1.x), static_cast<int>(a1.y))));
+      f(bits(max(static_cast<int>(a2.x), static_cast<int>(a2.y))));
+      f(bits(max(static_cast<int>(a3.x), static_cast<int>(a3.y))));
+    } else {
+      for_values<true>(v, [&](uint32_t b, int) { f(b); });
+    }
+  } else {
+    const int32_t w0 = static_cast<int32_t>(v[0]), w1 = static_cast<int32_t>(v[1]);
+    const int32_t w2 = static_cast<int32_t>(v[2]), w3 = static_cast<int32_t>(v[3]);
+    if constexpr (GS >= 4) {
+      f(static_cast<uint32_t>(max(max(w0, w1), max(w2, w3))));
+    } else if constexpr (GS == 2) {
+      f(static_cast<uint32_t>(max(w0, w1)));
+      f(static_cast<uint32_t>(max(w2, w3)));
+    } else {
+      f(v[0]);
+      f(v[1]);
+      f(v[2]);
+      f(v[3]);
+    }
+  }
+}
+
 // The start threshold from a 256-bin histogram over the window of keys just
 // below `maxkey` (the chunk's largest key): bin j holds keys
-// maxkey - (j+1)*2^s < key <= maxkey - j*2^s, s = 16 first (one bin per bf16
-// value, 1/128 octave for fp32), then s = 24 (the window spans every key)
-// when the first window holds fewer than m.  With LANEMAX only each lane's
-// largest value is binned.  Returns T = (edge key << 32): at least m values
-// of the chunk are at or above it.  Leaves the histogram zeroed.
-template <bool BF16, bool LANEMAX, int CAP>
+// maxkey - (j+1)*2^s < key <= maxkey - j*2^s.  GS == 0 bins each lane's
+// largest value (lane_max), with s = 16 (one bin per bf16 value, 1/128
+// octave for fp32), then s = 24 (the window spans every key) when the first
+// window holds fewer than m.  GS > 0 bins one representative per group of GS
+// values (for_reps), with s = 16, then 20 (16 bf16 values per bin, 32 octaves
+// in all), then 24.  Returns T = (edge key << 32): at least m values of the
+// chunk are at or above it (m binned members are, each a distinct value of
+// the chunk).  Leaves the histogram zeroed.  Every binned key is at most
+// maxkey: a lane maximum is, and a chunk holding a NaN (whose maxkey may lie
+// below other lanes' values) does not come here with GS > 0.
+template <bool BF16, int GS, int CAP>
 __device__ __forceinline__ u64 start_threshold(Smem<CAP>& sm, const u32x4 (&r)[V],
-                                               uint32_t maxkey, uint32_t lane_max, uint32_t m) {
-  for (int pass = 0; pass < 2; ++pass) {
-    const uint32_t s = pass == 0 ? 16u : 24u;
+                                               uint32_t maxkey, uint32_t lane_max, uint32_t m,
+                                               uint32_t nv) {
+  constexpr int NP = GS == 0 ? 2 : 3;
+  for (int pass = 0; pass < NP; ++pass) {
+    const uint32_t s = pass == 0 ? 16u : (pass == NP - 1 ? 24u : 20u);
     const u64 span = static_cast<u64>(kWinBins) << s;   // keys the window covers
     const uint32_t lo_key = static_cast<u64>(maxkey) - kNegInfKey >= span
                                 ? static_cast<uint32_t>(maxkey - span + 1u)
                                 : kNegInfKey;
-    if (LANEMAX) {
+    if constexpr (GS == 0) {
       if (lane_max >= lo_key) atomicAdd(&sm.hist[(maxkey - lane_max) >> s], 1u);
     } else {
       const float flo = __uint_as_float(bits_of_key(lo_key));
 #pragma unroll
       for (int i = 0; i < V; ++i) {
-        for_values<BF16>(r[i], [&](uint32_t b, int) {
+        if (static_cast<uint32_t>(i) >= nv) continue;   // padding: binned nowhere
+        for_reps<BF16, GS>(r[i], [&](uint32_t b) {
           if (__uint_as_float(b) >= flo) atomicAdd(&sm.hist[(maxkey - key_of_bits(b)) >> s], 1u);
         });
       }
@@ -494,7 +572,7 @@ __device__ __forceinline__ u64 start_threshold(Smem<CAP>& sm, const u32x4 (&r)[V
     }
     if (lo_key == kNegInfKey) return kTAll;
   }
-  return kTAll;   // not reached: the second window spans every key
+  return kTAll;   // not reached: the last window spans every key
 }
 
 // ---------------------------------------------------------------- the cut
@@ -703,24 +781,25 @@ __device__ __forceinline__ void append_vec(Smem<CAP>& sm, Buf& B, const u32x4& r
 // later step keeps the buffer a superset of the values >= T.
 template <bool BF16, int CAP>
 __device__ __forceinline__ void append_chunk(Smem<CAP>& sm, Buf& B, const u32x4 (&r)[V], uint32_t c,
-                                             uint32_t k, uint32_t cap) {
+                                             uint32_t k, uint32_t cap, uint32_t nv = V) {
   const float f = __uint_as_float(bits_of_key(key_of(B.T)));
   uint32_t n = 0;
 #pragma unroll
-  for (int i = 0; i < V; ++i) n += vec_count<BF16>(r[i], f);
+  for (int i = 0; i < V; ++i) if (static_cast<uint32_t>(i) < nv) n += vec_count<BF16>(r[i], f);
   uint32_t total, wb;
   block_excl(sm, n, B.par, &total, &wb);
   B.par ^= 1;
   if (B.count + total <= cap) {
     uint32_t pos = B.count + wb;
 #pragma unroll
-    for (int i = 0; i < V; ++i) pos = vec_write<BF16>(sm, r[i], i, c, f, pos);
+    for (int i = 0; i < V; ++i) if (static_cast<uint32_t>(i) < nv) pos = vec_write<BF16>(sm, r[i], i, c, f, pos);
     B.count += total;
     return;
   }
   // Piecewise: one vector per lane at a time (a cut leaves room for one).
 #pragma unroll
   for (int i = 0; i < V; ++i) {
+    if (static_cast<uint32_t>(i) >= nv) break;
     append_vec<BF16>(sm, B, r[i], i, c, k, cap);
     if (uniform(sm.err)) return;
   }
@@ -739,9 +818,10 @@ __device__ __forceinline__ bool start_chunk(Smem<CAP>& sm, Buf& B, u32x4 (&r)[V]
   bool nan = false;
   const bool rag = (c + 1) * G::CE > L;
   if (rag) nan = sanitize_ragged<BF16>(r, c, L);
+  const uint32_t nv = chunk_nv<BF16>(c, L);
   uint32_t mk;
   bool nn;
-  if (rag) chunk_max_nan<BF16, false>(r, &mk, &nn);
+  if (rag) chunk_max_nan<BF16, false>(r, &mk, &nn, nv);
   else chunk_max_nan<BF16, true>(r, &mk, &nn);
   nan |= nn;
   const uint32_t wm = wave_max_u32(mk);
@@ -765,8 +845,20 @@ __device__ __forceinline__ bool start_chunk(Smem<CAP>& sm, Buf& B, u32x4 (&r)[V]
   }
   u64 T = kTAll;
   if (maxkey != 0 && m < nvalid) {
-    if (m <= static_cast<uint32_t>(NT / 2)) T = start_threshold<BF16, true>(sm, r, maxkey, mk, m);
-    else T = start_threshold<BF16, false>(sm, r, maxkey, mk, m);
+    if (m <= static_cast<uint32_t>(NT / 2)) {
+      T = start_threshold<BF16, 0>(sm, r, maxkey, mk, m, nv);
+    } else if (!nan) {
+      // One representative per group of g values, g the largest power of
+      // two (at most one 16-byte vector) that leaves about 3m groups: the
+      // m-th largest representative then has about 1.1m values at or above
+      // it, at an eighth of the histogram work of binning every value.
+      const uint32_t q = nvalid / (3u * m);
+      const uint32_t g = q >= 8u && BF16 ? 8u : q >= 4u ? 4u : q >= 2u ? 2u : 1u;
+      if (g == 8u) T = start_threshold<BF16, 8>(sm, r, maxkey, mk, m, nv);
+      else if (g == 4u) T = start_threshold<BF16, 4>(sm, r, maxkey, mk, m, nv);
+      else if (g == 2u) T = start_threshold<BF16, 2>(sm, r, maxkey, mk, m, nv);
+      else T = start_threshold<BF16, 1>(sm, r, maxkey, mk, m, nv);
+    }
   }
   *spec = !exact && m < k && T != kTAll;
   B.T = T;
@@ -925,6 +1017,135 @@ __device__ __forceinline__ uint32_t region_write(Smem<CAP>& sm, const u32x4 (&r)
   }
 }
 
+// Append every value of chunk c with key >= key(B.T), without a count pass:
+// each wave tests each 16-byte vector once (its largest value against T),
+// copies the vectors that hold a candidate, with their first column, to a
+// staging area of its own at the top of buf (64 at a time), and compacts
+// their values slot by slot, reserving room for each batch with one LDS
+// atomic.  Candidates go to buf[B.count, lim), lim leaving the staging areas
+// free.  Returns false, with B unchanged and buf past B.count undefined,
+// when they would not fit there (or the buffer already reaches lim): the
+// caller then appends the chunk the counted way (append_chunk), which cuts
+// as it goes.
+template <bool BF16, int CAP>
+__device__ __forceinline__ bool append_fast(Smem<CAP>& sm, Buf& B, const u32x4 (&r)[V], uint32_t c,
+                                            uint32_t cap, uint32_t nv) {
+  using G = Geo<BF16>;
+  constexpr uint32_t SM = 64;                  // staged vectors per wave
+  constexpr uint32_t STG = SM * 2 + SM / 2;    // u64 slots per wave: vectors, then columns
+  constexpr uint32_t TOP = (CAP - NW * STG) & ~1u;
+  static_assert(CAP > NW * STG, "staging fits in the buffer");
+  const uint32_t lim = min(cap, TOP);
+  // The staging areas lie above lim: a buffer already past it (filled by
+  // append_chunk) holds candidates there.
+  if (B.count >= lim) return false;
+  const int t = threadIdx.x;
+  if (t == 0) {
+    sm.acnt = B.count;
+    sm.aovf = 0u;
+  }
+  __syncthreads();
+  const uint32_t w = static_cast<uint32_t>(t) >> 6;
+  u32x4* sv = reinterpret_cast<u32x4*>(sm.buf + TOP + w * STG);
+  uint32_t* sc = reinterpret_cast<uint32_t*>(sm.buf + TOP + w * STG + 2 * SM);
+  const float f = __uint_as_float(bits_of_key(key_of(B.T)));
+  const uint32_t fb = __float_as_uint(f);
+  // bf16 above zero: integer compares of each half's pattern with the
+  // smallest bf16 pattern >= f (positive floats order like their patterns;
+  // negative values and the ragged padding lie below).  Else float compares.
+  const bool ipath = BF16 && static_cast<int32_t>(fb) > 0;
+  const uint32_t tb = (fb + 0xFFFFu) >> 16;
+  const int16_t tlo = static_cast<int16_t>(tb);
+  const int32_t thi = static_cast<int32_t>(tb << 16);
+  auto val_bits = [&](uint32_t d, int h) -> uint32_t {
+    if constexpr (BF16) return h ? (d & 0xFFFF0000u) : lo_half(d);
+    else return d;
+  };
+  auto ok = [&](uint32_t d, int h) -> bool {
+    if (BF16 && ipath) return h ? static_cast<int32_t>(d) >= thi : static_cast<int16_t>(d) >= tlo;
+    return __uint_as_float(val_bits(d, h)) >= f;
+  };
+  auto hit = [&](const u32x4& v) -> bool {
+    if constexpr (BF16) {
+      if (ipath) {
+        const uint32_t w0 = v[0], w1 = v[1], w2 = v[2], w3 = v[3];
+        const i16x2 a = __builtin_elementwise_max(__builtin_bit_cast(i16x2, w0), __builtin_bit_cast(i16x2, w1));
+        const i16x2 b = __builtin_elementwise_max(__builtin_bit_cast(i16x2, w2), __builtin_bit_cast(i16x2, w3));
+        const i16x2 mx = __builtin_elementwise_max(a, b);
+        return max(mx.x, mx.y) >= tlo;
+      }
+      bool any = false;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) any |= ok(v[q >> 1], q & 1);
+      return any;
+    } else {
+      return fmaxf(fmaxf(__uint_as_float(v[0]), __uint_as_float(v[1])),
+                   fmaxf(__uint_as_float(v[2]), __uint_as_float(v[3]))) >= f;
+    }
+  };
+  // Compact the wave's nh staged vectors (one per lane; lanes past them hold
+  // negative NaNs, which pass no test).
+  auto flush = [&](uint32_t nh) {
+    u32x4 v = {~0u, ~0u, ~0u, ~0u};
+    uint32_t cb = 0;
+    if (lane_id() < nh) {
+      v = sv[lane_id()];
+      cb = sc[lane_id()];
+    }
+    u64 mq[G::EPV];
+    uint32_t pbits = 0, tot = 0;
+#pragma unroll
+    for (int q = 0; q < G::EPV; ++q) {
+      const bool p = ok(v[BF16 ? q >> 1 : q], q & 1);
+      mq[q] = ballot(p);
+      pbits |= p ? (1u << q) : 0u;
+      tot += static_cast<uint32_t>(__popcll(mq[q]));
+    }
+    uint32_t base = 0;
+    if (lane_id() == 0) base = atomicAdd(&sm.acnt, tot);
+    base = uniform(base);
+    if (base + tot > lim) {
+      if (lane_id() == 0) sm.aovf = 1u;
+      return;
+    }
+#pragma unroll
+    for (int q = 0; q < G::EPV; ++q) {
+      if (mq[q]) {
+        if ((pbits >> q) & 1u)
+          sm.buf[base + mbcnt64(mq[q])] = comp_of(key_of_bits(val_bits(v[BF16 ? q >> 1 : q], q & 1)), cb + static_cast<uint32_t>(q));
+        base += static_cast<uint32_t>(__popcll(mq[q]));
+      }
+    }
+  };
+  const uint32_t col0 = c * G::CE + static_cast<uint32_t>(t) * G::EPV;
+  uint32_t nh = 0;
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    if (static_cast<uint32_t>(i) >= nv) continue;   // padding: no candidate
+    const bool hl = hit(r[i]);
+    const u64 hv = ballot(hl);
+    if (hv) {
+      const uint32_t nv = static_cast<uint32_t>(__popcll(hv));
+      if (nh + nv > SM) {
+        flush(nh);
+        nh = 0;
+      }
+      if (hl) {
+        const uint32_t j = nh + mbcnt64(hv);
+        sv[j] = r[i];
+        sc[j] = col0 + static_cast<uint32_t>(i * NT * G::EPV);
+      }
+      nh += nv;
+    }
+  }
+  if (nh) flush(nh);
+  __syncthreads();
+  const uint32_t n = uniform(sm.acnt), bad = uniform(sm.aovf);
+  if (bad) return false;
+  B.count = n;
+  return true;
+}
+
 // A later chunk of a whole row.
 template <bool BF16, int CAP>
 __device__ __forceinline__ bool next_chunk(Smem<CAP>& sm, Buf& B, u32x4 (&r)[V], uint32_t c,
@@ -939,7 +1160,8 @@ __device__ __forceinline__ bool next_chunk(Smem<CAP>& sm, Buf& B, u32x4 (&r)[V],
     chunk_max_nan<BF16, true>(r, &mk, &nn);
     nan = nn;
   }
-  append_chunk<BF16>(sm, B, r, c, k, cap);
+  const uint32_t nv = chunk_nv<BF16>(c, L);
+  if (!append_fast<BF16>(sm, B, r, c, cap, nv)) append_chunk<BF16>(sm, B, r, c, k, cap, nv);
   return nan;
 }
 
@@ -956,7 +1178,7 @@ __device__ __noinline__ Buf restream(Smem<CAP>& sm, int par, const char* xrow, u
     u32x4 r[V];
     load_chunk<BF16>(r, xrow, j, L);
     if ((j + 1) * G::CE > L) sanitize_ragged<BF16>(r, j, L);
-    append_chunk<BF16>(sm, B, r, j, k, cap);
+    append_chunk<BF16>(sm, B, r, j, k, cap, chunk_nv<BF16>(j, L));
     if (uniform(sm.err)) break;
   }
   return B;
@@ -975,7 +1197,7 @@ __device__ __noinline__ Buf reappend_chunk(Smem<CAP>& sm, Buf B, const char* xro
   if ((c + 1) * G::CE > L) sanitize_ragged<BF16>(r, c, L);
   __syncthreads();
   B.count = 0;
-  append_chunk<BF16>(sm, B, r, c, k, cap);
+  append_chunk<BF16>(sm, B, r, c, k, cap, chunk_nv<BF16>(c, L));
   return B;
 }
 
@@ -1699,7 +1921,8 @@ __global__ __launch_bounds__(NT, waves_per_simd(NT == 256 ? (KC >= 2 ? 3 : 4) : 
     u32x4 ra[V];
     load_chunk<BF16>(ra, xrow, chunk_at(0), L);
     nan = start_chunk<BF16>(sm, B, ra, chunk_at(0), L, k, nch == 1, &spec);
-    append_chunk<BF16>(sm, B, ra, chunk_at(0), k, cap);
+    const uint32_t nv0 = chunk_nv<BF16>(chunk_at(0), L);
+    if (!append_fast<BF16>(sm, B, ra, chunk_at(0), cap, nv0)) append_chunk<BF16>(sm, B, ra, chunk_at(0), k, cap, nv0);
     for (uint32_t j = 1; j < nch && !uniform(sm.err); ++j) {
       load_chunk<BF16>(ra, xrow, chunk_at(j), L);
       nan |= next_chunk<BF16>(sm, B, ra, chunk_at(j), L, k, cap);
