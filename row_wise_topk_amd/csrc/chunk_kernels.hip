@@ -1083,8 +1083,15 @@ __device__ __forceinline__ bool append_fast(Smem<CAP>& sm, Buf& B, const u32x4 (
                    fmaxf(__uint_as_float(v[2]), __uint_as_float(v[3]))) >= f;
     }
   };
+  // The key of a passing value: above zero on the integer path, where the
+  // offset-binary key is the pattern with the sign bit set.
+  auto key_at = [&](uint32_t d, int h) -> uint32_t {
+    if (BF16 && ipath) return (h ? (d & 0xFFFF0000u) : (d << 16)) | kBias;
+    return key_of_bits(val_bits(d, h));
+  };
   // Compact the wave's nh staged vectors (one per lane; lanes past them hold
-  // negative NaNs, which pass no test).
+  // negative NaNs, which pass no test): each lane writes its own passing
+  // values one after another from its place in the wave's prefix sum.
   auto flush = [&](uint32_t nh) {
     u32x4 v = {~0u, ~0u, ~0u, ~0u};
     uint32_t cb = 0;
@@ -1092,15 +1099,12 @@ __device__ __forceinline__ bool append_fast(Smem<CAP>& sm, Buf& B, const u32x4 (
       v = sv[lane_id()];
       cb = sc[lane_id()];
     }
-    u64 mq[G::EPV];
-    uint32_t pbits = 0, tot = 0;
+    uint32_t pbits = 0;
 #pragma unroll
-    for (int q = 0; q < G::EPV; ++q) {
-      const bool p = ok(v[BF16 ? q >> 1 : q], q & 1);
-      mq[q] = ballot(p);
-      pbits |= p ? (1u << q) : 0u;
-      tot += static_cast<uint32_t>(__popcll(mq[q]));
-    }
+    for (int q = 0; q < G::EPV; ++q) pbits |= ok(v[BF16 ? q >> 1 : q], q & 1) ? (1u << q) : 0u;
+    const uint32_t cnt = static_cast<uint32_t>(__builtin_popcount(pbits));
+    const uint32_t incl = wave_incl_sum(cnt);
+    const uint32_t tot = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(incl), 63));
     uint32_t base = 0;
     if (lane_id() == 0) base = atomicAdd(&sm.acnt, tot);
     base = uniform(base);
@@ -1108,12 +1112,12 @@ __device__ __forceinline__ bool append_fast(Smem<CAP>& sm, Buf& B, const u32x4 (
       if (lane_id() == 0) sm.aovf = 1u;
       return;
     }
+    uint32_t pos = base + incl - cnt;
 #pragma unroll
     for (int q = 0; q < G::EPV; ++q) {
-      if (mq[q]) {
-        if ((pbits >> q) & 1u)
-          sm.buf[base + mbcnt64(mq[q])] = comp_of(key_of_bits(val_bits(v[BF16 ? q >> 1 : q], q & 1)), cb + static_cast<uint32_t>(q));
-        base += static_cast<uint32_t>(__popcll(mq[q]));
+      if ((pbits >> q) & 1u) {
+        sm.buf[pos] = comp_of(key_at(v[BF16 ? q >> 1 : q], q & 1), cb + static_cast<uint32_t>(q));
+        ++pos;
       }
     }
   };
