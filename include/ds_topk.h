@@ -72,8 +72,9 @@ typedef enum {
   DS_ERR_WORKSPACE = 8,     /* workspace NULL, too small or not 16-B aligned       */
   DS_ERR_HIP = 9,           /* the HIP runtime reported an error at launch         */
   DS_ERR_PLAN = 10,         /* a ds_topk_plan_t field is out of range              */
-  DS_ERR_SCRATCH_LIMIT = 11 /* ds_topk_noalloc: the problem needs more workspace than
+  DS_ERR_SCRATCH_LIMIT = 11, /* ds_topk_noalloc: the problem needs more workspace than
                                DS_TOPK_NOALLOC_SCRATCH_BYTES                        */
+  DS_ERR_SAMPLER_PARAM = 12 /* ds_sampler_tail: temperature is NaN, or top_p is NaN or <= 0 */
 } ds_status_t;
 
 #define DS_TOPK_MAX_K 4096            /* [NC coverage]: topk must be 4096 or less   */
@@ -260,6 +261,50 @@ const char* ds_topk_status_string(ds_status_t status);
 ds_status_t ds_read_ceiling(const void* x, ds_dtype_t dtype, int64_t batch, int64_t n_cols,
                             int64_t row_stride, const int32_t* end, int32_t k,
                             const ds_topk_plan_t* plan, uint32_t* sink, hipStream_t stream);
+
+/*
+ * ds_sampler_tail -- the sampling step after the sampler's TopK, on its
+ * output.  During sampling TopK selects the candidate tokens from a large
+ * vocabulary [NC motive paragraph]; the generation settings around it include
+ * a temperature and a top-p [IT, the recipe's generation settings].  Per row i
+ * of the top-k output (candidates: the entries with index >= 0, sorted by
+ * value, larger first, as ds_topk returns them with sorted = 1):
+ *   w_j = exp((v_j - v_max) / temperature) (if v_max is infinite: 1 where
+ *   v_j == v_max, else 0); c_j = w_0 + ... + w_j; S = c at the last candidate;
+ *   K = min(1 + #{j : c_j < top_p * S}, number of candidates);
+ *   token = indices[i][j*] with j* the first j < K such that
+ *   c_j > u_i * c_{K-1}; its probability after the cut is w_j* / c_{K-1}.
+ *   temperature <= 0 takes the first candidate (greedy, probability 1).
+ * Computed in fp32 with a fixed summation order (the same draw on every call).
+ *
+ *   values       device [batch, k] of dtype (fp32 or bf16), sorted by value
+ *                within each row.
+ *   indices      device [batch, k] of index_dtype; negative entries are not
+ *                candidates (ds_topk pads a row shorter than k with -1).
+ *   row_status   device [batch] or NULL: a row with a non-zero status (a NaN
+ *                row of ds_topk) draws nothing.
+ *   batch, k     rows and candidates per row (1 <= k <= DS_TOPK_MAX_K).
+ *   temperature  > 0: the softmax temperature; <= 0: greedy.
+ *   top_p        the nucleus mass, > 0; 1 or more keeps every candidate.
+ *   uniforms     device [batch] fp32: the row's uniform draw u in [0, 1)
+ *                (clamped to [0, 1]; NaN counts as 0).  The caller owns the
+ *                random numbers.
+ *   tokens       device [batch] int64 out: the drawn index, or -1 for a row
+ *                that draws nothing (a status bit set, or no candidate).
+ *   probs        device [batch] fp32 out or NULL: the drawn token's
+ *                probability after the nucleus cut (qNaN when none).
+ *   stream       HIP stream the single launch is queued on.
+ * Every pointer is caller-owned device memory, naturally aligned for its
+ * element type.  Returns DS_OK, DS_ERR_DTYPE, DS_ERR_INDEX_DTYPE,
+ * DS_ERR_K_RANGE, DS_ERR_SHAPE (batch < 0 or > INT32_MAX),
+ * DS_ERR_SAMPLER_PARAM, DS_ERR_NULL, DS_ERR_ALIGN (checked in that order,
+ * before any launch) or DS_ERR_HIP.  batch == 0 queues nothing.
+ */
+ds_status_t ds_sampler_tail(const void* values, ds_dtype_t dtype, const void* indices,
+                            ds_index_dtype_t index_dtype, const int32_t* row_status,
+                            int64_t batch, int32_t k, float temperature, float top_p,
+                            const float* uniforms, int64_t* tokens, float* probs,
+                            hipStream_t stream);
 
 #ifdef __cplusplus
 }

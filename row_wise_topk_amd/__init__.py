@@ -8,7 +8,8 @@ and the current stream.
 Raw entry points carry the C names and arguments (``ds_topk``, ``ds_topk_ex``,
 ``ds_topk_validate``, ``ds_topk_workspace_size``, ``ds_topk_workspace_size_ex``,
 ``ds_topk_stride_requirement``, ``ds_topk_status_string``, the allocation-free
-``ds_topk_noalloc`` and the measurement aid ``ds_read_ceiling``).  :func:`topk` is the
+``ds_topk_noalloc``, the sampling step ``ds_sampler_tail`` and the measurement
+aid ``ds_read_ceiling``).  :func:`topk` is the
 tensor-level call, the counterpart of ``deep_select.topk(x, topk, sorted_index,
 indices_type, return_value)`` described on xhh.club, "DeepSeek开源DeepSelect：
 比torch.topk快二十倍！" (Q&A), with a per-row ``end`` as described on
@@ -40,8 +41,9 @@ DS_KERNEL_AUTO, DS_KERNEL_STREAM, DS_KERNEL_CHUNK = 0, 1, 2
 DS_TOPK_MAX_K = 4096
 STATUS_NAMES = ["DS_OK", "DS_ERR_NULL", "DS_ERR_DTYPE", "DS_ERR_INDEX_DTYPE", "DS_ERR_K_RANGE",
                 "DS_ERR_SHAPE", "DS_ERR_ALIGN", "DS_ERR_SORTED_MODE", "DS_ERR_WORKSPACE",
-                "DS_ERR_HIP", "DS_ERR_PLAN", "DS_ERR_SCRATCH_LIMIT"]
+                "DS_ERR_HIP", "DS_ERR_PLAN", "DS_ERR_SCRATCH_LIMIT", "DS_ERR_SAMPLER_PARAM"]
 DS_ERR_SCRATCH_LIMIT = 11
+DS_ERR_SAMPLER_PARAM = 12
 DS_TOPK_NOALLOC_SCRATCH_BYTES = 16 << 20
 DS_TOPK_WS_HEADER_BYTES = 256 << 10
 DS_STAT_ROW_REREADS, DS_STAT_CHUNK_REREADS, DS_STAT_CUTS, DS_STAT_FINAL_CANDIDATES = 0, 1, 2, 3
@@ -84,6 +86,9 @@ _lib.ds_read_ceiling.restype = ctypes.c_int
 _lib.ds_topk_noalloc.argtypes = [_vp, ctypes.c_int, _i64, _i64, _i64, _vp, _i32, _i32, _i32,
                                  ctypes.c_int, _vp, _vp, _vp, _vp, ctypes.POINTER(Plan)]
 _lib.ds_topk_noalloc.restype = ctypes.c_int
+_lib.ds_sampler_tail.argtypes = [_vp, ctypes.c_int, _vp, ctypes.c_int, _vp, _i64, _i32,
+                                 ctypes.c_float, ctypes.c_float, _vp, _vp, _vp, _vp]
+_lib.ds_sampler_tail.restype = ctypes.c_int
 
 
 def exported_names() -> list[str]:
@@ -151,6 +156,12 @@ def ds_topk_status_string(status) -> str:
 def ds_read_ceiling(x, dtype, batch, n_cols, row_stride, end, k, plan, sink, stream) -> int:
     return _lib.ds_read_ceiling(x, dtype, batch, n_cols, row_stride, end, k, _plan_ptr(plan),
                                 sink, stream)
+
+
+def ds_sampler_tail(values, dtype, indices, index_dtype, row_status, batch, k, temperature,
+                    top_p, uniforms, tokens, probs, stream) -> int:
+    return _lib.ds_sampler_tail(values, dtype, indices, index_dtype, row_status, batch, k,
+                                temperature, top_p, uniforms, tokens, probs, stream)
 
 
 # ---------------------------------------------------------------- tensor-level call
@@ -269,6 +280,40 @@ def read_ceiling(x: torch.Tensor, k: int, *, end: torch.Tensor | None = None,
                          sink.data_ptr(), stream)
     if rc != DS_OK:
         raise TopkError(rc)
+
+
+def sample_from_topk(values: torch.Tensor, indices: torch.Tensor, row_status=None, *,
+                     temperature: float, top_p: float, uniforms: torch.Tensor):
+    """The sampling step after :func:`topk` (sorted by value): temperature
+    softmax over each row's candidates, nucleus cut at ``top_p``, inverse-CDF
+    draw with the row's ``uniforms`` entry (see ``ds_sampler_tail``).  Returns
+    ``(tokens int64 [batch], probs float32 [batch])``; a row that draws
+    nothing gets token -1."""
+    if values.dim() != 2 or values.shape != indices.shape or not values.is_cuda:
+        raise ValueError("values and indices must be CUDA tensors of one shape [batch, k]")
+    if values.dtype not in _DT or indices.dtype not in _IT:
+        raise TypeError("values must be float32 / bfloat16 and indices int32 / int64")
+    batch, k = values.shape
+    dev = values.device
+    for name, t in (("values", values), ("indices", indices)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if uniforms.dtype != torch.float32 or uniforms.shape != (batch,) or uniforms.device != dev:
+        raise ValueError("uniforms must be a float32 tensor of shape [batch] on values' device")
+    if row_status is not None and (row_status.dtype != torch.int32 or row_status.shape != (batch,)
+                                   or row_status.device != dev):
+        raise ValueError("row_status must be an int32 tensor of shape [batch] on values' device")
+    uniforms = uniforms.contiguous()
+    tokens = torch.empty((batch,), dtype=torch.int64, device=dev)
+    probs = torch.empty((batch,), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = ds_sampler_tail(values.data_ptr(), _DT[values.dtype], indices.data_ptr(), _IT[indices.dtype],
+                         row_status.contiguous().data_ptr() if row_status is not None else None,
+                         batch, k, float(temperature), float(top_p), uniforms.data_ptr(),
+                         tokens.data_ptr(), probs.data_ptr(), stream)
+    if rc != DS_OK:
+        raise TopkError(rc)
+    return tokens, probs
 
 
 def pad_rows(x: torch.Tensor) -> torch.Tensor:

@@ -45,8 +45,11 @@ def build(verbose: bool = False, extra: list[str] | None = None) -> str:
           "-o", a_obj], verbose)
     _run([HIPCC, *COMMON, *DEVICE, *extra, "-c", os.path.join(CSRC, "noalloc.hip"), "-o", n_obj],
          verbose)
+    s_obj = os.path.join(bdir, "sampler_tail.o")
+    _run([HIPCC, *COMMON, *DEVICE, *extra, "-c", os.path.join(CSRC, "sampler_tail.hip"), "-o", s_obj],
+         verbose)
     tmp = LIB + ".tmp"
-    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", k_obj, c_obj, c2_obj, a_obj, n_obj, "-o", tmp],
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", k_obj, c_obj, c2_obj, a_obj, n_obj, s_obj, "-o", tmp],
          verbose)
     os.replace(tmp, LIB)
     return LIB

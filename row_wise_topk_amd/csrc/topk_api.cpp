@@ -404,6 +404,7 @@ const char* ds_topk_status_string(ds_status_t status) {
     case DS_ERR_HIP: return "HIP launch error";
     case DS_ERR_PLAN: return "plan field out of range";
     case DS_ERR_SCRATCH_LIMIT: return "problem needs more workspace than the allocation-free entry point's scratch";
+    case DS_ERR_SAMPLER_PARAM: return "temperature is NaN, or top_p is NaN or not above zero";
   }
   return "unknown status";
 }

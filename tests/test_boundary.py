@@ -23,7 +23,7 @@ def test_every_declared_symbol_is_exported():
     names = rt.exported_names()
     assert {"ds_topk", "ds_topk_ex", "ds_topk_validate", "ds_topk_workspace_size",
             "ds_topk_workspace_size_ex", "ds_topk_stride_requirement",
-            "ds_topk_status_string", "ds_read_ceiling"} <= set(names)
+            "ds_topk_status_string", "ds_read_ceiling", "ds_sampler_tail"} <= set(names)
     lib = ctypes.CDLL(rt.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -219,3 +219,41 @@ def test_noalloc_refusals_need_no_gpu():
     rc = rt.ds_topk_noalloc(None, rt.DS_BF16, 4, 1000, 1000, None, 0, 1, 0, rt.DS_INT32, None,
                             None, None, None, None)
     assert rt.STATUS_NAMES[rc] == "DS_ERR_K_RANGE"
+
+
+_C = {name: i for i, name in enumerate(rt.STATUS_NAMES)}
+
+
+# ds_sampler_tail's argument checks, in their documented order, before any
+# launch (fake device addresses: nothing is dereferenced).
+_TAIL = dict(values=A16, dtype=rt.DS_FP32, indices=A16b, index_dtype=rt.DS_INT64, row_status=None,
+             batch=4, k=1024, temperature=0.7, top_p=0.9, uniforms=A16c, tokens=A16d, probs=A16w,
+             stream=None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=5), _C["DS_ERR_DTYPE"]),
+    (dict(index_dtype=9), _C["DS_ERR_INDEX_DTYPE"]),
+    (dict(k=0), _C["DS_ERR_K_RANGE"]),
+    (dict(k=4097), _C["DS_ERR_K_RANGE"]),
+    (dict(batch=-1), _C["DS_ERR_SHAPE"]),
+    (dict(batch=1 << 31), _C["DS_ERR_SHAPE"]),
+    (dict(temperature=float("nan")), _C["DS_ERR_SAMPLER_PARAM"]),
+    (dict(top_p=0.0), _C["DS_ERR_SAMPLER_PARAM"]),
+    (dict(top_p=-0.5), _C["DS_ERR_SAMPLER_PARAM"]),
+    (dict(top_p=float("nan")), _C["DS_ERR_SAMPLER_PARAM"]),
+    (dict(values=None), _C["DS_ERR_NULL"]),
+    (dict(indices=None), _C["DS_ERR_NULL"]),
+    (dict(uniforms=None), _C["DS_ERR_NULL"]),
+    (dict(tokens=None), _C["DS_ERR_NULL"]),
+    (dict(values=A16 + 2), _C["DS_ERR_ALIGN"]),
+    (dict(indices=A16b + 4), _C["DS_ERR_ALIGN"]),
+    (dict(tokens=A16d + 4), _C["DS_ERR_ALIGN"]),
+    (dict(probs=A16w + 2), _C["DS_ERR_ALIGN"]),
+    (dict(batch=0, values=None, tokens=None), _C["DS_OK"]),
+])
+def test_sampler_tail_argument_errors(kw, code):
+    a = dict(_TAIL, **kw)
+    assert rt.ds_sampler_tail(a["values"], a["dtype"], a["indices"], a["index_dtype"], a["row_status"],
+                              a["batch"], a["k"], a["temperature"], a["top_p"], a["uniforms"],
+                              a["tokens"], a["probs"], a["stream"]) == code
