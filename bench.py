@@ -29,6 +29,8 @@ cpu_baseline the CPU oracle (full stable sort per row) on the host cores, on a
              bounded sample of each workload.
 read_ceiling the same input bytes read by a kernel with the same grid, chunk
              order and loads that does nothing else (ds_read_ceiling).
+sampler_tail the sampling step after the sampler's TopK (ds_sampler_tail:
+             temperature softmax, nucleus cut, draw) on that call's outputs.
 
   python bench.py [--steps K] [--warmup W] [--config N] [--no-cpu]
        --config 0 (default) both workloads; N alone: that workload only
@@ -381,6 +383,23 @@ def main():
                   "without_values_us": round(alt_ms * 1e3, 3)}
             break
 
+    # The sampling step after the sampler's TopK (ds_sampler_tail), on that
+    # call's outputs, timed the same way.
+    tail = None
+    for c in cases:
+        if c.w.num == 2 and c.w.sorted == 1 and c.w.return_values and not args.no_graph:
+            u = torch.rand(c.w.batch, generator=torch.Generator().manual_seed(7)).to(dev)
+            vals, idx, st = c.out
+            fn = lambda i, vals=vals, idx=idx, st=st, u=u: rt.sample_from_topk(  # noqa: E731
+                vals, idx, st, temperature=0.8, top_p=0.95, uniforms=u)
+            with torch.cuda.stream(stream):
+                fn(0)
+            g = graph_of(fn, K)
+            tail_ms, _ = graph_time(g, K)
+            del g
+            tail = {"workload": c.w.name + " outputs", "temperature": 0.8, "top_p": 0.95,
+                    "us_per_call": round(tail_ms * 1e3, 3)}
+
     torch_us = {}
     if not args.no_torch:
         for c in cases:
@@ -473,6 +492,7 @@ def main():
         "workloads": rows,
         "roofline": roof,
         "return_values_ab": ab,
+        "sampler_tail": tail,
         "torch_topk_us": torch_us or None,
         "cpu_baseline": cpu,
     }

@@ -1664,63 +1664,73 @@ __device__ __forceinline__ bool select_core(Smem<CAP>& sm, const CArgs& a, bool 
   const u64 blo = lo + (static_cast<u64>((kCutBins - 1) - b) << shift);
   const u64 bhi_full = blo + ((1ull << shift) - 1ull);
   const u64 bhi = bhi_full < hi ? bhi_full : hi;
-  u64 T = blo;
-  if (hb != need) {
-    if (hb > kRankMax) return false;
-    // The boundary bin's members, ranked by one wave.  Each wave takes its
-    // span of the side buffer with one atomic.
-    {
-      u64 mk[RPT];
-      uint32_t wn = 0;
-#pragma unroll
-      for (int i = 0; i < RPT; ++i) if (i < nit) {
-        mk[i] = ballot((v[i] != 0ull) & (v[i] >= blo) & (v[i] <= bhi));
-        wn += static_cast<uint32_t>(__popcll(mk[i]));
-      }
-      if (wn) {
-        uint32_t base = 0;
-        if (lane_id() == 0) base = atomicAdd(&sm.side_n, wn);
-        base = uniform(base);
-#pragma unroll
-        for (int i = 0; i < RPT; ++i) if (i < nit) {
-          if ((mk[i] >> lane_id()) & 1ull) sm.side[base + mbcnt64(mk[i])] = v[i];
-          base += static_cast<uint32_t>(__popcll(mk[i]));
-        }
-      }
-    }
-    __syncthreads();
-    if (t < 64) {
-      const uint32_t ns = uniform(sm.side_n);
-      const u64 mine = static_cast<uint32_t>(t) < ns ? sm.side[t] : 0ull;
-      const uint32_t mlo = static_cast<uint32_t>(mine), mhi = static_cast<uint32_t>(mine >> 32);
-      uint32_t above = 0;
-      for (uint32_t j = 0; j < ns; ++j) {
-        const uint32_t olo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(mlo), static_cast<int>(j)));
-        const uint32_t ohi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(mhi), static_cast<int>(j)));
-        above += ((static_cast<u64>(ohi) << 32) | olo) > mine ? 1u : 0u;
-      }
-      if (static_cast<uint32_t>(t) < ns && above + 1u == need) sm.res64 = mine;
-    }
-    __syncthreads();
-    T = uniform64(sm.res64);
-  }
-  // Each wave takes its span of the output with one atomic, then stores its
-  // kept candidates in lane order.
-  u64 mk[RPT];
-  uint32_t wn = 0;
-#pragma unroll
-  for (int i = 0; i < RPT; ++i) if (i < nit) {
-    mk[i] = ballot((v[i] != 0ull) & (v[i] >= T));
-    wn += static_cast<uint32_t>(__popcll(mk[i]));
-  }
-  uint32_t base = 0;
-  if (lane_id() == 0 && wn) base = atomicAdd(&sm.cnt_out, wn);
-  base = uniform(base);
   bool z = false;
+  if (hb == need) {   // the whole boundary bin is kept: every candidate >= blo
+    u64 mk[RPT];
+    uint32_t wn = 0;
 #pragma unroll
-  for (int i = 0; i < RPT; ++i) if (i < nit) {
-    if ((mk[i] >> lane_id()) & 1ull) z |= store_one(a, bf16, xrow, out0 + base + mbcnt64(mk[i]), v[i], true, status);
-    base += static_cast<uint32_t>(__popcll(mk[i]));
+    for (int i = 0; i < RPT; ++i) if (i < nit) {
+      mk[i] = ballot((v[i] != 0ull) & (v[i] >= blo));
+      wn += static_cast<uint32_t>(__popcll(mk[i]));
+    }
+    uint32_t base = 0;
+    if (lane_id() == 0 && wn) base = atomicAdd(&sm.cnt_out, wn);
+    base = uniform(base);
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) if (i < nit) {
+      if ((mk[i] >> lane_id()) & 1ull) z |= store_one(a, bf16, xrow, out0 + base + mbcnt64(mk[i]), v[i], true, status);
+      base += static_cast<uint32_t>(__popcll(mk[i]));
+    }
+    if (z) sm.zeros = 1u;
+    return true;
+  }
+  if (hb > kRankMax) return false;
+  // Candidates above the boundary bin are stored at once; the bin's members
+  // go to the side buffer (each wave takes its spans with one atomic each).
+  {
+    u64 mk[RPT], ms[RPT];
+    uint32_t wn = 0, sn = 0;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) if (i < nit) {
+      const bool live = v[i] != 0ull;
+      mk[i] = ballot(live & (v[i] > bhi));
+      ms[i] = ballot(live & (v[i] >= blo) & (v[i] <= bhi));
+      wn += static_cast<uint32_t>(__popcll(mk[i]));
+      sn += static_cast<uint32_t>(__popcll(ms[i]));
+    }
+    uint32_t base = 0, sbase = 0;
+    if (lane_id() == 0) {
+      if (wn) base = atomicAdd(&sm.cnt_out, wn);
+      if (sn) sbase = atomicAdd(&sm.side_n, sn);
+    }
+    base = uniform(base);
+    sbase = uniform(sbase);
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) if (i < nit) {
+      if (((ms[i] >> lane_id()) & 1ull) && sbase + mbcnt64(ms[i]) < kRankMax) sm.side[sbase + mbcnt64(ms[i])] = v[i];
+      sbase += static_cast<uint32_t>(__popcll(ms[i]));
+      if ((mk[i] >> lane_id()) & 1ull) z |= store_one(a, bf16, xrow, out0 + base + mbcnt64(mk[i]), v[i], true, status);
+      base += static_cast<uint32_t>(__popcll(mk[i]));
+    }
+  }
+  __syncthreads();
+  // Wave 0 ranks the bin's members (one per lane, the others read by
+  // readlane) and stores the `need` largest after the others' stores.
+  if (t < 64) {
+    const uint32_t ns = min(uniform(sm.side_n), kRankMax);   // == hb for a consistent buffer
+    const u64 mine = static_cast<uint32_t>(t) < ns ? sm.side[t] : 0ull;
+    const uint32_t mlo = static_cast<uint32_t>(mine), mhi = static_cast<uint32_t>(mine >> 32);
+    uint32_t above = 0;
+    for (uint32_t j = 0; j < ns; ++j) {
+      const uint32_t olo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(mlo), static_cast<int>(j)));
+      const uint32_t ohi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(mhi), static_cast<int>(j)));
+      above += ((static_cast<u64>(ohi) << 32) | olo) > mine ? 1u : 0u;
+    }
+    const u64 mk = ballot(static_cast<uint32_t>(t) < ns && above < need);
+    uint32_t base = 0;
+    if (lane_id() == 0 && mk) base = atomicAdd(&sm.cnt_out, static_cast<uint32_t>(__popcll(mk)));
+    base = uniform(base);
+    if ((mk >> lane_id()) & 1ull) z |= store_one(a, bf16, xrow, out0 + base + mbcnt64(mk), mine, true, status);
   }
   if (z) sm.zeros = 1u;
   return true;
