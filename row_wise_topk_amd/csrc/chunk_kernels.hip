@@ -204,6 +204,7 @@ struct Smem {
   uint32_t n_cut;                     // cuts back to k made by this workgroup (statistics)
   uint32_t is_last;
   uint32_t zeros;                     // a zero was stored as an output value
+  uint32_t rowmax;                    // whole rows: largest key of the chunks after the first
   uint32_t acnt;                      // append_fast: candidates reserved so far
   uint32_t aovf;                      // append_fast: a reservation ran past its limit
   u64 res64;
@@ -1160,10 +1161,14 @@ __device__ __forceinline__ bool next_chunk(Smem<CAP>& sm, Buf& B, u32x4 (&r)[V],
   bool nn;
   if ((c + 1) * G::CE > L) {
     nan = sanitize_ragged<BF16>(r, c, L);
+    chunk_max_nan<BF16, false>(r, &mk, &nn, chunk_nv<BF16>(c, L));
   } else {
     chunk_max_nan<BF16, true>(r, &mk, &nn);
     nan = nn;
   }
+  // The row's largest key, for the epilogue's range (read after a barrier).
+  const uint32_t wm = wave_max_u32(mk);
+  if (lane_id() == 0) atomicMax(&sm.rowmax, wm);
   const uint32_t nv = chunk_nv<BF16>(c, L);
   if (!append_fast<BF16>(sm, B, r, c, cap, nv)) append_chunk<BF16>(sm, B, r, c, k, cap, nv);
   return nan;
@@ -1538,6 +1543,12 @@ __device__ __forceinline__ bool rank_core(Smem<CAP>& sm, const CArgs& a, bool bf
   // reads need no bound.  Positions are taken eight per lane at a time, each
   // batch's values and bin bounds read together.
   const uint32_t npos = uniform((n + NT - 1) / NT);
+  // A kept candidate goes to stage[rank] (the buffer past the candidates and
+  // their padding, room the caller's class always leaves: n + m <= CAP),
+  // and the row's outputs are then stored in order, coalesced, instead of
+  // one scattered store per candidate.
+  const bool staged = n + m <= static_cast<uint32_t>(CAP);
+  u64* stage = sm.buf + n + 8;
   bool z = false;
 #pragma unroll
   for (int g = 0; g < RPT; g += 8) if (static_cast<uint32_t>(g) < npos) {
@@ -1569,8 +1580,15 @@ __device__ __forceinline__ bool rank_core(Smem<CAP>& sm, const CArgs& a, bool bf
           for (int j = 0; j < 8; ++j) r += y[j] > x[i] ? 1u : 0u;
         }
       }
-      if (r < m) z |= store_one(a, bf16, xrow, out0 + r, x[i], true, status);
+      if (r < m) {
+        if (staged) stage[r] = x[i];
+        else z |= store_one(a, bf16, xrow, out0 + r, x[i], true, status);
+      }
     }
+  }
+  if (staged) {
+    __syncthreads();
+    for (uint32_t e = t; e < m; e += NT) z |= store_one(a, bf16, xrow, out0 + e, stage[e], true, status);
   }
   if (z) sm.zeros = 1u;
   __syncthreads();
@@ -1583,7 +1601,7 @@ __device__ __forceinline__ bool rank_core(Smem<CAP>& sm, const CArgs& a, bool bf
 template <int CAP>
 __device__ __forceinline__ bool rank_store(Smem<CAP>& sm, const CArgs& a, bool bf16,
                                            const char* xrow, int64_t out0, uint32_t n, uint32_t m,
-                                           uint32_t status) {
+                                           uint32_t status, u64 lo_in = 0, u64 hi_in = 0) {
   const uint32_t t = threadIdx.x;
   // Iterations past the last candidate are skipped as a whole (n is uniform).
   const uint32_t nit = uniform((n + NT - 1) / NT);
@@ -1593,7 +1611,7 @@ __device__ __forceinline__ bool rank_store(Smem<CAP>& sm, const CArgs& a, bool b
     const uint32_t j = i * NT + t;
     v[i] = j < n ? sm.buf[j] : 0ull;
   }
-  return rank_core(sm, a, bf16, xrow, out0, v, nit, m, status);
+  return rank_core(sm, a, bf16, xrow, out0, v, nit, m, status, lo_in, hi_in);
 }
 
 // Selection without order (unsorted output): the m largest of buf[0, n)
@@ -1764,7 +1782,7 @@ __device__ __forceinline__ void stat_add(const CArgs& a, int row, int field, uin
 template <int KMAX, int CAP>
 __device__ __forceinline__ void finish_row(Smem<CAP>& sm, const CArgs& a, bool bf16, int row,
                                            uint32_t count, uint32_t L, uint32_t status,
-                                           bool direct = true) {
+                                           bool direct = true, u64 lo_in = 0, u64 hi_in = 0) {
   constexpr int PER = KMAX > NT ? KMAX / NT : 1;
   const int t = threadIdx.x;
   const uint32_t k = static_cast<uint32_t>(a.k);
@@ -1778,7 +1796,7 @@ __device__ __forceinline__ void finish_row(Smem<CAP>& sm, const CArgs& a, bool b
   // order: every candidate's rank, stored directly.
   if (direct && m > 0 && count >= m && count <= static_cast<uint32_t>(kRankPerLane * NT) &&
       ((a.sorted == 0 && select_store(sm, a, bf16, xrow, out0, count, m, status)) ||
-       (a.sorted == 1 && rank_store(sm, a, bf16, xrow, out0, count, m, status)))) {
+       (a.sorted == 1 && rank_store(sm, a, bf16, xrow, out0, count, m, status, lo_in, hi_in)))) {
     for (uint32_t e = m + t; e < k; e += NT) store_one(a, bf16, xrow, out0 + e, 0ull, false, status);
     if (t == 0) a.row_status[row] = static_cast<int32_t>(status);
     stat_add(a, row, DS_STAT_CUTS, sm.n_cut);
@@ -1927,14 +1945,16 @@ __global__ __launch_bounds__(NT, waves_per_simd(NT == 256 ? (KC >= 2 ? 3 : 4) : 
     sm.n_cut = 0u;
   }
 
+  if (t == 0) sm.rowmax = 0u;
   Buf B{0u, kTAll, 0};
   bool spec = false, nan = false;
+  uint32_t top0 = 0;   // the first chunk's largest key
   if (status == 0 && nch > 0) {
     // One chunk in registers at a time: the workgroups sharing a CU (many
     // rows) keep the loads in flight while this one filters.
     u32x4 ra[V];
     load_chunk<BF16>(ra, xrow, chunk_at(0), L);
-    nan = start_chunk<BF16>(sm, B, ra, chunk_at(0), L, k, nch == 1, &spec);
+    nan = start_chunk<BF16>(sm, B, ra, chunk_at(0), L, k, nch == 1, &spec, &top0);
     const uint32_t nv0 = chunk_nv<BF16>(chunk_at(0), L);
     if (!append_fast<BF16>(sm, B, ra, chunk_at(0), cap, nv0)) append_chunk<BF16>(sm, B, ra, chunk_at(0), k, cap, nv0);
     for (uint32_t j = 1; j < nch && !uniform(sm.err); ++j) {
@@ -1952,7 +1972,14 @@ __global__ __launch_bounds__(NT, waves_per_simd(NT == 256 ? (KC >= 2 ? 3 : 4) : 
     stat_add(a, row, DS_STAT_ROW_REREADS, 1u);
     if (uniform(sm.err)) status |= DS_ROW_INTERNAL;
   }
-  finish_row<KMAX>(sm, a, BF16, row, B.count, L, status);
+  // Every candidate lies in [key(T), the row's largest key]: the value-order
+  // epilogue bins that range without measuring it (unless T admits all).
+  const uint32_t rmax = max(top0, uniform(sm.rowmax));
+  const uint32_t tkey = key_of(B.T);
+  const bool known = B.T != kTAll && rmax != 0u && tkey <= rmax;
+  finish_row<KMAX>(sm, a, BF16, row, B.count, L, status, true,
+                   known ? static_cast<u64>(tkey) << 32 : 0ull,
+                   known ? (static_cast<u64>(rmax) << 32) | 0xFFFFFFFFull : 0ull);
 }
 
 // One chunk of a row per workgroup; the last workgroup of the row to finish
