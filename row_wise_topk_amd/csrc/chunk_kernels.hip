@@ -286,8 +286,16 @@ __device__ __forceinline__ uint32_t chunk_nv(uint32_t c, uint32_t L) {
   return L > c0 ? min(static_cast<uint32_t>(V), (L - c0 + VW - 1) / VW) : 0u;
 }
 
+// Vectors per lane that load_chunk loads: every vector for split rows (their
+// chunks are full but for a row's last), only those below chunk_nv for whole
+// rows (a short row's chunk is mostly past L).
+template <bool BF16>
+__device__ __forceinline__ uint32_t loaded_nv(uint32_t c, uint32_t L) {
+  return kSplit ? static_cast<uint32_t>(V) : chunk_nv<BF16>(c, L);
+}
+
 // Chunk c of a row: lane t's vector i covers columns c*CE + (i*NT + t)*EPV ...
-// Vectors past chunk_nv are not loaded: they hold negative NaNs (the ragged
+// Vectors past loaded_nv are not loaded: they hold negative NaNs (the ragged
 // padding, see sanitize_ragged).  A vector below it that starts at or past L
 // is loaded from column 0 instead (a valid address); its values are replaced
 // before use (sanitize_ragged).
@@ -296,7 +304,7 @@ __device__ __forceinline__ void load_chunk(u32x4 (&r)[V], const char* xrow, uint
                                            uint32_t L) {
   using G = Geo<BF16>;
   const uint32_t e0 = c * G::CE + threadIdx.x * G::EPV;
-  const uint32_t nv = chunk_nv<BF16>(c, L);
+  const uint32_t nv = loaded_nv<BF16>(c, L);
 #pragma unroll
   for (int i = 0; i < V; ++i) {
     if (static_cast<uint32_t>(i) < nv) {
@@ -354,10 +362,10 @@ __device__ __forceinline__ void for_values(const u32x4& r, F&& f) {
 template <bool BF16>
 __device__ __forceinline__ bool sanitize_ragged(u32x4 (&r)[V], uint32_t c, uint32_t L) {
   bool nan = false;
-  const uint32_t nv = chunk_nv<BF16>(c, L);
+  const uint32_t nv = loaded_nv<BF16>(c, L);
 #pragma unroll
   for (int i = 0; i < V; ++i) {
-    if (static_cast<uint32_t>(i) >= nv) continue;   // padding already
+    if (static_cast<uint32_t>(i) >= nv) continue;   // padding already (not loaded)
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const uint32_t d = r[i][w];
@@ -533,7 +541,7 @@ __device__ __forceinline__ void for_reps(const u32x4& v, F&& f) {
 // octave for fp32), then s = 24 (the window spans every key) when the first
 // window holds fewer than m.  GS > 0 bins one representative per group of GS
 // values (for_reps), with s = 16, then 20 (16 bf16 values per bin, 32 octaves
-// in all), then 24.  Returns T = (edge key << 32): at least m values of the
+// in all), then 24 (split rows: 16, then 24).  Returns T = (edge key << 32): at least m values of the
 // chunk are at or above it (m binned members are, each a distinct value of
 // the chunk).  Leaves the histogram zeroed.  Every binned key is at most
 // maxkey: a lane maximum is, and a chunk holding a NaN (whose maxkey may lie
@@ -542,7 +550,8 @@ template <bool BF16, int GS, int CAP>
 __device__ __forceinline__ u64 start_threshold(Smem<CAP>& sm, const u32x4 (&r)[V],
                                                uint32_t maxkey, uint32_t lane_max, uint32_t m,
                                                uint32_t nv) {
-  constexpr int NP = GS == 0 ? 2 : 3;
+  // (Split rows keep two scales: their start bins lane maxima or small shares.)
+  constexpr int NP = (GS == 0 || kSplit) ? 2 : 3;
   for (int pass = 0; pass < NP; ++pass) {
     const uint32_t s = pass == 0 ? 16u : (pass == NP - 1 ? 24u : 20u);
     const u64 span = static_cast<u64>(kWinBins) << s;   // keys the window covers
@@ -819,7 +828,7 @@ __device__ __forceinline__ bool start_chunk(Smem<CAP>& sm, Buf& B, u32x4 (&r)[V]
   bool nan = false;
   const bool rag = (c + 1) * G::CE > L;
   if (rag) nan = sanitize_ragged<BF16>(r, c, L);
-  const uint32_t nv = chunk_nv<BF16>(c, L);
+  const uint32_t nv = loaded_nv<BF16>(c, L);
   uint32_t mk;
   bool nn;
   if (rag) chunk_max_nan<BF16, false>(r, &mk, &nn, nv);
@@ -853,11 +862,12 @@ __device__ __forceinline__ bool start_chunk(Smem<CAP>& sm, Buf& B, u32x4 (&r)[V]
       // two (at most one 16-byte vector) that leaves about 3m groups: the
       // m-th largest representative then has about 1.1m values at or above
       // it, at an eighth of the histogram work of binning every value.
-      const uint32_t q = nvalid / (3u * m);
+      // (Split rows, whose shares are small, bin every value: one variant.)
+      const uint32_t q = kSplit ? 0u : nvalid / (3u * m);
       const uint32_t g = q >= 8u && BF16 ? 8u : q >= 4u ? 4u : q >= 2u ? 2u : 1u;
-      if (g == 8u) T = start_threshold<BF16, 8>(sm, r, maxkey, mk, m, nv);
-      else if (g == 4u) T = start_threshold<BF16, 4>(sm, r, maxkey, mk, m, nv);
-      else if (g == 2u) T = start_threshold<BF16, 2>(sm, r, maxkey, mk, m, nv);
+      if (!kSplit && g == 8u) T = start_threshold<BF16, 8>(sm, r, maxkey, mk, m, nv);
+      else if (!kSplit && g == 4u) T = start_threshold<BF16, 4>(sm, r, maxkey, mk, m, nv);
+      else if (!kSplit && g == 2u) T = start_threshold<BF16, 2>(sm, r, maxkey, mk, m, nv);
       else T = start_threshold<BF16, 1>(sm, r, maxkey, mk, m, nv);
     }
   }
@@ -1543,12 +1553,6 @@ __device__ __forceinline__ bool rank_core(Smem<CAP>& sm, const CArgs& a, bool bf
   // reads need no bound.  Positions are taken eight per lane at a time, each
   // batch's values and bin bounds read together.
   const uint32_t npos = uniform((n + NT - 1) / NT);
-  // A kept candidate goes to stage[rank] (the buffer past the candidates and
-  // their padding, room the caller's class always leaves: n + m <= CAP),
-  // and the row's outputs are then stored in order, coalesced, instead of
-  // one scattered store per candidate.
-  const bool staged = n + m <= static_cast<uint32_t>(CAP);
-  u64* stage = sm.buf + n + 8;
   bool z = false;
 #pragma unroll
   for (int g = 0; g < RPT; g += 8) if (static_cast<uint32_t>(g) < npos) {
@@ -1580,15 +1584,8 @@ __device__ __forceinline__ bool rank_core(Smem<CAP>& sm, const CArgs& a, bool bf
           for (int j = 0; j < 8; ++j) r += y[j] > x[i] ? 1u : 0u;
         }
       }
-      if (r < m) {
-        if (staged) stage[r] = x[i];
-        else z |= store_one(a, bf16, xrow, out0 + r, x[i], true, status);
-      }
+      if (r < m) z |= store_one(a, bf16, xrow, out0 + r, x[i], true, status);
     }
-  }
-  if (staged) {
-    __syncthreads();
-    for (uint32_t e = t; e < m; e += NT) z |= store_one(a, bf16, xrow, out0 + e, stage[e], true, status);
   }
   if (z) sm.zeros = 1u;
   __syncthreads();
@@ -1682,73 +1679,63 @@ __device__ __forceinline__ bool select_core(Smem<CAP>& sm, const CArgs& a, bool 
   const u64 blo = lo + (static_cast<u64>((kCutBins - 1) - b) << shift);
   const u64 bhi_full = blo + ((1ull << shift) - 1ull);
   const u64 bhi = bhi_full < hi ? bhi_full : hi;
+  u64 T = blo;
+  if (hb != need) {
+    if (hb > kRankMax) return false;
+    // The boundary bin's members, ranked by one wave.  Each wave takes its
+    // span of the side buffer with one atomic.
+    {
+      u64 mk[RPT];
+      uint32_t wn = 0;
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) if (i < nit) {
+        mk[i] = ballot((v[i] != 0ull) & (v[i] >= blo) & (v[i] <= bhi));
+        wn += static_cast<uint32_t>(__popcll(mk[i]));
+      }
+      if (wn) {
+        uint32_t base = 0;
+        if (lane_id() == 0) base = atomicAdd(&sm.side_n, wn);
+        base = uniform(base);
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) if (i < nit) {
+          if ((mk[i] >> lane_id()) & 1ull) sm.side[base + mbcnt64(mk[i])] = v[i];
+          base += static_cast<uint32_t>(__popcll(mk[i]));
+        }
+      }
+    }
+    __syncthreads();
+    if (t < 64) {
+      const uint32_t ns = uniform(sm.side_n);
+      const u64 mine = static_cast<uint32_t>(t) < ns ? sm.side[t] : 0ull;
+      const uint32_t mlo = static_cast<uint32_t>(mine), mhi = static_cast<uint32_t>(mine >> 32);
+      uint32_t above = 0;
+      for (uint32_t j = 0; j < ns; ++j) {
+        const uint32_t olo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(mlo), static_cast<int>(j)));
+        const uint32_t ohi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(mhi), static_cast<int>(j)));
+        above += ((static_cast<u64>(ohi) << 32) | olo) > mine ? 1u : 0u;
+      }
+      if (static_cast<uint32_t>(t) < ns && above + 1u == need) sm.res64 = mine;
+    }
+    __syncthreads();
+    T = uniform64(sm.res64);
+  }
+  // Each wave takes its span of the output with one atomic, then stores its
+  // kept candidates in lane order.
+  u64 mk[RPT];
+  uint32_t wn = 0;
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) if (i < nit) {
+    mk[i] = ballot((v[i] != 0ull) & (v[i] >= T));
+    wn += static_cast<uint32_t>(__popcll(mk[i]));
+  }
+  uint32_t base = 0;
+  if (lane_id() == 0 && wn) base = atomicAdd(&sm.cnt_out, wn);
+  base = uniform(base);
   bool z = false;
-  if (hb == need) {   // the whole boundary bin is kept: every candidate >= blo
-    u64 mk[RPT];
-    uint32_t wn = 0;
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) if (i < nit) {
-      mk[i] = ballot((v[i] != 0ull) & (v[i] >= blo));
-      wn += static_cast<uint32_t>(__popcll(mk[i]));
-    }
-    uint32_t base = 0;
-    if (lane_id() == 0 && wn) base = atomicAdd(&sm.cnt_out, wn);
-    base = uniform(base);
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) if (i < nit) {
-      if ((mk[i] >> lane_id()) & 1ull) z |= store_one(a, bf16, xrow, out0 + base + mbcnt64(mk[i]), v[i], true, status);
-      base += static_cast<uint32_t>(__popcll(mk[i]));
-    }
-    if (z) sm.zeros = 1u;
-    return true;
-  }
-  if (hb > kRankMax) return false;
-  // Candidates above the boundary bin are stored at once; the bin's members
-  // go to the side buffer (each wave takes its spans with one atomic each).
-  {
-    u64 mk[RPT], ms[RPT];
-    uint32_t wn = 0, sn = 0;
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) if (i < nit) {
-      const bool live = v[i] != 0ull;
-      mk[i] = ballot(live & (v[i] > bhi));
-      ms[i] = ballot(live & (v[i] >= blo) & (v[i] <= bhi));
-      wn += static_cast<uint32_t>(__popcll(mk[i]));
-      sn += static_cast<uint32_t>(__popcll(ms[i]));
-    }
-    uint32_t base = 0, sbase = 0;
-    if (lane_id() == 0) {
-      if (wn) base = atomicAdd(&sm.cnt_out, wn);
-      if (sn) sbase = atomicAdd(&sm.side_n, sn);
-    }
-    base = uniform(base);
-    sbase = uniform(sbase);
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) if (i < nit) {
-      if (((ms[i] >> lane_id()) & 1ull) && sbase + mbcnt64(ms[i]) < kRankMax) sm.side[sbase + mbcnt64(ms[i])] = v[i];
-      sbase += static_cast<uint32_t>(__popcll(ms[i]));
-      if ((mk[i] >> lane_id()) & 1ull) z |= store_one(a, bf16, xrow, out0 + base + mbcnt64(mk[i]), v[i], true, status);
-      base += static_cast<uint32_t>(__popcll(mk[i]));
-    }
-  }
-  __syncthreads();
-  // Wave 0 ranks the bin's members (one per lane, the others read by
-  // readlane) and stores the `need` largest after the others' stores.
-  if (t < 64) {
-    const uint32_t ns = min(uniform(sm.side_n), kRankMax);   // == hb for a consistent buffer
-    const u64 mine = static_cast<uint32_t>(t) < ns ? sm.side[t] : 0ull;
-    const uint32_t mlo = static_cast<uint32_t>(mine), mhi = static_cast<uint32_t>(mine >> 32);
-    uint32_t above = 0;
-    for (uint32_t j = 0; j < ns; ++j) {
-      const uint32_t olo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(mlo), static_cast<int>(j)));
-      const uint32_t ohi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(mhi), static_cast<int>(j)));
-      above += ((static_cast<u64>(ohi) << 32) | olo) > mine ? 1u : 0u;
-    }
-    const u64 mk = ballot(static_cast<uint32_t>(t) < ns && above < need);
-    uint32_t base = 0;
-    if (lane_id() == 0 && mk) base = atomicAdd(&sm.cnt_out, static_cast<uint32_t>(__popcll(mk)));
-    base = uniform(base);
-    if ((mk >> lane_id()) & 1ull) z |= store_one(a, bf16, xrow, out0 + base + mbcnt64(mk), mine, true, status);
+  for (int i = 0; i < RPT; ++i) if (i < nit) {
+    if ((mk[i] >> lane_id()) & 1ull) z |= store_one(a, bf16, xrow, out0 + base + mbcnt64(mk[i]), v[i], true, status);
+    base += static_cast<uint32_t>(__popcll(mk[i]));
   }
   if (z) sm.zeros = 1u;
   return true;
