@@ -541,7 +541,8 @@ __device__ __forceinline__ void for_reps(const u32x4& v, F&& f) {
 // octave for fp32), then s = 24 (the window spans every key) when the first
 // window holds fewer than m.  GS > 0 bins one representative per group of GS
 // values (for_reps), with s = 16, then 20 (16 bf16 values per bin, 32 octaves
-// in all), then 24 (split rows: 16, then 24).  Returns T = (edge key << 32): at least m values of the
+// in all), then 24 (split rows: 16, then 24); with `wide`, when the m-th
+// value is expected far below the maximum, from 20.  Returns T = (edge key << 32): at least m values of the
 // chunk are at or above it (m binned members are, each a distinct value of
 // the chunk).  Leaves the histogram zeroed.  Every binned key is at most
 // maxkey: a lane maximum is, and a chunk holding a NaN (whose maxkey may lie
@@ -549,10 +550,10 @@ __device__ __forceinline__ void for_reps(const u32x4& v, F&& f) {
 template <bool BF16, int GS, int CAP>
 __device__ __forceinline__ u64 start_threshold(Smem<CAP>& sm, const u32x4 (&r)[V],
                                                uint32_t maxkey, uint32_t lane_max, uint32_t m,
-                                               uint32_t nv) {
+                                               uint32_t nv, bool wide = false) {
   // (Split rows keep two scales: their start bins lane maxima or small shares.)
   constexpr int NP = (GS == 0 || kSplit) ? 2 : 3;
-  for (int pass = 0; pass < NP; ++pass) {
+  for (int pass = (NP == 3 && wide) ? 1 : 0; pass < NP; ++pass) {
     const uint32_t s = pass == 0 ? 16u : (pass == NP - 1 ? 24u : 20u);
     const u64 span = static_cast<u64>(kWinBins) << s;   // keys the window covers
     const uint32_t lo_key = static_cast<u64>(maxkey) - kNegInfKey >= span
@@ -574,7 +575,7 @@ __device__ __forceinline__ u64 start_threshold(Smem<CAP>& sm, const u32x4 (&r)[V
     uint32_t h[1];
     h[0] = sm.hist[threadIdx.x];
     sm.hist[threadIdx.x] = 0u;   // own bin: no other lane touches it until the next barrier
-    const uint32_t b = find_rank<1>(sm, h, m, pass);
+    const uint32_t b = find_rank<1>(sm, h, m, pass & 1);   // parity 0 / 1 (wscan has two rows)
     if (b != kNone) {
       const int64_t e = static_cast<int64_t>(maxkey) - (static_cast<int64_t>(b + 1) << s) + 1;
       const uint32_t edge = e > static_cast<int64_t>(lo_key) ? static_cast<uint32_t>(e) : lo_key;
@@ -865,10 +866,13 @@ __device__ __forceinline__ bool start_chunk(Smem<CAP>& sm, Buf& B, u32x4 (&r)[V]
       // (Split rows, whose shares are small, bin every value: one variant.)
       const uint32_t q = kSplit ? 0u : nvalid / (3u * m);
       const uint32_t g = q >= 8u && BF16 ? 8u : q >= 4u ? 4u : q >= 2u ? 2u : 1u;
-      if (!kSplit && g == 8u) T = start_threshold<BF16, 8>(sm, r, maxkey, mk, m, nv);
-      else if (!kSplit && g == 4u) T = start_threshold<BF16, 4>(sm, r, maxkey, mk, m, nv);
-      else if (!kSplit && g == 2u) T = start_threshold<BF16, 2>(sm, r, maxkey, mk, m, nv);
-      else T = start_threshold<BF16, 1>(sm, r, maxkey, mk, m, nv);
+      // More than an eighth of the chunk above the start: the first window
+      // (two octaves below the maximum) would rarely hold it.
+      const bool wide = 8u * m > nvalid;
+      if (!kSplit && g == 8u) T = start_threshold<BF16, 8>(sm, r, maxkey, mk, m, nv, wide);
+      else if (!kSplit && g == 4u) T = start_threshold<BF16, 4>(sm, r, maxkey, mk, m, nv, wide);
+      else if (!kSplit && g == 2u) T = start_threshold<BF16, 2>(sm, r, maxkey, mk, m, nv, wide);
+      else T = start_threshold<BF16, 1>(sm, r, maxkey, mk, m, nv, wide);
     }
   }
   *spec = !exact && m < k && T != kTAll;

@@ -51,10 +51,12 @@ void* scratch_for_current_device(hipStream_t stream, ds_status_t* st) {
     *st = DS_ERR_HIP;
     return nullptr;
   }
-  const size_t n = kScratchBytes / 8;
-  hipLaunchKernelGGL(clear_scratch, dim3(1024), dim3(256), 0, stream,
-                     static_cast<unsigned long long*>(ptr), n);
-  if (hipGetLastError() != hipSuccess) {
+  unsigned long long* p64 = static_cast<unsigned long long*>(ptr);
+  size_t n = kScratchBytes / 8;
+  void* args[] = {&p64, &n};
+  // The launch's own error code (an earlier error of the thread is left alone).
+  if (hipLaunchKernel(reinterpret_cast<const void*>(&clear_scratch), dim3(1024), dim3(256), args, 0,
+                      stream) != hipSuccess) {
     *st = DS_ERR_HIP;
     return nullptr;
   }

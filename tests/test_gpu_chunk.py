@@ -175,3 +175,17 @@ def test_split_hand_over_capped_at_k(dtype):
     x = _bits(f, dtype)
     for k in (2048, 4096):
         check_case(x, dtype, n, k, 1, True, "int64", plan=SPLIT, name=f"capped k={k}")
+
+
+# Rows whose values span about 240 octaves: a whole row's start then finds
+# its m-th representative only in the widest window (every key), after the
+# one-value-per-bin and the 32-octave windows hold too few.
+@pytest.mark.parametrize("dtype", [FP32, BF16])
+def test_wide_dynamic_range_start(dtype):
+    rng = np.random.Generator(np.random.PCG64(41 + dtype))
+    for n, k in ((8192, 2000), (40000, 1500), (3000, 700)):
+        e = rng.uniform(-120.0, 120.0, size=(3, n))
+        f = (np.exp2(e) * np.where(rng.random((3, n)) < 0.3, -1.0, 1.0)).astype(np.float32)
+        x = _bits(f, dtype)
+        for sm in (1, 0):
+            check_case(x, dtype, n, k, sm, True, "int32", plan=WHOLE, name=f"wide range n={n} k={k}")
