@@ -96,12 +96,14 @@ def test_sampler_workload_full_size():
     _compare(x, w.dtype, w.k, w.index_dtype, end, temps, us, w.name)
 
 
+# k = 512 and k = 2500: four and ten candidates per lane.
+@pytest.mark.parametrize("k", [512, 2500])
 @pytest.mark.parametrize("dtype,index_dtype", [(FP32, "int32"), (BF16, "int64"), (BF16, "int32")])
-def test_edge_rows(dtype, index_dtype):
+def test_edge_rows(dtype, index_dtype, k):
     """Padding (end < k), an empty row, a NaN row, -inf and +inf candidates,
     all-equal rows, and uniforms at 0, 1 and just below 1."""
     rng = np.random.Generator(np.random.PCG64(31 + dtype))
-    n, k = 3000, 512
+    n = 3000
     f = (2.0 * rng.standard_normal((10, n))).astype(np.float32)
     f[3, 77] = np.nan
     f[4, :] = -np.inf
@@ -113,7 +115,7 @@ def test_edge_rows(dtype, index_dtype):
     x = workloads.to_bf16_bits(f) if dtype == BF16 else f
     us = np.array([0.3, 0.0, 0.5, 0.5, 0.999, 0.2, 0.7, 0.61, 1.0, np.nextafter(1.0, 0.0)])
     temps = [(1.0, 1.0), (0.8, 0.9), (0.0, 0.5), (0.3, 0.2)]
-    _compare(x, dtype, k, index_dtype, end, temps, us, f"edge rows {dtype} {index_dtype}", max_near=1)
+    _compare(x, dtype, k, index_dtype, end, temps, us, f"edge rows {dtype} {index_dtype} k={k}", max_near=1)
 
 
 def test_same_draw_on_every_call():
