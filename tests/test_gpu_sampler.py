@@ -96,7 +96,7 @@ def test_sampler_workload_full_size():
     _compare(x, w.dtype, w.k, w.index_dtype, end, temps, us, w.name)
 
 
-# k = 512 and k = 2500: four and ten candidates per lane.
+# k = 512 and k = 2500: two and ten candidates per lane.
 @pytest.mark.parametrize("k", [512, 2500])
 @pytest.mark.parametrize("dtype,index_dtype", [(FP32, "int32"), (BF16, "int64"), (BF16, "int32")])
 def test_edge_rows(dtype, index_dtype, k):
