@@ -1544,6 +1544,67 @@ __device__ __forceinline__ bool rank_core(Smem<CAP>& sm, const CArgs& a, bool bf
     run += h[i];
   }
   __syncthreads();
+  bool z = false;
+  if (narrow) {
+    // The same scatter and ranking on the 32-bit form, which is exact for
+    // these rows (16 key bits, then 16 column bits): half the LDS words read
+    // per bin-mate and one compare each.  A kept candidate's composite is
+    // rebuilt from it: a bf16 value's key (offset binary of its fp32
+    // pattern) has zero low 16 bits, whatever the sign, and the column is
+    // 0xFFFF minus the low 16 bits.
+    uint32_t* b32 = reinterpret_cast<uint32_t*>(sm.buf);
+    const uint32_t rlo32 = static_cast<uint32_t>(rlo);
+    auto bin32 = [&](uint32_t x) { return (kCutBins - 1) - ((x - rlo32) >> shift); };
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) if (i < nit)
+      if (v[i] != 0ull) {
+        const uint32_t x = static_cast<uint32_t>(red(v[i]));
+        b32[atomicAdd(&sm.hist[bin32(x)], 1u)] = x;
+      }
+    if (t < 8) b32[n + t] = 0u;   // below every 32-bit form (keys of values are >= 0x0080 << 16)
+    __syncthreads();
+    const uint32_t npos = uniform((n + NT - 1) / NT);
+#pragma unroll
+    for (int g = 0; g < RPT; g += 8) if (static_cast<uint32_t>(g) < npos) {
+      constexpr int RB = 8;
+      uint32_t x[RB], st[RB], en[RB];
+#pragma unroll
+      for (int i = 0; i < RB; ++i) {
+        const uint32_t p = (g + i) * NT + t;
+        x[i] = b32[p < n ? p : 0u];
+      }
+#pragma unroll
+      for (int i = 0; i < RB; ++i) {
+        const uint32_t b = bin32(x[i]);
+        st[i] = b ? sm.hist[b - 1] : 0u;
+        en[i] = sm.hist[b];
+      }
+#pragma unroll
+      for (int i = 0; i < RB; ++i) {
+        const uint32_t p = (g + i) * NT + t;
+        if (p >= n) continue;
+        uint32_t r = st[i];
+        if (en[i] - st[i] > 1u) {
+          for (uint32_t q0 = st[i]; q0 < en[i]; q0 += 8) {
+            uint32_t y[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) y[j] = b32[q0 + j];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) r += y[j] > x[i] ? 1u : 0u;
+          }
+        }
+        if (r < m) {
+          const uint32_t key = x[i] & 0xFFFF0000u;
+          z |= store_one(a, bf16, xrow, out0 + r, comp_of(key, 0xFFFFu - (x[i] & 0xFFFFu)), true, status);
+        }
+      }
+    }
+    if (z) sm.zeros = 1u;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kCutBPT; ++i) sm.hist[t * kCutBPT + i] = 0u;
+    return true;
+  }
   // Scatter: afterwards hist[b] is the end of bin b, and bin b starts where
   // bin b-1 ends (bin 0 at 0).
 #pragma unroll
@@ -1557,7 +1618,6 @@ __device__ __forceinline__ bool rank_core(Smem<CAP>& sm, const CArgs& a, bool bf
   // reads need no bound.  Positions are taken eight per lane at a time, each
   // batch's values and bin bounds read together.
   const uint32_t npos = uniform((n + NT - 1) / NT);
-  bool z = false;
 #pragma unroll
   for (int g = 0; g < RPT; g += 8) if (static_cast<uint32_t>(g) < npos) {
     constexpr int RB = 8;
