@@ -9,11 +9,12 @@
 // the cost is not the stream but the serial chain of a workgroup's steps; they
 // are laid out to keep that chain short on CDNA4:
 //
-//  * a chunk is 8 16-byte loads per lane of a 256-lane workgroup (8192 fp32 or
-//    16384 bf16 values, 32 KiB), all issued at once and held in registers; a
-//    workgroup takes either one chunk of a row (a row split into one
-//    workgroup per chunk, when the batch alone cannot fill the chip) or a
-//    whole row, chunk by chunk with the next chunk's loads in flight;
+//  * a chunk is 8 16-byte loads per lane of a 512-lane workgroup (16384 fp32
+//    or 32768 bf16 values, 64 KiB), all issued at once and held in
+//    registers; a workgroup takes either one chunk of a row (a row split
+//    into one workgroup per chunk, when the batch alone cannot fill the
+//    chip) or a whole row, chunk by chunk, two workgroups per CU keeping
+//    each other's loads in flight;
 //  * the first chunk sets T before anything is appended.  A workgroup that
 //    holds a whole row sets the row's exact start (at least min(k, L) of its
 //    values pass); otherwise T is an estimate, at least m values of the chunk
@@ -22,12 +23,13 @@
 //    complete: if fewer than min(k, L) candidates passed, the row is read
 //    again from a valid bound;
 //  * T comes from a 256-bin histogram anchored at the chunk's largest value,
-//    one bin per bf16 value (1/128 octave for fp32), over either every value
-//    in the window or, when m is small, only each lane's largest value (at
-//    least m values lie at or above the m-th largest lane maximum);
-//  * a chunk is filtered in two passes over the registers: a count (so that
-//    every wave knows where its candidates go) and a write, where a slot no
-//    lane of the wave keeps costs one compare;
+//    one bin per bf16 value (1/128 octave for fp32) and coarser windows after
+//    it, over each lane's largest value when m is small, else (whole rows)
+//    one representative per group of values: a member of each group, so the
+//    m-th largest representative has m values at or above it;
+//  * a split row's chunk is filtered in one pass over the registers into a
+//    region of LDS per wave; a whole row's chunk tests each 16-byte vector
+//    once and compacts only the vectors holding a candidate, staged in LDS;
 //  * a candidate is the 64-bit composite (key(v) << 32) | ~column, so one
 //    unsigned compare orders candidates exactly as the output (larger value
 //    first, then lower column: xhh.club, "DeepSeek开源DeepSelect：比torch.topk快二十倍！",
@@ -39,10 +41,14 @@
 //    LDS histograms, at most six levels), which ranks a boundary bin of at
 //    most 64 members directly; it keeps exactly the requested count;
 //  * a split row hands its candidates over through the workspace, with the
-//    chunk's threshold, and the last workgroup of the row to arrive (a
-//    release / acquire pair on the row's arrival counter) merges them;
-//  * the output is ordered by a bitonic sort in registers (cross-lane steps
-//    by ds_bpermute, cross-wave steps through LDS).
+//    chunk's threshold (agent-scope stores, all waited for before the row's
+//    arrival counter moves), and the last workgroup of the row to arrive
+//    merges them;
+//  * value order comes from every candidate's rank (a 2048-bin histogram,
+//    a scatter into bin order, the bin-mates above it); any order from the
+//    boundary bin ranked by one wave; a bitonic sort in registers
+//    (cross-lane steps on the VALU, cross-wave steps through LDS) serves
+//    the rows these cannot (long runs of equal values).
 //
 // NaN (narracomm.com, NaN paragraph): always checked over [0, end); a NaN sets
 // a status bit for the row instead of trapping.
