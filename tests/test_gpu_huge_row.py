@@ -16,7 +16,8 @@ Together these pin the result to the k first elements of the row in that order.
 
 A row of 2^24 values with the same k and planner (16 blocks per workgroup,
 so the estimated start applies) is compared with the oracle element by
-element.
+element, and so is a row of 2^27 values shared by all 256 workgroups, as at
+full size: 128 blocks per workgroup, many cuts each.
 """
 from __future__ import annotations
 
@@ -59,3 +60,10 @@ def test_long_row_top1000_vs_oracle(sorted_mode):
     x, _ = workloads.make_input(w)
     check_case(x, FP32, w.n_cols, w.k, sorted_mode, True, "int64",
                name=f"long row 1x{w.n_cols} k={w.k} sorted={sorted_mode}")
+
+
+def test_long_row_256_workgroups_vs_oracle():
+    w = workloads.workload(6, n_cols=1 << 27)
+    x, _ = workloads.make_input(w)
+    check_case(x, FP32, w.n_cols, w.k, 1, True, "int64", plan={"kernel": 1, "segments": 256},
+               name=f"long row 1x{w.n_cols} k={w.k}, 256 workgroups")
