@@ -189,3 +189,16 @@ def test_wide_dynamic_range_start(dtype):
         x = _bits(f, dtype)
         for sm in (1, 0):
             check_case(x, dtype, n, k, sm, True, "int32", plan=WHOLE, name=f"wide range n={n} k={k}")
+
+
+# The value-order epilogue's 32-bit form (bf16 rows of at most 2^16 columns):
+# both zeros, negative values, -inf and heavy ties, on one and two chunks.
+@pytest.mark.parametrize("n", [20000, 40000, 65536])
+def test_narrow_rank_signed_zeros_and_ties(n):
+    rng = np.random.Generator(np.random.PCG64(57 + n))
+    alpha = np.array([-0.0, 0.0, 0.5, -0.5, 1.0, -np.inf, 2.0, -3.0], dtype=np.float32)
+    f = alpha[rng.integers(0, len(alpha), size=(3, n))]
+    f[1] = rng.standard_normal(n).astype(np.float32) * np.float32(0.01)   # many values near zero
+    x = _bits(f, BF16)
+    for k in (5, 512, 2048, 3000):
+        check_case(x, BF16, n, k, 1, True, "int32", plan=WHOLE, name=f"narrow rank n={n} k={k}")
