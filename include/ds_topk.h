@@ -270,7 +270,7 @@ ds_status_t ds_read_ceiling(const void* x, ds_dtype_t dtype, int64_t batch, int6
  * of the top-k output (candidates: the entries with index >= 0, sorted by
  * value, larger first, as ds_topk returns them with sorted = 1):
  *   w_j = exp((v_j - v_max) / temperature) (if v_max is infinite: 1 where
- *   v_j == v_max, else 0); c_j = w_0 + ... + w_j; S = c at the last candidate;
+ *   v_j == v_max, else 0); c_j = w_0 + ... + w_j; S = the weights' total;
  *   K = min(1 + #{j : c_j < top_p * S}, number of candidates);
  *   token = indices[i][j*] with j* the first j < K such that
  *   c_j > u_i * c_{K-1}; its probability after the cut is w_j* / c_{K-1}.

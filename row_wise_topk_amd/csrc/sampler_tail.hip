@@ -10,7 +10,7 @@
 //   weights   w_j = exp((v_j - v_max) / temperature) over the candidates
 //             (index >= 0); if v_max is infinite, w_j = 1 where v_j == v_max,
 //             else 0; temperature <= 0 draws the first candidate (greedy);
-//   nucleus   c_j = w_0 + ... + w_j, S = c at the last candidate; keep the
+//   nucleus   c_j = w_0 + ... + w_j, S = the weights' total; keep the
 //             K = 1 + #{j : c_j < top_p * S} first candidates (at most all);
 //   draw      the first j < K with c_j > u * c_{K-1}, u the row's uniform
 //             (clamped to [0, 1]); its index is the token, w_j / c_{K-1} its
@@ -89,7 +89,7 @@ __global__ __launch_bounds__(kNT) void sampler_tail_kernel(TailArgs a) {
   __shared__ float s_max[kNW];
   __shared__ float s_wsum[kNW];
   __shared__ uint32_t s_cnt[4][kNW];
-  __shared__ float s_at[2];
+  __shared__ float s_at[1];
   const int row = static_cast<int>(blockIdx.x);
   const int t = static_cast<int>(threadIdx.x);
   const int w = t >> 6;
@@ -163,19 +163,18 @@ __global__ __launch_bounds__(kNT) void sampler_tail_kernel(TailArgs a) {
   if (lane == 0) excl = 0.0f;
   if (lane == 63) s_wsum[w] = incl;
   __syncthreads();
-  float off = 0.0f;
+  float off = 0.0f, total = 0.0f;
 #pragma unroll
-  for (int q = 0; q < kNW; ++q) off += q < w ? s_wsum[q] : 0.0f;
+  for (int q = 0; q < kNW; ++q) {
+    off += q < w ? s_wsum[q] : 0.0f;
+    total += s_wsum[q];
+  }
   off += excl;
 #pragma unroll
   for (int i = 0; i < kPer; ++i) c[i] = off + c[i];
 
-  // S: the prefix sum at the last candidate.
-#pragma unroll
-  for (int i = 0; i < kPer; ++i)
-    if (i < per && j0 + i == static_cast<int>(m) - 1) s_at[0] = c[i];
-  __syncthreads();
-  const float pS = a.top_p * s_at[0];
+  // S: the weights' total (the waves' sums in order; padding weighs 0).
+  const float pS = a.top_p * total;
   uint32_t below = 0;
 #pragma unroll
   for (int i = 0; i < kPer; ++i) below += (ix[i] >= 0 && c[i] < pS) ? 1u : 0u;
@@ -184,9 +183,9 @@ __global__ __launch_bounds__(kNT) void sampler_tail_kernel(TailArgs a) {
   // The draw: j* = #{j < K : c_j <= u * c_{K-1}}, at most K - 1.
 #pragma unroll
   for (int i = 0; i < kPer; ++i)
-    if (i < per && j0 + i == static_cast<int>(K) - 1) s_at[1] = c[i];
+    if (i < per && j0 + i == static_cast<int>(K) - 1) s_at[0] = c[i];
   __syncthreads();
-  const float CK = s_at[1];
+  const float CK = s_at[0];
   const float u = fminf(fmaxf(a.uniforms[row], 0.0f), 1.0f);
   const float target = u * CK;
   uint32_t le = 0;
